@@ -1,0 +1,626 @@
+/*
+ * CPU oracle for the dropless-MoE expert layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU path.
+ *
+ * What it computes (George Lin's Blog, MegaBlocks/FlexMoE post, section 1.2):
+ * the block-sparse formulation is a mathematically equivalent rewrite of the
+ * per-expert MLP, so the oracle is the plain definition: a loop over tokens
+ * that applies each chosen expert's two-layer MLP densely (first layer
+ * x @ W1_e, activation, second layer @ W2_e) and combines the k expert
+ * outputs with the gate weights.  Integer outputs (routing, permutation,
+ * topology) follow the steps of sections 1.3 and 1.4 of the same post in
+ * their order: route, group by expert, pad each group to a multiple of 128,
+ * then the hybrid BCSR-COO topology and its transpose index.
+ *
+ * Arithmetic: every sum is accumulated in fp64 in ascending index order and
+ * never reassociated.  Values are rounded to the storage precision at the
+ * points where the layer stores an intermediate (A, H, Yp, y, dYp, dH, dXp,
+ * dx, dW); ORC_F64 disables every rounding (used by the finite-difference
+ * and library cross-checks).
+ *
+ * Readings of points the pages leave open (each is listed with its reason in
+ * the design notes):
+ *   - top-k on raw logits, ties to the lower expert id, slots in rank order;
+ *   - gate = softmax over all E logits, optionally renormalised over the k
+ *     picks;
+ *   - stable order inside an expert's bin (ascending assignment id
+ *     a = t*k + j), bins in ascending expert id, empty experts get 0 rows,
+ *     pad rows are zero;
+ *   - exact erf GeLU; SwiGLU = silu(x W1) * (x W3);
+ *   - the block-diagonal matrix is the first layer's output [Tp x E*f].
+ *
+ * Parity pins: none of the pages prints a worked numeric example, so every
+ * function here is pinned by closed forms, invariants, library routines on
+ * special cases, brute force and finite differences in the not-gpu tests.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F64 0
+#define ORC_F32 1
+#define ORC_BF16 2
+
+#define ORC_ACT_GELU 0
+#define ORC_ACT_SWIGLU 1
+
+#define BLK 128
+
+/* ---------------------------------------------------------------- rounding */
+
+/* Round to bf16 (8 significant bits, fp32 exponent range) with ties to even.
+ * The quantum of a value in [2^(e-1), 2^e) is 2^(e-8); below the smallest
+ * normal (2^-126) it stays 2^-133. */
+static double rd_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    (void)frexp(fabs(v), &e);
+    int qexp = e - 8;
+    if (qexp < -133) qexp = -133;
+    double r = nearbyint(ldexp(fabs(v), -qexp));   /* default mode: ties to even */
+    r = ldexp(r, qexp);
+    if (r > 3.3895313892515355e38) r = INFINITY; /* beyond the largest bf16 */
+    return copysign(r, v);
+}
+
+static double rd(double v, int prec) {
+    switch (prec) {
+    case ORC_F32: return (double)(float)v;
+    case ORC_BF16: return rd_bf16(v);
+    default: return v;
+    }
+}
+
+double orc_round(double v, int prec) { return rd(v, prec); }
+
+/* ------------------------------------------------------------ activations */
+
+static double gelu(double h) { return 0.5 * h * (1.0 + erf(h / sqrt(2.0))); }
+
+static double gelu_grad(double h) {
+    return 0.5 * (1.0 + erf(h / sqrt(2.0))) + h * exp(-0.5 * h * h) / sqrt(2.0 * M_PI);
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+double orc_gelu(double h) { return gelu(h); }
+double orc_gelu_grad(double h) { return gelu_grad(h); }
+double orc_silu(double z) { return silu(z); }
+
+/* ---------------------------------------------------------------- threads */
+
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/*
+ * Gate network and router (section 1.4 of the MegaBlocks part; the gate and
+ * router roles of the FlexMoE section 2.2 component list).  For each token:
+ * pick the k experts with the largest logits (ties: lower id first), in rank
+ * order; gate = softmax probability over all E experts, renormalised over
+ * the k picks when renorm != 0.  Then count tokens per expert, pad each
+ * count up to a multiple of 128, lay the bins out in ascending expert order
+ * (exclusive scan), and give every assignment a = t*k + j the next free row
+ * of its expert's bin, visiting assignments in ascending a.
+ *
+ * row_src (length row_src_len >= Tp) receives the inverse map: the
+ * assignment that fills each row, or -1 for a pad row.
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_route(const float* logits, int64_t T, int E, int k, int renorm,
+              int32_t* expert_idx, float* gate, int32_t* counts, int32_t* bin_offsets,
+              int32_t* dest_row, int32_t* row_src, int64_t row_src_len) {
+    if (!logits || T < 0 || E < 1 || k < 1 || k > E) return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        /* selection: k passes of "largest not yet taken, lower id on ties" */
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int q = 0; q < j; ++q)
+                    if (expert_idx[t * k + q] == e) taken = 1;
+                if (taken) continue;
+                if (best < 0 || l[e] > l[best]) best = e;
+            }
+            expert_idx[t * k + j] = best;
+        }
+        /* softmax over all experts in fp64 (max-subtracted) */
+        double mx = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > mx) mx = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) z += exp((double)l[e] - mx);
+        double p[64];
+        double* pk = k <= 64 ? p : (double*)malloc(sizeof(double) * k);
+        double psum = 0.0;
+        for (int j = 0; j < k; ++j) {
+            pk[j] = exp((double)l[expert_idx[t * k + j]] - mx) / z;
+            psum += pk[j];
+        }
+        for (int j = 0; j < k; ++j)
+            gate[t * k + j] = (float)(renorm ? pk[j] / psum : pk[j]);
+        if (pk != p) free(pk);
+    }
+    /* histogram */
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < T * k; ++a) counts[expert_idx[a]]++;
+    /* padded bins, ascending expert id */
+    bin_offsets[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t padded = ((int64_t)counts[e] + BLK - 1) / BLK * BLK;
+        bin_offsets[e + 1] = (int32_t)(bin_offsets[e] + padded);
+    }
+    /* stable placement */
+    int64_t Tp = bin_offsets[E];
+    if (row_src && row_src_len < Tp) return -1;
+    int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (row_src)
+        for (int64_t r = 0; r < Tp; ++r) row_src[r] = -1;
+    for (int64_t a = 0; a < T * k; ++a) {
+        int e = expert_idx[a];
+        int32_t row = bin_offsets[e] + fill[e]++;
+        dest_row[a] = row;
+        if (row_src) row_src[row] = (int32_t)a;
+    }
+    free(fill);
+    return 0;
+}
+
+/*
+ * Fused permutation + padding (section 1.3 "block size" and section 1.4):
+ * row dest_row[a] of xp receives token t = a / k's row of x (times scale[a]
+ * when scale is given, rounded to prec); rows that no assignment fills are
+ * pad rows and are zero.  xp has Tp rows of d values.
+ */
+int orc_permute_pad(const float* x, int64_t T, int d, int k, const int32_t* dest_row,
+                    const float* scale, int prec, int64_t Tp, double* xp) {
+    if (!x || !dest_row || !xp || d < 1 || k < 1) return -1;
+    memset(xp, 0, sizeof(double) * (size_t)Tp * (size_t)d);
+    for (int64_t a = 0; a < T * k; ++a) {
+        int64_t t = a / k;
+        int64_t row = dest_row[a];
+        if (row < 0 || row >= Tp) return -1;
+        for (int i = 0; i < d; ++i) {
+            double v = x[t * d + i];
+            if (scale) v = (double)scale[a] * v;
+            xp[row * d + i] = rd(v, prec);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- topology */
+
+/*
+ * Hybrid BCSR-COO topology of the first layer's output, a [Tp x E*f] matrix
+ * of 128x128 blocks, and its transpose index (section 1.3, "hybrid BCSR-COO
+ * format" and "transpose indices").  Block (r, c) is nonzero when row block r
+ * lies in expert e's bin and column block c lies in expert e's f columns.
+ *
+ * Built the generic way: scan the block grid row by row (BCSR: row_ptr,
+ * col_idx; the COO half: row_idx per block), then a stable counting sort of
+ * the blocks by column gives col_ptr and trans_idx (BCSR block ids listed in
+ * column order, ascending block id inside a column).
+ * Output sizes: row_ptr [Tp/128 + 1], col_ptr [E*F + 1], the others [nnz].
+ * Returns nnz, or -1 on bad arguments.
+ */
+int64_t orc_topology(const int32_t* bin_offsets, int E, int F, int32_t* row_ptr, int32_t* col_idx,
+                     int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx) {
+    if (!bin_offsets || E < 1 || F < 1) return -1;
+    int64_t Tp = bin_offsets[E];
+    if (Tp % BLK) return -1;
+    int64_t R = Tp / BLK, C = (int64_t)E * F;
+    int64_t nnz = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        row_ptr[r] = (int32_t)nnz;
+        int owner = -1;
+        for (int e = 0; e < E; ++e)
+            if (r * BLK >= bin_offsets[e] && r * BLK < bin_offsets[e + 1]) owner = e;
+        for (int64_t c = 0; c < C; ++c) {
+            if (c / F == owner) {
+                col_idx[nnz] = (int32_t)c;
+                row_idx[nnz] = (int32_t)r;
+                ++nnz;
+            }
+        }
+    }
+    row_ptr[R] = (int32_t)nnz;
+    /* transpose: counting sort by column, stable in block id */
+    int64_t* cnt = (int64_t*)calloc((size_t)C + 1, sizeof(int64_t));
+    for (int64_t b = 0; b < nnz; ++b) cnt[col_idx[b] + 1]++;
+    for (int64_t c = 0; c < C; ++c) cnt[c + 1] += cnt[c];
+    for (int64_t c = 0; c <= C; ++c) col_ptr[c] = (int32_t)cnt[c];
+    for (int64_t b = 0; b < nnz; ++b) trans_idx[cnt[col_idx[b]]++] = (int32_t)b;
+    free(cnt);
+    return nnz;
+}
+
+/* ------------------------------------------------------------ float layer */
+
+typedef struct {
+    int64_t T;
+    int d, E, f, k;
+    int act;      /* ORC_ACT_GELU or ORC_ACT_SWIGLU */
+    int prec;     /* storage precision of A, H, dYp, dH, y, dx, dW */
+    int prec_yp;  /* storage precision of Yp and dXp */
+    const float* x;   /* [T, d] */
+    const float* W1;  /* [d, E*f]: expert e owns columns e*f .. e*f+f-1 */
+    const float* W3;  /* [d, E*f] (swiglu only) */
+    const float* W2;  /* [E*f, d]: expert e owns rows e*f .. e*f+f-1 */
+    const float* dy;  /* [T, d] (backward only) */
+    const int32_t* expert_idx; /* [T*k] */
+    const float* gate;         /* [T*k] */
+} orc_layer;
+
+static int layer_ok(const orc_layer* L) {
+    return L && L->x && L->W1 && L->W2 && L->expert_idx && L->gate && L->d > 0 && L->E > 0 &&
+           L->f > 0 && L->k > 0 && (L->act != ORC_ACT_SWIGLU || L->W3);
+}
+
+/* First layer and activation for one assignment (section 1.2: layer one,
+ * activation):  h[n] = sum_i x[t,i] W1[i, e*f+n];  A = act(h).
+ * h_out gets the unrounded pre-activation (fp64), H_out its stored copy. */
+static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, double* H_out,
+                        double* A_out) {
+    const int64_t t = a / L->k;
+    const int e = L->expert_idx[a];
+    const int64_t ldw = (int64_t)L->E * L->f;
+    const float* xr = L->x + t * L->d;
+    for (int n = 0; n < L->f; ++n) h[n] = 0.0;
+    if (hu)
+        for (int n = 0; n < L->f; ++n) hu[n] = 0.0;
+    /* i outer keeps every h[n] summed in ascending i */
+    for (int i = 0; i < L->d; ++i) {
+        const double xi = xr[i];
+        const float* w = L->W1 + i * ldw + (int64_t)e * L->f;
+        for (int n = 0; n < L->f; ++n) h[n] += xi * (double)w[n];
+        if (hu) {
+            const float* w3 = L->W3 + i * ldw + (int64_t)e * L->f;
+            for (int n = 0; n < L->f; ++n) hu[n] += xi * (double)w3[n];
+        }
+    }
+    for (int n = 0; n < L->f; ++n) {
+        double av;
+        if (L->act == ORC_ACT_SWIGLU)
+            av = silu(h[n]) * hu[n];
+        else
+            av = gelu(h[n]);
+        if (A_out) A_out[n] = rd(av, L->prec);
+        if (H_out) H_out[n] = rd(h[n], L->prec);
+    }
+}
+
+/* Second layer for one assignment: Yp[m] = sum_n A[n] W2[e*f+n, m]. */
+static void second_layer(const orc_layer* L, int64_t a, const double* A, double* acc, double* Yp) {
+    const int e = L->expert_idx[a];
+    for (int m = 0; m < L->d; ++m) acc[m] = 0.0;
+    for (int n = 0; n < L->f; ++n) {
+        const double an = A[n];
+        const float* w = L->W2 + ((int64_t)e * L->f + n) * L->d;
+        for (int m = 0; m < L->d; ++m) acc[m] += an * (double)w[m];
+    }
+    for (int m = 0; m < L->d; ++m) Yp[m] = rd(acc[m], L->prec_yp);
+}
+
+/*
+ * Per-assignment forward: H (stored pre-activation, gelu only; may be NULL),
+ * A (stored activation) [n, f], Yp (expert output) [n, d] for the listed
+ * assignments.
+ */
+int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, double* H,
+                       double* A, double* Yp) {
+    if (!layer_ok(L) || !assigns || !A || !Yp) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * L->f);
+        double* hu = L->act == ORC_ACT_SWIGLU ? (double*)malloc(sizeof(double) * L->f) : NULL;
+        double* acc = (double*)malloc(sizeof(double) * L->d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < n; ++q) {
+            int64_t a = assigns[q];
+            if (a < 0 || a >= L->T * L->k) {
+                bad = 1;
+                continue;
+            }
+            first_layer(L, a, h, hu, H ? H + q * L->f : NULL, A + q * L->f);
+            second_layer(L, a, A + q * L->f, acc, Yp + q * L->d);
+        }
+        free(h);
+        free(hu);
+        free(acc);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Layer output for the listed tokens: y[t, m] = sum_j gate[t,j] Yp_{t,j}[m]
+ * (j ascending), rounded once.  This is the per-token loop that applies each
+ * chosen expert's MLP densely and combines the results with the gates.
+ */
+int orc_forward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, double* y) {
+    if (!layer_ok(L) || !tokens || !y) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * L->f);
+        double* hu = L->act == ORC_ACT_SWIGLU ? (double*)malloc(sizeof(double) * L->f) : NULL;
+        double* A = (double*)malloc(sizeof(double) * L->f);
+        double* acc = (double*)malloc(sizeof(double) * L->d);
+        double* yp = (double*)malloc(sizeof(double) * L->d);
+        double* sum = (double*)malloc(sizeof(double) * L->d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < n; ++q) {
+            int64_t t = tokens[q];
+            if (t < 0 || t >= L->T) {
+                bad = 1;
+                continue;
+            }
+            for (int m = 0; m < L->d; ++m) sum[m] = 0.0;
+            for (int j = 0; j < L->k; ++j) {
+                int64_t a = t * L->k + j;
+                first_layer(L, a, h, hu, NULL, A);
+                second_layer(L, a, A, acc, yp);
+                const double g = L->gate[a];
+                for (int m = 0; m < L->d; ++m) sum[m] += g * yp[m];
+            }
+            for (int m = 0; m < L->d; ++m) y[q * L->d + m] = rd(sum[m], L->prec);
+        }
+        free(h);
+        free(hu);
+        free(A);
+        free(acc);
+        free(yp);
+        free(sum);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------- backward */
+
+/*
+ * Backward data path of one assignment (plain calculus on section 1.2's
+ * SDD -> activation -> DSD; GeLU experts only):
+ *   dYp[m] = rd(gate * dy[t, m])
+ *   da[n]  = sum_m dYp[m] W2[e*f+n, m]
+ *   dH[n]  = rd(da[n] * gelu'(H[n]))      H = stored pre-activation
+ *   dXp[i] = rd_yp(sum_n dH[n] W1[i, e*f+n])
+ */
+static void assign_backward(const orc_layer* L, int64_t a, double* h, double* H, double* dYp,
+                            double* dH, double* dXp) {
+    const int64_t t = a / L->k;
+    const int e = L->expert_idx[a];
+    const int64_t ldw = (int64_t)L->E * L->f;
+    const double g = L->gate[a];
+    first_layer(L, a, h, NULL, H, NULL);
+    for (int m = 0; m < L->d; ++m) dYp[m] = rd(g * (double)L->dy[t * L->d + m], L->prec);
+    for (int n = 0; n < L->f; ++n) {
+        const float* w = L->W2 + ((int64_t)e * L->f + n) * L->d;
+        double da = 0.0;
+        for (int m = 0; m < L->d; ++m) da += dYp[m] * (double)w[m];
+        dH[n] = rd(da * gelu_grad(H[n]), L->prec);
+    }
+    for (int i = 0; i < L->d; ++i) {
+        const float* w = L->W1 + i * ldw + (int64_t)e * L->f;
+        double s = 0.0;
+        for (int n = 0; n < L->f; ++n) s += dH[n] * (double)w[n];
+        dXp[i] = rd(s, L->prec_yp);
+    }
+}
+
+/* Per-assignment backward rows: dYp [n,d], dH [n,f], dXp [n,d]. */
+int orc_assign_backward(const orc_layer* L, const int64_t* assigns, int64_t n, double* dYp,
+                        double* dH, double* dXp) {
+    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !assigns) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * L->f);
+        double* H = (double*)malloc(sizeof(double) * L->f);
+        double* ldyp = (double*)malloc(sizeof(double) * L->d);
+        double* ldh = (double*)malloc(sizeof(double) * L->f);
+        double* ldxp = (double*)malloc(sizeof(double) * L->d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < n; ++q) {
+            int64_t a = assigns[q];
+            if (a < 0 || a >= L->T * L->k) {
+                bad = 1;
+                continue;
+            }
+            assign_backward(L, a, h, H, ldyp, ldh, ldxp);
+            if (dYp) memcpy(dYp + q * L->d, ldyp, sizeof(double) * L->d);
+            if (dH) memcpy(dH + q * L->f, ldh, sizeof(double) * L->f);
+            if (dXp) memcpy(dXp + q * L->d, ldxp, sizeof(double) * L->d);
+        }
+        free(h);
+        free(H);
+        free(ldyp);
+        free(ldh);
+        free(ldxp);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Input gradient for the listed tokens: dx[t, i] = rd(sum_j dXp_{t,j}[i]). */
+int orc_backward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, double* dx) {
+    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !tokens || !dx) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * L->f);
+        double* H = (double*)malloc(sizeof(double) * L->f);
+        double* dYp = (double*)malloc(sizeof(double) * L->d);
+        double* dH = (double*)malloc(sizeof(double) * L->f);
+        double* dXp = (double*)malloc(sizeof(double) * L->d);
+        double* sum = (double*)malloc(sizeof(double) * L->d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < n; ++q) {
+            int64_t t = tokens[q];
+            if (t < 0 || t >= L->T) {
+                bad = 1;
+                continue;
+            }
+            for (int i = 0; i < L->d; ++i) sum[i] = 0.0;
+            for (int j = 0; j < L->k; ++j) {
+                assign_backward(L, t * L->k + j, h, H, dYp, dH, dXp);
+                for (int i = 0; i < L->d; ++i) sum[i] += dXp[i];
+            }
+            for (int i = 0; i < L->d; ++i) dx[q * L->d + i] = rd(sum[i], L->prec);
+        }
+        free(h);
+        free(H);
+        free(dYp);
+        free(dH);
+        free(dXp);
+        free(sum);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Assignments of expert e in ascending order; returns their count. */
+static int64_t expert_assignments(const orc_layer* L, int e, int64_t* out) {
+    int64_t c = 0;
+    for (int64_t a = 0; a < L->T * L->k; ++a)
+        if (L->expert_idx[a] == e) out[c++] = a;
+    return c;
+}
+
+/*
+ * Weight gradient of the second layer (section 1.3 "transpose indices": the
+ * weight gradient is the product of the transposed sparse activation with
+ * the dense output gradient):
+ *   dW2[e*f+n, m] = rd(sum over assignments a of expert e, ascending,
+ *                      of A_a[n] * dYp_a[m])
+ * for every (rows[p], cols[q]) pair; out is [nr, nc].  Experts with no
+ * assignment give exact zeros.
+ */
+int orc_dW2_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int64_t* cols,
+                  int64_t nc, double* out) {
+    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !rows || !cols || !out) return -1;
+    const int64_t ldw = (int64_t)L->E * L->f;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t* as = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L->T * L->k));
+        double* an = (double*)malloc(sizeof(double) * (size_t)(L->T * L->k));
+        double* wcol = (double*)malloc(sizeof(double) * L->d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < nr; ++p) {
+            int64_t row = rows[p];
+            if (row < 0 || row >= ldw) {
+                bad = 1;
+                continue;
+            }
+            int e = (int)(row / L->f);
+            int64_t c = expert_assignments(L, e, as);
+            for (int i = 0; i < L->d; ++i) wcol[i] = L->W1[i * ldw + row];
+            /* A_a[n] for every assignment of the expert */
+            for (int64_t q = 0; q < c; ++q) {
+                const float* xr = L->x + (as[q] / L->k) * L->d;
+                double h = 0.0;
+                for (int i = 0; i < L->d; ++i) h += (double)xr[i] * wcol[i];
+                an[q] = rd(gelu(h), L->prec);
+            }
+            for (int64_t s = 0; s < nc; ++s) {
+                int64_t m = cols[s];
+                if (m < 0 || m >= L->d) {
+                    bad = 1;
+                    continue;
+                }
+                double acc = 0.0;
+                for (int64_t q = 0; q < c; ++q) {
+                    int64_t a = as[q];
+                    double dyp = rd((double)L->gate[a] * (double)L->dy[(a / L->k) * L->d + m],
+                                    L->prec);
+                    acc += an[q] * dyp;
+                }
+                out[p * nc + s] = rd(acc, L->prec);
+            }
+        }
+        free(as);
+        free(an);
+        free(wcol);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Weight gradient of the first layer:
+ *   dW1[i, e*f+n] = rd(sum over assignments a of expert e, ascending,
+ *                      of x[t_a, i] * dH_a[n])
+ * for every (rows[p] = i, cols[q] = e*f+n) pair; out is [nr, nc].
+ */
+int orc_dW1_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int64_t* cols,
+                  int64_t nc, double* out) {
+    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !rows || !cols || !out) return -1;
+    const int64_t ldw = (int64_t)L->E * L->f;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t* as = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L->T * L->k));
+        double* dh = (double*)malloc(sizeof(double) * (size_t)(L->T * L->k));
+        double* wcol = (double*)malloc(sizeof(double) * L->d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t s = 0; s < nc; ++s) {
+            int64_t col = cols[s];
+            if (col < 0 || col >= ldw) {
+                bad = 1;
+                continue;
+            }
+            int e = (int)(col / L->f);
+            int64_t c = expert_assignments(L, e, as);
+            for (int i = 0; i < L->d; ++i) wcol[i] = L->W1[i * ldw + col];
+            const float* w2 = L->W2 + col * L->d;
+            for (int64_t q = 0; q < c; ++q) {
+                int64_t a = as[q];
+                const int64_t t = a / L->k;
+                const float* xr = L->x + t * L->d;
+                double h = 0.0;
+                for (int i = 0; i < L->d; ++i) h += (double)xr[i] * wcol[i];
+                double da = 0.0;
+                for (int m = 0; m < L->d; ++m) {
+                    double dyp = rd((double)L->gate[a] * (double)L->dy[t * L->d + m], L->prec);
+                    da += dyp * (double)w2[m];
+                }
+                dh[q] = rd(da * gelu_grad(rd(h, L->prec)), L->prec);
+            }
+            for (int64_t p = 0; p < nr; ++p) {
+                int64_t i = rows[p];
+                if (i < 0 || i >= L->d) {
+                    bad = 1;
+                    continue;
+                }
+                double acc = 0.0;
+                for (int64_t q = 0; q < c; ++q)
+                    acc += (double)L->x[(as[q] / L->k) * L->d + i] * dh[q];
+                out[p * nc + s] = rd(acc, L->prec);
+            }
+        }
+        free(as);
+        free(dh);
+        free(wcol);
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,271 @@
+"""ctypes wrapper around the C oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()``
+and the benchmark's ``cpu_baseline`` leg, never by the product path.  It does
+not import the GPU package.  Inputs are numpy arrays holding the exact values
+of the stored inputs (bf16 inputs widened to fp32); float outputs come back as
+fp64 arrays holding values already rounded to the requested storage precision.
+
+See ``oracle.c`` for what each function computes and which passage of the
+pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+SRC_PATH = os.path.join(HERE, "oracle.c")
+
+PREC = {"f64": 0, "f32": 1, "bf16": 2}
+ACT = {"gelu": 0, "swiglu": 1}
+
+_i64p = C.POINTER(C.c_int64)
+_i32p = C.POINTER(C.c_int32)
+_f32p = C.POINTER(C.c_float)
+_f64p = C.POINTER(C.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP, no FP contraction)."""
+    if not force and os.path.exists(LIB_PATH) and \
+            os.path.getmtime(LIB_PATH) >= os.path.getmtime(SRC_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", SRC_PATH, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class _Layer(C.Structure):
+    _fields_ = [
+        ("T", C.c_int64), ("d", C.c_int), ("E", C.c_int), ("f", C.c_int), ("k", C.c_int),
+        ("act", C.c_int), ("prec", C.c_int), ("prec_yp", C.c_int),
+        ("x", _f32p), ("W1", _f32p), ("W3", _f32p), ("W2", _f32p), ("dy", _f32p),
+        ("expert_idx", _i32p), ("gate", _f32p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = C.CDLL(LIB_PATH)
+        L.orc_round.restype = C.c_double
+        L.orc_round.argtypes = [C.c_double, C.c_int]
+        for name in ("orc_gelu", "orc_gelu_grad", "orc_silu"):
+            getattr(L, name).restype = C.c_double
+            getattr(L, name).argtypes = [C.c_double]
+        L.orc_set_threads.argtypes = [C.c_int]
+        L.orc_get_threads.restype = C.c_int
+        L.orc_route.restype = C.c_int
+        L.orc_route.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, C.c_int, _i32p, _f32p, _i32p,
+                                _i32p, _i32p, _i32p, C.c_int64]
+        L.orc_permute_pad.restype = C.c_int
+        L.orc_permute_pad.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, _i32p, _f32p, C.c_int,
+                                      C.c_int64, _f64p]
+        L.orc_topology.restype = C.c_int64
+        L.orc_topology.argtypes = [_i32p, C.c_int, C.c_int, _i32p, _i32p, _i32p, _i32p, _i32p]
+        lp = C.POINTER(_Layer)
+        L.orc_assign_forward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p]
+        L.orc_forward_tokens.argtypes = [lp, _i64p, C.c_int64, _f64p]
+        L.orc_assign_backward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p]
+        L.orc_backward_tokens.argtypes = [lp, _i64p, C.c_int64, _f64p]
+        L.orc_dW2_block.argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
+        L.orc_dW1_block.argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
+        for n in ("orc_assign_forward", "orc_forward_tokens", "orc_assign_backward",
+                  "orc_backward_tokens", "orc_dW2_block", "orc_dW1_block"):
+            getattr(L, n).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t) if a is not None else None
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
+
+
+def rd(v: float, prec: str) -> float:
+    return lib().orc_round(float(v), PREC[prec])
+
+
+def gelu(h: float) -> float:
+    return lib().orc_gelu(float(h))
+
+
+def gelu_grad(h: float) -> float:
+    return lib().orc_gelu_grad(float(h))
+
+
+def silu(z: float) -> float:
+    return lib().orc_silu(float(z))
+
+
+def route(logits: np.ndarray, k: int, renorm: bool = False) -> dict:
+    """Top-k routing, gates, histogram, padded bins, stable placement."""
+    logits = _f32(logits)
+    T, E = logits.shape
+    out = {
+        "expert_idx": np.zeros(T * k, np.int32),
+        "gate": np.zeros(T * k, np.float32),
+        "counts": np.zeros(E, np.int32),
+        "bin_offsets": np.zeros(E + 1, np.int32),
+        "dest_row": np.zeros(T * k, np.int32),
+    }
+    bound = T * k + 127 * min(E, T * k) + 128
+    row_src = np.zeros(bound, np.int32)
+    rc = lib().orc_route(_p(logits, _f32p), T, E, k, int(bool(renorm)),
+                         _p(out["expert_idx"], _i32p), _p(out["gate"], _f32p),
+                         _p(out["counts"], _i32p), _p(out["bin_offsets"], _i32p),
+                         _p(out["dest_row"], _i32p), _p(row_src, _i32p), bound)
+    if rc != 0:
+        raise ValueError("orc_route rejected its arguments")
+    out["row_src"] = row_src[: int(out["bin_offsets"][E])].copy()
+    return out
+
+
+def permute_pad(x: np.ndarray, k: int, dest_row: np.ndarray, Tp: int, scale=None,
+                prec: str = "bf16") -> np.ndarray:
+    """Expert-grouped, zero-padded copy of x: [Tp, d] float64."""
+    x = _f32(x)
+    T, d = x.shape
+    dest_row = np.ascontiguousarray(dest_row, np.int32)
+    xp = np.zeros((Tp, d), np.float64)
+    sc = _f32(scale)
+    rc = lib().orc_permute_pad(_p(x, _f32p), T, d, k, _p(dest_row, _i32p), _p(sc, _f32p),
+                               PREC[prec], Tp, _p(xp, _f64p))
+    if rc != 0:
+        raise ValueError("orc_permute_pad rejected its arguments")
+    return xp
+
+
+def topology(bin_offsets: np.ndarray, E: int, F: int) -> dict:
+    """Hybrid BCSR-COO topology and transpose index of the block-diagonal
+    first-layer output."""
+    bo = np.ascontiguousarray(bin_offsets, np.int32)
+    R = int(bo[E]) // 128
+    cap = R * F
+    row_ptr = np.zeros(R + 1, np.int32)
+    col_idx = np.zeros(cap, np.int32)
+    row_idx = np.zeros(cap, np.int32)
+    col_ptr = np.zeros(E * F + 1, np.int32)
+    trans_idx = np.zeros(cap, np.int32)
+    nnz = lib().orc_topology(_p(bo, _i32p), E, F, _p(row_ptr, _i32p), _p(col_idx, _i32p),
+                             _p(row_idx, _i32p), _p(col_ptr, _i32p), _p(trans_idx, _i32p))
+    if nnz < 0:
+        raise ValueError("orc_topology rejected its arguments")
+    return {"nnz": int(nnz), "row_ptr": row_ptr, "col_idx": col_idx[:nnz],
+            "row_idx": row_idx[:nnz], "col_ptr": col_ptr, "trans_idx": trans_idx[:nnz]}
+
+
+class Layer:
+    """Float oracle of one layer call.
+
+    ``prec`` is the storage precision of A, H, dYp, dH, y, dx and the weight
+    gradients; ``prec_yp`` that of Yp and dXp ("f64" disables rounding)."""
+
+    def __init__(self, x, W1, W2, expert_idx, gate, k, E, act="gelu", W3=None, dy=None,
+                 prec="bf16", prec_yp=None):
+        self.x = _f32(x)
+        self.W1 = _f32(W1)
+        self.W2 = _f32(W2)
+        self.W3 = _f32(W3)
+        self.dy = _f32(dy)
+        self.expert_idx = np.ascontiguousarray(expert_idx, np.int32)
+        self.gate = _f32(gate)
+        T, d = self.x.shape
+        Ef = self.W1.shape[1]
+        if Ef % E or self.W2.shape != (Ef, d) or self.W1.shape[0] != d:
+            raise ValueError("inconsistent layer shapes")
+        self.T, self.d, self.k, self.E, self.f = T, d, k, E, Ef // E
+        s = self._s = _Layer()
+        s.T, s.d, s.E, s.f, s.k = T, d, E, Ef // E, k
+        s.act = ACT[act]
+        s.prec = PREC[prec]
+        s.prec_yp = PREC[prec_yp or prec]
+        s.x = _p(self.x, _f32p)
+        s.W1 = _p(self.W1, _f32p)
+        s.W3 = _p(self.W3, _f32p)
+        s.W2 = _p(self.W2, _f32p)
+        s.dy = _p(self.dy, _f32p)
+        s.expert_idx = _p(self.expert_idx, _i32p)
+        s.gate = _p(self.gate, _f32p)
+
+    def _call(self, name, *args):
+        rc = getattr(lib(), name)(C.byref(self._s), *args)
+        if rc != 0:
+            raise ValueError(f"{name} rejected its arguments")
+
+    def assign_forward(self, assigns):
+        a = np.ascontiguousarray(assigns, np.int64)
+        n = len(a)
+        H = np.zeros((n, self.f))
+        A = np.zeros((n, self.f))
+        Yp = np.zeros((n, self.d))
+        self._call("orc_assign_forward", _p(a, _i64p), n, _p(H, _f64p), _p(A, _f64p),
+                   _p(Yp, _f64p))
+        return H, A, Yp
+
+    def forward_tokens(self, tokens):
+        t = np.ascontiguousarray(tokens, np.int64)
+        y = np.zeros((len(t), self.d))
+        self._call("orc_forward_tokens", _p(t, _i64p), len(t), _p(y, _f64p))
+        return y
+
+    def assign_backward(self, assigns):
+        a = np.ascontiguousarray(assigns, np.int64)
+        n = len(a)
+        dYp = np.zeros((n, self.d))
+        dH = np.zeros((n, self.f))
+        dXp = np.zeros((n, self.d))
+        self._call("orc_assign_backward", _p(a, _i64p), n, _p(dYp, _f64p), _p(dH, _f64p),
+                   _p(dXp, _f64p))
+        return dYp, dH, dXp
+
+    def backward_tokens(self, tokens):
+        t = np.ascontiguousarray(tokens, np.int64)
+        dx = np.zeros((len(t), self.d))
+        self._call("orc_backward_tokens", _p(t, _i64p), len(t), _p(dx, _f64p))
+        return dx
+
+    def dW2_block(self, rows, cols):
+        r = np.ascontiguousarray(rows, np.int64)
+        c = np.ascontiguousarray(cols, np.int64)
+        out = np.zeros((len(r), len(c)))
+        self._call("orc_dW2_block", _p(r, _i64p), len(r), _p(c, _i64p), len(c), _p(out, _f64p))
+        return out
+
+    def dW1_block(self, rows, cols):
+        r = np.ascontiguousarray(rows, np.int64)
+        c = np.ascontiguousarray(cols, np.int64)
+        out = np.zeros((len(r), len(c)))
+        self._call("orc_dW1_block", _p(r, _i64p), len(r), _p(c, _i64p), len(c), _p(out, _f64p))
+        return out
+
+
+def make_layer(x, W1, W2, route_out, k, E, act="gelu", W3=None, dy=None, prec="bf16",
+               prec_yp=None) -> Layer:
+    """Convenience: a :class:`Layer` over the oracle's own routing."""
+    return Layer(x, W1, W2, route_out["expert_idx"], route_out["gate"], k, E, act=act, W3=W3,
+                 dy=dy, prec=prec, prec_yp=prec_yp)

@@ -1,0 +1,194 @@
+"""Pins of the oracle's integer outputs: routing, bins, placement, topology.
+
+Each check is independent of the oracle's own code: hand-worked fixtures
+(tests/golden), brute force with Python's sort, closed forms of the
+block-diagonal topology, and invariants stated by the pages (every token
+appears k times, bins are multiples of 128 with at most 127 pad rows,
+one row index per block, the transpose index lists the same block set).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from block_sparse_gemm_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def brute_route(logits, k):
+    """Top-k by sorting (value descending, id ascending) with Python's sort."""
+    T, E = logits.shape
+    sel = []
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))
+        sel.append(order[:k])
+    return np.array(sel, dtype=np.int32).reshape(-1)
+
+
+def check_placement(r, T, E, k):
+    ei, dest, counts, bo = r["expert_idx"], r["dest_row"], r["counts"], r["bin_offsets"]
+    # histogram
+    assert np.array_equal(counts, np.bincount(ei, minlength=E))
+    # padded bins: multiples of 128, 0..127 pad rows, empty expert -> 0 rows
+    P = np.diff(bo)
+    assert bo[0] == 0
+    assert np.all(P % 128 == 0)
+    assert np.all((P - counts >= 0) & (P - counts <= 127))
+    assert np.all((P == 0) == (counts == 0))
+    # stable placement == numpy stable argsort by expert id
+    order = np.argsort(ei, kind="stable")
+    want = np.empty(T * k, np.int64)
+    start = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    for pos, a in enumerate(order):
+        e = ei[a]
+        want[a] = bo[e] + (pos - start[e])
+    assert np.array_equal(dest, want)
+    # inverse map: row_src o dest_row = id; pad rows are -1; each token k times
+    rs = r["row_src"]
+    assert len(rs) == bo[E]
+    assert np.array_equal(rs[dest], np.arange(T * k))
+    assert np.sum(rs == -1) == bo[E] - T * k
+    tok = rs[rs >= 0] // k
+    assert np.array_equal(np.bincount(tok, minlength=T), np.full(T, k))
+
+
+def test_route_golden(orc):
+    g = json.load(open(os.path.join(GOLD, "route_small.json")))
+    logits = np.array(g["logits"], np.float32)
+    r = orc.route(logits, g["k"])
+    for key in ("expert_idx", "counts", "bin_offsets", "dest_row"):
+        assert r[key].tolist() == g[key], key
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(1, 1, 1, 0), (7, 3, 2, 1), (300, 8, 2, 2),
+                                        (513, 64, 1, 3), (200, 5, 5, 4), (129, 16, 3, 5)])
+def test_route_brute_force(orc, T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    # integer-valued logits force many ties
+    logits = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+    r = orc.route(logits, k)
+    assert np.array_equal(r["expert_idx"], brute_route(logits, k))
+    check_placement(r, T, E, k)
+
+
+def test_gate_closed_forms(orc):
+    rng = np.random.default_rng(7)
+    T, E = 50, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    # k = E: the gates are the whole softmax: they sum to 1 and their ratios
+    # are exp(l_i - l_j)
+    r = orc.route(logits, E)
+    g = r["gate"].reshape(T, E).astype(np.float64)
+    ei = r["expert_idx"].reshape(T, E)
+    assert np.allclose(g.sum(1), 1.0, rtol=0, atol=1e-6)
+    for t in range(T):
+        for j in range(1, E):
+            want = math.exp(float(logits[t, ei[t, j]]) - float(logits[t, ei[t, 0]]))
+            assert abs(g[t, j] / g[t, 0] - want) <= 1e-6 * want
+    # renormalised top-2 sums to 1 and keeps the ratio
+    r2 = orc.route(logits, 2, renorm=True)
+    g2 = r2["gate"].reshape(T, 2).astype(np.float64)
+    assert np.allclose(g2.sum(1), 1.0, atol=1e-6)
+    e2 = r2["expert_idx"].reshape(T, 2)
+    ratio = np.exp(logits[np.arange(T), e2[:, 1]].astype(np.float64) -
+                   logits[np.arange(T), e2[:, 0]])
+    assert np.allclose(g2[:, 1] / g2[:, 0], ratio, rtol=1e-6)
+    # equal logits: every gate is 1/E
+    r3 = orc.route(np.zeros((3, 4), np.float32), 2)
+    assert np.allclose(r3["gate"], 0.25, atol=1e-7)
+    # one expert: gate 1
+    r4 = orc.route(rng.standard_normal((5, 1)).astype(np.float32), 1)
+    assert np.all(r4["gate"] == 1.0) and np.all(r4["expert_idx"] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "moe_xs", "moe_small", "skew"])
+def test_route_workloads(orc, name):
+    cfg = synth.CONFIGS[name]
+    logits = synth.make_logits(cfg, np.random.default_rng(0))
+    r = orc.route(logits, cfg.k, cfg.renorm)
+    if cfg.T * cfg.E <= 2_000_000:
+        assert np.array_equal(r["expert_idx"], brute_route(logits, cfg.k))
+    check_placement(r, cfg.T, cfg.E, cfg.k)
+    if name == "skew":
+        counts = np.sort(r["counts"])[::-1]
+        share = counts[:10].sum() / counts.sum()
+        # the recipe targets the ~75% hot share quoted for GPT-MoE
+        assert 0.74 <= share <= 0.76, share
+        assert counts[-1] > 0 and np.sum(counts < 128) >= 6
+
+
+def closed_form_topology(bo, E, F):
+    """The block-diagonal MoE topology written out directly."""
+    R_e = np.diff(bo) // 128
+    s_e = bo[:-1] // 128
+    R = int(bo[E]) // 128
+    owner = np.repeat(np.arange(E), R_e)
+    row_ptr = np.arange(R + 1) * F
+    col_idx = (owner[:, None] * F + np.arange(F)[None, :]).reshape(-1)
+    row_idx = np.repeat(np.arange(R), F)
+    col_ptr = np.zeros(E * F + 1, np.int64)
+    trans = []
+    for e in range(E):
+        for j in range(F):
+            c = e * F + j
+            col_ptr[c] = s_e[e] * F + j * R_e[e]
+            for i in range(R_e[e]):
+                trans.append((s_e[e] + i) * F + j)
+    col_ptr[E * F] = R * F
+    return row_ptr, col_idx, row_idx, col_ptr, np.array(trans, np.int64)
+
+
+def test_topology_golden(orc):
+    g = json.load(open(os.path.join(GOLD, "topology_small.json")))
+    t = orc.topology(np.array(g["bin_offsets"], np.int32), g["E"], g["F"])
+    for key in ("row_ptr", "col_idx", "row_idx", "col_ptr", "trans_idx"):
+        assert t[key].tolist() == g[key], key
+
+
+@pytest.mark.parametrize("counts,F", [([3, 4, 3], 2), ([0, 300, 0, 129, 1], 3), ([128], 1),
+                                      ([0, 0, 5], 4), ([1000, 0, 256, 17, 128, 129], 5)])
+def test_topology_closed_form_and_invariants(orc, counts, F):
+    E = len(counts)
+    P = [(c + 127) // 128 * 128 for c in counts]
+    bo = np.concatenate([[0], np.cumsum(P)]).astype(np.int32)
+    t = orc.topology(bo, E, F)
+    cf = closed_form_topology(bo, E, F)
+    for key, want in zip(("row_ptr", "col_idx", "row_idx", "col_ptr", "trans_idx"), cf):
+        assert np.array_equal(t[key], want), key
+    nnz = t["nnz"]
+    assert nnz == (bo[E] // 128) * F
+    # one materialised row index per block, consistent with the row pointer
+    assert len(t["row_idx"]) == nnz
+    for r in range(len(t["row_ptr"]) - 1):
+        assert np.all(t["row_idx"][t["row_ptr"][r]:t["row_ptr"][r + 1]] == r)
+    # the transpose index lists exactly the same blocks, (r, c) -> (c, r),
+    # in column order with ascending row inside a column
+    tr = t["trans_idx"]
+    assert sorted(tr.tolist()) == list(range(nnz))
+    keys = [(t["col_idx"][b], t["row_idx"][b]) for b in tr]
+    assert keys == sorted(keys)
+    for c in range(E * F):
+        blk = tr[t["col_ptr"][c]:t["col_ptr"][c + 1]]
+        assert np.all(t["col_idx"][blk] == c)
+
+
+def test_permute_pad_invariants(orc):
+    rng = np.random.default_rng(3)
+    T, E, k, d = 300, 5, 2, 16
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = orc.route(logits, k)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    Tp = int(r["bin_offsets"][E])
+    xp = orc.permute_pad(x, k, r["dest_row"], Tp, prec="f32")
+    rs = r["row_src"]
+    # pad rows are exactly zero; every other row is its source token's row
+    assert np.all(xp[rs < 0] == 0)
+    assert np.array_equal(xp[rs >= 0], x[rs[rs >= 0] // k].astype(np.float64))
+    # scaled variant (backward dy * gate): exact product, rounded once
+    sc = r["gate"]
+    xps = orc.permute_pad(x, k, r["dest_row"], Tp, scale=sc, prec="f64")
+    a = rs[rs >= 0]
+    assert np.array_equal(xps[rs >= 0], x[a // k].astype(np.float64) * sc[a, None].astype(np.float64))
