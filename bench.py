@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = one pass of the whole dropless-MoE hot path.
+
+Workload (default): the MoE-Small-shaped layer, T = 32768 tokens (32 x 1024),
+d = 768, E = 64 experts, f = 3072 per expert, top-1, GeLU, bf16 with fp32
+accumulation, per-expert logit bias N(0, 0.5); forward + backward:
+route, permute_pad, build_topology, SDD(+GeLU), DSD, unpermute_combine,
+then permute_pad(dy * gate), SDD(GeLU'), DSD, unpermute_combine,
+DSTD (dW2), DSTD (dW1).  Inputs are seeded synthetic draws resident in HBM
+before the timed region.
+
+Prints ONE JSON line.  ``value`` is the useful TFLOP/s of the step
+(useful flops = 2 * T * k * d * f per product, 6 products; padded rows are
+excluded).  ``roofline`` reports the step's dominant kernel (largest time)
+against the bf16 dense MFMA peak, timed with HIP events on the stream the
+kernels run on.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_BF16 = 2500.0   # TFLOP/s, dense bf16 (MI355X published figure)
+MFMA_PEAK_F32 = 157.3
+HBM_PEAK = 8000.0         # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="moe_small")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def useful_flops(cfg):
+    per = 2.0 * cfg.T * cfg.k * cfg.d * cfg.f
+    products = 3 if cfg.act == "swiglu" else 2
+    if cfg.backward:
+        products += 4
+    return per, per * products
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """Time the oracle (as it stands) on a bounded token sample: forward
+    (2 products) and the input-gradient path (2 products) per token."""
+    from oracle import oracle as orc
+    from block_sparse_gemm_amd import synth
+    r = orc.route(inp["logits"], cfg.k, cfg.renorm)
+    O = orc.make_layer(inp["x"].values, inp["W1"].values, inp["W2"].values, r, cfg.k, cfg.E,
+                       act=cfg.act, W3=inp["W3"].values if "W3" in inp else None,
+                       dy=inp["dy"].values if "dy" in inp else None, prec=cfg.dtype,
+                       prec_yp=cfg.yp)
+    per_tok = 2.0 * cfg.k * cfg.d * cfg.f * (2 + (2 if cfg.backward else 0))
+
+    def run(n):
+        toks = synth.sample_tokens(cfg.T, n, seed=7)
+        t0 = time.perf_counter()
+        O.forward_tokens(toks)
+        if cfg.backward:
+            O.backward_tokens(toks)
+        return len(toks), time.perf_counter() - t0
+
+    n0, t0 = run(32)
+    n = int(min(cfg.T, max(32, n0 * target_s / max(t0, 1e-3))))
+    n, t = run(n)
+    return {"value": per_tok * n / t / 1e12, "unit": "TFLOP/s", "cores": orc.get_threads(),
+            "kind": "oracle",
+            "sample": f"{n} tokens of the {cfg.name} workload, forward + input-gradient path "
+                      f"(4 of the 6 products per token; weight gradients not sampled), "
+                      f"{t:.1f} s wall on {orc.get_threads()} OpenMP threads"}
+
+
+def traffic_for(kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, valid
+    only while the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        src = os.path.join(ROOT, "block_sparse_gemm_amd", "csrc", "gemm.hip")
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        ent = data.get(kernel_name)
+        if not ent or ent.get("source_sha") != h:
+            return None
+        return ent.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's "
+              "multi-GPU sharding is described in DESIGN.md and not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_sparse_gemm_amd import layer, synth
+
+    cfg = synth.CONFIGS[args.config]
+    print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg, 0)
+    s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
+                    cfg.backward)
+    L = layer.Layer(s)
+    up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
+    x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        L.step(x, logits, W1, W2, W3, dy)
+    torch.cuda.synchronize()
+
+    # per-call events on the current stream (the stream every call uses)
+    marks = []
+    L.mark = (lambda name, _m=marks: (_m.append((name, torch.cuda.Event(enable_timing=True))),
+                                      _m[-1][1].record()))
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.step(x, logits, W1, W2, W3, dy)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    L.mark = None
+
+    # per-kernel averages from consecutive events
+    per = {}
+    for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
+        if n1 == "start":
+            continue
+        per.setdefault(n1, []).append(e0.elapsed_time(e1))
+    kern = {k: float(np.mean(v)) for k, v in per.items()}
+    step_ms = wall * 1e3 / args.steps
+
+    per_product, total = useful_flops(cfg)
+    tflops = total / (step_ms * 1e-3) / 1e12
+    gemms = [k for k in kern if k.startswith(("sdd", "dsd", "dstd"))]
+    dom = max(gemms, key=lambda k: kern[k])
+    achieved = per_product / (kern[dom] * 1e-3) / 1e12
+    peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
+
+    kernels = {}
+    es = 2 if cfg.dtype == "bf16" else 4
+    Tp = int(L.bin_offsets[-1].item())
+    A_n = cfg.T * cfg.k
+    for k, ms in kern.items():
+        ent = {"ms": round(ms, 4)}
+        if k in gemms:
+            ent["useful_tflops"] = round(per_product / (ms * 1e-3) / 1e12, 1)
+            ent["pct_bf16_peak"] = round(100 * per_product / (ms * 1e-3) / 1e12 / peak, 1)
+        elif k.startswith("permute_pad"):
+            b = cfg.T * cfg.d * es + Tp * cfg.d * es + 4 * A_n + 4 * Tp
+            ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
+        elif k.startswith("unpermute_combine"):
+            ypes = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
+            b = A_n * cfg.d * ypes + cfg.T * cfg.d * es + 8 * A_n
+            ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
+        kernels[k] = ent
+
+    out = {
+        "metric": "dMoE layer useful TFLOP/s + % of bf16 MFMA peak (1 GPU); tokens/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) logits + per-expert bias, N(0,1) x, N(0,0.02) weights)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T}, d={cfg.d}, E={cfg.E}, f={cfg.f}, "
+                               f"k={cfg.k}, {cfg.act}, "
+                               f"{'forward+backward' if cfg.backward else 'forward'}",
+                   "padded_rows": Tp, "padding_frac": round(1 - A_n / Tp, 4)},
+        "pct_of_bf16_peak": round(100 * tflops / peak, 2),
+        "tokens_per_s": round(cfg.T / (step_ms * 1e-3), 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for(dom)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

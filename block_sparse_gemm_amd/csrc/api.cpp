@@ -1,0 +1,301 @@
+// C ABI of the block-sparse expert layer: argument validation, size
+// queries and kernel launches.  Every check runs before any HIP call, so
+// argument errors are reported without touching a GPU.
+#include "../../include/bsg.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsg_status fail(bsg_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bsg_status ok() {
+    g_err[0] = '\0';
+    return BSG_OK;
+}
+
+bsg_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(BSG_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elt_bytes(int dtype) { return dtype == BSG_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == BSG_F32 || dtype == BSG_BF16; }
+
+#define REQUIRE(cond, ...)                                 \
+    do {                                                   \
+        if (!(cond)) return fail(BSG_EINVAL, __VA_ARGS__); \
+    } while (0)
+
+// A device array read or written with 16-byte vectors.
+#define REQUIRE_VEC_PTR(p) REQUIRE((p) != nullptr && aligned((p), 16), #p " must be a non-null 16-byte aligned device pointer")
+// A device array of 4-byte elements.
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr && aligned((p), 4), #p " must be a non-null 4-byte aligned device pointer")
+
+bsg_status check_topology(const bsg_topology* t) {
+    REQUIRE(t != nullptr, "topo is NULL");
+    REQUIRE(t->E >= 1 && t->E <= BSG_MAX_EXPERTS, "topo->E out of range");
+    REQUIRE(t->F >= 1, "topo->F must be positive");
+    REQUIRE(t->Tp_max >= BSG_BLOCK && t->Tp_max % BSG_BLOCK == 0,
+            "topo->Tp_max must be a positive multiple of 128");
+    REQUIRE((t->Tp_max / BSG_BLOCK) * (int64_t)t->F < INT32_MAX, "too many blocks for int32 ids");
+    REQUIRE_PTR(t->row_ptr);
+    REQUIRE_PTR(t->col_idx);
+    REQUIRE_PTR(t->row_idx);
+    REQUIRE_PTR(t->col_ptr);
+    REQUIRE_PTR(t->trans_idx);
+    REQUIRE_PTR(t->meta);
+    return BSG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsg_status_string(bsg_status s) {
+    switch (s) {
+    case BSG_OK: return "ok";
+    case BSG_EINVAL: return "invalid argument";
+    case BSG_EUNSUPPORTED: return "unsupported combination";
+    case BSG_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* bsg_last_error(void) { return g_err; }
+
+int64_t bsg_max_padded_rows(int64_t T, int k, int E) {
+    if (T < 1 || k < 1 || E < 1 || k > E) return -1;
+    const int64_t A = T * k;
+    const int64_t ne = A < E ? A : E;
+    return (A + 127 * ne) / BSG_BLOCK * BSG_BLOCK;
+}
+
+bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out) {
+    REQUIRE(out != nullptr, "out is NULL");
+    REQUIRE(Tp_max >= BSG_BLOCK && Tp_max % BSG_BLOCK == 0,
+            "Tp_max must be a positive multiple of 128");
+    REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
+    REQUIRE(f >= BSG_BLOCK && f % BSG_BLOCK == 0, "f must be a positive multiple of 128");
+    const int64_t F = f / BSG_BLOCK;
+    out->row_blocks_max = Tp_max / BSG_BLOCK;
+    out->nnz_max = out->row_blocks_max * F;
+    out->n_cols = (int64_t)E * F;
+    REQUIRE(out->nnz_max < INT32_MAX && out->n_cols < INT32_MAX, "too many blocks for int32 ids");
+    return ok();
+}
+
+size_t bsg_route_workspace_bytes(int64_t T, int k, int E) {
+    if (T < 1 || k < 1 || E < 1 || k > E) return 0;
+    const int64_t nchunks = (T + bsg::kRouteChunk - 1) / bsg::kRouteChunk;
+    return (size_t)(nchunks * E * (int64_t)sizeof(int32_t));
+}
+
+bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm,
+                     int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
+                     int32_t* bin_offsets, void* workspace, size_t workspace_bytes,
+                     bsg_stream_t stream) {
+    REQUIRE(T >= 1, "T must be positive");
+    REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
+    REQUIRE(k >= 1 && k <= E, "k must be in [1, E]");
+    if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
+    REQUIRE(T * k < INT32_MAX, "T*k must fit int32 assignment ids");
+    REQUIRE(bsg_max_padded_rows(T, k, E) < INT32_MAX, "padded rows must fit int32");
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(expert_idx);
+    REQUIRE_PTR(gate);
+    REQUIRE_PTR(dest_row);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(bin_offsets);
+    REQUIRE_PTR(workspace);
+    REQUIRE(workspace_bytes >= bsg_route_workspace_bytes(T, k, E), "workspace too small (%zu < %zu)",
+            workspace_bytes, bsg_route_workspace_bytes(T, k, E));
+    return hip_status(bsg::launch_route(logits, T, E, k, renorm, expert_idx, gate, dest_row,
+                                        counts, bin_offsets, (int32_t*)workspace,
+                                        (hipStream_t)stream),
+                      "route");
+}
+
+bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
+                           const int32_t* dest_row, const float* scale, const int32_t* counts,
+                           const int32_t* bin_offsets, int E, int64_t Tp_max, int32_t* row_src,
+                           void* xp, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
+    REQUIRE(T >= 1 && k >= 1 && E >= 1 && E <= BSG_MAX_EXPERTS && k <= E, "bad T, k or E");
+    REQUIRE(k <= BSG_MAX_TOPK, "k > %d", BSG_MAX_TOPK);
+    REQUIRE(T * k < INT32_MAX, "T*k must fit int32");
+    REQUIRE(d >= 1 && (d * elt_bytes(dtype)) % 16 == 0, "d must keep rows 16-byte aligned");
+    REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E), "Tp_max below the padded-row bound");
+    REQUIRE_VEC_PTR(x);
+    REQUIRE_VEC_PTR(xp);
+    REQUIRE_PTR(dest_row);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(bin_offsets);
+    REQUIRE_PTR(row_src);
+    REQUIRE(scale == nullptr || aligned(scale, 4), "scale must be 4-byte aligned");
+    return hip_status(bsg::launch_permute_pad(x, dtype, T, d, k, dest_row, scale, counts,
+                                              bin_offsets, E, row_src, xp, (hipStream_t)stream),
+                      "permute_pad");
+}
+
+bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
+                              const bsg_topology* topo, bsg_stream_t stream) {
+    REQUIRE_PTR(bin_offsets);
+    REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
+    REQUIRE(f >= BSG_BLOCK && f % BSG_BLOCK == 0, "f must be a positive multiple of 128");
+    bsg_status s = check_topology(topo);
+    if (s != BSG_OK) return s;
+    REQUIRE(topo->E == E && topo->F == f / BSG_BLOCK && topo->Tp_max == Tp_max,
+            "topo capacity does not match E, f, Tp_max");
+    return hip_status(
+        bsg::launch_build_topology(bin_offsets, E, topo->F, Tp_max / BSG_BLOCK, topo->row_ptr,
+                                   topo->col_idx, topo->row_idx, topo->col_ptr, topo->trans_idx,
+                                   topo->meta, (hipStream_t)stream),
+        "build_topology");
+}
+
+static bsg::GemmParams gemm_params(const bsg_topology* t) {
+    bsg::GemmParams p{};
+    p.row_ptr = t->row_ptr;
+    p.col_idx = t->col_idx;
+    p.row_idx = t->row_idx;
+    p.col_ptr = t->col_ptr;
+    p.trans_idx = t->trans_idx;
+    p.meta = t->meta;
+    p.ncols = t->E * t->F;
+    return p;
+}
+
+bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, int64_t ldb,
+                   int trans_b, int K, const bsg_topology* topo, int epilogue, const void* aux_in,
+                   void* out_blocks, void* aux_out, int dtype, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
+    bsg_status s = check_topology(topo);
+    if (s != BSG_OK) return s;
+    REQUIRE(epilogue >= BSG_EPI_NONE && epilogue <= BSG_EPI_GELU_BWD, "unknown epilogue %d", epilogue);
+    const int es = elt_bytes(dtype);
+    const int kt = dtype == BSG_BF16 ? 64 : 32;
+    const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
+    REQUIRE(K >= kt && K % kt == 0, "K must be a positive multiple of %d", kt);
+    REQUIRE(lda >= K && (lda * es) % 16 == 0, "lda must be >= K with 16-byte aligned rows");
+    REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
+    REQUIRE(ldb >= (trans_b ? K : ncol) && (ldb * es) % 16 == 0,
+            "ldb too small or rows not 16-byte aligned");
+    REQUIRE_VEC_PTR(a);
+    REQUIRE_VEC_PTR(b);
+    REQUIRE_VEC_PTR(out_blocks);
+    if (epilogue == BSG_EPI_SILU_MUL) {
+        REQUIRE_VEC_PTR(b2);
+        if (trans_b) return fail(BSG_EUNSUPPORTED, "SILU_MUL with trans_b is not implemented");
+    } else {
+        REQUIRE(b2 == nullptr, "b2 is only used by BSG_EPI_SILU_MUL");
+    }
+    if (epilogue == BSG_EPI_GELU_BWD) REQUIRE_VEC_PTR(aux_in);
+    else REQUIRE(aux_in == nullptr, "aux_in is only used by BSG_EPI_GELU_BWD");
+    if (epilogue != BSG_EPI_GELU) REQUIRE(aux_out == nullptr, "aux_out is only used by BSG_EPI_GELU");
+    else REQUIRE(aux_out == nullptr || aligned(aux_out, 16), "aux_out must be 16-byte aligned");
+    bsg::GemmParams p = gemm_params(topo);
+    p.a = a;
+    p.b = b;
+    p.b2 = b2;
+    p.aux_in = aux_in;
+    p.out = out_blocks;
+    p.aux_out = aux_out;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.K = K;
+    const int64_t nnz_max = (topo->Tp_max / BSG_BLOCK) * topo->F;
+    return hip_status(bsg::launch_sdd(p, nnz_max, topo->F, trans_b, epilogue, dtype, (hipStream_t)stream),
+                      "sdd");
+}
+
+bsg_status bsg_dsd(const void* blocks, const bsg_topology* topo, const void* b, int64_t ldb,
+                   int trans_b, int N, void* c, int64_t ldc, int c_dtype, int dtype,
+                   bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dtype) && dtype_ok(c_dtype), "unknown dtype");
+    if (dtype == BSG_F32 && c_dtype != BSG_F32)
+        return fail(BSG_EUNSUPPORTED, "fp32 operands need an fp32 output");
+    bsg_status s = check_topology(topo);
+    if (s != BSG_OK) return s;
+    const int es = elt_bytes(dtype), ces = elt_bytes(c_dtype);
+    const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
+    REQUIRE(N >= BSG_BLOCK && N % BSG_BLOCK == 0, "N must be a positive multiple of 128");
+    REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
+    REQUIRE(ldb >= (trans_b ? ncol : N) && (ldb * es) % 16 == 0,
+            "ldb too small or rows not 16-byte aligned");
+    REQUIRE(ldc >= N && (ldc * ces) % 16 == 0, "ldc must be >= N with 16-byte aligned rows");
+    REQUIRE_VEC_PTR(blocks);
+    REQUIRE_VEC_PTR(b);
+    REQUIRE_VEC_PTR(c);
+    bsg::GemmParams p = gemm_params(topo);
+    p.a = blocks;
+    p.b = b;
+    p.out = c;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.N = N;
+    p.ntn = (N + 255) / 256;
+    return hip_status(bsg::launch_dsd(p, topo->Tp_max / BSG_BLOCK, trans_b, c_dtype, dtype,
+                                      (hipStream_t)stream),
+                      "dsd");
+}
+
+bsg_status bsg_dstd(const void* blocks, const bsg_topology* topo, const void* dmat, int64_t ldd,
+                    int N, void* c, int64_t ldc, int trans_c, int dtype, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
+    bsg_status s = check_topology(topo);
+    if (s != BSG_OK) return s;
+    const int es = elt_bytes(dtype);
+    const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
+    REQUIRE(N >= BSG_BLOCK && N % BSG_BLOCK == 0, "N must be a positive multiple of 128");
+    REQUIRE(trans_c == 0 || trans_c == 1, "trans_c must be 0 or 1");
+    REQUIRE(ldd >= N && (ldd * es) % 16 == 0, "ldd must be >= N with 16-byte aligned rows");
+    REQUIRE(ldc >= (trans_c ? ncol : N) && (ldc * es) % 16 == 0,
+            "ldc too small or rows not 16-byte aligned");
+    REQUIRE_VEC_PTR(blocks);
+    REQUIRE_VEC_PTR(dmat);
+    REQUIRE_VEC_PTR(c);
+    bsg::GemmParams p = gemm_params(topo);
+    p.a = blocks;
+    p.b = dmat;
+    p.out = c;
+    p.ldb = ldd;
+    p.ldc = ldc;
+    p.N = N;
+    p.ntn = (N + 255) / 256;
+    return hip_status(bsg::launch_dstd(p, trans_c, dtype, (hipStream_t)stream), "dstd");
+}
+
+bsg_status bsg_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
+                                 const int32_t* dest_row, const float* gate, int64_t T, int k,
+                                 int d, void* y, int y_dtype, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(yp_dtype) && dtype_ok(y_dtype), "unknown dtype");
+    REQUIRE(T >= 1 && k >= 1 && k <= BSG_MAX_TOPK && T * k < INT32_MAX, "bad T or k");
+    REQUIRE(d >= 8 && d % 8 == 0, "d must be a positive multiple of 8");
+    REQUIRE(ld_yp >= d && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
+            "ld_yp must be >= d with 16-byte aligned rows");
+    REQUIRE_VEC_PTR(yp);
+    REQUIRE_VEC_PTR(y);
+    REQUIRE_PTR(dest_row);
+    REQUIRE(gate == nullptr || aligned(gate, 4), "gate must be 4-byte aligned");
+    return hip_status(bsg::launch_unpermute_combine(yp, yp_dtype, ld_yp, dest_row, gate, T, k, d,
+                                                    y, y_dtype, (hipStream_t)stream),
+                      "unpermute_combine");
+}
+
+}  // extern "C"

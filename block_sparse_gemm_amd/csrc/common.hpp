@@ -1,0 +1,115 @@
+// Device-side helpers shared by the gfx950 kernels of the block-sparse
+// expert layer: vector types, bf16 conversion, wave reductions, the
+// XCD-aware workgroup remap and the fp32 activation functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBlock = 128;       // block edge of the sparse layout
+constexpr int kWave = 64;         // CDNA wavefront width
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// fp64 -> bf16 rounded ONCE to nearest even: truncate to fp32, make the
+// result sticky-odd when inexact (round to odd keeps enough bits), then
+// round to nearest even into bf16.
+__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
+    float f = __double2float_rz(v);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != v) u |= 1u;
+    return f32_to_bf16(__uint_as_float(u));
+}
+
+// ---------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// ------------------------------------------------------------ XCD remap
+//
+// Workgroup w of an n-workgroup launch runs on XCD w % 8.  Give each XCD a
+// contiguous range of logical tiles so that neighbouring tiles, which share
+// operand panels, hit the same L2.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+    const int q = n / kXcds, r = n % kXcds, x = w % kXcds, i = w / kXcds;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// ------------------------------------------------------------ activations
+//
+// GeLU in the exact form 0.5 h (1 + erf(h / sqrt 2)).  erf is evaluated with
+// the Abramowitz & Stegun 7.1.26 approximation
+//   erfc(z) ~ (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z),  |error in erf| <= 1.5e-7  (z >= 0),
+// with the hardware reciprocal and exp2.  q below is 0.5 erfc(|h|/sqrt 2),
+// i.e. Phi(-|h|).
+struct ErfcHalf {
+    float q;  // Phi(-|h|)
+    float e;  // exp(-h^2 / 2)
+};
+
+__device__ __forceinline__ ErfcHalf erfc_half(float h) {
+    const float z = fabsf(h) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float p = fmaf(1.061405429f * 0.5f, t, -1.453152027f * 0.5f);
+    p = fmaf(p, t, 1.421413741f * 0.5f);
+    p = fmaf(p, t, -0.284496736f * 0.5f);
+    p = fmaf(p, t, 0.254829592f * 0.5f);
+    p *= t;
+    const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.44269504088896341f);
+    return {p * e, e};
+}
+
+__device__ __forceinline__ float gelu_f(float h) {
+    const ErfcHalf r = erfc_half(h);
+    const float phi = h >= 0.0f ? 1.0f - r.q : r.q;
+    return h * phi;
+}
+
+// d/dh gelu(h) = Phi(h) + h phi(h),  phi(h) = exp(-h^2/2) / sqrt(2 pi)
+__device__ __forceinline__ float gelu_grad_f(float h) {
+    const ErfcHalf r = erfc_half(h);
+    const float phi = h >= 0.0f ? 1.0f - r.q : r.q;
+    return fmaf(h * r.e, 0.398942280401432678f, phi);
+}
+
+// silu(g) = g / (1 + exp(-g))
+__device__ __forceinline__ float silu_f(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
+}
+
+}  // namespace bsg

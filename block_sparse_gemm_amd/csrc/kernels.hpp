@@ -1,0 +1,70 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+constexpr int kF32 = 0;   // matches BSG_F32
+constexpr int kBf16 = 1;  // matches BSG_BF16
+
+constexpr int kEpiNone = 0;
+constexpr int kEpiGelu = 1;
+constexpr int kEpiSiluMul = 2;
+constexpr int kEpiGeluBwd = 3;
+
+constexpr int kModeSdd = 0;
+constexpr int kModeSddOne = 1;
+constexpr int kModeDsd = 2;
+constexpr int kModeDstd = 3;
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kRouteChunk = 64;  // tokens per routing chunk
+
+struct GemmParams {
+    const void* a;       // SDD: dense rows; DSD / DSTD: sparse blocks
+    const void* b;       // SDD / DSD: dense B; DSTD: dense rows (dmat)
+    const void* b2;      // SDD dual-B second operand (SwiGLU up projection)
+    const void* aux_in;  // SDD GELU_BWD: saved pre-activation blocks
+    void* out;
+    void* aux_out;       // SDD GELU: optional saved pre-activation blocks
+    int64_t lda, ldb, ldc;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const int32_t* row_idx;
+    const int32_t* col_ptr;
+    const int32_t* trans_idx;
+    const int32_t* meta;  // {nnz, R} written by build_topology
+    int K;                // SDD reduction length
+    int N;                // DSD / DSTD output width
+    int ntn;              // 256-wide output tiles along N
+    int ncols;            // E * F column blocks
+};
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
+                        int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
+                        int32_t* bin_offsets, int32_t* workspace, hipStream_t stream);
+
+hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
+                              const int32_t* dest_row, const float* scale, const int32_t* counts,
+                              const int32_t* bin_offsets, int E, int32_t* row_src, void* xp,
+                              hipStream_t stream);
+
+hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
+                                 int32_t* row_ptr, int32_t* col_idx, int32_t* row_idx,
+                                 int32_t* col_ptr, int32_t* trans_idx, int32_t* meta,
+                                 hipStream_t stream);
+
+hipError_t launch_sdd(const GemmParams& p, int64_t nnz_max, int F, int trans_b, int epi,
+                      int dtype, hipStream_t s);
+hipError_t launch_dsd(const GemmParams& p, int64_t row_blocks_max, int trans_b, int c_dtype,
+                      int dtype, hipStream_t s);
+hipError_t launch_dstd(const GemmParams& p, int trans_c, int dtype, hipStream_t s);
+
+hipError_t launch_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
+                                    const int32_t* dest_row, const float* gate, int64_t T, int k,
+                                    int d, void* y, int y_dtype, hipStream_t stream);
+
+}  // namespace bsg

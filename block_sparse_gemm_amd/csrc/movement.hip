@@ -1,0 +1,197 @@
+// Data movement: the fused permutation + padding gather, and the weighted
+// un-permute/combine.
+//
+// permute_pad follows George Lin's Blog (MegaBlocks/FlexMoE post),
+// section 1.4: one kernel reorders tokens from batch order into expert
+// order AND pads each expert group to the 128 block size (section 1.3,
+// "block size"), so the padding costs no extra pass.  unpermute_combine is
+// the reverse layout transform (restore batch order) fused with the
+// gate-weighted sum of each token's k expert outputs.
+//
+// Both are HBM-bound.  A wavefront owns one row at a time and moves it with
+// 16-byte vector accesses, so every row transfer is a run of fully
+// coalesced 1 KiB wave accesses.  permute_pad reads each token row ONCE and
+// writes it to its k destinations.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bsg {
+
+constexpr int kMoveThreads = 256;
+constexpr int kMoveWaves = kMoveThreads / kWave;
+
+template <int DT>
+struct Row;  // 16-byte vector of a row: 8 bf16 or 4 fp32
+
+template <>
+struct Row<kBf16> {
+    static constexpr int kVec = 8;
+    static __device__ __forceinline__ void load_f32(const void* p, float* out) {
+        const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(v[i] << 16);
+            out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store_f32(void* p, const float* in) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(in[2 * i], in[2 * i + 1]);
+        *(u32x4*)p = v;
+    }
+};
+
+template <>
+struct Row<kF32> {
+    static constexpr int kVec = 4;
+    static __device__ __forceinline__ void load_f32(const void* p, float* out) {
+        const f32x4 v = *(const f32x4*)p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = v[i];
+    }
+    static __device__ __forceinline__ void store_f32(void* p, const float* in) {
+        *(f32x4*)p = f32x4{in[0], in[1], in[2], in[3]};
+    }
+};
+
+// Scaled copy of one 16-byte chunk: each product rounded once.
+template <int DT>
+__device__ __forceinline__ u32x4 scale_chunk(u32x4 v, float s);
+
+template <>
+__device__ __forceinline__ u32x4 scale_chunk<kBf16>(u32x4 v, float s) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double lo = (double)s * (double)__uint_as_float(v[i] << 16);
+        const double hi = (double)s * (double)__uint_as_float(v[i] & 0xffff0000u);
+        o[i] = f64_to_bf16(lo) | (f64_to_bf16(hi) << 16);
+    }
+    return o;
+}
+
+template <>
+__device__ __forceinline__ u32x4 scale_chunk<kF32>(u32x4 v, float s) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = __float_as_uint((float)((double)s * (double)__uint_as_float(v[i])));
+    return o;
+}
+
+// Jobs: token rows [0, T) then pad slots [T, T + E*128).  A pad slot (e, i)
+// is row bin_offsets[e] + counts[e] + i when that row is still in e's bin.
+template <int DT>
+__global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
+    const u32x4* __restrict__ x, int64_t T, int chunks, int k, const int32_t* __restrict__ dest_row,
+    const float* __restrict__ scale, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ bin_offsets, int E, int32_t* __restrict__ row_src,
+    u32x4* __restrict__ xp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t nwaves = (int64_t)gridDim.x * kMoveWaves;
+    const int64_t njobs = T + (int64_t)E * kBlock;
+    for (int64_t job = (int64_t)blockIdx.x * kMoveWaves + threadIdx.x / kWave; job < njobs;
+         job += nwaves) {
+        if (job < T) {
+            const int64_t t = job;
+            const u32x4* src = x + t * chunks;
+            for (int c = lane; c < chunks; c += kWave) {
+                const u32x4 v = src[c];
+                for (int j = 0; j < k; ++j) {
+                    const int64_t a = t * k + j;
+                    const int64_t row = dest_row[a];
+                    xp[row * chunks + c] = scale ? scale_chunk<DT>(v, scale[a]) : v;
+                }
+            }
+            if (lane < k) row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
+        } else {
+            const int64_t p = job - T;
+            const int e = (int)(p / kBlock);
+            const int64_t row = (int64_t)bin_offsets[e] + counts[e] + p % kBlock;
+            if (row >= bin_offsets[e + 1]) continue;
+            u32x4* dst = xp + row * chunks;
+            for (int c = lane; c < chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
+            if (lane == 0) row_src[row] = -1;
+        }
+    }
+}
+
+// y[t] = sum_j g_j * yp[dest_row[t*k + j]], fp32 accumulation in ascending j.
+template <int DT_IN, int DT_OUT>
+__global__ __launch_bounds__(kMoveThreads) void combine_kernel(
+    const char* __restrict__ yp, int64_t ld_yp_bytes, const int32_t* __restrict__ dest_row,
+    const float* __restrict__ gate, int64_t T, int k, int d, char* __restrict__ y) {
+    constexpr int V = Row<DT_IN>::kVec;
+    constexpr int ES_IN = DT_IN == kBf16 ? 2 : 4;
+    constexpr int ES_OUT = DT_OUT == kBf16 ? 2 : 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t nwaves = (int64_t)gridDim.x * kMoveWaves;
+    const int groups = d / V;
+    for (int64_t t = (int64_t)blockIdx.x * kMoveWaves + threadIdx.x / kWave; t < T; t += nwaves) {
+        for (int c = lane; c < groups; c += kWave) {
+            float acc[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                const int64_t a = t * k + j;
+                const float g = gate ? gate[a] : 1.0f;
+                float v[V];
+                Row<DT_IN>::load_f32(yp + (int64_t)dest_row[a] * ld_yp_bytes +
+                                         (int64_t)c * V * ES_IN, v);
+#pragma unroll
+                for (int i = 0; i < V; ++i) acc[i] += g * v[i];
+            }
+            char* dst = y + (t * d + (int64_t)c * V) * ES_OUT;
+            if constexpr (ES_OUT * V == 16) {
+                Row<DT_OUT>::store_f32(dst, acc);  // same width in and out
+            } else if constexpr (DT_OUT == kBf16) {  // 4 fp32 in -> 4 bf16 = 8 bytes
+                *(u32x2*)dst = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            } else {  // 8 bf16 in -> 8 fp32 out = two 16-byte stores
+                Row<kF32>::store_f32(dst, acc);
+                Row<kF32>::store_f32(dst + 16, acc + 4);
+            }
+        }
+    }
+}
+
+static int move_grid(int64_t jobs) {
+    int64_t g = (jobs + kMoveWaves - 1) / kMoveWaves;
+    return (int)(g < 8192 ? (g < 1 ? 1 : g) : 8192);
+}
+
+hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
+                              const int32_t* dest_row, const float* scale, const int32_t* counts,
+                              const int32_t* bin_offsets, int E, int32_t* row_src, void* xp,
+                              hipStream_t stream) {
+    const int es = dtype == kBf16 ? 2 : 4;
+    const int chunks = d * es / 16;
+    const int grid = move_grid(T + (int64_t)E * kBlock);
+    if (dtype == kBf16)
+        hipLaunchKernelGGL(permute_pad_kernel<kBf16>, dim3(grid), dim3(kMoveThreads), 0, stream,
+                           (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
+                           row_src, (u32x4*)xp);
+    else
+        hipLaunchKernelGGL(permute_pad_kernel<kF32>, dim3(grid), dim3(kMoveThreads), 0, stream,
+                           (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
+                           row_src, (u32x4*)xp);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
+                                    const int32_t* dest_row, const float* gate, int64_t T, int k,
+                                    int d, void* y, int y_dtype, hipStream_t stream) {
+    const int grid = move_grid(T);
+    const int64_t ldb = ld_yp * (yp_dtype == kBf16 ? 2 : 4);
+#define BSG_COMBINE(I, O)                                                                        \
+    hipLaunchKernelGGL((combine_kernel<I, O>), dim3(grid), dim3(kMoveThreads), 0, stream,        \
+                       (const char*)yp, ldb, dest_row, gate, T, k, d, (char*)y)
+    if (yp_dtype == kBf16 && y_dtype == kBf16) BSG_COMBINE(kBf16, kBf16);
+    else if (yp_dtype == kBf16) BSG_COMBINE(kBf16, kF32);
+    else if (y_dtype == kBf16) BSG_COMBINE(kF32, kBf16);
+    else BSG_COMBINE(kF32, kF32);
+#undef BSG_COMBINE
+    return hipGetLastError();
+}
+
+}  // namespace bsg

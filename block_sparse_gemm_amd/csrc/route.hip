@@ -1,0 +1,219 @@
+// Routing: gate + router, histogram, padded bins and stable placement.
+//
+// George Lin's Blog (MegaBlocks/FlexMoE post), section 1.4: tokens are
+// routed to experts and regrouped from batch order into expert order, each
+// group padded to a multiple of the 128 block size (section 1.3).  The
+// pages leave the gate's form open; this follows top-k on the logits with a
+// softmax gate.
+//
+// Three launches, no atomics on global memory, so every integer result is
+// identical on every run:
+//   1. route_topk     one wavefront per token: top-k by wave reductions,
+//                     softmax gate; per 64-token chunk an LDS histogram.
+//   2. route_scan     one workgroup per expert: exclusive scan of that
+//                     expert's per-chunk counts (in place) and its total.
+//   3. route_place    one workgroup per chunk: padded bin offsets, then the
+//                     rank of each assignment among the chunk's earlier
+//                     assignments to the same expert, found with wave64
+//                     ballots on the expert id bits.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bsg {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kPerLane = kMaxExperts / kWave;  // logits held per lane
+
+__global__ __launch_bounds__(kRouteThreads) void route_topk(
+    const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
+    int32_t* __restrict__ expert_idx, float* __restrict__ gate,
+    int32_t* __restrict__ chunk_counts, int nchunks) {
+    __shared__ int hist[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteChunk;
+    const int nvals = (E + kWave - 1) / kWave;
+
+    for (int tt = wave; tt < kRouteChunk; tt += kRouteWaves) {
+        const int64_t t = t0 + tt;
+        if (t >= T) break;
+        const float* row = logits + t * E;
+        float v[kPerLane];
+        uint32_t taken = 0;  // bit i: expert lane + 64 i already picked
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = lane + kWave * i;
+            v[i] = (i < nvals && e < E) ? row[e] : 0.0f;
+        }
+        int my_sel = -1;
+        float my_val = 0.0f;
+        float top_val = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            // lane-local best among untaken experts: larger logit, then lower id
+            int bi = -1;
+            float bv = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                const int e = lane + kWave * i;
+                if (i < nvals && e < E && !((taken >> i) & 1u) && (bi < 0 || v[i] > bv)) {
+                    bi = e;
+                    bv = v[i];
+                }
+            }
+            // butterfly: a total order, so every lane ends with the same winner
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off, kWave);
+                const int oi = __shfl_xor(bi, off, kWave);
+                if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+                    bi = oi;
+                    bv = ov;
+                }
+            }
+            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+            if (lane == j) {
+                my_sel = bi;
+                my_val = bv;
+            }
+            if (j == 0) top_val = bv;
+        }
+        // softmax over all experts, max-subtracted (the first pick is the max)
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = lane + kWave * i;
+            if (i < nvals && e < E) z += expf(v[i] - top_val);
+        }
+        z = wave_sum(z);
+        const float p = lane < k ? expf(my_val - top_val) : 0.0f;
+        const float denom = renorm ? wave_sum(p) : z;
+        if (lane < k) {
+            expert_idx[t * k + lane] = my_sel;
+            gate[t * k + lane] = p / denom;
+            atomicAdd(&hist[my_sel], 1);  // LDS only: the count is order-free
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRouteThreads)
+        chunk_counts[(int64_t)e * nchunks + blockIdx.x] = hist[e];
+}
+
+// Exclusive scan of one expert's chunk counts, in place; total -> counts[e].
+__global__ __launch_bounds__(kRouteThreads) void route_scan(int32_t* __restrict__ chunk_counts,
+                                                            int nchunks,
+                                                            int32_t* __restrict__ counts) {
+    __shared__ int part[kRouteThreads];
+    int32_t* row = chunk_counts + (int64_t)blockIdx.x * nchunks;
+    const int per = (nchunks + kRouteThreads - 1) / kRouteThreads;
+    const int lo = threadIdx.x * per;
+    const int hi = min(lo + per, nchunks);
+    int s = 0;
+    for (int c = lo; c < hi; ++c) s += row[c];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the 256 partial sums
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+        const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int run = part[threadIdx.x] - s;  // exclusive prefix of this segment
+    for (int c = lo; c < hi; ++c) {
+        const int v = row[c];
+        row[c] = run;
+        run += v;
+    }
+    if (threadIdx.x == kRouteThreads - 1) counts[blockIdx.x] = part[kRouteThreads - 1];
+}
+
+// Bin offsets + stable in-chunk ranks -> dest_row.
+__global__ __launch_bounds__(kRouteThreads) void route_place(
+    const int32_t* __restrict__ expert_idx, int64_t T, int E, int k,
+    const int32_t* __restrict__ chunk_base, int nchunks, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ dest_row, int32_t* __restrict__ bin_offsets) {
+    __shared__ int bins[kMaxExperts + 1];
+    __shared__ int part[kRouteThreads];
+    __shared__ int running[kMaxExperts];
+    __shared__ int wcnt[kRouteWaves][kMaxExperts];
+
+    // padded sizes, exclusive scan over ascending expert id
+    const int per = (E + kRouteThreads - 1) / kRouteThreads;
+    const int lo = threadIdx.x * per;
+    const int hi = min(lo + per, E);
+    int s = 0;
+    for (int e = lo; e < hi; ++e) s += (counts[e] + kBlock - 1) / kBlock * kBlock;
+    part[threadIdx.x] = s;
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) running[e] = 0;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+        const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int run = part[threadIdx.x] - s;
+    for (int e = lo; e < hi; ++e) {
+        bins[e] = run;
+        run += (counts[e] + kBlock - 1) / kBlock * kBlock;
+    }
+    if (threadIdx.x == kRouteThreads - 1) bins[E] = part[kRouteThreads - 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e <= E; e += kRouteThreads) bin_offsets[e] = bins[e];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const int64_t a0 = (int64_t)blockIdx.x * kRouteChunk * k;
+    const int64_t a1 = min(a0 + (int64_t)kRouteChunk * k, T * k);
+
+    for (int64_t base = a0; base < a1; base += kRouteThreads) {
+        for (int i = threadIdx.x; i < kRouteWaves * E; i += kRouteThreads)
+            (&wcnt[0][0])[(i / E) * kMaxExperts + i % E] = 0;
+        __syncthreads();
+        const int64_t a = base + threadIdx.x;
+        const bool valid = a < a1;
+        const int e = valid ? expert_idx[a] : 0;
+        // lanes of this wave holding the same expert id
+        uint64_t match = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+            match &= ((e >> b) & 1) ? ones : ~ones;
+        }
+        const int rank = __popcll(match & lanemask_lt());
+        if (valid && rank == 0) wcnt[wave][e] = __popcll(match);
+        __syncthreads();
+        if (valid) {
+            int off = running[e];
+            for (int w = 0; w < wave; ++w) off += wcnt[w][e];
+            dest_row[a] = bins[e] + chunk_base[(int64_t)e * nchunks + blockIdx.x] + off + rank;
+        }
+        __syncthreads();
+        for (int x = threadIdx.x; x < E; x += kRouteThreads) {
+            int add = 0;
+            for (int w = 0; w < kRouteWaves; ++w) add += wcnt[w][x];
+            running[x] += add;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
+                        int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
+                        int32_t* bin_offsets, int32_t* workspace, hipStream_t stream) {
+    const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
+    hipLaunchKernelGGL(route_topk, dim3(nchunks), dim3(kRouteThreads), 0, stream, logits, T, E,
+                       k, renorm, expert_idx, gate, workspace, nchunks);
+    hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace, nchunks,
+                       counts);
+    hipLaunchKernelGGL(route_place, dim3(nchunks), dim3(kRouteThreads), 0, stream, expert_idx, T,
+                       E, k, workspace, nchunks, counts, dest_row, bin_offsets);
+    return hipGetLastError();
+}
+
+}  // namespace bsg

@@ -1,0 +1,103 @@
+// Topology + transpose metadata in one launch.
+//
+// George Lin's Blog (MegaBlocks/FlexMoE post): section 1.3 defines the
+// hybrid BCSR-COO format (BCSR row pointer + column index, plus a
+// materialised row index per nonzero block) and the transpose index (the
+// same blocks listed in column order, no data copied); section 1.4 builds
+// this metadata, mapping each (expert, token-row range) to its nonzero
+// blocks, together with the transpose metadata in a single kernel.
+//
+// The first layer's output is block-diagonal: row block r belongs to the
+// expert whose bin holds row 128 r, and that expert owns the F column
+// blocks e*F .. e*F + F - 1.  So every entry is computed independently from
+// the bin offsets: thread g fills row_ptr[g], BCSR entry g and transpose
+// entry g.  Each workgroup first stages s_e = bin_offsets[e] / 128 in LDS
+// and finds the owner of a row block by binary search.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bsg {
+
+constexpr int kTopoThreads = 256;
+
+// Largest e in [0, E) with s[e] <= r; s is non-decreasing.  Empty experts
+// share their start with the next expert, so this is the owner of r.
+__device__ __forceinline__ int owner_of(const int* s, int E, int64_t r) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
+    const int32_t* __restrict__ bin_offsets, int E, int F, int64_t row_blocks_max,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ row_idx,
+    int32_t* __restrict__ col_ptr, int32_t* __restrict__ trans_idx, int32_t* __restrict__ meta) {
+    __shared__ int s[kMaxExperts + 1];  // bin start in row blocks
+    for (int e = threadIdx.x; e <= E; e += kTopoThreads) s[e] = bin_offsets[e] / kBlock;
+    __syncthreads();
+    const int64_t R = s[E];
+    const int64_t nnz = R * F;
+    const int64_t g = (int64_t)blockIdx.x * kTopoThreads + threadIdx.x;
+
+    if (R > row_blocks_max) {
+        // the routing needs more rows than the topology holds: publish an
+        // empty topology (every product then writes nothing / zeros) and
+        // raise the overflow flag instead of writing out of bounds
+        if (g == 0) {
+            meta[0] = 0;
+            meta[1] = 0;
+            meta[2] = 1;
+        }
+        if (g <= row_blocks_max) row_ptr[g] = 0;
+        if (g <= (int64_t)E * F) col_ptr[g] = 0;
+        return;
+    }
+    if (g == 0) {
+        meta[0] = (int32_t)nnz;
+        meta[1] = (int32_t)R;
+        meta[2] = 0;
+    }
+    // BCSR block pointer: every non-empty row block holds F blocks
+    if (g <= row_blocks_max) row_ptr[g] = (int32_t)((g < R ? g : R) * F);
+    if (g < nnz) {
+        // BCSR entry g = (row block r, j-th block of the row) + its COO row
+        const int64_t r = g / F;
+        const int j = (int)(g % F);
+        const int e = owner_of(s, E, r);
+        col_idx[g] = e * F + j;
+        row_idx[g] = (int32_t)r;
+        // transpose entry g: expert e' owns positions [s_e' F, s_(e'+1) F);
+        // inside it, column j' holds R_e' blocks in ascending row order
+        const int et = owner_of(s, E, g / F);
+        const int64_t Re = s[et + 1] - s[et];
+        const int64_t local = g - (int64_t)s[et] * F;
+        const int64_t jt = local / Re, it = local % Re;
+        trans_idx[g] = (int32_t)((s[et] + it) * F + jt);
+    }
+    if (g < (int64_t)E * F) {
+        const int e = (int)(g / F);
+        const int j = (int)(g % F);
+        col_ptr[g] = (int32_t)((int64_t)s[e] * F + (int64_t)j * (s[e + 1] - s[e]));
+    }
+    if (g == (int64_t)E * F) col_ptr[g] = (int32_t)nnz;
+}
+
+hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
+                                 int32_t* row_ptr, int32_t* col_idx, int32_t* row_idx,
+                                 int32_t* col_ptr, int32_t* trans_idx, int32_t* meta,
+                                 hipStream_t stream) {
+    int64_t n = row_blocks_max * F;
+    if (row_blocks_max + 1 > n) n = row_blocks_max + 1;
+    if ((int64_t)E * F + 1 > n) n = (int64_t)E * F + 1;
+    const int grid = (int)((n + kTopoThreads - 1) / kTopoThreads);
+    hipLaunchKernelGGL(build_topology_kernel, dim3(grid), dim3(kTopoThreads), 0, stream,
+                       bin_offsets, E, F, row_blocks_max, row_ptr, col_idx, row_idx, col_ptr,
+                       trans_idx, meta);
+    return hipGetLastError();
+}
+
+}  // namespace bsg

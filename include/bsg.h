@@ -1,0 +1,243 @@
+/*
+ * bsg.h - C ABI of the MI355X (gfx950) dropless-MoE block-sparse expert layer.
+ *
+ * The layer follows the MegaBlocks formulation described in George Lin's
+ * Blog (post on MegaBlocks and FlexMoE, part 1): the expert MLP over a
+ * variable number of tokens per expert is one block-sparse product with
+ * 128x128 blocks (section 1.2), SDD for the first layer, the activation,
+ * DSD for the second layer, and DSTD for the weight gradients through a
+ * transpose index (section 1.3); routing, a fused permutation + padding
+ * kernel and a one-launch topology builder come first (section 1.4).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer unless stated otherwise,
+ *    allocated and freed by the caller; the library never allocates, frees,
+ *    synchronises the host or keeps global mutable state.
+ *  - Every kernel is enqueued on `stream` (a hipStream_t; NULL means the
+ *    null stream) and runs asynchronously; results are valid once the
+ *    stream has reached them.
+ *  - Arrays of activations, weights and blocks are moved with 16-byte
+ *    vectors and must be 16-byte aligned; index, count and gate arrays
+ *    must be 4-byte aligned.  Leading dimensions are in elements and must
+ *    keep every row 16-byte aligned.
+ *  - Arguments are validated BEFORE any HIP call.  An invalid argument
+ *    returns BSG_EINVAL, a valid but unimplemented combination
+ *    BSG_EUNSUPPORTED, a failed launch BSG_EHIP; bsg_last_error() then
+ *    describes the failure (per thread).  Faults inside a kernel surface at
+ *    the caller's next synchronisation.
+ *  - Sizes that depend on the routing (Tp, the number of nonzero blocks) are
+ *    produced on the device; buffers are sized for their upper bounds from
+ *    the size queries below, so no call needs a host round trip.
+ *  - dtype codes: BSG_F32 (fp32) or BSG_BF16 (bf16 storage, fp32
+ *    accumulation).
+ *
+ * Symbols: T tokens, d model width, E experts, f per-expert hidden width,
+ * k experts per token, F = f/128 column blocks per expert, A = T*k
+ * assignments, Tp = padded row count, R = Tp/128 row blocks,
+ * nnz = R*F nonzero blocks.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSG_OK = 0,
+    BSG_EINVAL = -1,       /* null pointer, bad size, misaligned pointer, bad code */
+    BSG_EUNSUPPORTED = -2, /* valid request this build does not implement */
+    BSG_EHIP = -3          /* the HIP runtime rejected a launch */
+} bsg_status;
+
+typedef enum { BSG_F32 = 0, BSG_BF16 = 1 } bsg_dtype;
+
+typedef enum {
+    BSG_EPI_NONE = 0,     /* out = acc */
+    BSG_EPI_GELU = 1,     /* out = gelu(acc) (exact erf form); optional aux_out = acc */
+    BSG_EPI_SILU_MUL = 2, /* dual B: out = silu(acc_b) * acc_b2 */
+    BSG_EPI_GELU_BWD = 3  /* out = acc * gelu'(aux_in) */
+} bsg_epilogue;
+
+/* A hipStream_t passed as an opaque pointer (NULL = null stream). */
+typedef void* bsg_stream_t;
+
+#define BSG_BLOCK 128
+#define BSG_MAX_EXPERTS 1024
+#define BSG_MAX_TOPK 32
+
+/* Upper bounds for the topology arrays (pure host function results). */
+typedef struct {
+    int64_t row_blocks_max; /* Tp_max / 128                      */
+    int64_t nnz_max;        /* row_blocks_max * F                 */
+    int64_t n_cols;         /* E * F column blocks                */
+} bsg_topo_sizes;
+
+/*
+ * Hybrid BCSR-COO topology of the first layer's output, a [Tp x E*f]
+ * matrix of 128x128 blocks where block (r, c) is nonzero when row block r
+ * lies in the bin of the expert that owns column block c (section 1.3,
+ * "hybrid BCSR-COO format" and "transpose indices").  All arrays are
+ * caller-allocated device int32 arrays of the stated capacity:
+ *   row_ptr   [row_blocks_max + 1] BCSR block pointer; entries past R hold nnz
+ *   col_idx   [nnz_max]  global column block of each block, BCSR order
+ *   row_idx   [nnz_max]  materialised row block of each block (COO half)
+ *   col_ptr   [E*F + 1]  start of each column's run in trans_idx
+ *   trans_idx [nnz_max]  BCSR block ids listed column by column,
+ *                        ascending row inside a column (no data copied)
+ *   meta      [4]        written on the device: {nnz, R, overflow, 0};
+ *                        overflow = 1 when the routing needs more than
+ *                        Tp_max rows: the topology is then published empty
+ *                        (nnz = R = 0, all pointers 0) and every product
+ *                        writes nothing, or zeros for dstd
+ * E, F and Tp_max are host values describing the capacity.
+ * Sparse operands ("blocks") are stored block-major, [nnz_max][128][128],
+ * each block row-major, in BCSR order.
+ */
+typedef struct {
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    int32_t* row_idx;
+    int32_t* col_ptr;
+    int32_t* trans_idx;
+    int32_t* meta;
+    int32_t E;
+    int32_t F;
+    int64_t Tp_max;
+} bsg_topology;
+
+/* ------------------------------------------------------------ size queries */
+
+/* Upper bound on Tp for any routing: 128 * floor((A + 127*min(E, A)) / 128)
+ * with A = T*k (each non-empty expert pads by at most 127 rows,
+ * section 1.3 "block size").  Returns -1 on invalid sizes. */
+int64_t bsg_max_padded_rows(int64_t T, int k, int E);
+
+/* Capacities of the topology arrays for Tp_max padded rows. */
+bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out /* host */);
+
+/* Bytes of device workspace bsg_route needs (0 on invalid sizes). */
+size_t bsg_route_workspace_bytes(int64_t T, int k, int E);
+
+/* ------------------------------------------------------------------ calls */
+
+/*
+ * route - gate + router (section 1.4: tokens are routed, then regrouped by
+ * expert; the pages leave the gate's form open, see the design notes).
+ *   logits      [T, E] fp32 row-major, finite values.
+ *   For each token the k largest logits are picked (ties: lower expert id),
+ *   in rank order: expert_idx [T*k] int32, slot j of token t at t*k + j.
+ *   gate [T*k] fp32 = softmax over all E logits of the picked expert;
+ *   renorm != 0 divides by the sum over the k picks.
+ *   counts [E] int32 tokens per expert; bin_offsets [E+1] int32 exclusive
+ *   scan of ceil(counts/128)*128 in ascending expert id (Tp = bin_offsets[E]).
+ *   dest_row [T*k] int32: row of the padded, expert-grouped layout that
+ *   assignment a = t*k + j occupies; inside a bin, ascending a.
+ *   workspace: bsg_route_workspace_bytes(T, k, E) device bytes.
+ *   Requires 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 1.
+ *   Deterministic: integer results are bit-identical on every run.
+ */
+bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, int32_t* expert_idx,
+                     float* gate, int32_t* dest_row, int32_t* counts, int32_t* bin_offsets,
+                     void* workspace, size_t workspace_bytes, bsg_stream_t stream);
+
+/*
+ * permute_pad - fused permutation + padding (section 1.4 and the padding
+ * paragraph of section 1.3): row dest_row[a] of xp receives row a/k of x,
+ * times scale[a] when scale is not NULL (the product is rounded once to the
+ * dtype); the rows of each bin past its count are zero-filled; row_src
+ * receives, for every row below Tp, the assignment that fills it or -1.
+ *   x [T, d] (dtype), xp [Tp_max, d] (dtype), row_src [Tp_max] int32,
+ *   counts/bin_offsets as produced by bsg_route.  Rows >= Tp are untouched.
+ *   d must be a positive multiple of 8 (bf16) or 4 (fp32).
+ */
+bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
+                           const int32_t* dest_row, const float* scale, const int32_t* counts,
+                           const int32_t* bin_offsets, int E, int64_t Tp_max, int32_t* row_src,
+                           void* xp, bsg_stream_t stream);
+
+/*
+ * build_topology - the topology + transpose metadata in ONE launch
+ * (section 1.4, last paragraph): maps each expert's token row range to its
+ * nonzero blocks.  Fills every array of *topo (see bsg_topology) from
+ * bin_offsets [E+1]; f is the per-expert hidden width (multiple of 128).
+ * topo->E, topo->F = f/128 and topo->Tp_max must match the arguments.
+ */
+bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
+                              const bsg_topology* topo /* host struct */, bsg_stream_t stream);
+
+/*
+ * sdd - sampled dense-dense product (section 1.2, first layer):
+ * for every nonzero block b = (r, c):
+ *   acc_b[m][n] = sum_k a[128r + m][k] * B[k][128c + n],  k < K,
+ * where a is [Tp_max, K] row-major with leading dimension lda and
+ *   trans_b = 0: B[k][n] = b[k*ldb + n]    (b is [K, E*f], e.g. W1)
+ *   trans_b = 1: B[k][n] = b[n*ldb + k]    (b is [E*f, K], e.g. W2 for dgrad)
+ * and the epilogue writes out_blocks[b] (block-major [nnz_max][128][128]):
+ *   NONE      acc
+ *   GELU      gelu(acc); if aux_out != NULL also aux_out[b] = acc (saved H)
+ *   SILU_MUL  silu(acc) * acc2 where acc2 uses b2 in place of b (SwiGLU)
+ *   GELU_BWD  acc * gelu'(aux_in[b])  (aux_in = saved H blocks)
+ * K must be a positive multiple of 64 (bf16) or 32 (fp32).
+ */
+bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, int64_t ldb,
+                   int trans_b, int K, const bsg_topology* topo, int epilogue,
+                   const void* aux_in, void* out_blocks, void* aux_out, int dtype,
+                   bsg_stream_t stream);
+
+/*
+ * dsd - dense = sparse x dense (section 1.2, second layer; walks each block
+ * row through the BCSR row pointer as section 1.3 describes):
+ *   c[128r + m][n] = sum over blocks b of row r, sum_j blocks[b][m][j] *
+ *                    B[128*col_idx[b] + j][n],  n < N,
+ *   trans_b = 0: B[k][n] = b[k*ldb + n]  (b is [E*f, N], e.g. W2)
+ *   trans_b = 1: B[k][n] = b[n*ldb + k]  (b is [N, E*f], e.g. W1 for dgrad)
+ * c is [Tp_max, N] with leading dimension ldc in c_dtype (bf16 or fp32);
+ * rows >= Tp are untouched.  N must be a positive multiple of 128.
+ */
+bsg_status bsg_dsd(const void* blocks, const bsg_topology* topo, const void* b, int64_t ldb,
+                   int trans_b, int N, void* c, int64_t ldc, int c_dtype, int dtype,
+                   bsg_stream_t stream);
+
+/*
+ * dstd - dense = sparse^T x dense, the weight gradient (section 1.3,
+ * "transpose indices": the blocks of each column are visited through
+ * trans_idx, their rows found through row_idx):
+ *   C[128c + m][n] = sum over blocks b of column c, sum_j blocks[b][j][m] *
+ *                    dmat[128*row_idx[b] + j][n],  n < N
+ * dmat is [Tp_max, N] with leading dimension ldd.  trans_c = 0 stores
+ * C at c[(128c + m)*ldc + n] ([E*f, N], e.g. dW2); trans_c = 1 stores it
+ * transposed at c[n*ldc + 128c + m] ([N, E*f], e.g. dW1).  Columns with no
+ * block (experts without tokens) are written as zeros.  N must be a
+ * positive multiple of 128.  The output dtype is dtype.
+ */
+bsg_status bsg_dstd(const void* blocks, const bsg_topology* topo, const void* dmat, int64_t ldd,
+                     int N, void* c, int64_t ldc, int trans_c, int dtype, bsg_stream_t stream);
+
+/*
+ * unpermute_combine - undo the permutation and combine the k expert
+ * outputs of each token (the inverse of the layout transform of
+ * section 1.4):  y[t][m] = sum_{j<k} gate[t*k+j] * yp[dest_row[t*k+j]][m],
+ * accumulated in fp32 in ascending j and rounded once to y_dtype;
+ * gate == NULL means every gate is 1 (input-gradient combine).
+ *   yp [Tp_max, d] (yp_dtype, leading dimension ld_yp), y [T, d] (y_dtype).
+ */
+bsg_status bsg_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
+                                 const int32_t* dest_row, const float* gate, int64_t T, int k,
+                                 int d, void* y, int y_dtype, bsg_stream_t stream);
+
+/* Static description of a status code. */
+const char* bsg_status_string(bsg_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* bsg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSG_H */

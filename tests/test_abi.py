@@ -1,0 +1,185 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, answers the size queries with their closed forms, and
+rejects bad arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_sparse_gemm_amd import bsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsg.h")
+
+P = C.c_void_p(0x10000)       # a fake, aligned, non-null pointer: never dereferenced
+MIS = C.c_void_p(0x10004)     # 4-byte but not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bsg.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bsg_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(bsg.SYMBOLS) == set(syms)
+
+
+def test_size_queries(L):
+    for T, k, E in [(1, 1, 1), (256, 1, 4), (16384, 1, 64), (32768, 1, 64), (8192, 2, 8),
+                    (65536, 2, 64), (3, 2, 64)]:
+        A = T * k
+        want = (A + 127 * min(E, A)) // 128 * 128
+        assert bsg.max_padded_rows(T, k, E) == want
+    assert bsg.max_padded_rows(0, 1, 1) == -1
+    assert bsg.max_padded_rows(4, 3, 2) == -1
+    s = bsg.topology_sizes(139136, 64, 4096)
+    assert (s.row_blocks_max, s.nnz_max, s.n_cols) == (1087, 1087 * 32, 64 * 32)
+    assert bsg.route_workspace_bytes(65536, 2, 64) == 1024 * 64 * 4
+    assert bsg.route_workspace_bytes(65, 1, 3) == 2 * 3 * 4
+    assert bsg.route_workspace_bytes(10, 3, 2) == 0
+    with pytest.raises(bsg.BsgError):
+        bsg.topology_sizes(100, 4, 256)
+    with pytest.raises(bsg.BsgError):
+        bsg.topology_sizes(1280, 4, 200)
+
+
+def _err(L):
+    return L.bsg_last_error().decode()
+
+
+def test_route_validation(L):
+    ws = 1 << 20
+    ok_args = [P, 100, 8, 2, 0, P, P, P, P, P, P, ws, None]
+
+    def call(**over):
+        a = list(ok_args)
+        names = ["logits", "T", "E", "k", "renorm", "expert_idx", "gate", "dest_row", "counts",
+                 "bin_offsets", "ws", "wsb", "stream"]
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_route(*a)
+
+    assert call(logits=None) == bsg.EINVAL
+    assert call(T=0) == bsg.EINVAL
+    assert call(E=0) == bsg.EINVAL
+    assert call(E=2000) == bsg.EINVAL
+    assert call(k=9) == bsg.EINVAL
+    assert call(k=0) == bsg.EINVAL
+    assert call(E=64, k=40) == bsg.EUNSUPPORTED
+    assert call(gate=None) == bsg.EINVAL
+    assert call(ws=None) == bsg.EINVAL
+    assert call(wsb=4) == bsg.EINVAL and "workspace" in _err(L)
+    assert call(counts=C.c_void_p(0x10002)) == bsg.EINVAL
+
+
+def test_permute_pad_validation(L):
+    T, d, k, E = 100, 128, 2, 8
+    Tp = bsg.max_padded_rows(T, k, E)
+    base = [P, bsg.BF16, T, d, k, P, None, P, P, E, Tp, P, P, None]
+    assert L.bsg_permute_pad(*[None if i == 0 else v for i, v in enumerate(base)]) == bsg.EINVAL
+    b = list(base); b[1] = 7
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL
+    b = list(base); b[3] = 100  # 200 bytes per row: not 16-byte aligned rows
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL
+    b = list(base); b[10] = Tp - 128
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL and "Tp_max" in _err(L)
+    b = list(base); b[12] = MIS
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL
+    b = list(base); b[4] = 9
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL
+
+
+def fake_topo(E=4, f=256, Tp=1024, **over):
+    t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, E, f // 128, Tp)
+    for k, v in over.items():
+        setattr(t, k, v)
+    return t
+
+
+def test_build_topology_validation(L):
+    t = fake_topo()
+    assert L.bsg_build_topology(None, 4, 256, 1024, C.byref(t), None) == bsg.EINVAL
+    assert L.bsg_build_topology(P, 4, 256, 1024, None, None) == bsg.EINVAL
+    assert L.bsg_build_topology(P, 4, 200, 1024, C.byref(t), None) == bsg.EINVAL
+    assert L.bsg_build_topology(P, 5, 256, 1024, C.byref(t), None) == bsg.EINVAL
+    assert "capacity" in _err(L)
+    t2 = fake_topo(row_idx=None)
+    assert L.bsg_build_topology(P, 4, 256, 1024, C.byref(t2), None) == bsg.EINVAL
+    t3 = fake_topo(Tp=1000)
+    assert L.bsg_build_topology(P, 4, 256, 1000, C.byref(t3), None) == bsg.EINVAL
+
+
+def test_sdd_validation(L):
+    t = fake_topo(E=4, f=256)
+    ncol = 4 * 256
+
+    def call(a=P, lda=256, b=P, b2=None, ldb=ncol, trans_b=0, K=256, topo=t, epi=bsg.EPI_GELU,
+             aux_in=None, out=P, aux_out=None, dtype=bsg.BF16):
+        return L.bsg_sdd(a, lda, b, b2, ldb, trans_b, K, C.byref(topo) if topo else None, epi,
+                         aux_in, out, aux_out, dtype, None)
+
+    assert call(a=None) == bsg.EINVAL
+    assert call(a=MIS) == bsg.EINVAL
+    assert call(K=100) == bsg.EINVAL
+    assert call(K=96) == bsg.EINVAL          # not a multiple of 64 for bf16
+    assert call(lda=128) == bsg.EINVAL       # lda < K
+    assert call(ldb=512) == bsg.EINVAL       # ldb < E*f for trans_b = 0
+    assert call(trans_b=2) == bsg.EINVAL
+    assert call(epi=9) == bsg.EINVAL
+    assert call(dtype=5) == bsg.EINVAL
+    assert call(topo=None) == bsg.EINVAL
+    assert call(epi=bsg.EPI_SILU_MUL) == bsg.EINVAL               # b2 missing
+    assert call(epi=bsg.EPI_SILU_MUL, b2=P, trans_b=1, ldb=256) == bsg.EUNSUPPORTED
+    assert call(epi=bsg.EPI_GELU_BWD) == bsg.EINVAL               # aux_in missing
+    assert call(epi=bsg.EPI_NONE, aux_in=P) == bsg.EINVAL
+    assert call(epi=bsg.EPI_NONE, aux_out=P) == bsg.EINVAL
+    assert call(epi=bsg.EPI_GELU, b2=P) == bsg.EINVAL
+
+
+def test_dsd_dstd_validation(L):
+    t = fake_topo(E=4, f=256)
+    ncol = 4 * 256
+    assert L.bsg_dsd(P, C.byref(t), P, 256, 0, 200, P, 256, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dsd(P, C.byref(t), P, 128, 0, 256, P, 256, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dsd(P, C.byref(t), P, 256, 1, 256, P, 256, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dsd(P, C.byref(t), P, 256, 0, 256, P, 128, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dsd(P, C.byref(t), P, 256, 0, 256, P, 256, bsg.BF16, bsg.F32,
+                     None) == bsg.EUNSUPPORTED
+    assert L.bsg_dsd(None, C.byref(t), P, 256, 0, 256, P, 256, bsg.BF16, bsg.BF16,
+                     None) == bsg.EINVAL
+    assert L.bsg_dstd(P, C.byref(t), P, 256, 256, P, 256, 1, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dstd(P, C.byref(t), P, 128, 256, P, 256, 0, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dstd(P, C.byref(t), P, 256, 256, P, ncol, 2, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dstd(P, C.byref(t), P, 256, 192, P, 256, 0, bsg.BF16, None) == bsg.EINVAL
+    assert L.bsg_dstd(P, C.byref(t), None, 256, 256, P, 256, 0, bsg.BF16, None) == bsg.EINVAL
+
+
+def test_combine_validation(L):
+    assert L.bsg_unpermute_combine(P, bsg.BF16, 256, P, None, 10, 2, 100, P, bsg.BF16,
+                                   None) == bsg.EINVAL
+    assert L.bsg_unpermute_combine(P, bsg.BF16, 64, P, None, 10, 2, 128, P, bsg.BF16,
+                                   None) == bsg.EINVAL
+    assert L.bsg_unpermute_combine(None, bsg.BF16, 128, P, None, 10, 2, 128, P, bsg.BF16,
+                                   None) == bsg.EINVAL
+    assert L.bsg_unpermute_combine(P, 3, 128, P, None, 10, 2, 128, P, bsg.BF16,
+                                   None) == bsg.EINVAL
+    assert L.bsg_unpermute_combine(P, bsg.BF16, 128, P, None, 10, 40, 128, P, bsg.BF16,
+                                   None) == bsg.EINVAL
+
+
+def test_status_strings(L):
+    assert L.bsg_status_string(0) == b"ok"
+    assert L.bsg_status_string(-1) == b"invalid argument"
+    assert L.bsg_status_string(-2) == b"unsupported combination"
+    assert L.bsg_status_string(-3) == b"HIP runtime error"
+    assert L.bsg_status_string(7) == b"unknown status"

@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: integer outputs (routing, bins, placement, row_src, topology, the
+permuted copy Xp, the scaled copy dYp) bit-exact; bf16 floats within
+|gpu - oracle| <= 1e-2 * max(1, |oracle|) elementwise (plus a reported
+self-check max|d| / max|o|); fp32 floats within max|d| <= 1e-4 * max|o| per
+tensor.  Small cases compare every element; the five full-size workloads
+compare every integer output and sampled float outputs (sampled tokens,
+assignments and weight-gradient entries, chosen to include the smallest
+and largest experts and the first and last token).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-2
+F32_TOL = 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def check_float(name, got, want, dtype, report):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    d = np.abs(got - want)
+    scale = max(np.max(np.abs(want)), 1e-30) if want.size else 1.0
+    rel = float(np.max(d) / scale) if want.size else 0.0
+    report[name] = rel
+    if dtype == "bf16":
+        bad = d > BF16_TOL * np.maximum(1.0, np.abs(want))
+        assert not bad.any(), f"{name}: {bad.sum()} elements out of tolerance, max|d|={d.max()}"
+        assert rel <= 1e-2, f"{name}: self-check max|d|/max|o| = {rel}"
+    else:
+        assert np.max(d) <= F32_TOL * scale, f"{name}: max|d|={d.max()} vs {F32_TOL * scale}"
+
+
+@dataclasses.dataclass
+class Case:
+    cfg: synth.LayerConfig
+    logits: np.ndarray = None      # override of the drawn logits
+    n_tokens: int = 0              # 0 = every token
+    n_wgrad: int = 0               # 0 = every weight-gradient entry
+
+
+def make_case_inputs(case: Case, seed=0):
+    inp = synth.make_inputs(case.cfg, seed)
+    if case.logits is not None:
+        inp["logits"] = np.ascontiguousarray(case.logits, np.float32)
+    return inp
+
+
+def run_gpu(cfg, inp):
+    from block_sparse_gemm_amd import layer
+    s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
+                    cfg.backward)
+    L = layer.Layer(s)
+    up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
+    x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    L.forward(x, logits, W1, W2, W3)
+    if cfg.backward:
+        L.backward(dy, W1, W2)
+    torch.cuda.synchronize()
+    return L, dict(x=x, W1=W1, W2=W2, W3=W3, dy=dy, logits=logits)
+
+
+def sample_assignments(cfg, r, n_tokens, seed=1):
+    if n_tokens == 0 or n_tokens >= cfg.T:
+        toks = np.arange(cfg.T)
+    else:
+        toks = synth.sample_tokens(cfg.T, n_tokens, seed)
+        # add a token of the smallest non-empty and of the largest expert
+        ei = r["expert_idx"]
+        counts = r["counts"]
+        nz = np.nonzero(counts)[0]
+        for e in (nz[np.argmin(counts[nz])], int(np.argmax(counts))):
+            a = int(np.nonzero(ei == e)[0][-1])
+            toks = np.union1d(toks, [a // cfg.k])
+    assigns = (toks[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
+    return toks.astype(np.int64), assigns.astype(np.int64)
+
+
+def wgrad_samples(cfg, r, n, seed=2):
+    rng = np.random.default_rng(seed)
+    Ef = cfg.E * cfg.f
+    if n == 0:
+        return np.arange(Ef), np.arange(cfg.d)
+    # rows of dW2 (columns of dW1): include the smallest, the largest and an
+    # empty expert when there is one
+    counts = r["counts"]
+    ex = [int(np.argmin(counts)), int(np.argmax(counts))]
+    rows = set(rng.choice(Ef, size=n, replace=False).tolist())
+    for e in ex:
+        rows.update([e * cfg.f, e * cfg.f + cfg.f - 1])
+    cols = set(rng.choice(cfg.d, size=min(n, cfg.d), replace=False).tolist()) | {0, cfg.d - 1}
+    return np.array(sorted(rows)), np.array(sorted(cols))
+
+
+def check_case(orc, case: Case, seed=0):
+    cfg = case.cfg
+    _say(f"[parity] case {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} k={cfg.k} "
+         f"act={cfg.act} dtype={cfg.dtype} bwd={cfg.backward} seed={seed}")
+    inp = make_case_inputs(case, seed)
+    L, dev = run_gpu(cfg, inp)
+    from block_sparse_gemm_amd import layer
+    f64 = layer.to_numpy_f64
+    report = {}
+
+    # ---- routing, bins, placement: bit-exact
+    r = orc.route(inp["logits"], cfg.k, cfg.renorm)
+    for key, t in (("expert_idx", L.expert_idx), ("dest_row", L.dest_row), ("counts", L.counts),
+                   ("bin_offsets", L.bin_offsets)):
+        assert np.array_equal(t.cpu().numpy(), r[key]), key
+    g = L.gate.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(g - r["gate"]) <= 1e-5 * np.abs(r["gate"]) + 1e-12), "gate"
+    Tp = int(r["bin_offsets"][cfg.E])
+    assert np.array_equal(L.row_src[:Tp].cpu().numpy(), r["row_src"]), "row_src"
+
+    # ---- topology: bit-exact
+    F = cfg.f // 128
+    t = orc.topology(r["bin_offsets"], cfg.E, F)
+    nnz, R = t["nnz"], Tp // 128
+    meta = L.topo.meta.cpu().numpy()
+    assert meta[0] == nnz and meta[1] == R
+    assert np.array_equal(L.topo.row_ptr[:R + 1].cpu().numpy(), t["row_ptr"])
+    assert np.all(L.topo.row_ptr[R + 1:].cpu().numpy() == nnz)
+    for key in ("col_idx", "row_idx", "trans_idx"):
+        assert np.array_equal(getattr(L.topo, key)[:nnz].cpu().numpy(), t[key]), key
+    assert np.array_equal(L.topo.col_ptr.cpu().numpy(), t["col_ptr"]), "col_ptr"
+
+    # ---- permuted, padded copy: bit-exact
+    prec = cfg.dtype
+    xp_want = orc.permute_pad(inp["x"].values, cfg.k, r["dest_row"], Tp, prec=prec)
+    assert np.array_equal(f64(L.xp[:Tp]), xp_want), "xp"
+    del xp_want
+
+    # ---- forward floats
+    toks, assigns = sample_assignments(cfg, r, case.n_tokens)
+    O = orc.make_layer(inp["x"].values, inp["W1"].values, inp["W2"].values, r, cfg.k, cfg.E,
+                       act=cfg.act, W3=inp["W3"].values if "W3" in inp else None,
+                       dy=inp["dy"].values if "dy" in inp else None, prec=prec, prec_yp=cfg.yp)
+    H, A, Yp = O.assign_forward(assigns)
+    rows = torch.from_numpy(r["dest_row"][assigns]).cuda()
+    check_float("A", f64(L.sparse_rows(L.act, rows)), A, prec, report)
+    if cfg.backward:
+        check_float("H", f64(L.sparse_rows(L.h, rows)), H, prec, report)
+    check_float("Yp", f64(L.yp[rows.long()]), Yp, cfg.yp if prec == "bf16" else prec, report)
+    check_float("y", f64(L.y[torch.from_numpy(toks).cuda()]), O.forward_tokens(toks), prec,
+                report)
+    # pad rows of A and Yp are exactly zero
+    pad = torch.from_numpy(np.nonzero(r["row_src"] < 0)[0]).cuda()
+    if len(pad):
+        assert torch.count_nonzero(L.yp[pad.long()]).item() == 0, "Yp pad rows"
+        assert torch.count_nonzero(L.sparse_rows(L.act, pad)).item() == 0, "A pad rows"
+
+    # ---- backward floats
+    if cfg.backward:
+        dYp, dH, dXp = O.assign_backward(assigns)
+        assert np.array_equal(f64(L.dyp[rows.long()]), dYp), "dYp (bit-exact scaled copy)"
+        check_float("dH", f64(L.sparse_rows(L.dh, rows)), dH, prec, report)
+        check_float("dXp", f64(L.dxp[rows.long()]), dXp, cfg.yp if prec == "bf16" else prec,
+                    report)
+        check_float("dx", f64(L.dx[torch.from_numpy(toks).cuda()]), O.backward_tokens(toks),
+                    prec, report)
+        wr, wc = wgrad_samples(cfg, r, case.n_wgrad)
+        got = f64(L.dW2[torch.from_numpy(wr).cuda()][:, torch.from_numpy(wc).cuda()])
+        check_float("dW2", got, O.dW2_block(wr, wc), prec, report)
+        # dW1 [d, E*f]: rows = model dims, cols = expert hidden units
+        got1 = f64(L.dW1[torch.from_numpy(wc).cuda()][:, torch.from_numpy(wr).cuda()])
+        check_float("dW1", got1, O.dW1_block(wc, wr), prec, report)
+        empty = np.nonzero(r["counts"] == 0)[0]
+        for e in empty:  # experts without tokens: exactly zero weight gradients
+            assert torch.count_nonzero(L.dW2[e * cfg.f:(e + 1) * cfg.f]).item() == 0
+            assert torch.count_nonzero(L.dW1[:, e * cfg.f:(e + 1) * cfg.f]).item() == 0
+    _say(f"[parity] {cfg.name} ok; max|d|/max|o|: " +
+         ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
+    return L, dev, inp
+
+
+# ------------------------------------------------------------ small cases
+
+def _small(name, **kw):
+    base = dict(T=1000, d=256, E=5, f=384, k=2, act="gelu", dtype="bf16", backward=True)
+    base.update(kw)
+    return synth.LayerConfig(name, **base)
+
+
+def _assign_logits(T, E, experts):
+    """Logits that send token t to experts[t] (top-1): 8 for the pick, 0 else."""
+    lg = np.zeros((T, E), np.float32)
+    lg[np.arange(T), experts] = 8.0
+    return lg
+
+
+SMALL = {
+    # several tiles and a ragged tail; F = 3 (odd: one block per SDD tile)
+    "ragged_bf16": Case(_small("ragged_bf16")),
+    "ragged_f32": Case(_small("ragged_f32", dtype="f32", x_std=0.5)),
+    # F = 2 (pairs of blocks per SDD tile), N not a multiple of 256
+    "pairs_bf16": Case(_small("pairs_bf16", T=700, d=384, E=3, f=256, k=1)),
+    "d_f_128": Case(_small("d_f_128", T=300, d=128, E=3, f=128, k=1)),
+    "k_equals_E": Case(_small("k_equals_E", T=200, d=128, E=4, f=256, k=4)),
+    "swiglu_small": Case(_small("swiglu_small", T=500, d=256, E=4, f=256, k=2, act="swiglu",
+                                renorm=True, yp_dtype="f32", backward=False)),
+    "swiglu_f32": Case(_small("swiglu_f32", T=300, d=128, E=3, f=256, k=2, act="swiglu",
+                              dtype="f32", renorm=True, backward=False, x_std=0.5)),
+}
+
+
+def _edge_cases():
+    cases = {}
+    # an expert that receives no token (dW must be zero, DSTD writes zeros)
+    cfg = _small("empty_expert", T=400, d=128, E=6, f=256, k=1)
+    lg = np.random.default_rng(3).standard_normal((400, 6)).astype(np.float32)
+    lg[:, 3] = -50.0
+    cases["empty_expert"] = Case(cfg, logits=lg)
+    # every token on one expert
+    cfg = _small("one_expert", T=300, d=128, E=4, f=256, k=1)
+    cases["one_expert"] = Case(cfg, logits=_assign_logits(300, 4, np.zeros(300, int)))
+    # counts that are exact multiples of 128: no pad rows at all
+    cfg = _small("no_padding", T=512, d=128, E=4, f=256, k=1)
+    cases["no_padding"] = Case(cfg, logits=_assign_logits(512, 4, np.arange(512) // 128))
+    # counts 1, 127, 128, 129
+    ex = np.repeat(np.arange(4), [1, 127, 128, 129])
+    cfg = _small("counts_1_127_128_129", T=385, d=128, E=4, f=128, k=1)
+    cases["counts_1_127_128_129"] = Case(cfg, logits=_assign_logits(385, 4, ex))
+    # ties in the logits (lower id wins)
+    cfg = _small("ties", T=256, d=128, E=8, f=128, k=2)
+    lg = np.random.default_rng(4).integers(-2, 3, size=(256, 8)).astype(np.float32)
+    cases["ties"] = Case(cfg, logits=lg)
+    return cases
+
+
+EDGE = _edge_cases()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small(orc, name):
+    check_case(orc, SMALL[name])
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge(orc, name):
+    check_case(orc, EDGE[name])
+
+
+def test_deterministic(orc):
+    """No atomics in the float path: two runs give bitwise identical outputs."""
+    cfg = _small("determinism", T=700, d=256, E=5, f=256, k=2)
+    inp = synth.make_inputs(cfg, 5)
+    L1, _ = run_gpu(cfg, inp)
+    L2, _ = run_gpu(cfg, inp)
+    for name in ("y", "dx", "dW1", "dW2", "act", "dest_row"):
+        assert torch.equal(getattr(L1, name), getattr(L2, name)), name
+
+
+# ------------------------------------------------------ full-size workloads
+
+FULL = {
+    "tiny": Case(synth.CONFIGS["tiny"]),
+    "moe_xs": Case(synth.CONFIGS["moe_xs"], n_tokens=96),
+    "moe_small": Case(synth.CONFIGS["moe_small"], n_tokens=64, n_wgrad=24),
+    "mixtral": Case(synth.CONFIGS["mixtral"], n_tokens=12),
+    "skew": Case(synth.CONFIGS["skew"], n_tokens=32, n_wgrad=16),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size(orc, name):
+    check_case(orc, FULL[name])
