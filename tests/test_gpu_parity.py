@@ -153,7 +153,9 @@ def check_case(orc, case: Case, seed=0):
     check_float("A", f64(L.sparse_rows(L.act, rows)), A, prec, report)
     if cfg.backward:
         check_float("H", f64(L.sparse_rows(L.h, rows)), H, prec, report)
-    check_float("Yp", f64(L.yp[rows.long()]), Yp, cfg.yp if prec == "bf16" else prec, report)
+    # the bar follows the workload's arithmetic (bf16 operands, fp32
+    # accumulation) even where Yp is stored in fp32
+    check_float("Yp", f64(L.yp[rows.long()]), Yp, prec, report)
     check_float("y", f64(L.y[torch.from_numpy(toks).cuda()]), O.forward_tokens(toks), prec,
                 report)
     # pad rows of A and Yp are exactly zero
@@ -165,10 +167,13 @@ def check_case(orc, case: Case, seed=0):
     # ---- backward floats
     if cfg.backward:
         dYp, dH, dXp = O.assign_backward(assigns)
-        assert np.array_equal(f64(L.dyp[rows.long()]), dYp), "dYp (bit-exact scaled copy)"
+        # dYp = rd(gate * dy) uses each side's own gate (compared with a
+        # tolerance above), so it is a float comparison here; the scaled copy
+        # itself is checked bit-exact with a shared scale in
+        # test_permute_pad_scaled_exact
+        check_float("dYp", f64(L.dyp[rows.long()]), dYp, prec, report)
         check_float("dH", f64(L.sparse_rows(L.dh, rows)), dH, prec, report)
-        check_float("dXp", f64(L.dxp[rows.long()]), dXp, cfg.yp if prec == "bf16" else prec,
-                    report)
+        check_float("dXp", f64(L.dxp[rows.long()]), dXp, prec, report)
         check_float("dx", f64(L.dx[torch.from_numpy(toks).cuda()]), O.backward_tokens(toks),
                     prec, report)
         wr, wc = wgrad_samples(cfg, r, case.n_wgrad)
@@ -277,3 +282,29 @@ FULL = {
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size(orc, name):
     check_case(orc, FULL[name])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_permute_pad_scaled_exact(orc, dtype):
+    """The scaled permutation rounds the exact product once: bit-exact
+    against the oracle when both get the same (seeded) scale."""
+    from block_sparse_gemm_amd import bsg, layer
+    cfg = _small("scaled", T=900, d=384, E=7, f=128, k=3, dtype=dtype)
+    inp = synth.make_inputs(cfg, 9, weights=False)
+    rng = np.random.default_rng(11)
+    scale = (rng.standard_normal(cfg.T * cfg.k) * 0.3).astype(np.float32)
+    r = orc.route(inp["logits"], cfg.k)
+    Tp = int(r["bin_offsets"][cfg.E])
+    Tp_max = bsg.max_padded_rows(cfg.T, cfg.k, cfg.E)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = layer.from_numpy(inp["x"], dtype)
+    xp = torch.full((Tp_max, cfg.d), 7.0, dtype=x.dtype, device="cuda")
+    row_src = torch.full((Tp_max,), 99, dtype=torch.int32, device="cuda")
+    bsg.permute_pad(x, cfg.k, dev(r["dest_row"]), dev(scale), dev(r["counts"]),
+                    dev(r["bin_offsets"]), cfg.E, Tp_max, row_src, xp)
+    torch.cuda.synchronize()
+    want = orc.permute_pad(inp["x"].values, cfg.k, r["dest_row"], Tp, scale=scale, prec=dtype)
+    assert np.array_equal(layer.to_numpy_f64(xp[:Tp]), want)
+    assert np.array_equal(row_src[:Tp].cpu().numpy(), r["row_src"])
+    # rows at and beyond Tp are untouched
+    assert torch.all(xp[Tp:] == 7.0).item() and torch.all(row_src[Tp:] == 99).item()
