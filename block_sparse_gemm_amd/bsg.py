@@ -39,12 +39,14 @@ class BsgError(RuntimeError):
 
 
 class TopoSizes(C.Structure):
-    _fields_ = [("row_blocks_max", C.c_int64), ("nnz_max", C.c_int64), ("n_cols", C.c_int64)]
+    _fields_ = [("row_blocks_max", C.c_int64), ("nnz_max", C.c_int64), ("n_cols", C.c_int64),
+                ("row_pairs_max", C.c_int64)]
 
 
 class TopologyStruct(C.Structure):
     _fields_ = [("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("row_idx", C.c_void_p),
-                ("col_ptr", C.c_void_p), ("trans_idx", C.c_void_p), ("meta", C.c_void_p),
+                ("col_ptr", C.c_void_p), ("trans_idx", C.c_void_p), ("row_pairs", C.c_void_p),
+                ("meta", C.c_void_p),
                 ("E", C.c_int32), ("F", C.c_int32), ("Tp_max", C.c_int64)]
 
 
@@ -154,11 +156,13 @@ class Topology:
         self.row_idx = torch.zeros(self.nnz_max, **i32)
         self.col_ptr = torch.zeros(E * self.F + 1, **i32)
         self.trans_idx = torch.zeros(self.nnz_max, **i32)
+        self.row_pairs_max = int(sz.row_pairs_max)
+        self.row_pairs = torch.zeros(self.row_pairs_max, **i32)
         self.meta = torch.zeros(4, **i32)
         self.struct = TopologyStruct(self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
                                      self.row_idx.data_ptr(), self.col_ptr.data_ptr(),
-                                     self.trans_idx.data_ptr(), self.meta.data_ptr(), E, self.F,
-                                     Tp_max)
+                                     self.trans_idx.data_ptr(), self.row_pairs.data_ptr(),
+                                     self.meta.data_ptr(), E, self.F, Tp_max)
 
 
 # ------------------------------------------------------------------- calls

@@ -54,13 +54,22 @@ bsg_status check_topology(const bsg_topology* t) {
     REQUIRE(t->Tp_max >= BSG_BLOCK && t->Tp_max % BSG_BLOCK == 0,
             "topo->Tp_max must be a positive multiple of 128");
     REQUIRE((t->Tp_max / BSG_BLOCK) * (int64_t)t->F < INT32_MAX, "too many blocks for int32 ids");
+    if (t->Tp_max / BSG_BLOCK > bsg::kMaxTileBlocks || t->F > bsg::kMaxTileBlocks)
+        return fail(BSG_EUNSUPPORTED, "more than %d blocks per block row or column",
+                    bsg::kMaxTileBlocks);
     REQUIRE_PTR(t->row_ptr);
     REQUIRE_PTR(t->col_idx);
     REQUIRE_PTR(t->row_idx);
     REQUIRE_PTR(t->col_ptr);
     REQUIRE_PTR(t->trans_idx);
+    REQUIRE_PTR(t->row_pairs);
     REQUIRE_PTR(t->meta);
     return BSG_OK;
+}
+
+int64_t row_pairs_max(int64_t row_blocks_max, int E) {
+    const int64_t ne = E < row_blocks_max ? E : row_blocks_max;
+    return (row_blocks_max + ne + 1) / 2;
 }
 
 }  // namespace
@@ -96,6 +105,7 @@ bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out)
     out->row_blocks_max = Tp_max / BSG_BLOCK;
     out->nnz_max = out->row_blocks_max * F;
     out->n_cols = (int64_t)E * F;
+    out->row_pairs_max = row_pairs_max(out->row_blocks_max, E);
     REQUIRE(out->nnz_max < INT32_MAX && out->n_cols < INT32_MAX, "too many blocks for int32 ids");
     return ok();
 }
@@ -163,9 +173,10 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
     REQUIRE(topo->E == E && topo->F == f / BSG_BLOCK && topo->Tp_max == Tp_max,
             "topo capacity does not match E, f, Tp_max");
     return hip_status(
-        bsg::launch_build_topology(bin_offsets, E, topo->F, Tp_max / BSG_BLOCK, topo->row_ptr,
+        bsg::launch_build_topology(bin_offsets, E, topo->F, Tp_max / BSG_BLOCK,
+                                   row_pairs_max(Tp_max / BSG_BLOCK, E), topo->row_ptr,
                                    topo->col_idx, topo->row_idx, topo->col_ptr, topo->trans_idx,
-                                   topo->meta, (hipStream_t)stream),
+                                   topo->row_pairs, topo->meta, (hipStream_t)stream),
         "build_topology");
 }
 
@@ -176,8 +187,10 @@ static bsg::GemmParams gemm_params(const bsg_topology* t) {
     p.row_idx = t->row_idx;
     p.col_ptr = t->col_ptr;
     p.trans_idx = t->trans_idx;
+    p.row_pairs = t->row_pairs;
     p.meta = t->meta;
-    p.ncols = t->E * t->F;
+    p.E = t->E;
+    p.F = t->F;
     return p;
 }
 
@@ -219,8 +232,8 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     p.lda = lda;
     p.ldb = ldb;
     p.K = K;
-    const int64_t nnz_max = (topo->Tp_max / BSG_BLOCK) * topo->F;
-    return hip_status(bsg::launch_sdd(p, nnz_max, topo->F, trans_b, epilogue, dtype, (hipStream_t)stream),
+    return hip_status(bsg::launch_sdd(p, row_pairs_max(topo->Tp_max / BSG_BLOCK, topo->E), trans_b,
+                                      epilogue, dtype, (hipStream_t)stream),
                       "sdd");
 }
 
@@ -250,8 +263,8 @@ bsg_status bsg_dsd(const void* blocks, const bsg_topology* topo, const void* b, 
     p.ldc = ldc;
     p.N = N;
     p.ntn = (N + 255) / 256;
-    return hip_status(bsg::launch_dsd(p, topo->Tp_max / BSG_BLOCK, trans_b, c_dtype, dtype,
-                                      (hipStream_t)stream),
+    return hip_status(bsg::launch_dsd(p, row_pairs_max(topo->Tp_max / BSG_BLOCK, topo->E), trans_b,
+                                      c_dtype, dtype, (hipStream_t)stream),
                       "dsd");
 }
 

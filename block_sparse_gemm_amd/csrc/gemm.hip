@@ -2,183 +2,172 @@
 //
 // George Lin's Blog (MegaBlocks/FlexMoE post):
 //  - section 1.2: one block-sparse product replaces the per-expert batched
-//    GEMMs; the first layer is SDD (a dense x dense product sampled at the
+//    GEMMs; the first layer is SDD (a dense x dense product kept only at the
 //    nonzero blocks), then the activation, then DSD (sparse x dense);
 //  - section 1.3: 128 x 128 blocks; BCSR walks a block row in order (DSD),
-//    the materialised row index gives random access to any block (SDD),
-//    and the transpose index lists each column's blocks for DSTD, the
-//    weight gradient (sparse^T x dense).
+//    the materialised row index gives random access to any block, and the
+//    transpose index lists each block column's blocks for DSTD, the weight
+//    gradient (sparse^T x dense).
 //
-// One kernel template serves all three.  A workgroup (256 threads = 4
-// wave64s) computes a 128 x 256 output tile with v_mfma_f32_32x32x16_bf16
+// One kernel template serves all three.  A workgroup of 4 wave64s computes
+// a 256 x 256 output tile (2 x 2 panels of 128); each wave owns one 128 x 128
+// quadrant as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators held in AGPRs
 // (fp32 operands: v_mfma_f32_32x32x2_f32), fp32 accumulation:
-//   SDD   two consecutive nonzero blocks of one block row (random access
-//         through row_idx), K = d, B columns from col_idx;
-//   DSD   one block row x 256 output columns, K walks the row's blocks via
-//         row_ptr / col_idx;
-//   DSTD  one block column x 256 output columns, K walks the column's
-//         blocks via col_ptr / trans_idx, their rows via row_idx.
-// Operands are staged through LDS in 128-byte rows (64 bf16 or 32 fp32 of
-// K per row), K-contiguous, with an XOR swizzle of the 16-byte chunks so
-// that both the 16-byte fragment reads and the stores are bank-conflict
-// free.  Operands whose contiguous dimension is M or N are transposed in
-// registers (8 x 8 bf16 / 4 x 4 fp32) on their way into LDS.  Global loads
-// for K-tile i+1 are in flight while the matrix cores work on K-tile i.
+//   SDD   a pair of block rows of one expert (same column list) x a pair of
+//         their nonzero blocks; K = d.  Dual-B (SwiGLU): one block of W1 and
+//         the same block of W3 side by side, combined as silu(g) * u.
+//   DSD   a pair of block rows x 256 output columns; K walks the rows'
+//         blocks through row_ptr, their weight rows through col_idx.
+//   DSTD  a pair of block columns x 256 output columns; K walks the
+//         columns' blocks through col_ptr / trans_idx, and their dense rows
+//         through row_idx.
 //
-// The MFMA operands are swapped (B fragment first) when the output is
-// row-major: each lane then holds 4 consecutive columns of one output row
-// and writes them with one 8- or 16-byte store.
+// Pipeline.  Operand panels go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register staging) through a ring of kStages
+// stages of 32 KB (K-tile = 64 bytes of K per row), so kStages - 1 K-tiles
+// of loads are in flight.  One barrier per K-tile sits in the middle of the
+// tile: the MFMAs of the first half run, the barrier publishes the next
+// K-tile, and the second half's MFMAs overlap the fragment reads of the
+// next K-tile and the issue of the loads kStages - 1 tiles ahead, so the
+// matrix cores do not wait on LDS latency at a tile boundary.
 //
-// Workgroup ids are remapped so each of the 8 XCDs runs a contiguous range
-// of tiles: consecutive tiles share the A panel (SDD, DSD) or the block
-// column (DSTD), which then stays in that XCD's L2.
+// LDS layouts.  K-contiguous panels are stored row-major (64-byte rows) with
+// an XOR swizzle of the 16-byte chunks and read with ds_read_b128.  Panels
+// contiguous along M or N (W1 and W2 in the forward pass, both operands of
+// DSTD) are stored k-major and read with ds_read_b64_tr_b16, which hands
+// each lane 4 consecutive k of its row: no transpose pass anywhere.
+//
+// Workgroup ids are remapped so each XCD runs a contiguous range of tiles:
+// neighbouring tiles share the A panels (SDD, DSD) or the block columns
+// (DSTD), which then stay in that XCD's L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace bsg {
 
 constexpr int kGemmThreads = 256;
-constexpr int kTileM = 128;
-constexpr int kTileN = 256;
-constexpr int kChunks = 8;  // 16-byte chunks per 128-byte LDS row
-constexpr int kLdsRows = kTileM + kTileN;
+constexpr int kRowBytes = 64;                  // K bytes per row and stage
+constexpr int kPanelBytes = 128 * kRowBytes;   // 8 KB: 128 rows
+constexpr int kSegs = kPanelBytes / 1024;      // 1 KB segments per panel
+constexpr int kStageBytes = 4 * kPanelBytes;   // A0 A1 B0 B1
+constexpr int kStages = 4;
+constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kSegsPerWave = kSegs / 4;          // per panel
+constexpr int kLoadsPerTile = 4 * kSegsPerWave;  // per wave and K-tile
+constexpr int kIdxCap = kMaxTileBlocks;          // K-blocks of one tile staged in LDS
 
 template <int DT>
 struct Elt;
 template <>
 struct Elt<kBf16> {
-    static constexpr int kVec = 8;   // elements per 16 bytes
-    static constexpr int kKt = 64;   // K per LDS row
+    static constexpr int kKt = 32;  // K per stage
     static constexpr int kBytes = 2;
 };
 template <>
 struct Elt<kF32> {
-    static constexpr int kVec = 4;
-    static constexpr int kKt = 32;
+    static constexpr int kKt = 16;
     static constexpr int kBytes = 4;
 };
 
-__device__ __forceinline__ int lds_idx(int row, int q) {
-    return row * kChunks + (q ^ ((row ^ (row >> 3)) & 7));
+typedef __attribute__((address_space(3))) char lds_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ------------------------------------------------------------ LDS layouts
+//
+// K-contiguous panel: 128 rows x 4 chunks of 16 bytes; chunk q of row r at
+// slot 4r + (q ^ ((r >> 2) & 3)): the 16 rows one phase of a fragment read
+// touches fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kslot(int r, int q) { return r * 4 + (q ^ ((r >> 2) & 3)); }
+
+// k-major panel: KT rows of 128 M/N values.  bf16: 16 chunks per row, chunk
+// q of row k at 16k + (q ^ 4(k & 3)), so the 4 k-rows a transposing read
+// touches per 16-lane group use disjoint bank ranges.  fp32: 32 chunks per
+// row, unswizzled.
+template <int DT>
+__device__ __forceinline__ int mnslot(int k, int q) {
+    if constexpr (DT == kBf16) return k * 16 + (q ^ ((k & 3) << 2));
+    else return k * 32 + q;
 }
 
-// ------------------------------------------------------------ LDS loaders
+// Byte offset (from the panel's origin in global memory) of the 16 bytes
+// lane `lane` fetches for segment s of a panel; ld = row stride in bytes.
+// The swizzle is applied here: lane L lands on byte 16 L of its segment.
+template <int DT, bool KC>
+__device__ __forceinline__ int64_t seg_offset(int s, int lane, int64_t ld) {
+    if constexpr (KC) {  // 16 rows of 64 bytes per segment
+        const int row = s * 16 + (lane >> 2);
+        const int q = (lane & 3) ^ ((row >> 2) & 3);
+        return (int64_t)row * ld + q * 16;
+    } else if constexpr (DT == kBf16) {  // 4 k-rows of 256 bytes
+        const int k = s * 4 + (lane >> 4);
+        const int q = (lane & 15) ^ ((k & 3) << 2);
+        return (int64_t)k * ld + q * 16;
+    } else {  // fp32: 2 k-rows of 512 bytes
+        const int k = s * 2 + (lane >> 5);
+        return (int64_t)k * ld + (lane & 31) * 16;
+    }
+}
 
-// NP panels of 128 rows, K contiguous (row stride ld bytes); 4 chunks per
-// thread per panel.
-template <int NP>
-struct KLoader {
-    u32x4 r[4 * NP];
-    __device__ __forceinline__ void load(const char* b0, const char* b1, int64_t ld0, int64_t ld1,
-                                         bool p0, bool p1) {
-        const int q = threadIdx.x & 7, row = threadIdx.x >> 3;
+// Direct global -> LDS load of 16 bytes per lane: lane L's bytes land at
+// LDS byte lds_addr + 16 L (lds_addr is wave-uniform, it goes to M0).  The
+// instruction is issued through inline asm in its SGPR-base form (base +
+// 32-bit lane offset) so the compiler does not model the LDS write: it would
+// otherwise drain every in-flight load (vmcnt(0)) before each LDS read it
+// cannot prove disjoint.  The kernel therefore orders these loads itself:
+// wait_tiles() below, before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const char* base, uint32_t off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"(base)
+                 : "memory");
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const lds_t* p) { return (uint32_t)(uintptr_t)p; }
+
+// -------------------------------------------------------- fragment reads
+//
+// Lane l of a 32 x 32 x 16 MFMA supplies row (l & 31) of its operand with
+// k = 8 (l >> 5) .. + 7 of the current 16.  `r0` is the fragment's first
+// row inside the panel, `c` the K-step (16 bf16 / 8 fp32 values).
+template <int DT, bool KC>
+__device__ __forceinline__ u32x4 frag(const lds_t* panel, int r0, int c) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (KC) {
+        return *(const __attribute__((address_space(3))) u32x4*)(
+            panel + kslot(r0 + (lane & 31), 2 * c + (lane >> 5)) * 16);
+    } else if constexpr (DT == kBf16) {
+        // two transposing reads: within each 16-lane group lane i receives
+        // element i % 4 of the 8 bytes fetched by lanes 4j + i / 4 (j = 0..3),
+        // so lane i addresses row k0 + i / 4, columns n0 + 4 (i % 4) .. + 3
+        const int g = lane >> 4, i = lane & 15;
+        const int n = r0 + 16 * (g & 1) + 4 * (i & 3);
+        const int k = 16 * c + 8 * (g >> 1) + (i >> 2);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(panel + mnslot<DT>(k, n >> 3) * 16 + (n & 7) * 2));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(panel + mnslot<DT>(k + 4, n >> 3) * 16 + (n & 7) * 2));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        return u32x4{a[0], a[1], b[0], b[1]};
+    } else {
+        // fp32 k-major: one element per MFMA step, k = 8c + 4 (l >> 5) + s
+        u32x4 v;
+        const int m = r0 + (lane & 31);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const char* b = p ? b1 : b0;
-            const int64_t ld = p ? ld1 : ld0;
-            if (p ? p1 : p0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    r[4 * p + i] = *(const u32x4*)(b + (int64_t)(row + 32 * i) * ld + q * 16);
-            }
+        for (int s = 0; s < 4; ++s) {
+            const int k = 8 * c + 4 * (lane >> 5) + s;
+            v[s] = *(const __attribute__((address_space(3))) uint32_t*)(panel + (k * 128 + m) * 4);
         }
+        return v;
     }
-    __device__ __forceinline__ void store(u32x4* lds, int row0, bool p0, bool p1) const {
-        const int q = threadIdx.x & 7, row = threadIdx.x >> 3;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            if (p ? p1 : p0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    lds[lds_idx(row0 + 128 * p + row + 32 * i, q)] = r[4 * p + i];
-            }
-        }
-    }
-};
-
-// NP panels of KT k-rows x 128 M/N columns, M/N contiguous (k stride ld
-// bytes).  A thread moves V k-rows x V columns (V = elements per 16 bytes)
-// and transposes them in registers; when there are fewer such blocks than
-// threads, two threads share a block, each taking V/2 of its k-rows.
-template <int DT, int NP>
-struct MNLoader {
-    static constexpr int V = Elt<DT>::kVec;
-    static constexpr int MO = 128 / V;
-    static constexpr int BPP = (Elt<DT>::kKt / V) * MO;  // blocks per panel
-    static constexpr int NB = NP * BPP;
-    static constexpr int SPLIT = NB >= kGemmThreads ? 1 : kGemmThreads / NB;
-    static constexpr int RV = V / SPLIT;                 // k-rows per thread and block
-    static constexpr int NBT = (NB * SPLIT + kGemmThreads - 1) / kGemmThreads;
-    u32x4 r[NBT][RV];
-
-    __device__ __forceinline__ void coords(int s, int& blk, int& sh) const {
-        const int t = threadIdx.x + kGemmThreads * s;
-        blk = t % NB;
-        sh = t / NB;  // which V/SPLIT k-rows of the block (0 when SPLIT == 1)
-    }
-
-    __device__ __forceinline__ void load(const char* b0, const char* b1, int64_t ld0, int64_t ld1,
-                                         bool p0, bool p1) {
-#pragma unroll
-        for (int s = 0; s < NBT; ++s) {
-            int blk, sh;
-            coords(s, blk, sh);
-            const int p = blk / BPP;
-            const int rem = blk % BPP, ko = rem / MO, mo = rem % MO;
-            if (p ? p1 : p0) {
-                const char* b = p ? b1 : b0;
-                const int64_t ld = p ? ld1 : ld0;
-#pragma unroll
-                for (int v = 0; v < RV; ++v)
-                    r[s][v] = *(const u32x4*)(b + (int64_t)(ko * V + sh * RV + v) * ld + mo * 16);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(u32x4* lds, int row0, bool p0, bool p1) const {
-#pragma unroll
-        for (int s = 0; s < NBT; ++s) {
-            int blk, sh;
-            coords(s, blk, sh);
-            const int p = blk / BPP;
-            const int rem = blk % BPP, ko = rem / MO, mo = rem % MO;
-            if (p ? p1 : p0) {
-#pragma unroll
-                for (int m = 0; m < V; ++m) {
-                    u32x4* dst = &lds[lds_idx(row0 + 128 * p + mo * V + m, ko)];
-                    if constexpr (DT == kBf16) {
-                        // dword i of column m = (k = 2i, k = 2i + 1) of this thread's rows
-                        uint32_t w[RV / 2];
-#pragma unroll
-                        for (int i = 0; i < RV / 2; ++i) {
-                            const uint32_t lo = r[s][2 * i][m >> 1], hi = r[s][2 * i + 1][m >> 1];
-                            w[i] = (m & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                           : ((lo & 0xffffu) | (hi << 16));
-                        }
-                        if constexpr (RV == 8)
-                            *dst = u32x4{w[0], w[1], w[2], w[3]};
-                        else
-                            ((u32x2*)dst)[sh] = u32x2{w[0], w[1]};
-                    } else {
-                        static_assert(SPLIT == 1, "fp32 blocks are never split");
-                        *dst = u32x4{r[s][0][m], r[s][1][m], r[s][2][m], r[s][3][m]};
-                    }
-                }
-            }
-        }
-    }
-};
-
-template <int DT, bool KC, int NP>
-struct LoaderSel {
-    using type = KLoader<NP>;
-};
-template <int DT, int NP>
-struct LoaderSel<DT, false, NP> {
-    using type = MNLoader<DT, NP>;
-};
-
-// --------------------------------------------------------------- MFMA step
+}
 
 template <int DT>
 __device__ __forceinline__ void mma(f32x16& acc, u32x4 x, u32x4 y);
@@ -189,8 +178,8 @@ __device__ __forceinline__ void mma<kBf16>(f32x16& acc, u32x4 x, u32x4 y) {
                                                   __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
 }
 
-// fp32: a 16-byte chunk holds 4 K values; lane half h of chunk pair c uses
-// k = 8c + 4h + s in step s, for both operands alike.
+// fp32: a 16-byte K chunk holds 4 consecutive k; lane half h of K-step c
+// uses k = 8c + 4h + s in step s, for both operands alike.
 template <>
 __device__ __forceinline__ void mma<kF32>(f32x16& acc, u32x4 x, u32x4 y) {
 #pragma unroll
@@ -199,7 +188,19 @@ __device__ __forceinline__ void mma<kF32>(f32x16& acc, u32x4 x, u32x4 y) {
                                                    acc, 0, 0, 0);
 }
 
-// ------------------------------------------------------------- epilogues
+// Wait until at most `tiles` K-tiles of this wave's direct loads are still
+// in flight (they retire in issue order); kLoadsPerTile loads per K-tile.
+__device__ __forceinline__ void wait_tiles(int tiles) {
+    switch (tiles) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    }
+}
+static_assert(kLoadsPerTile == 8, "wait_tiles encodes 8 loads per K-tile");
+static_assert(kStages <= 4, "wait_tiles covers up to 2 K-tiles in flight behind the waited one");
+
+// ------------------------------------------------------------- epilogue io
 
 template <int OUT>
 __device__ __forceinline__ void store4(char* dst, const float* v) {
@@ -223,212 +224,312 @@ __device__ __forceinline__ void load4(const char* src, float* v) {
     }
 }
 
-// ----------------------------------------------------------------- kernel
-
-// Block and source row of K-block p (DSD: block of the row and its column;
-// DSTD: block of the column and its row), fetched ahead of use so the index
-// latency hides behind the MFMA work.
-struct BlockIdx {
-    int blk, row;
+// Indices of one K-block for both M halves.
+struct KIdx {
+    int b0, b1;  // block of M half 0 / 1
+    int row;     // DSD: weight row block (column of the block); DSTD: dense row block
 };
 
-// MODE: kModeSdd (pairs of blocks of one row; F even so a pair never
-// straddles two rows), kModeSddOne (one block per tile, also the dual-B
-// SwiGLU form), kModeDsd, kModeDstd.
+// MODE: kModeSdd, kModeSddOne (dual-B SwiGLU: one block per tile),
+// kModeDsd, kModeDstd.  BK: B operand K-contiguous.
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams P) {
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     constexpr int ES = Elt<DT>::kBytes;
     constexpr int KT = Elt<DT>::kKt;
     constexpr int KPB = kBlock / KT;  // K-tiles per block
     constexpr int OES = OUT == kBf16 ? 2 : 4;
-    constexpr bool AK = MODE != kModeDstd;  // A operand K-contiguous?
+    constexpr bool AK = MODE != kModeDstd;
     constexpr bool DUAL = EPI == kEpiSiluMul;
     constexpr bool SDD = MODE == kModeSdd || MODE == kModeSddOne;
-    using ALoad = typename LoaderSel<DT, AK, 1>::type;
-    using BLoad = typename LoaderSel<DT, BK, 2>::type;
+    static_assert(KT / (DT == kBf16 ? 16 : 8) == 2, "two MFMA K-steps per K-tile");
 
-    __shared__ u32x4 lds[kLdsRows * kChunks];
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + 3 * kIdxCap * 4];
+    lds_t* lds = (lds_t*)smem;
 
     // ---- tile count (device-side sizes) and XCD-aware remap
-    const int nnz = P.meta[0];
-    int ntiles;
-    if constexpr (MODE == kModeSdd) ntiles = nnz / 2;
-    else if constexpr (MODE == kModeSddOne) ntiles = nnz;
-    else if constexpr (MODE == kModeDsd) ntiles = P.meta[1] * P.ntn;
-    else ntiles = P.ncols * P.ntn;
+    const int F = P.F;
+    int ntiles, tn;  // tiles, tiles along N
+    if constexpr (MODE == kModeSdd) tn = (F + 1) / 2;
+    else if constexpr (MODE == kModeSddOne) tn = F;
+    else tn = P.ntn;
+    if constexpr (MODE == kModeDstd) ntiles = P.E * ((F + 1) / 2) * tn;
+    else ntiles = P.meta[3] * tn;
     if ((int)blockIdx.x >= ntiles) return;
     const int tile = xcd_remap(blockIdx.x, ntiles);
+    const int tm = tile / tn, tq = tile % tn;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int l32 = lane & 31, lh = lane >> 5;
 
-    // ---- tile -> output rows / blocks
-    int row;          // SDD, DSD: block row; DSTD: block column
-    int blk0 = 0, blk1 = 0;
-    bool bp1;         // second 128-wide half of B / of the output present
-    int nt = 0;
-    if constexpr (MODE == kModeSdd) {
-        blk0 = 2 * tile;
-        blk1 = blk0 + 1;
-        row = P.row_idx[blk0];  // COO row index: random access to any block
-        bp1 = true;
-    } else if constexpr (MODE == kModeSddOne) {
-        blk0 = blk1 = tile;
-        row = P.row_idx[tile];
-        bp1 = DUAL;
+    // ---- the tile's two M halves (block rows, or block columns for DSTD)
+    int mrow0, mrow1;
+    bool m1;
+    if constexpr (MODE == kModeDstd) {
+        const int cpe = (F + 1) / 2;
+        const int e = tm / cpe, j = tm % cpe;
+        mrow0 = e * F + 2 * j;
+        m1 = 2 * j + 1 < F;
     } else {
-        row = tile / P.ntn;
-        nt = tile % P.ntn;
-        bp1 = nt * kTileN + 128 < P.N;
+        const int ent = P.row_pairs[tm];
+        mrow0 = ent >> 1;
+        m1 = (ent & 1) != 0;
     }
-    int bcol0 = 0, bcol1 = 0;
-    if constexpr (SDD) {
-        bcol0 = P.col_idx[blk0];
-        bcol1 = DUAL ? bcol0 : (bp1 ? P.col_idx[blk1] : 0);
+    mrow1 = m1 ? mrow0 + 1 : mrow0;  // an absent half mirrors half 0 (loaded, never stored)
+    // ---- N halves
+    bool n1;
+    int bcol0 = 0, bcol1 = 0;  // SDD: column blocks of B
+    int rp0 = 0, rp1 = 0;      // SDD / DSD: row_ptr of the two rows
+    if constexpr (SDD || MODE == kModeDsd) {
+        rp0 = P.row_ptr[mrow0];
+        rp1 = P.row_ptr[mrow1];
     }
-    // K extent
-    int nk, kbase = 0;
+    if constexpr (MODE == kModeSdd) {
+        const int nr = P.row_ptr[mrow0 + 1] - rp0;
+        n1 = 2 * tq + 1 < nr;
+        bcol0 = P.col_idx[rp0 + 2 * tq];
+        bcol1 = n1 ? P.col_idx[rp0 + 2 * tq + 1] : bcol0;
+    } else if constexpr (MODE == kModeSddOne) {
+        n1 = DUAL;
+        bcol0 = bcol1 = P.col_idx[rp0 + tq];
+    } else {
+        n1 = tq * 256 + 128 < P.N;
+    }
+    const int64_t n0 = (int64_t)tq * 256;
+    const int64_t n1off = n1 ? 128 : 0;  // an absent N half mirrors half 0
+
+    // ---- K extent
+    int nk, cp0 = 0, cp1 = 0;
     if constexpr (SDD) {
         nk = P.K / KT;
     } else if constexpr (MODE == kModeDsd) {
-        kbase = P.row_ptr[row];
-        nk = (P.row_ptr[row + 1] - kbase) * KPB;
+        nk = (P.row_ptr[mrow0 + 1] - rp0) * KPB;
     } else {
-        kbase = P.col_ptr[row];
-        nk = (P.col_ptr[row + 1] - kbase) * KPB;
+        cp0 = P.col_ptr[mrow0];
+        cp1 = P.col_ptr[mrow1];
+        nk = (P.col_ptr[mrow0 + 1] - cp0) * KPB;
     }
     const int nblk = nk / KPB;
+    auto fetch = [&](int p) -> KIdx {
+        KIdx r{0, 0, 0};
+        if constexpr (MODE == kModeDsd) {
+            r.b0 = rp0 + p;
+            r.b1 = rp1 + p;
+            r.row = P.col_idx[r.b0];
+        } else if constexpr (MODE == kModeDstd) {
+            r.b0 = P.trans_idx[cp0 + p];
+            r.b1 = P.trans_idx[cp1 + p];
+            r.row = P.row_idx[r.b0];
+        }
+        return r;
+    };
 
-    auto fetch_blk = [&](int p) -> int {
-        if constexpr (MODE == kModeDsd) return kbase + p;
-        else return P.trans_idx[kbase + p];
-    };
-    auto fetch_row = [&](int b) -> int {
-        if constexpr (MODE == kModeDsd) return P.col_idx[b];
-        else return P.row_idx[b];
-    };
-    BlockIdx cur{0, 0}, nx1{0, 0};
-    int nx2blk = 0;
+    // ---- K-block indices of this tile, staged once in LDS (DSD / DSTD):
+    // block of each M half and its dense row block, read in order per K-tile
+    int* ib0 = (int*)(smem + kLdsBytes);
+    int* ib1 = ib0 + kIdxCap;
+    int* irow = ib1 + kIdxCap;
     if constexpr (!SDD) {
-        if (nblk > 0) {
-            cur.blk = fetch_blk(0);
-            cur.row = fetch_row(cur.blk);
+        for (int p = threadIdx.x; p < nblk; p += kGemmThreads) {
+            const KIdx r = fetch(p);
+            ib0[p] = r.b0;
+            ib1[p] = r.b1;
+            irow[p] = r.row;
         }
-        if (nblk > 1) {
-            nx1.blk = fetch_blk(1);
-            nx1.row = fetch_row(nx1.blk);
-        }
-        if (nblk > 2) nx2blk = fetch_blk(2);
+        __syncthreads();
     }
 
-    f32x16 acc[2][4];
+    // ---- per-lane load offsets (constant over K)
+    const int64_t lda_b = (SDD ? P.lda : kBlock) * ES;  // A row (or k-row) stride
+    const int64_t ldb_b = P.ldb * ES;
+    uint32_t aoff[kSegsPerWave], boff[kSegsPerWave];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < kSegsPerWave; ++j) {
+        const int s = wave * kSegsPerWave + j;
+        aoff[j] = (uint32_t)seg_offset<DT, AK>(s, lane, lda_b);
+        boff[j] = (uint32_t)seg_offset<DT, BK>(s, lane, ldb_b);
+    }
+    // uniform global origins of the four panels of K-tile t
+    struct Bases {
+        const char *a0, *a1, *b0, *b1;
+    };
+    // the K-block indices of K-tile t (DSD / DSTD), read from LDS ahead of use
+    struct TIdx {
+        int b0, b1, row;
+    };
+    auto tidx = [&](int t) -> TIdx {
+        TIdx r{0, 0, 0};
+        if constexpr (!SDD) {
+            const int p = t / KPB;
+            r.b0 = ib0[p];
+            r.b1 = ib1[p];
+            r.row = irow[p];
+        }
+        return r;
+    };
+    auto bases = [&](int t, const TIdx& ti) -> Bases {
+        Bases r;
+        const int koff = (t % KPB) * KT;
+        if constexpr (SDD) {
+            const char* A = (const char*)P.a + (int64_t)t * KT * ES;
+            r.a0 = A + (int64_t)kBlock * mrow0 * P.lda * ES;
+            r.a1 = A + (int64_t)kBlock * mrow1 * P.lda * ES;
+            const char* B1 = DUAL ? (const char*)P.b2 : (const char*)P.b;
+            if constexpr (BK) {
+                r.b0 = (const char*)P.b + ((int64_t)kBlock * bcol0 * P.ldb + (int64_t)t * KT) * ES;
+                r.b1 = B1 + ((int64_t)kBlock * bcol1 * P.ldb + (int64_t)t * KT) * ES;
+            } else {
+                r.b0 = (const char*)P.b + ((int64_t)t * KT * P.ldb + (int64_t)kBlock * bcol0) * ES;
+                r.b1 = B1 + ((int64_t)t * KT * P.ldb + (int64_t)kBlock * bcol1) * ES;
+            }
+        } else {
+            const int blk0 = __builtin_amdgcn_readfirstlane(ti.b0);
+            const int blk1 = __builtin_amdgcn_readfirstlane(ti.b1);
+            const int rowb = __builtin_amdgcn_readfirstlane(ti.row);
+            if constexpr (MODE == kModeDsd) {
+                r.a0 = (const char*)P.a + ((int64_t)blk0 * kBlock * kBlock + koff) * ES;
+                r.a1 = (const char*)P.a + ((int64_t)blk1 * kBlock * kBlock + koff) * ES;
+                const int64_t krow = (int64_t)kBlock * rowb + koff;
+                if constexpr (BK) {
+                    r.b0 = (const char*)P.b + (n0 * P.ldb + krow) * ES;
+                    r.b1 = r.b0 + n1off * P.ldb * ES;
+                } else {
+                    r.b0 = (const char*)P.b + (krow * P.ldb + n0) * ES;
+                    r.b1 = r.b0 + n1off * ES;
+                }
+            } else {  // DSTD: A = block^T (k-major as stored), B = dense rows
+                r.a0 = (const char*)P.a + ((int64_t)blk0 * kBlock * kBlock + (int64_t)koff * kBlock) * ES;
+                r.a1 = (const char*)P.a + ((int64_t)blk1 * kBlock * kBlock + (int64_t)koff * kBlock) * ES;
+                const int64_t drow = (int64_t)kBlock * rowb + koff;
+                r.b0 = (const char*)P.b + (drow * P.ldb + n0) * ES;
+                r.b1 = r.b0 + n1off * ES;
+            }
+        }
+        r.a0 = uniform_ptr(r.a0);
+        r.a1 = uniform_ptr(r.a1);
+        r.b0 = uniform_ptr(r.b0);
+        r.b1 = uniform_ptr(r.b1);
+        return r;
+    };
+    // load j (0..7) of K-tile t into its stage: panel j & 3, segment j >> 2
+    const uint32_t lds0 = lds_u32(lds) + wave * kSegsPerWave * 1024;
+    auto dma = [&](int t, const Bases& b, int j) {
+        const int pnl = j & 3, sg = j >> 2;
+        const uint32_t dst = lds0 + (t % kStages) * kStageBytes + pnl * kPanelBytes + sg * 1024;
+        const char* base = pnl == 0 ? b.a0 : pnl == 1 ? b.a1 : pnl == 2 ? b.b0 : b.b1;
+        dma16(dst, base, pnl < 2 ? aoff[sg] : boff[sg]);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    ALoad la;
-    BLoad lb;
-    // issue the global loads of K-tile kt (block indices in `cur`)
-    auto issue = [&](int kt) {
-        const int koff = (kt % KPB) * KT;
-        if constexpr (SDD) {
-            const char* a = (const char*)P.a + ((int64_t)kBlock * row * P.lda + (int64_t)kt * KT) * ES;
-            la.load(a, a, P.lda * ES, 0, true, false);
-            const char* bs0 = (const char*)P.b;
-            const char* bs1 = DUAL ? (const char*)P.b2 : (const char*)P.b;
-            if constexpr (BK) {
-                const char* p0 = bs0 + ((int64_t)kBlock * bcol0 * P.ldb + (int64_t)kt * KT) * ES;
-                const char* p1 = bs1 + ((int64_t)kBlock * bcol1 * P.ldb + (int64_t)kt * KT) * ES;
-                lb.load(p0, p1, P.ldb * ES, P.ldb * ES, true, bp1);
-            } else {
-                const char* p0 = bs0 + ((int64_t)kt * KT * P.ldb + (int64_t)kBlock * bcol0) * ES;
-                const char* p1 = bs1 + ((int64_t)kt * KT * P.ldb + (int64_t)kBlock * bcol1) * ES;
-                lb.load(p0, p1, P.ldb * ES, P.ldb * ES, true, bp1);
-            }
-        } else if constexpr (MODE == kModeDsd) {
-            const char* a = (const char*)P.a + ((int64_t)cur.blk * kBlock * kBlock + koff) * ES;
-            la.load(a, a, kBlock * ES, 0, true, false);
-            const int64_t krow = (int64_t)kBlock * cur.row + koff;
-            const int64_t n0 = (int64_t)nt * kTileN;
-            if constexpr (BK) {
-                const char* p0 = (const char*)P.b + (n0 * P.ldb + krow) * ES;
-                lb.load(p0, p0 + 128 * P.ldb * ES, P.ldb * ES, P.ldb * ES, true, bp1);
-            } else {
-                const char* p0 = (const char*)P.b + (krow * P.ldb + n0) * ES;
-                lb.load(p0, p0 + 128 * ES, P.ldb * ES, P.ldb * ES, true, bp1);
-            }
-        } else {  // DSTD: A = block^T (M contiguous), B = dmat rows (N contiguous)
-            const char* a = (const char*)P.a +
-                            ((int64_t)cur.blk * kBlock * kBlock + (int64_t)koff * kBlock) * ES;
-            la.load(a, a, kBlock * ES, 0, true, false);
-            const int64_t drow = (int64_t)kBlock * cur.row + koff;
-            const char* p0 = (const char*)P.b + (drow * P.ldb + (int64_t)nt * kTileN) * ES;
-            lb.load(p0, p0 + 128 * ES, P.ldb * ES, P.ldb * ES, true, bp1);
-        }
-    };
-    // before issuing K-tile kt_next: rotate the prefetched block indices
-    auto advance = [&](int kt_next) {
-        if constexpr (!SDD) {
-            if (kt_next % KPB == 0) {
-                const int p = kt_next / KPB;
-                cur = nx1;
-                nx1.blk = nx2blk;
-                if (p + 1 < nblk) nx1.row = fetch_row(nx1.blk);
-                if (p + 2 < nblk) nx2blk = fetch_blk(p + 2);
-            }
-        }
-    };
-
-    const bool active = wn == 0 || bp1;
-    int brow[4];
+    // rows of this wave's fragments inside its panels
+    int bpanel[4], brow[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-        if constexpr (DUAL)  // gate columns in sub-tiles 0,1, up columns in 2,3
-            brow[ni] = kTileM + (ni < 2 ? wn * 64 + 32 * ni : 128 + wn * 64 + 32 * (ni - 2));
-        else
-            brow[ni] = kTileM + wn * 128 + 32 * ni;
+        if constexpr (DUAL) {  // gate columns in sub-tiles 0,1 (panel B0), up in 2,3 (B1)
+            bpanel[ni] = 2 + (ni < 2 ? 0 : 1);
+            brow[ni] = wn * 64 + 32 * (ni & 1);
+        } else {
+            bpanel[ni] = 2 + wn;
+            brow[ni] = 32 * ni;
+        }
+    }
+    // fragment g of K-step c of K-tile t: g < 4 -> A row tile g, else B tile g - 4
+    auto read1 = [&](int t, int c, int g, u32x4* af, u32x4* bf) {
+        const lds_t* st = lds + (t % kStages) * kStageBytes;
+        if (g < 4) af[g] = frag<DT, AK>(st + wm * kPanelBytes, 32 * g, c);
+        else bf[g - 4] = frag<DT, BK>(st + bpanel[g - 4] * kPanelBytes, brow[g - 4], c);
+    };
+    auto mma2 = [&](int g, const u32x4* af, const u32x4* bf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int mi = (2 * g + h) >> 2, ni = (2 * g + h) & 3;
+            if constexpr (SWAP) mma<DT>(acc[mi][ni], bf[ni], af[mi]);
+            else mma<DT>(acc[mi][ni], af[mi], bf[ni]);
+        }
+    };
+
+    // ---- main loop, software pipelined; every wave runs the MFMAs (also a
+    // wave whose half of a half tile is absent: stale data, nothing stored),
+    // so no branch ever sits around the accumulators.
+    //   first half : 16 MFMAs of K-step 0, interleaved with the fragment
+    //                reads of K-step 1 (same K-tile)
+    //   publish    : wait for K-tile kt + 1's loads, barrier
+    //   second half: 16 MFMAs of K-step 1, interleaved with the fragment
+    //                reads of K-step 0 of K-tile kt + 1 and the 8 loads of
+    //                K-tile kt + kStages - 1 (into the stage freed by kt - 1)
+    u32x4 a0f[4], b0f[4], a1f[4], b1f[4];
+    TIdx nti{0, 0, 0};  // indices of the next K-tile to load
+    auto first_half = [&](int kt) {
+        if (kt + kStages - 1 < nk) nti = tidx(kt + kStages - 1);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            read1(kt, 1, g, a1f, b1f);
+            mma2(g, a0f, b0f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto second_half = [&](int kt, bool publish, bool load) {
+        if (publish) {
+            const Bases nb = load ? bases(kt + kStages - 1, nti) : Bases{};
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                read1(kt + 1, 0, g, a0f, b0f);
+                if (load) dma(kt + kStages - 1, nb, g);
+                mma2(g, a1f, b1f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) mma2(g, a1f, b1f);
+        }
+    };
+    if (nk > 0) {
+        for (int t = 0; t < kStages - 1 && t < nk; ++t) {
+            const Bases b = bases(t, tidx(t));
+#pragma unroll
+            for (int j = 0; j < kLoadsPerTile; ++j) dma(t, b, j);
+        }
+        wait_tiles(min(kStages - 2, nk - 1));
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < 8; ++g) read1(0, 0, g, a0f, b0f);
+        int kt = 0;
+        // steady state: publish K-tile kt + 1, load K-tile kt + kStages - 1
+        for (; kt + kStages - 1 < nk; ++kt) {
+            first_half(kt);
+            wait_tiles(kStages - 3);
+            __syncthreads();
+            second_half(kt, true, true);
+        }
+        // tail: publish without new loads
+        for (; kt + 1 < nk; ++kt) {
+            first_half(kt);
+            wait_tiles(min(kStages - 3, nk - 2 - kt));
+            __syncthreads();
+            second_half(kt, true, false);
+        }
+        // last K-tile
+        first_half(kt);
+        second_half(kt, false, false);
     }
 
-    if (nk > 0) issue(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();  // every wave is done reading the previous K-tile
-        la.store(lds, 0, true, false);
-        lb.store(lds, kTileM, true, bp1);
-        __syncthreads();
-        if (kt + 1 < nk) {
-            advance(kt + 1);
-            issue(kt + 1);
-        }
-        if (active) {
-#pragma unroll
-            for (int c = 0; c < kChunks / 2; ++c) {
-                const int q = 2 * c + lh;
-                u32x4 af[2], bf[4];
-#pragma unroll
-                for (int mi = 0; mi < 2; ++mi) af[mi] = lds[lds_idx(wm * 64 + 32 * mi + l32, q)];
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) bf[ni] = lds[lds_idx(brow[ni] + l32, q)];
-#pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        if constexpr (SWAP) mma<DT>(acc[mi][ni], bf[ni], af[mi]);
-                        else mma<DT>(acc[mi][ni], af[mi], bf[ni]);
-                    }
-            }
-        }
-    }
+    const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
     if (!active) return;
 
     // ---- epilogue
-    const int oblk = (MODE == kModeSdd && wn == 1) ? blk1 : blk0;
+    const int mrow = wm ? mrow1 : mrow0;  // this wave's block row / column
+    int oblk = 0;
+    if constexpr (MODE == kModeSdd) oblk = (wm ? rp1 : rp0) + 2 * tq + wn;
+    else if constexpr (MODE == kModeSddOne) oblk = (wm ? rp1 : rp0) + tq;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const int mrow = wm * 64 + 32 * mi;  // first row of the 32 x 32 sub-tile
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
 #pragma unroll
@@ -438,7 +539,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams P) {
                 for (int s = 0; s < 4; ++s) v[s] = acc[mi][ni][4 * g + s];
                 if constexpr (SDD) {
                     // block-major output: (m, n) of block b at b*16384 + m*128 + n
-                    const int m = mrow + l32;
+                    const int m = 32 * mi + l32;
                     int nloc;
                     if constexpr (DUAL) {
                         nloc = wn * 64 + 32 * ni + 8 * g + 4 * lh;
@@ -448,8 +549,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams P) {
                         nloc = 32 * ni + 8 * g + 4 * lh;
                     }
                     const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
-                    if constexpr (EPI == kEpiGelu) {
-                        if (P.aux_out) store4<OUT>((char*)P.aux_out + off * OES, v);
+                    if constexpr (EPI == kEpiGelu || EPI == kEpiGeluSave) {
+                        if constexpr (EPI == kEpiGeluSave)
+                            store4<OUT>((char*)P.aux_out + off * OES, v);
 #pragma unroll
                         for (int s = 0; s < 4; ++s) v[s] = gelu_f(v[s]);
                     } else if constexpr (EPI == kEpiGeluBwd) {
@@ -460,17 +562,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams P) {
                     }
                     store4<OUT>((char*)P.out + off * OES, v);
                 } else if constexpr (SWAP) {  // DSD, or DSTD with row-major C
-                    const int m = mrow + l32;
-                    const int64_t col = (int64_t)nt * kTileN + wn * 128 + 32 * ni + 8 * g + 4 * lh;
-                    const int64_t off = ((int64_t)kBlock * row + m) * P.ldc + col;
+                    const int m = 32 * mi + l32;
+                    const int64_t col = n0 + wn * 128 + 32 * ni + 8 * g + 4 * lh;
+                    const int64_t off = ((int64_t)kBlock * mrow + m) * P.ldc + col;
                     store4<OUT>((char*)P.out + off * OES, v);
                 } else {  // DSTD, transposed C: lane holds 4 consecutive m of column n
-                    const int m0 = mrow + 8 * g + 4 * lh;
-                    const int64_t n = (int64_t)nt * kTileN + wn * 128 + 32 * ni + l32;
-                    const int64_t off = n * P.ldc + (int64_t)kBlock * row + m0;
+                    const int m0 = 32 * mi + 8 * g + 4 * lh;
+                    const int64_t n = n0 + wn * 128 + 32 * ni + l32;
+                    const int64_t off = n * P.ldc + (int64_t)kBlock * mrow + m0;
                     store4<OUT>((char*)P.out + off * OES, v);
                 }
             }
+            // keep the scheduler from hoisting every accumulator read of the
+            // epilogue at once (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -478,72 +583,68 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams P) {
 // ----------------------------------------------------------------- launch
 
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP>
-static hipError_t launch(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<DT, MODE, BK, EPI, OUT, SWAP>), dim3(grid), dim3(kGemmThreads),
-                       0, s, p);
+static hipError_t launch(const GemmParams& p, int64_t grid, hipStream_t s) {
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_kernel<DT, MODE, BK, EPI, OUT, SWAP>), dim3((unsigned)grid),
+                       dim3(kGemmThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <int DT, int MODE>
-static hipError_t dispatch_sdd(const GemmParams& p, int grid, int trans_b, int epi, hipStream_t s) {
+template <int DT>
+static hipError_t dispatch_sdd(const GemmParams& p, int64_t grid, int trans_b, int epi,
+                               hipStream_t s) {
     switch (epi) {
     case kEpiNone:
-        return trans_b ? launch<DT, MODE, true, kEpiNone, DT, true>(p, grid, s)
-                       : launch<DT, MODE, false, kEpiNone, DT, true>(p, grid, s);
+        return trans_b ? launch<DT, kModeSdd, true, kEpiNone, DT, true>(p, grid, s)
+                       : launch<DT, kModeSdd, false, kEpiNone, DT, true>(p, grid, s);
     case kEpiGelu:
-        return trans_b ? launch<DT, MODE, true, kEpiGelu, DT, true>(p, grid, s)
-                       : launch<DT, MODE, false, kEpiGelu, DT, true>(p, grid, s);
+        if (p.aux_out)
+            return trans_b ? launch<DT, kModeSdd, true, kEpiGeluSave, DT, true>(p, grid, s)
+                           : launch<DT, kModeSdd, false, kEpiGeluSave, DT, true>(p, grid, s);
+        return trans_b ? launch<DT, kModeSdd, true, kEpiGelu, DT, true>(p, grid, s)
+                       : launch<DT, kModeSdd, false, kEpiGelu, DT, true>(p, grid, s);
     case kEpiGeluBwd:
-        return trans_b ? launch<DT, MODE, true, kEpiGeluBwd, DT, true>(p, grid, s)
-                       : launch<DT, MODE, false, kEpiGeluBwd, DT, true>(p, grid, s);
+        return trans_b ? launch<DT, kModeSdd, true, kEpiGeluBwd, DT, true>(p, grid, s)
+                       : launch<DT, kModeSdd, false, kEpiGeluBwd, DT, true>(p, grid, s);
     default:
         return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_sdd(const GemmParams& p, int64_t nnz_max, int F, int trans_b, int epi,
-                      int dtype, hipStream_t s) {
-    if (epi == kEpiSiluMul) {  // dual B: one block per tile, both halves = gate | up
-        if (trans_b || nnz_max <= 0) return trans_b ? hipErrorInvalidValue : hipSuccess;
+hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int epi, int dtype,
+                      hipStream_t s) {
+    if (epi == kEpiSiluMul) {  // dual B: one block per tile, B halves = W1 | W3
+        if (trans_b) return hipErrorInvalidValue;
+        const int64_t grid = row_pairs_max * p.F;
         return dtype == kBf16
-                   ? launch<kBf16, kModeSddOne, false, kEpiSiluMul, kBf16, true>(p, (int)nnz_max, s)
-                   : launch<kF32, kModeSddOne, false, kEpiSiluMul, kF32, true>(p, (int)nnz_max, s);
+                   ? launch<kBf16, kModeSddOne, false, kEpiSiluMul, kBf16, true>(p, grid, s)
+                   : launch<kF32, kModeSddOne, false, kEpiSiluMul, kF32, true>(p, grid, s);
     }
-    if (F % 2 == 0) {  // every row holds F blocks: consecutive pairs stay in one row
-        const int grid = (int)(nnz_max / 2);
-        if (grid <= 0) return hipSuccess;
-        return dtype == kBf16 ? dispatch_sdd<kBf16, kModeSdd>(p, grid, trans_b, epi, s)
-                              : dispatch_sdd<kF32, kModeSdd>(p, grid, trans_b, epi, s);
-    }
-    const int grid = (int)nnz_max;
-    if (grid <= 0) return hipSuccess;
-    return dtype == kBf16 ? dispatch_sdd<kBf16, kModeSddOne>(p, grid, trans_b, epi, s)
-                          : dispatch_sdd<kF32, kModeSddOne>(p, grid, trans_b, epi, s);
+    const int64_t grid = row_pairs_max * ((p.F + 1) / 2);
+    return dtype == kBf16 ? dispatch_sdd<kBf16>(p, grid, trans_b, epi, s)
+                          : dispatch_sdd<kF32>(p, grid, trans_b, epi, s);
 }
 
-hipError_t launch_dsd(const GemmParams& p, int64_t row_blocks_max, int trans_b, int c_dtype,
+hipError_t launch_dsd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int c_dtype,
                       int dtype, hipStream_t s) {
-    const int64_t grid = row_blocks_max * p.ntn;
-    if (grid <= 0) return hipSuccess;
-    if (dtype == kF32) {
-        return trans_b ? launch<kF32, kModeDsd, true, kEpiNone, kF32, true>(p, (int)grid, s)
-                       : launch<kF32, kModeDsd, false, kEpiNone, kF32, true>(p, (int)grid, s);
-    }
+    const int64_t grid = row_pairs_max * p.ntn;
+    if (dtype == kF32)
+        return trans_b ? launch<kF32, kModeDsd, true, kEpiNone, kF32, true>(p, grid, s)
+                       : launch<kF32, kModeDsd, false, kEpiNone, kF32, true>(p, grid, s);
     if (c_dtype == kBf16)
-        return trans_b ? launch<kBf16, kModeDsd, true, kEpiNone, kBf16, true>(p, (int)grid, s)
-                       : launch<kBf16, kModeDsd, false, kEpiNone, kBf16, true>(p, (int)grid, s);
-    return trans_b ? launch<kBf16, kModeDsd, true, kEpiNone, kF32, true>(p, (int)grid, s)
-                   : launch<kBf16, kModeDsd, false, kEpiNone, kF32, true>(p, (int)grid, s);
+        return trans_b ? launch<kBf16, kModeDsd, true, kEpiNone, kBf16, true>(p, grid, s)
+                       : launch<kBf16, kModeDsd, false, kEpiNone, kBf16, true>(p, grid, s);
+    return trans_b ? launch<kBf16, kModeDsd, true, kEpiNone, kF32, true>(p, grid, s)
+                   : launch<kBf16, kModeDsd, false, kEpiNone, kF32, true>(p, grid, s);
 }
 
 hipError_t launch_dstd(const GemmParams& p, int trans_c, int dtype, hipStream_t s) {
-    const int64_t grid = (int64_t)p.ncols * p.ntn;
-    if (grid <= 0) return hipSuccess;
+    const int64_t grid = (int64_t)p.E * ((p.F + 1) / 2) * p.ntn;
     if (dtype == kF32)
-        return trans_c ? launch<kF32, kModeDstd, false, kEpiNone, kF32, false>(p, (int)grid, s)
-                       : launch<kF32, kModeDstd, false, kEpiNone, kF32, true>(p, (int)grid, s);
-    return trans_c ? launch<kBf16, kModeDstd, false, kEpiNone, kBf16, false>(p, (int)grid, s)
-                   : launch<kBf16, kModeDstd, false, kEpiNone, kBf16, true>(p, (int)grid, s);
+        return trans_c ? launch<kF32, kModeDstd, false, kEpiNone, kF32, false>(p, grid, s)
+                       : launch<kF32, kModeDstd, false, kEpiNone, kF32, true>(p, grid, s);
+    return trans_c ? launch<kBf16, kModeDstd, false, kEpiNone, kBf16, false>(p, grid, s)
+                   : launch<kBf16, kModeDstd, false, kEpiNone, kBf16, true>(p, grid, s);
 }
 
 }  // namespace bsg

@@ -13,6 +13,7 @@ constexpr int kEpiNone = 0;
 constexpr int kEpiGelu = 1;
 constexpr int kEpiSiluMul = 2;
 constexpr int kEpiGeluBwd = 3;
+constexpr int kEpiGeluSave = 4;  // internal: GeLU that also stores the pre-activation
 
 constexpr int kModeSdd = 0;
 constexpr int kModeSddOne = 1;
@@ -22,6 +23,7 @@ constexpr int kModeDstd = 3;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kRouteChunk = 64;  // tokens per routing chunk
+constexpr int kMaxTileBlocks = 2048;  // K-blocks one DSD / DSTD tile may walk
 
 struct GemmParams {
     const void* a;       // SDD: dense rows; DSD / DSTD: sparse blocks
@@ -36,11 +38,12 @@ struct GemmParams {
     const int32_t* row_idx;
     const int32_t* col_ptr;
     const int32_t* trans_idx;
-    const int32_t* meta;  // {nnz, R} written by build_topology
+    const int32_t* row_pairs;  // pairs of block rows sharing a column list
+    const int32_t* meta;  // {nnz, R, overflow, row pairs} written by build_topology
     int K;                // SDD reduction length
     int N;                // DSD / DSTD output width
     int ntn;              // 256-wide output tiles along N
-    int ncols;            // E * F column blocks
+    int E, F;             // experts, column blocks per expert
 };
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
@@ -53,13 +56,13 @@ hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               hipStream_t stream);
 
 hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
-                                 int32_t* row_ptr, int32_t* col_idx, int32_t* row_idx,
-                                 int32_t* col_ptr, int32_t* trans_idx, int32_t* meta,
-                                 hipStream_t stream);
+                                 int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
+                                 int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
+                                 int32_t* row_pairs, int32_t* meta, hipStream_t stream);
 
-hipError_t launch_sdd(const GemmParams& p, int64_t nnz_max, int F, int trans_b, int epi,
-                      int dtype, hipStream_t s);
-hipError_t launch_dsd(const GemmParams& p, int64_t row_blocks_max, int trans_b, int c_dtype,
+hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int epi, int dtype,
+                      hipStream_t s);
+hipError_t launch_dsd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int c_dtype,
                       int dtype, hipStream_t s);
 hipError_t launch_dstd(const GemmParams& p, int trans_c, int dtype, hipStream_t s);
 

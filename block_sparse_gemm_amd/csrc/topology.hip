@@ -7,6 +7,10 @@
 // this metadata, mapping each (expert, token-row range) to its nonzero
 // blocks, together with the transpose metadata in a single kernel.
 //
+// It also emits the row-pair schedule the products run on: consecutive
+// block rows of one expert share their column list, so a 256-row tile of
+// two such rows reads one set of weight columns.
+//
 // The first layer's output is block-diagonal: row block r belongs to the
 // expert whose bin holds row 128 r, and that expert owns the F column
 // blocks e*F .. e*F + F - 1.  So every entry is computed independently from
@@ -35,9 +39,33 @@ __device__ __forceinline__ int owner_of(const int* s, int E, int64_t r) {
 __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     const int32_t* __restrict__ bin_offsets, int E, int F, int64_t row_blocks_max,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ row_idx,
-    int32_t* __restrict__ col_ptr, int32_t* __restrict__ trans_idx, int32_t* __restrict__ meta) {
-    __shared__ int s[kMaxExperts + 1];  // bin start in row blocks
+    int32_t* __restrict__ col_ptr, int32_t* __restrict__ trans_idx,
+    int32_t* __restrict__ row_pairs, int32_t* __restrict__ meta) {
+    __shared__ int s[kMaxExperts + 1];   // bin start in row blocks
+    __shared__ int pp[kMaxExperts + 1];  // first row pair of each expert
+    __shared__ int part[kTopoThreads];
     for (int e = threadIdx.x; e <= E; e += kTopoThreads) s[e] = bin_offsets[e] / kBlock;
+    __syncthreads();
+    // row pairs: expert e's R_e row blocks form ceil(R_e / 2) pairs of
+    // consecutive rows (the last one single when R_e is odd); exclusive scan
+    const int per = (E + kTopoThreads - 1) / kTopoThreads;
+    const int lo = threadIdx.x * per, hi = min(lo + per, E);
+    int sum = 0;
+    for (int e = lo; e < hi; ++e) sum += (s[e + 1] - s[e] + 1) / 2;
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < kTopoThreads; off <<= 1) {
+        const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int run = part[threadIdx.x] - sum;
+    for (int e = lo; e < hi; ++e) {
+        pp[e] = run;
+        run += (s[e + 1] - s[e] + 1) / 2;
+    }
+    if (threadIdx.x == kTopoThreads - 1) pp[E] = part[kTopoThreads - 1];
     __syncthreads();
     const int64_t R = s[E];
     const int64_t nnz = R * F;
@@ -51,6 +79,7 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
             meta[0] = 0;
             meta[1] = 0;
             meta[2] = 1;
+            meta[3] = 0;
         }
         if (g <= row_blocks_max) row_ptr[g] = 0;
         if (g <= (int64_t)E * F) col_ptr[g] = 0;
@@ -60,6 +89,14 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
         meta[0] = (int32_t)nnz;
         meta[1] = (int32_t)R;
         meta[2] = 0;
+        meta[3] = pp[E];
+    }
+    if (g < pp[E]) {
+        const int e = owner_of(pp, E, g);
+        const int j = (int)(g - pp[e]);
+        const int Re = s[e + 1] - s[e];
+        const int r0 = s[e] + 2 * j;
+        row_pairs[g] = (r0 << 1) | (2 * j + 1 < Re ? 1 : 0);
     }
     // BCSR block pointer: every non-empty row block holds F blocks
     if (g <= row_blocks_max) row_ptr[g] = (int32_t)((g < R ? g : R) * F);
@@ -87,16 +124,17 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
 }
 
 hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
-                                 int32_t* row_ptr, int32_t* col_idx, int32_t* row_idx,
-                                 int32_t* col_ptr, int32_t* trans_idx, int32_t* meta,
-                                 hipStream_t stream) {
+                                 int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
+                                 int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
+                                 int32_t* row_pairs, int32_t* meta, hipStream_t stream) {
     int64_t n = row_blocks_max * F;
+    if (row_pairs_max > n) n = row_pairs_max;
     if (row_blocks_max + 1 > n) n = row_blocks_max + 1;
     if ((int64_t)E * F + 1 > n) n = (int64_t)E * F + 1;
     const int grid = (int)((n + kTopoThreads - 1) / kTopoThreads);
     hipLaunchKernelGGL(build_topology_kernel, dim3(grid), dim3(kTopoThreads), 0, stream,
                        bin_offsets, E, F, row_blocks_max, row_ptr, col_idx, row_idx, col_ptr,
-                       trans_idx, meta);
+                       trans_idx, row_pairs, meta);
     return hipGetLastError();
 }
 

@@ -72,9 +72,10 @@ typedef void* bsg_stream_t;
 
 /* Upper bounds for the topology arrays (pure host function results). */
 typedef struct {
-    int64_t row_blocks_max; /* Tp_max / 128                      */
-    int64_t nnz_max;        /* row_blocks_max * F                 */
-    int64_t n_cols;         /* E * F column blocks                */
+    int64_t row_blocks_max; /* Tp_max / 128                              */
+    int64_t nnz_max;        /* row_blocks_max * F                         */
+    int64_t n_cols;         /* E * F column blocks                        */
+    int64_t row_pairs_max;  /* (row_blocks_max + min(E, row_blocks_max) + 1) / 2 */
 } bsg_topo_sizes;
 
 /*
@@ -89,7 +90,11 @@ typedef struct {
  *   col_ptr   [E*F + 1]  start of each column's run in trans_idx
  *   trans_idx [nnz_max]  BCSR block ids listed column by column,
  *                        ascending row inside a column (no data copied)
- *   meta      [4]        written on the device: {nnz, R, overflow, 0};
+ *   row_pairs [row_pairs_max] the schedule of the products: consecutive
+ *                        block rows of one expert taken two at a time
+ *                        (a last single row when the expert has an odd
+ *                        number); entry = (first row << 1) | (pair ? 1 : 0)
+ *   meta      [4]        written on the device: {nnz, R, overflow, pairs};
  *                        overflow = 1 when the routing needs more than
  *                        Tp_max rows: the topology is then published empty
  *                        (nnz = R = 0, all pointers 0) and every product
@@ -104,6 +109,7 @@ typedef struct {
     int32_t* row_idx;
     int32_t* col_ptr;
     int32_t* trans_idx;
+    int32_t* row_pairs;
     int32_t* meta;
     int32_t E;
     int32_t F;

@@ -44,6 +44,7 @@ def test_size_queries(L):
     assert bsg.max_padded_rows(4, 3, 2) == -1
     s = bsg.topology_sizes(139136, 64, 4096)
     assert (s.row_blocks_max, s.nnz_max, s.n_cols) == (1087, 1087 * 32, 64 * 32)
+    assert s.row_pairs_max == (1087 + 64 + 1) // 2
     assert bsg.route_workspace_bytes(65536, 2, 64) == 1024 * 64 * 4
     assert bsg.route_workspace_bytes(65, 1, 3) == 2 * 3 * 4
     assert bsg.route_workspace_bytes(10, 3, 2) == 0
@@ -100,7 +101,8 @@ def test_permute_pad_validation(L):
 
 
 def fake_topo(E=4, f=256, Tp=1024, **over):
-    t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000, E, f // 128, Tp)
+    t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x70000, 0x60000, E,
+                           f // 128, Tp)
     for k, v in over.items():
         setattr(t, k, v)
     return t

@@ -136,6 +136,14 @@ def check_case(orc, case: Case, seed=0):
     for key in ("col_idx", "row_idx", "trans_idx"):
         assert np.array_equal(getattr(L.topo, key)[:nnz].cpu().numpy(), t[key]), key
     assert np.array_equal(L.topo.col_ptr.cpu().numpy(), t["col_ptr"]), "col_ptr"
+    # the products' schedule: each expert's block rows two at a time
+    want_pairs = []
+    for e in range(cfg.E):
+        s0, s1 = r["bin_offsets"][e] // 128, r["bin_offsets"][e + 1] // 128
+        for r0 in range(s0, s1, 2):
+            want_pairs.append((r0 << 1) | (1 if r0 + 1 < s1 else 0))
+    assert meta[3] == len(want_pairs)
+    assert L.topo.row_pairs[:len(want_pairs)].cpu().numpy().tolist() == want_pairs
 
     # ---- permuted, padded copy: bit-exact
     prec = cfg.dtype
