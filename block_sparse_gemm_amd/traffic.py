@@ -1,0 +1,160 @@
+"""HBM traffic per kernel launch from rocprofv3 counters.
+
+Two modes:
+
+``python3 -m block_sparse_gemm_amd.traffic run [--config moe_small] [--steps 2]``
+    The workload for a counter pass: a plain copy of a known size (the
+    calibration), then ``--steps`` steps of the layer.  Run it under
+    ``rocprofv3 --pmc FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``.
+
+``python3 -m block_sparse_gemm_amd.traffic summarize --fetch F.csv --write W.csv``
+    Reads the two ``*_counter_collection.csv`` files, scales each kernel's
+    mean counter value per dispatch by what the copy kernel reads for its
+    known byte count, and writes ``profiles/traffic.json`` (bytes per launch,
+    keyed by the layer's call names, stamped with the hash of the GEMM
+    source so stale figures are ignored) and a Markdown table.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GEMM_SRC = os.path.join(ROOT, "block_sparse_gemm_amd", "csrc", "gemm.hip")
+COPY_BYTES = 1 << 29           # 512 MiB read and 512 MiB written by the calibration copy
+COPY_NAMES = ("copyBuffer", "MulFunctor")   # the memcpy blit kernel, else x * 1
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def call_name(kernel: str):
+    """Map a kernel symbol to the layer's call name (None if not a layer kernel)."""
+    m = re.search(r"gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)>", kernel)
+    if m:
+        _, mode, b_kc, epi, _, swap = m.groups()
+        if mode in ("0", "1"):
+            return "sdd_bwd" if epi == "3" else "sdd"
+        if mode == "2":
+            return "dsd_bwd" if b_kc == "true" else "dsd"
+        if mode == "3":
+            return "dstd_dw2" if swap == "true" else "dstd_dw1"
+    for k in ("route_topk", "route_scan", "route_place", "permute_pad", "build_topology", "combine"):
+        if k in kernel:
+            return k
+    return None
+
+
+def run(args):
+    import torch
+    from block_sparse_gemm_amd import layer, synth
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    print("[traffic] calibration copy", flush=True)
+    dst.copy_(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+    cfg = synth.CONFIGS[args.config]
+    inp = synth.make_inputs(cfg, 0)
+    s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
+                    cfg.backward)
+    L = layer.Layer(s)
+    up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
+    x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        L.step(x, logits, W1, W2, W3, dy)
+        torch.cuda.synchronize()
+        print(f"[traffic] step {i} done", flush=True)
+
+
+def per_dispatch(path):
+    """{kernel name: [value per dispatch, ...]} in KiB, summed over counter instances."""
+    acc = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        key = r["Dispatch_Id"]
+        acc[key] += float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for key, v in acc.items():
+        out[names[key]].append(v)
+    return out
+
+
+def summarize(args):
+    fetch, write = per_dispatch(args.fetch), per_dispatch(args.write)
+
+    def copy_factor(table, label):
+        for pat in COPY_NAMES:
+            cands = [v for k, vs in table.items() if pat in k for v in vs]
+            if cands and max(cands) > 0:
+                big = max(cands)
+                return COPY_BYTES / (big * 1024.0), big
+        raise SystemExit(f"no calibration copy found in the {label} counters")
+
+    f_fac, f_raw = copy_factor(fetch, "FETCH_SIZE")
+    w_fac, w_raw = copy_factor(write, "WRITE_SIZE")
+    sha = source_sha()
+    result = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": f_raw, "write_kib": w_raw,
+                               "fetch_factor": f_fac, "write_factor": w_fac,
+                               "workload": args.config}}
+    rows = []
+    for kern in sorted(set(fetch) | set(write)):
+        name = call_name(kern)
+        if name is None:
+            continue
+        fk = sum(fetch.get(kern, [0])) / max(1, len(fetch.get(kern, [])))
+        wk = sum(write.get(kern, [0])) / max(1, len(write.get(kern, [])))
+        fb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
+        ent = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+               "kernel": kern[:120]}
+        if kern.find("gemm_kernel") >= 0:
+            ent["source_sha"] = sha
+        result[name] = ent
+        rows.append((name, fb / 1e6, wb / 1e6, kern[:80]))
+    os.makedirs(os.path.dirname(args.out), exist_ok=True)
+    json.dump(result, open(args.out, "w"), indent=1)
+    lines = [f"# HBM traffic per launch: {args.config} layer step", "",
+             "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over L2 channels), each scaled",
+             f"by the reading of a plain {COPY_BYTES >> 20} MiB copy: fetch factor {f_fac:.4f}, write factor "
+             f"{w_fac:.4f}.", "", "Commands:", "", "```"] + args.cmd + ["```", "",
+             "| call | fetch MB | write MB | kernel |", "|---|---|---|---|"]
+    for name, fm, wm, k in rows:
+        lines.append(f"| {name} | {fm:.1f} | {wm:.1f} | `{k}` |")
+    open(args.md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--config", default="moe_small")
+    r.add_argument("--steps", type=int, default=2)
+    s = sub.add_parser("summarize")
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--config", default="moe_small")
+    s.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    s.add_argument("--md", default=os.path.join(ROOT, "profiles", "moe_small_traffic.md"))
+    s.add_argument("--cmd", nargs="*", default=[])
+    a = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    run(a) if a.mode == "run" else summarize(a)
+
+
+if __name__ == "__main__":
+    main()
