@@ -54,9 +54,6 @@ bsg_status check_topology(const bsg_topology* t) {
     REQUIRE(t->Tp_max >= BSG_BLOCK && t->Tp_max % BSG_BLOCK == 0,
             "topo->Tp_max must be a positive multiple of 128");
     REQUIRE((t->Tp_max / BSG_BLOCK) * (int64_t)t->F < INT32_MAX, "too many blocks for int32 ids");
-    if (t->Tp_max / BSG_BLOCK > bsg::kMaxTileBlocks || t->F > bsg::kMaxTileBlocks)
-        return fail(BSG_EUNSUPPORTED, "more than %d blocks per block row or column",
-                    bsg::kMaxTileBlocks);
     REQUIRE_PTR(t->row_ptr);
     REQUIRE_PTR(t->col_idx);
     REQUIRE_PTR(t->row_idx);

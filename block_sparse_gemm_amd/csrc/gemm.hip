@@ -54,7 +54,7 @@ constexpr int kStages = 4;
 constexpr int kLdsBytes = kStages * kStageBytes;
 constexpr int kSegsPerWave = kSegs / 4;          // per panel
 constexpr int kLoadsPerTile = 4 * kSegsPerWave;  // per wave and K-tile
-constexpr int kIdxCap = kMaxTileBlocks;          // K-blocks of one tile staged in LDS
+constexpr int kIdxCap = 2048;                    // K-blocks of one tile staged in LDS at a time
 
 template <int DT>
 struct Elt;
@@ -194,11 +194,12 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
     switch (tiles) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
     }
 }
 static_assert(kLoadsPerTile == 8, "wait_tiles encodes 8 loads per K-tile");
-static_assert(kStages <= 4, "wait_tiles covers up to 2 K-tiles in flight behind the waited one");
+static_assert(kStages <= 4, "wait_tiles covers up to 3 K-tiles in flight behind the waited one");
 
 // ------------------------------------------------------------- epilogue io
 
@@ -298,18 +299,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     const int64_t n0 = (int64_t)tq * 256;
     const int64_t n1off = n1 ? 128 : 0;  // an absent N half mirrors half 0
 
-    // ---- K extent
-    int nk, cp0 = 0, cp1 = 0;
-    if constexpr (SDD) {
-        nk = P.K / KT;
-    } else if constexpr (MODE == kModeDsd) {
-        nk = (P.row_ptr[mrow0 + 1] - rp0) * KPB;
-    } else {
+    // ---- K extent in K-blocks (DSD / DSTD)
+    int nblk = 0, cp0 = 0, cp1 = 0;
+    if constexpr (MODE == kModeDsd) {
+        nblk = P.row_ptr[mrow0 + 1] - rp0;
+    } else if constexpr (MODE == kModeDstd) {
         cp0 = P.col_ptr[mrow0];
         cp1 = P.col_ptr[mrow1];
-        nk = (P.col_ptr[mrow0 + 1] - cp0) * KPB;
+        nblk = P.col_ptr[mrow0 + 1] - cp0;
     }
-    const int nblk = nk / KPB;
     auto fetch = [&](int p) -> KIdx {
         KIdx r{0, 0, 0};
         if constexpr (MODE == kModeDsd) {
@@ -324,20 +322,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         return r;
     };
 
-    // ---- K-block indices of this tile, staged once in LDS (DSD / DSTD):
-    // block of each M half and its dense row block, read in order per K-tile
+    // ---- K-block indices of the current chunk of the tile's K-blocks,
+    // staged in LDS (DSD / DSTD): block of each M half and its dense row
+    // block, read in order per K-tile
     int* ib0 = (int*)(smem + kLdsBytes);
     int* ib1 = ib0 + kIdxCap;
     int* irow = ib1 + kIdxCap;
-    if constexpr (!SDD) {
-        for (int p = threadIdx.x; p < nblk; p += kGemmThreads) {
-            const KIdx r = fetch(p);
-            ib0[p] = r.b0;
-            ib1[p] = r.b1;
-            irow[p] = r.row;
-        }
-        __syncthreads();
-    }
 
     // ---- per-lane load offsets (constant over K)
     const int64_t lda_b = (SDD ? P.lda : kBlock) * ES;  // A row (or k-row) stride
@@ -466,8 +456,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     //                K-tile kt + kStages - 1 (into the stage freed by kt - 1)
     u32x4 a0f[4], b0f[4], a1f[4], b1f[4];
     TIdx nti{0, 0, 0};  // indices of the next K-tile to load
-    auto first_half = [&](int kt) {
-        if (kt + kStages - 1 < nk) nti = tidx(kt + kStages - 1);
+    auto first_half = [&](int kt, int nk) {
+        if (kt + kStages < nk) nti = tidx(kt + kStages);
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             read1(kt, 1, g, a1f, b1f);
@@ -477,11 +467,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     };
     auto second_half = [&](int kt, bool publish, bool load) {
         if (publish) {
-            const Bases nb = load ? bases(kt + kStages - 1, nti) : Bases{};
+            const Bases nb = load ? bases(kt + kStages, nti) : Bases{};
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
                 read1(kt + 1, 0, g, a0f, b0f);
-                if (load) dma(kt + kStages - 1, nb, g);
+                if (load) dma(kt + kStages, nb, g);
                 mma2(g, a1f, b1f);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -490,92 +480,209 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             for (int g = 0; g < 8; ++g) mma2(g, a1f, b1f);
         }
     };
-    if (nk > 0) {
-        for (int t = 0; t < kStages - 1 && t < nk; ++t) {
+    auto run = [&](int nk) {
+        if (nk <= 0) return;
+        for (int t = 0; t < kStages && t < nk; ++t) {
             const Bases b = bases(t, tidx(t));
 #pragma unroll
             for (int j = 0; j < kLoadsPerTile; ++j) dma(t, b, j);
         }
-        wait_tiles(min(kStages - 2, nk - 1));
+        wait_tiles(min(kStages - 1, nk - 1));
         __syncthreads();
 #pragma unroll
         for (int g = 0; g < 8; ++g) read1(0, 0, g, a0f, b0f);
         int kt = 0;
-        // steady state: publish K-tile kt + 1, load K-tile kt + kStages - 1
-        for (; kt + kStages - 1 < nk; ++kt) {
-            first_half(kt);
-            wait_tiles(kStages - 3);
+        // steady state: publish K-tile kt + 1, load K-tile kt + kStages
+        for (; kt + kStages < nk; ++kt) {
+            first_half(kt, nk);
+            wait_tiles(kStages - 2);
             __syncthreads();
             second_half(kt, true, true);
         }
         // tail: publish without new loads
         for (; kt + 1 < nk; ++kt) {
-            first_half(kt);
-            wait_tiles(min(kStages - 3, nk - 2 - kt));
+            first_half(kt, nk);
+            wait_tiles(min(kStages - 2, nk - 2 - kt));
             __syncthreads();
             second_half(kt, true, false);
         }
         // last K-tile
-        first_half(kt);
+        first_half(kt, nk);
         second_half(kt, false, false);
+    };
+
+    if constexpr (SDD) {
+        run(P.K / KT);
+    } else {
+        // the tile's K-blocks in chunks of kIdxCap, their indices staged per chunk
+        for (int c0 = 0; c0 < nblk; c0 += kIdxCap) {
+            const int nb = min(kIdxCap, nblk - c0);
+            if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+            for (int p = threadIdx.x; p < nb; p += kGemmThreads) {
+                const KIdx r = fetch(c0 + p);
+                ib0[p] = r.b0;
+                ib1[p] = r.b1;
+                irow[p] = r.row;
+            }
+            __syncthreads();
+            run(nb * KPB);
+        }
     }
 
+    // ---- epilogue.  bf16 results (except dual B) go out through LDS: each
+    // wave writes half of its 128 x 128 quarter (64 rows) at a time into a
+    // private 32 KB region in the accumulator layout, then reads it back row
+    // by row, so every store instruction writes 4 whole 256-byte rows
+    // (16 contiguous bytes a lane).  GeLU with the pre-activation kept stages
+    // both halves side by side (pre-activation, then activation).
+    constexpr bool STAGE = OUT == kBf16 && !DUAL;
+    if constexpr (STAGE) __syncthreads();  // every wave is done with the operand ring
     const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
     if (!active) return;
 
-    // ---- epilogue
     const int mrow = wm ? mrow1 : mrow0;  // this wave's block row / column
     int oblk = 0;
     if constexpr (MODE == kModeSdd) oblk = (wm ? rp1 : rp0) + 2 * tq + wn;
     else if constexpr (MODE == kModeSddOne) oblk = (wm ? rp1 : rp0) + tq;
+    constexpr int NI = DUAL ? 2 : 4;
+
+    // staging: row r (256 bytes) of a 64-row sub-region holds 16 chunks of
+    // 16 bytes, chunk c at slot c ^ (r & 15), so the 16 lanes reading one row
+    // and the 16 rows one accumulator write touches both spread over all banks
+    lds_t* region = lds + wave * (kLdsBytes / 4);
+    auto stage_put = [&](lds_t* sub, int mi, int ni, int g, const float* v) {
+        const int row = (SWAP ? 32 * mi : 32 * ni) % 64 + l32;
+        const int chunk = SWAP ? 4 * ni + g : 4 * mi + g;
+        *(__attribute__((address_space(3))) u32x2*)(sub + row * 256 +
+                                                      ((chunk ^ (row & 15)) << 4) + lh * 8) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    auto stage_flush = [&](const lds_t* sub, char* base, int64_t row_bytes) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int chunk = lane & 15;
+#pragma unroll 4
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 4 * rr + (lane >> 4);
+            const u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(
+                sub + row * 256 + ((chunk ^ (row & 15)) << 4));
+            *(u32x4*)(base + row * row_bytes + chunk * 16) = u;
+        }
+    };
+    // origin and row pitch (bytes) of this wave's quarter in the output
+    char* obase;
+    int64_t orow;
+    if constexpr (SDD) {
+        obase = (char*)P.out + (int64_t)oblk * kBlock * kBlock * OES;
+        orow = kBlock * OES;
+    } else if constexpr (SWAP) {
+        obase = (char*)P.out + (((int64_t)kBlock * mrow) * P.ldc + n0 + wn * 128) * OES;
+        orow = P.ldc * OES;
+    } else {
+        obase = (char*)P.out + ((n0 + wn * 128) * P.ldc + (int64_t)kBlock * mrow) * OES;
+        orow = P.ldc * OES;
+    }
+
+    // GeLU backward (bf16): the saved pre-activation, read one 32-row slab
+    // ahead of its use so the loads of slab mi + 1 overlap the work on slab mi
+    constexpr bool PRE = EPI == kEpiGeluBwd && OUT == kBf16;
+    u32x2 hsave[2][NI][4];
+    auto hload = [&](int mi, u32x2 (&dst)[NI][4]) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
+        for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float v[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) v[s] = acc[mi][ni][4 * g + s];
-                if constexpr (SDD) {
-                    // block-major output: (m, n) of block b at b*16384 + m*128 + n
-                    const int m = 32 * mi + l32;
-                    int nloc;
-                    if constexpr (DUAL) {
-                        nloc = wn * 64 + 32 * ni + 8 * g + 4 * lh;
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) v[s] = silu_f(v[s]) * acc[mi][ni + 2][4 * g + s];
-                    } else {
-                        nloc = 32 * ni + 8 * g + 4 * lh;
-                    }
-                    const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
-                    if constexpr (EPI == kEpiGelu || EPI == kEpiGeluSave) {
-                        if constexpr (EPI == kEpiGeluSave)
-                            store4<OUT>((char*)P.aux_out + off * OES, v);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) v[s] = gelu_f(v[s]);
-                    } else if constexpr (EPI == kEpiGeluBwd) {
-                        float h[4];
-                        load4<OUT>((const char*)P.aux_in + off * OES, h);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) v[s] *= gelu_grad_f(h[s]);
-                    }
-                    store4<OUT>((char*)P.out + off * OES, v);
-                } else if constexpr (SWAP) {  // DSD, or DSTD with row-major C
-                    const int m = 32 * mi + l32;
-                    const int64_t col = n0 + wn * 128 + 32 * ni + 8 * g + 4 * lh;
-                    const int64_t off = ((int64_t)kBlock * mrow + m) * P.ldc + col;
-                    store4<OUT>((char*)P.out + off * OES, v);
-                } else {  // DSTD, transposed C: lane holds 4 consecutive m of column n
-                    const int m0 = 32 * mi + 8 * g + 4 * lh;
-                    const int64_t n = n0 + wn * 128 + 32 * ni + l32;
-                    const int64_t off = n * P.ldc + (int64_t)kBlock * mrow + m0;
-                    store4<OUT>((char*)P.out + off * OES, v);
-                }
+                const int m = 32 * mi + l32;
+                const int nloc = 32 * ni + 8 * g + 4 * lh;
+                const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
+                dst[ni][g] = *(const u32x2*)((const char*)P.aux_in + off * 2);
             }
-            // keep the scheduler from hoisting every accumulator read of the
-            // epilogue at once (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (PRE) hload(0, hsave[0]);
+
+    // two halves of 64 staging rows: M slabs (mi) 2h, 2h + 1 with a
+    // row-major output, N slabs (ni) 2h, 2h + 1 with the transposed one
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int b = 0; b < (SWAP ? NI : 4); ++b) {
+                const int mi = SWAP || !STAGE ? 2 * h + a : b;
+                const int ni = SWAP || !STAGE ? b : 2 * h + a;
+                if constexpr (PRE) {
+                    if (b == 0 && mi + 1 < 4) hload(mi + 1, hsave[(mi + 1) & 1]);
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) v[s] = acc[mi][ni][4 * g + s];
+                    if constexpr (SDD) {
+                        // block-major output: (m, n) of block b at b*16384 + m*128 + n
+                        const int m = 32 * mi + l32;
+                        int nloc;
+                        if constexpr (DUAL) {
+                            nloc = wn * 64 + 32 * ni + 8 * g + 4 * lh;
+#pragma unroll
+                            for (int s = 0; s < 4; ++s)
+                                v[s] = silu_f(v[s]) * acc[mi][ni + 2][4 * g + s];
+                        } else {
+                            nloc = 32 * ni + 8 * g + 4 * lh;
+                        }
+                        const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
+                        if constexpr (EPI == kEpiGelu || EPI == kEpiGeluSave) {
+                            if constexpr (EPI == kEpiGeluSave) {
+                                if constexpr (STAGE) stage_put(region, mi, ni, g, v);
+                                else store4<OUT>((char*)P.aux_out + off * OES, v);
+                            }
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) v[s] = gelu_f(v[s]);
+                        } else if constexpr (EPI == kEpiGeluBwd) {
+                            float hv[4];
+                            if constexpr (PRE) {
+                                const u32x2 u = hsave[mi & 1][ni][g];
+                                hv[0] = __uint_as_float(u[0] << 16);
+                                hv[1] = __uint_as_float(u[0] & 0xffff0000u);
+                                hv[2] = __uint_as_float(u[1] << 16);
+                                hv[3] = __uint_as_float(u[1] & 0xffff0000u);
+                            } else {
+                                load4<OUT>((const char*)P.aux_in + off * OES, hv);
+                            }
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) v[s] *= gelu_grad_f(hv[s]);
+                        }
+                        if constexpr (STAGE) {
+                            stage_put(EPI == kEpiGeluSave ? region + 16384 : region, mi, ni, g, v);
+                        } else {
+                            store4<OUT>((char*)P.out + off * OES, v);
+                        }
+                    } else if constexpr (STAGE) {
+                        stage_put(region, mi, ni, g, v);
+                    } else if constexpr (SWAP) {  // DSD, or DSTD with row-major C
+                        const int m = 32 * mi + l32;
+                        const int64_t col = n0 + wn * 128 + 32 * ni + 8 * g + 4 * lh;
+                        const int64_t off = ((int64_t)kBlock * mrow + m) * P.ldc + col;
+                        store4<OUT>((char*)P.out + off * OES, v);
+                    } else {  // DSTD, transposed C: lane holds 4 consecutive m of column n
+                        const int m0 = 32 * mi + 8 * g + 4 * lh;
+                        const int64_t n = n0 + wn * 128 + 32 * ni + l32;
+                        const int64_t off = n * P.ldc + (int64_t)kBlock * mrow + m0;
+                        store4<OUT>((char*)P.out + off * OES, v);
+                    }
+                }
+                // keep the scheduler from hoisting every accumulator read of
+                // the epilogue at once (register pressure)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if constexpr (STAGE) {
+            if constexpr (EPI == kEpiGeluSave) {
+                stage_flush(region, (char*)P.aux_out + (int64_t)oblk * kBlock * kBlock * OES +
+                                        h * 64 * orow, orow);
+                stage_flush(region + 16384, obase + h * 64 * orow, orow);
+            } else {
+                stage_flush(region, obase + h * 64 * orow, orow);
+            }
         }
     }
 }

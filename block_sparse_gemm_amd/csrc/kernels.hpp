@@ -23,7 +23,6 @@ constexpr int kModeDstd = 3;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kRouteChunk = 64;  // tokens per routing chunk
-constexpr int kMaxTileBlocks = 2048;  // K-blocks one DSD / DSTD tile may walk
 
 struct GemmParams {
     const void* a;       // SDD: dense rows; DSD / DSTD: sparse blocks
