@@ -59,14 +59,33 @@ struct Row<kF32> {
 template <int DT>
 __device__ __forceinline__ u32x4 scale_chunk(u32x4 v, float s);
 
+// bf16(s * v) rounded once, without fp64 in the common case: p = fl(s v)
+// and its exact error e = s v - p (one FMA) give the product rounded to
+// odd at fp32 precision (truncate towards zero, set the last bit when
+// inexact), and rounding that to bf16 equals rounding s v itself, since
+// fp32 keeps more than two bits beyond bf16's.  Products too small or too
+// large for e to be exact, zeros and non-finite values take the fp64 path.
+__device__ __forceinline__ uint32_t scaled_bf16(float s, float v) {
+    const float p = s * v;
+    const float ap = fabsf(p);
+    if (!(ap >= 0x1p-100f) || !(ap <= 0x1p+100f)) return f64_to_bf16((double)s * (double)v);
+    const float e = fmaf(s, v, -p);
+    uint32_t u = __float_as_uint(p);
+    if (e != 0.0f) {
+        if ((e < 0.0f) != (p < 0.0f)) u -= 1u;  // |s v| < |p|: step towards zero
+        u |= 1u;
+    }
+    return f32_to_bf16(__uint_as_float(u));
+}
+
 template <>
 __device__ __forceinline__ u32x4 scale_chunk<kBf16>(u32x4 v, float s) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const double lo = (double)s * (double)__uint_as_float(v[i] << 16);
-        const double hi = (double)s * (double)__uint_as_float(v[i] & 0xffff0000u);
-        o[i] = f64_to_bf16(lo) | (f64_to_bf16(hi) << 16);
+        const uint32_t lo = scaled_bf16(s, __uint_as_float(v[i] << 16));
+        const uint32_t hi = scaled_bf16(s, __uint_as_float(v[i] & 0xffff0000u));
+        o[i] = lo | (hi << 16);
     }
     return o;
 }

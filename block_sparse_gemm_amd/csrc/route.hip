@@ -8,8 +8,9 @@
 //
 // Three launches, no atomics on global memory, so every integer result is
 // identical on every run:
-//   1. route_topk     one wavefront per token: top-k by wave reductions,
-//                     softmax gate; per 64-token chunk an LDS histogram.
+//   1. route_topk     one workgroup per 64-token chunk, one wavefront per
+//                     token at a time (4 each, loaded up front): top-k by
+//                     wave reductions, softmax gate; an LDS histogram.
 //   2. route_scan     one workgroup per expert: exclusive scan of that
 //                     expert's per-chunk counts (in place) and its total.
 //   3. route_place    one workgroup per chunk: padded bin offsets, then the
@@ -23,32 +24,42 @@ namespace bsg {
 
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kPerLane = kMaxExperts / kWave;  // logits held per lane
+constexpr int kTopkThreads = 1024;                       // one workgroup per 64-token chunk
+constexpr int kTopkWaves = kTopkThreads / kWave;         // 16
+constexpr int kTokPerWave = kRouteChunk / kTopkWaves;    // 4 tokens per wave
 
-__global__ __launch_bounds__(kRouteThreads) void route_topk(
+// NV = logits per lane (E <= 64 NV).  Each wave first loads the logits of
+// all its tokens, so the loads overlap one another, then works through them.
+template <int NV>
+__global__ __launch_bounds__(kTopkThreads) void route_topk(
     const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
     int32_t* __restrict__ expert_idx, float* __restrict__ gate,
     int32_t* __restrict__ chunk_counts, int nchunks) {
     __shared__ int hist[kMaxExperts];
-    for (int e = threadIdx.x; e < E; e += kRouteThreads) hist[e] = 0;
-    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kTopkThreads) hist[e] = 0;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t t0 = (int64_t)blockIdx.x * kRouteChunk;
-    const int nvals = (E + kWave - 1) / kWave;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteChunk + wave * kTokPerWave;
 
-    for (int tt = wave; tt < kRouteChunk; tt += kRouteWaves) {
-        const int64_t t = t0 + tt;
-        if (t >= T) break;
-        const float* row = logits + t * E;
-        float v[kPerLane];
-        uint32_t taken = 0;  // bit i: expert lane + 64 i already picked
+    float v[kTokPerWave][NV];
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+    for (int u = 0; u < kTokPerWave; ++u) {
+        const int64_t t = t0 + u;
+        const float* row = logits + t * E;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
             const int e = lane + kWave * i;
-            v[i] = (i < nvals && e < E) ? row[e] : 0.0f;
+            v[u][i] = (t < T && e < E) ? row[e] : 0.0f;
         }
+    }
+    __syncthreads();  // histogram cleared
+
+#pragma unroll
+    for (int u = 0; u < kTokPerWave; ++u) {
+        const int64_t t = t0 + u;
+        if (t >= T) break;
+        uint32_t taken = 0;  // bit i: expert lane + 64 i already picked
         int my_sel = -1;
         float my_val = 0.0f;
         float top_val = 0.0f;
@@ -57,11 +68,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk(
             int bi = -1;
             float bv = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kPerLane; ++i) {
+            for (int i = 0; i < NV; ++i) {
                 const int e = lane + kWave * i;
-                if (i < nvals && e < E && !((taken >> i) & 1u) && (bi < 0 || v[i] > bv)) {
+                if (e < E && !((taken >> i) & 1u) && (bi < 0 || v[u][i] > bv)) {
                     bi = e;
-                    bv = v[i];
+                    bv = v[u][i];
                 }
             }
             // butterfly: a total order, so every lane ends with the same winner
@@ -84,9 +95,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk(
         // softmax over all experts, max-subtracted (the first pick is the max)
         float z = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const int e = lane + kWave * i;
-            if (i < nvals && e < E) z += expf(v[i] - top_val);
+            if (e < E) z += expf(v[u][i] - top_val);
         }
         z = wave_sum(z);
         const float p = lane < k ? expf(my_val - top_val) : 0.0f;
@@ -98,7 +109,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk(
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kRouteThreads)
+    for (int e = threadIdx.x; e < E; e += kTopkThreads)
         chunk_counts[(int64_t)e * nchunks + blockIdx.x] = hist[e];
 }
 
@@ -207,8 +218,15 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, hipStream_t stream) {
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
-    hipLaunchKernelGGL(route_topk, dim3(nchunks), dim3(kRouteThreads), 0, stream, logits, T, E,
-                       k, renorm, expert_idx, gate, workspace, nchunks);
+#define BSG_TOPK(NV)                                                                         \
+    hipLaunchKernelGGL(route_topk<NV>, dim3(nchunks), dim3(kTopkThreads), 0, stream, logits, T, \
+                       E, k, renorm, expert_idx, gate, workspace, nchunks)
+    if (E <= 64) BSG_TOPK(1);
+    else if (E <= 128) BSG_TOPK(2);
+    else if (E <= 256) BSG_TOPK(4);
+    else if (E <= 512) BSG_TOPK(8);
+    else BSG_TOPK(16);
+#undef BSG_TOPK
     hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace, nchunks,
                        counts);
     hipLaunchKernelGGL(route_place, dim3(nchunks), dim3(kRouteThreads), 0, stream, expert_idx, T,
