@@ -128,10 +128,15 @@ def main():
         L.step(x, logits, W1, W2, W3, dy)
     torch.cuda.synchronize()
 
-    # per-call events on the current stream (the stream every call uses)
+    # per-call event pairs, each recorded on the stream the call runs on
     marks = []
-    L.mark = (lambda name, _m=marks: (_m.append((name, torch.cuda.Event(enable_timing=True))),
-                                      _m[-1][1].record()))
+
+    def mark(name, phase, _m=marks):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        _m.append((name, phase, ev))
+
+    L.mark = mark
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -141,13 +146,29 @@ def main():
     wall = time.perf_counter() - t0
     L.mark = None
 
-    # per-kernel averages from consecutive events
-    per = {}
-    for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
-        if n1 == "start":
-            continue
-        per.setdefault(n1, []).append(e0.elapsed_time(e1))
+    # per-kernel averages from each call's begin/end events
+    per, open_ev = {}, {}
+    for name, phase, ev in marks:
+        if phase == "begin":
+            open_ev[name] = ev
+        else:
+            per.setdefault(name, []).append(open_ev.pop(name).elapsed_time(ev))
     kern = {k: float(np.mean(v)) for k, v in per.items()}
+
+    # context: each call alone (the weight gradients not overlapped), a few
+    # steps after the timed region
+    serial, ser = [], {}
+    L.overlap, L.mark = False, (lambda n, p, _m=serial: mark(n, p, _m))
+    for _ in range(3):
+        L.step(x, logits, W1, W2, W3, dy)
+    torch.cuda.synchronize()
+    L.overlap, L.mark = True, None
+    for name, phase, ev in serial:
+        if phase == "begin":
+            open_ev[name] = ev
+        else:
+            ser.setdefault(name, []).append(open_ev.pop(name).elapsed_time(ev))
+    kern_serial = {k: round(float(np.mean(v)), 4) for k, v in ser.items()}
     step_ms = wall * 1e3 / args.steps
 
     per_product, total = useful_flops(cfg)
@@ -198,6 +219,7 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_for(dom)},
         "kernels": kernels,
+        "kernels_serial_ms": kern_serial,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

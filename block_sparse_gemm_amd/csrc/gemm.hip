@@ -259,7 +259,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     const int tile = xcd_remap(blockIdx.x, ntiles);
     const int tm = tile / tn, tq = tile % tn;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform: keep it (and every LDS stage address derived
+    // from it) in scalar registers
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int l32 = lane & 31, lh = lane >> 5;
 

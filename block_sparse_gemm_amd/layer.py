@@ -7,6 +7,9 @@ Backward (plain calculus on the same products, weight gradients through the
 transpose index as section 1.3 describes):
     permute_pad(dy, scale = gate) -> sdd(dYp, W2^T, GeLU') -> dsd(dH, W1^T)
     -> unpermute_combine(gate = 1) ; dstd(A, dYp) = dW2 ; dstd(dH, Xp)^T = dW1
+The two weight gradients run on a second stream, each as soon as its inputs
+exist (dW2 beside the GeLU' product, dW1 beside the input-gradient product),
+so the tail of one product's grid and the other's fill the GPU together.
 
 torch only allocates device memory and provides the stream; every step runs
 in libbsg.so.  All buffers are sized once for the worst-case routing
@@ -49,8 +52,12 @@ class Layer:
 
     def __init__(self, s: Shape, device="cuda"):
         self.s = s
-        # optional callable(name) run after each library call (timing hooks)
+        # optional callable(name, phase) run on the call's stream before
+        # (phase "begin") and after (phase "end") each library call
         self.mark = None
+        # weight gradients on the second stream (False: everything in order
+        # on the caller's stream, e.g. to time each call alone)
+        self.overlap = True
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         A = s.T * s.k
@@ -81,49 +88,68 @@ class Layer:
             self.dx = torch.zeros(s.T, s.d, dtype=dt, device=dev)
             self.dW1 = torch.zeros(s.d, s.E * s.f, dtype=dt, device=dev)
             self.dW2 = torch.zeros(s.E * s.f, s.d, dtype=dt, device=dev)
+            self.side = torch.cuda.Stream(device=dev)  # default priority
+            self.ev_dyp = torch.cuda.Event()
+            self.ev_dh = torch.cuda.Event()
+            self.ev_wgrad = torch.cuda.Event()
 
     # ---------------------------------------------------------------- steps
-    def _m(self, name):
+    def _m(self, name, phase):
         if self.mark is not None:
-            self.mark(name)
+            self.mark(name, phase)
+
+    def _call(self, name, fn, *args, **kw):
+        self._m(name, "begin")
+        fn(*args, **kw)
+        self._m(name, "end")
 
     def forward(self, x, logits, W1, W2, W3=None):
         s, t = self.s, self.topo
-        self._m("start")
-        bsg.route(logits, s.k, s.renorm, self.expert_idx, self.gate, self.dest_row, self.counts,
-                  self.bin_offsets, self.route_ws)
-        self._m("route")
-        bsg.permute_pad(x, s.k, self.dest_row, None, self.counts, self.bin_offsets, s.E,
-                        self.Tp_max, self.row_src, self.xp)
-        self._m("permute_pad")
-        bsg.build_topology(self.bin_offsets, s.E, s.f, self.Tp_max, t)
-        self._m("build_topology")
+        c = self._call
+        c("route", bsg.route, logits, s.k, s.renorm, self.expert_idx, self.gate, self.dest_row,
+          self.counts, self.bin_offsets, self.route_ws)
+        c("permute_pad", bsg.permute_pad, x, s.k, self.dest_row, None, self.counts,
+          self.bin_offsets, s.E, self.Tp_max, self.row_src, self.xp)
+        c("build_topology", bsg.build_topology, self.bin_offsets, s.E, s.f, self.Tp_max, t)
         if s.act == "swiglu":
-            bsg.sdd(self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3)
+            c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3)
         else:
-            bsg.sdd(self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.h)
-        self._m("sdd")
-        bsg.dsd(self.act, t, W2, s.d, self.yp)
-        self._m("dsd")
-        bsg.unpermute_combine(self.yp, self.dest_row, self.gate, s.T, s.k, s.d, self.y)
-        self._m("unpermute_combine")
+            c("sdd", bsg.sdd, self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.h)
+        c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp)
+        c("unpermute_combine", bsg.unpermute_combine, self.yp, self.dest_row, self.gate, s.T,
+          s.k, s.d, self.y)
         return self.y
 
     def backward(self, dy, W1, W2):
         s, t = self.s, self.topo
-        bsg.permute_pad(dy, s.k, self.dest_row, self.gate, self.counts, self.bin_offsets, s.E,
-                        self.Tp_max, self.row_src_b, self.dyp)
-        self._m("permute_pad_bwd")
-        bsg.sdd(self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True, aux_in=self.h)
-        self._m("sdd_bwd")
-        bsg.dsd(self.dh, t, W1, s.d, self.dxp, trans_b=True)
-        self._m("dsd_bwd")
-        bsg.unpermute_combine(self.dxp, self.dest_row, None, s.T, s.k, s.d, self.dx)
-        self._m("unpermute_combine_bwd")
-        bsg.dstd(self.act, t, self.dyp, s.d, self.dW2)
-        self._m("dstd_dw2")
-        bsg.dstd(self.dh, t, self.xp, s.d, self.dW1, trans_c=True)
-        self._m("dstd_dw1")
+        c = self._call
+        main = torch.cuda.current_stream()
+        c("permute_pad_bwd", bsg.permute_pad, dy, s.k, self.dest_row, self.gate, self.counts,
+          self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp)
+        if not self.overlap:
+            c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
+              aux_in=self.h)
+            c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
+            c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None,
+              s.T, s.k, s.d, self.dx)
+            c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
+            c("dstd_dw1", bsg.dstd, self.dh, t, self.xp, s.d, self.dW1, trans_c=True)
+            return self.dx, self.dW1, self.dW2
+        self.ev_dyp.record(main)
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(self.ev_dyp)
+            c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
+        c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
+          aux_in=self.h)
+        self.ev_dh.record(main)
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(self.ev_dh)
+            c("dstd_dw1", bsg.dstd, self.dh, t, self.xp, s.d, self.dW1, trans_c=True)
+            self.ev_wgrad.record(self.side)
+        c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
+        c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None, s.T,
+          s.k, s.d, self.dx)
+        main.wait_event(self.ev_wgrad)  # the step ends when both streams have
         return self.dx, self.dW1, self.dW2
 
     def step(self, x, logits, W1, W2, W3=None, dy=None):
