@@ -17,7 +17,7 @@
  *
  * Arithmetic: every sum is accumulated in fp64 in ascending index order and
  * never reassociated.  Values are rounded to the storage precision at the
- * points where the layer stores an intermediate (A, H, Yp, y, dYp, dH, dXp,
+ * points where the layer stores an intermediate (A, G, Yp, y, dYp, dH, dXp,
  * dx, dW); ORC_F64 disables every rounding (used by the finite-difference
  * and library cross-checks).
  *
@@ -30,7 +30,9 @@
  *     a = t*k + j), bins in ascending expert id, empty experts get 0 rows,
  *     pad rows are zero;
  *   - exact erf GeLU; SwiGLU = silu(x W1) * (x W3);
- *   - the block-diagonal matrix is the first layer's output [Tp x E*f].
+ *   - the block-diagonal matrix is the first layer's output [Tp x E*f];
+ *   - what the backward keeps of the forward is GeLU'(h), stored (rounded)
+ *     next to A; the backward multiplies by it.
  *
  * Parity pins: none of the pages prints a worked numeric example, so every
  * function here is pinned by closed forms, invariants, library routines on
@@ -263,7 +265,7 @@ typedef struct {
     int64_t T;
     int d, E, f, k;
     int act;      /* ORC_ACT_GELU or ORC_ACT_SWIGLU */
-    int prec;     /* storage precision of A, H, dYp, dH, y, dx, dW */
+    int prec;     /* storage precision of A, G, dYp, dH, y, dx, dW */
     int prec_yp;  /* storage precision of Yp and dXp */
     const float* x;   /* [T, d] */
     const float* W1;  /* [d, E*f]: expert e owns columns e*f .. e*f+f-1 */
@@ -281,8 +283,10 @@ static int layer_ok(const orc_layer* L) {
 
 /* First layer and activation for one assignment (section 1.2: layer one,
  * activation):  h[n] = sum_i x[t,i] W1[i, e*f+n];  A = act(h).
- * h_out gets the unrounded pre-activation (fp64), H_out its stored copy. */
-static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, double* H_out,
+ * h gets the unrounded pre-activation (fp64); G_out (GeLU only) the stored
+ * derivative act'(h), which is what the backward pass keeps of the forward
+ * (its one rounding point between the passes). */
+static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, double* G_out,
                         double* A_out) {
     const int64_t t = a / L->k;
     const int e = L->expert_idx[a];
@@ -308,7 +312,7 @@ static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, do
         else
             av = gelu(h[n]);
         if (A_out) A_out[n] = rd(av, L->prec);
-        if (H_out) H_out[n] = rd(h[n], L->prec);
+        if (G_out) G_out[n] = rd(gelu_grad(h[n]), L->prec);
     }
 }
 
@@ -325,11 +329,11 @@ static void second_layer(const orc_layer* L, int64_t a, const double* A, double*
 }
 
 /*
- * Per-assignment forward: H (stored pre-activation, gelu only; may be NULL),
- * A (stored activation) [n, f], Yp (expert output) [n, d] for the listed
- * assignments.
+ * Per-assignment forward: G (stored activation derivative, gelu only; may be
+ * NULL), A (stored activation) [n, f], Yp (expert output) [n, d] for the
+ * listed assignments.
  */
-int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, double* H,
+int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, double* G,
                        double* A, double* Yp) {
     if (!layer_ok(L) || !assigns || !A || !Yp) return -1;
     int bad = 0;
@@ -345,7 +349,7 @@ int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, do
                 bad = 1;
                 continue;
             }
-            first_layer(L, a, h, hu, H ? H + q * L->f : NULL, A + q * L->f);
+            first_layer(L, a, h, hu, G ? G + q * L->f : NULL, A + q * L->f);
             second_layer(L, a, A + q * L->f, acc, Yp + q * L->d);
         }
         free(h);
@@ -405,22 +409,22 @@ int orc_forward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, dou
  * SDD -> activation -> DSD; GeLU experts only):
  *   dYp[m] = rd(gate * dy[t, m])
  *   da[n]  = sum_m dYp[m] W2[e*f+n, m]
- *   dH[n]  = rd(da[n] * gelu'(H[n]))      H = stored pre-activation
+ *   dH[n]  = rd(da[n] * G[n])             G = rd(gelu'(h)), stored by the forward
  *   dXp[i] = rd_yp(sum_n dH[n] W1[i, e*f+n])
  */
-static void assign_backward(const orc_layer* L, int64_t a, double* h, double* H, double* dYp,
+static void assign_backward(const orc_layer* L, int64_t a, double* h, double* G, double* dYp,
                             double* dH, double* dXp) {
     const int64_t t = a / L->k;
     const int e = L->expert_idx[a];
     const int64_t ldw = (int64_t)L->E * L->f;
     const double g = L->gate[a];
-    first_layer(L, a, h, NULL, H, NULL);
+    first_layer(L, a, h, NULL, G, NULL);
     for (int m = 0; m < L->d; ++m) dYp[m] = rd(g * (double)L->dy[t * L->d + m], L->prec);
     for (int n = 0; n < L->f; ++n) {
         const float* w = L->W2 + ((int64_t)e * L->f + n) * L->d;
         double da = 0.0;
         for (int m = 0; m < L->d; ++m) da += dYp[m] * (double)w[m];
-        dH[n] = rd(da * gelu_grad(H[n]), L->prec);
+        dH[n] = rd(da * G[n], L->prec);
     }
     for (int i = 0; i < L->d; ++i) {
         const float* w = L->W1 + i * ldw + (int64_t)e * L->f;
@@ -438,7 +442,7 @@ int orc_assign_backward(const orc_layer* L, const int64_t* assigns, int64_t n, d
 #pragma omp parallel
     {
         double* h = (double*)malloc(sizeof(double) * L->f);
-        double* H = (double*)malloc(sizeof(double) * L->f);
+        double* G = (double*)malloc(sizeof(double) * L->f);
         double* ldyp = (double*)malloc(sizeof(double) * L->d);
         double* ldh = (double*)malloc(sizeof(double) * L->f);
         double* ldxp = (double*)malloc(sizeof(double) * L->d);
@@ -449,13 +453,13 @@ int orc_assign_backward(const orc_layer* L, const int64_t* assigns, int64_t n, d
                 bad = 1;
                 continue;
             }
-            assign_backward(L, a, h, H, ldyp, ldh, ldxp);
+            assign_backward(L, a, h, G, ldyp, ldh, ldxp);
             if (dYp) memcpy(dYp + q * L->d, ldyp, sizeof(double) * L->d);
             if (dH) memcpy(dH + q * L->f, ldh, sizeof(double) * L->f);
             if (dXp) memcpy(dXp + q * L->d, ldxp, sizeof(double) * L->d);
         }
         free(h);
-        free(H);
+        free(G);
         free(ldyp);
         free(ldh);
         free(ldxp);
@@ -470,7 +474,7 @@ int orc_backward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, do
 #pragma omp parallel
     {
         double* h = (double*)malloc(sizeof(double) * L->f);
-        double* H = (double*)malloc(sizeof(double) * L->f);
+        double* G = (double*)malloc(sizeof(double) * L->f);
         double* dYp = (double*)malloc(sizeof(double) * L->d);
         double* dH = (double*)malloc(sizeof(double) * L->f);
         double* dXp = (double*)malloc(sizeof(double) * L->d);
@@ -484,13 +488,13 @@ int orc_backward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, do
             }
             for (int i = 0; i < L->d; ++i) sum[i] = 0.0;
             for (int j = 0; j < L->k; ++j) {
-                assign_backward(L, t * L->k + j, h, H, dYp, dH, dXp);
+                assign_backward(L, t * L->k + j, h, G, dYp, dH, dXp);
                 for (int i = 0; i < L->d; ++i) sum[i] += dXp[i];
             }
             for (int i = 0; i < L->d; ++i) dx[q * L->d + i] = rd(sum[i], L->prec);
         }
         free(h);
-        free(H);
+        free(G);
         free(dYp);
         free(dH);
         free(dXp);
@@ -604,7 +608,7 @@ int orc_dW1_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
                     double dyp = rd((double)L->gate[a] * (double)L->dy[t * L->d + m], L->prec);
                     da += dyp * (double)w2[m];
                 }
-                dh[q] = rd(da * gelu_grad(rd(h, L->prec)), L->prec);
+                dh[q] = rd(da * rd(gelu_grad(h), L->prec), L->prec);
             }
             for (int64_t p = 0; p < nr; ++p) {
                 int64_t i = rows[p];

@@ -182,8 +182,9 @@ def topology(bin_offsets: np.ndarray, E: int, F: int) -> dict:
 class Layer:
     """Float oracle of one layer call.
 
-    ``prec`` is the storage precision of A, H, dYp, dH, y, dx and the weight
-    gradients; ``prec_yp`` that of Yp and dXp ("f64" disables rounding)."""
+    ``prec`` is the storage precision of A, G (= GeLU'(h), what the backward
+    keeps), dYp, dH, y, dx and the weight gradients; ``prec_yp`` that of Yp
+    and dXp ("f64" disables rounding)."""
 
     def __init__(self, x, W1, W2, expert_idx, gate, k, E, act="gelu", W3=None, dy=None,
                  prec="bf16", prec_yp=None):
@@ -218,14 +219,15 @@ class Layer:
             raise ValueError(f"{name} rejected its arguments")
 
     def assign_forward(self, assigns):
+        """Per assignment: G = rd(GeLU'(h)) (GeLU only), A = rd(act(h)), Yp."""
         a = np.ascontiguousarray(assigns, np.int64)
         n = len(a)
-        H = np.zeros((n, self.f))
+        G = np.zeros((n, self.f))
         A = np.zeros((n, self.f))
         Yp = np.zeros((n, self.d))
-        self._call("orc_assign_forward", _p(a, _i64p), n, _p(H, _f64p), _p(A, _f64p),
+        self._call("orc_assign_forward", _p(a, _i64p), n, _p(G, _f64p), _p(A, _f64p),
                    _p(Yp, _f64p))
-        return H, A, Yp
+        return G, A, Yp
 
     def forward_tokens(self, tokens):
         t = np.ascontiguousarray(tokens, np.int64)

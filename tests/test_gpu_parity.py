@@ -156,11 +156,11 @@ def check_case(orc, case: Case, seed=0):
     O = orc.make_layer(inp["x"].values, inp["W1"].values, inp["W2"].values, r, cfg.k, cfg.E,
                        act=cfg.act, W3=inp["W3"].values if "W3" in inp else None,
                        dy=inp["dy"].values if "dy" in inp else None, prec=prec, prec_yp=cfg.yp)
-    H, A, Yp = O.assign_forward(assigns)
+    G, A, Yp = O.assign_forward(assigns)
     rows = torch.from_numpy(r["dest_row"][assigns]).cuda()
     check_float("A", f64(L.sparse_rows(L.act, rows)), A, prec, report)
     if cfg.backward:
-        check_float("H", f64(L.sparse_rows(L.h, rows)), H, prec, report)
+        check_float("G", f64(L.sparse_rows(L.gp, rows)), G, prec, report)
     # the bar follows the workload's arithmetic (bf16 operands, fp32
     # accumulation) even where Yp is stored in fp32
     check_float("Yp", f64(L.yp[rows.long()]), Yp, prec, report)

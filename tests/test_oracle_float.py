@@ -114,7 +114,7 @@ def test_forward_equals_batched_gemm_f64(orc, act):
     want, yp = batched_gemm_forward(inp["x"], inp["W1"], inp["W2"], inp["W3"], r["expert_idx"],
                                     r["gate"], L.k, L.E, act)
     assert np.max(np.abs(y - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
-    H, A, Yp = L.assign_forward(np.arange(L.T * L.k))
+    G, A, Yp = L.assign_forward(np.arange(L.T * L.k))
     assert np.max(np.abs(Yp - yp)) <= 1e-12 * max(1.0, np.max(np.abs(yp)))
 
 
@@ -124,7 +124,7 @@ def test_forward_bf16_within_one_ulp_of_batched_gemm(orc):
         np.float64)
     want, yp = batched_gemm_forward(inp["x"], inp["W1"], inp["W2"], None, r["expert_idx"],
                                     r["gate"], L.k, L.E, "gelu", rnd=q)
-    H, A, Yp = L.assign_forward(np.arange(L.T * L.k))
+    G, A, Yp = L.assign_forward(np.arange(L.T * L.k))
     # summation order differs (BLAS vs ascending), so a rounding may flip by
     # one bf16 ulp (2^-7 relative at most); nothing more
     assert np.all(np.abs(Yp - yp) <= np.abs(yp) * 2.0 ** -7 + 1e-30)
@@ -169,12 +169,21 @@ def test_forward_invariants(orc):
 
 def test_forward_tokens_consistent_with_assignment_rows(orc):
     L, r, inp = small_layer(orc, T=50, prec="bf16", seed=5)
-    H, A, Yp = L.assign_forward(np.arange(100))
+    G, A, Yp = L.assign_forward(np.arange(100))
     y = L.forward_tokens(np.arange(50))
     g = r["gate"].astype(np.float64)
     s = g[0::2, None] * Yp[0::2] + g[1::2, None] * Yp[1::2]
     q = lambda a: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a.astype(np.float32)))
     assert np.max(np.abs(y - s)) <= np.max(np.abs(s)) * 2.0 ** -7
-    # stored H and A agree with the activation of H to one rounding
-    assert np.max(np.abs(A - q(torch.nn.functional.gelu(torch.from_numpy(H)).numpy()))) <= \
-        np.max(np.abs(A)) * 2.0 ** -6
+    # stored A and G are the activation and its derivative at h = x W1 (a
+    # numpy product here), each to one bf16 rounding; the derivative from
+    # torch autograd of the exact GeLU
+    a = np.arange(100)
+    e = r["expert_idx"][a]
+    W1 = inp["W1"].astype(np.float64).reshape(L.d, L.E, L.f)
+    h = np.einsum("ai,aif->af", inp["x"].astype(np.float64)[a // 2], W1[:, e, :].transpose(1, 0, 2))
+    ht = torch.from_numpy(h).requires_grad_()
+    gl = torch.nn.functional.gelu(ht)
+    gl.sum().backward()
+    assert np.max(np.abs(A - q(gl.detach().numpy()))) <= np.max(np.abs(A)) * 2.0 ** -7
+    assert np.max(np.abs(G - q(ht.grad.numpy()))) <= np.max(np.abs(G)) * 2.0 ** -7
