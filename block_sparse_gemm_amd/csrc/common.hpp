@@ -106,6 +106,14 @@ __device__ __forceinline__ float gelu_grad_f(float h) {
     return fmaf(h * r.e, 0.398942280401432678f, phi);
 }
 
+// Both at once (one erfc evaluation): what the training forward stores.
+__device__ __forceinline__ void gelu_and_grad(float h, float& g, float& gp) {
+    const ErfcHalf r = erfc_half(h);
+    const float phi = h >= 0.0f ? 1.0f - r.q : r.q;
+    g = h * phi;
+    gp = fmaf(h * r.e, 0.398942280401432678f, phi);
+}
+
 // silu(g) = g / (1 + exp(-g))
 __device__ __forceinline__ float silu_f(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));

@@ -535,8 +535,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     // wave writes half of its 128 x 128 quarter (64 rows) at a time into a
     // private 32 KB region in the accumulator layout, then reads it back row
     // by row, so every store instruction writes 4 whole 256-byte rows
-    // (16 contiguous bytes a lane).  GeLU with the pre-activation kept stages
-    // both halves side by side (pre-activation, then activation).
+    // (16 contiguous bytes a lane).  GeLU with the derivative kept stages
+    // both side by side (derivative, then activation).
     constexpr bool STAGE = OUT == kBf16 && !DUAL;
     if constexpr (STAGE) __syncthreads();  // every wave is done with the operand ring
     const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
@@ -584,8 +584,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         orow = P.ldc * OES;
     }
 
-    // GeLU backward (bf16): the saved pre-activation, read one 32-row slab
-    // ahead of its use so the loads of slab mi + 1 overlap the work on slab mi
+    // GeLU backward (bf16): the saved derivative, read one 32-row slab ahead
+    // of its use so the loads of slab mi + 1 overlap the work on slab mi
     constexpr bool PRE = EPI == kEpiGeluBwd && OUT == kBf16;
     u32x2 hsave[2][NI][4];
     auto hload = [&](int mi, u32x2 (&dst)[NI][4]) {
@@ -632,26 +632,30 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                             nloc = 32 * ni + 8 * g + 4 * lh;
                         }
                         const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
-                        if constexpr (EPI == kEpiGelu || EPI == kEpiGeluSave) {
-                            if constexpr (EPI == kEpiGeluSave) {
-                                if constexpr (STAGE) stage_put(region, mi, ni, g, v);
-                                else store4<OUT>((char*)P.aux_out + off * OES, v);
-                            }
+                        if constexpr (EPI == kEpiGelu) {
 #pragma unroll
                             for (int s = 0; s < 4; ++s) v[s] = gelu_f(v[s]);
+                        } else if constexpr (EPI == kEpiGeluSave) {
+                            // the activation and, for the backward, its derivative
+                            float gp[4];
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) gelu_and_grad(v[s], v[s], gp[s]);
+                            if constexpr (STAGE) stage_put(region, mi, ni, g, gp);
+                            else store4<OUT>((char*)P.aux_out + off * OES, gp);
                         } else if constexpr (EPI == kEpiGeluBwd) {
-                            float hv[4];
+                            // dH = dA * GeLU'(h), the derivative saved by the forward
+                            float gv[4];
                             if constexpr (PRE) {
                                 const u32x2 u = hsave[mi & 1][ni][g];
-                                hv[0] = __uint_as_float(u[0] << 16);
-                                hv[1] = __uint_as_float(u[0] & 0xffff0000u);
-                                hv[2] = __uint_as_float(u[1] << 16);
-                                hv[3] = __uint_as_float(u[1] & 0xffff0000u);
+                                gv[0] = __uint_as_float(u[0] << 16);
+                                gv[1] = __uint_as_float(u[0] & 0xffff0000u);
+                                gv[2] = __uint_as_float(u[1] << 16);
+                                gv[3] = __uint_as_float(u[1] & 0xffff0000u);
                             } else {
-                                load4<OUT>((const char*)P.aux_in + off * OES, hv);
+                                load4<OUT>((const char*)P.aux_in + off * OES, gv);
                             }
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) v[s] *= gelu_grad_f(hv[s]);
+                            for (int s = 0; s < 4; ++s) v[s] *= gv[s];
                         }
                         if constexpr (STAGE) {
                             stage_put(EPI == kEpiGeluSave ? region + 16384 : region, mi, ni, g, v);

@@ -13,7 +13,7 @@ constexpr int kEpiNone = 0;
 constexpr int kEpiGelu = 1;
 constexpr int kEpiSiluMul = 2;
 constexpr int kEpiGeluBwd = 3;
-constexpr int kEpiGeluSave = 4;  // internal: GeLU that also stores the pre-activation
+constexpr int kEpiGeluSave = 4;  // internal: GeLU that also stores its derivative
 
 constexpr int kModeSdd = 0;
 constexpr int kModeSddOne = 1;
@@ -28,9 +28,9 @@ struct GemmParams {
     const void* a;       // SDD: dense rows; DSD / DSTD: sparse blocks
     const void* b;       // SDD / DSD: dense B; DSTD: dense rows (dmat)
     const void* b2;      // SDD dual-B second operand (SwiGLU up projection)
-    const void* aux_in;  // SDD GELU_BWD: saved pre-activation blocks
+    const void* aux_in;  // SDD GELU_BWD: saved GeLU derivative blocks
     void* out;
-    void* aux_out;       // SDD GELU: optional saved pre-activation blocks
+    void* aux_out;       // SDD GELU: optional saved GeLU derivative blocks
     int64_t lda, ldb, ldc;
     const int32_t* row_ptr;
     const int32_t* col_idx;

@@ -75,7 +75,8 @@ class Layer:
         self.row_src = torch.zeros(self.Tp_max, **i32)
         self.xp = torch.zeros(self.Tp_max, s.d, dtype=dt, device=dev)
         self.act = torch.zeros(nnz_max * bsg.BLOCK, bsg.BLOCK, dtype=dt, device=dev)
-        self.h = torch.zeros_like(self.act) if s.backward else None
+        # what the backward keeps of the forward: GeLU'(h), block-major like A
+        self.gp = torch.zeros_like(self.act) if s.backward else None
         self.yp = torch.zeros(self.Tp_max, s.d, dtype=ydt, device=dev)
         self.y = torch.zeros(s.T, s.d, dtype=dt, device=dev)
         if s.backward:
@@ -114,7 +115,7 @@ class Layer:
         if s.act == "swiglu":
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3)
         else:
-            c("sdd", bsg.sdd, self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.h)
+            c("sdd", bsg.sdd, self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.gp)
         c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp)
         c("unpermute_combine", bsg.unpermute_combine, self.yp, self.dest_row, self.gate, s.T,
           s.k, s.d, self.y)
@@ -128,7 +129,7 @@ class Layer:
           self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp)
         if not self.overlap:
             c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
-              aux_in=self.h)
+              aux_in=self.gp)
             c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
             c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None,
               s.T, s.k, s.d, self.dx)
@@ -140,7 +141,7 @@ class Layer:
             self.side.wait_event(self.ev_dyp)
             c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
         c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
-          aux_in=self.h)
+          aux_in=self.gp)
         self.ev_dh.record(main)
         with torch.cuda.stream(self.side):
             self.side.wait_event(self.ev_dh)

@@ -58,9 +58,9 @@ typedef enum { BSG_F32 = 0, BSG_BF16 = 1 } bsg_dtype;
 
 typedef enum {
     BSG_EPI_NONE = 0,     /* out = acc */
-    BSG_EPI_GELU = 1,     /* out = gelu(acc) (exact erf form); optional aux_out = acc */
+    BSG_EPI_GELU = 1,     /* out = gelu(acc) (exact erf form); optional aux_out = gelu'(acc) */
     BSG_EPI_SILU_MUL = 2, /* dual B: out = silu(acc_b) * acc_b2 */
-    BSG_EPI_GELU_BWD = 3  /* out = acc * gelu'(aux_in) */
+    BSG_EPI_GELU_BWD = 3  /* out = acc * aux_in (aux_in = saved gelu') */
 } bsg_epilogue;
 
 /* A hipStream_t passed as an opaque pointer (NULL = null stream). */
@@ -185,9 +185,10 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
  *   trans_b = 1: B[k][n] = b[n*ldb + k]    (b is [E*f, K], e.g. W2 for dgrad)
  * and the epilogue writes out_blocks[b] (block-major [nnz_max][128][128]):
  *   NONE      acc
- *   GELU      gelu(acc); if aux_out != NULL also aux_out[b] = acc (saved H)
+ *   GELU      gelu(acc); if aux_out != NULL also aux_out[b] = gelu'(acc), the
+ *             derivative the backward needs (stored in dtype)
  *   SILU_MUL  silu(acc) * acc2 where acc2 uses b2 in place of b (SwiGLU)
- *   GELU_BWD  acc * gelu'(aux_in[b])  (aux_in = saved H blocks)
+ *   GELU_BWD  acc * aux_in[b]  (aux_in = the derivative blocks saved by GELU)
  * K must be a positive multiple of 64 (bf16) or 32 (fp32).
  */
 bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, int64_t ldb,
