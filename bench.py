@@ -11,10 +11,15 @@ before the timed region.
 
 Prints ONE JSON line.  ``value`` is the useful TFLOP/s of the step
 (useful flops = 2 * T * k * d * f per product, 6 products; padded rows are
-excluded).  ``roofline`` reports the step's dominant kernel (largest time)
-against the bf16 dense MFMA peak, timed with HIP events on the stream the
-kernels run on.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
-the same workload on this host's cores.
+excluded).  In the backward the weight gradients run on a second stream
+beside the data-gradient chain.  ``roofline`` reports the step's dominant
+kernel (largest mean duration in the timed steps) against the bf16 dense
+MFMA peak, timed with HIP events on the stream each call runs on;
+``roofline_serial`` the same for a few steps after the timed region with
+every call alone.  ``traffic`` is HBM bytes per launch from the committed
+counter summary (null once the GEMM source has changed since).
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -221,6 +226,16 @@ def main():
         "kernels": kernels,
         "kernels_serial_ms": kern_serial,
     }
+    # the same figure for the kernel that dominates when every call runs
+    # alone (context: in the timed steps the weight gradients share the GPU
+    # with the data-gradient chain, which stretches both durations)
+    sg = [k for k in kern_serial if k in gemms]
+    if sg:
+        sdom = max(sg, key=lambda k: kern_serial[k])
+        sach = per_product / (kern_serial[sdom] * 1e-3) / 1e12
+        out["roofline_serial"] = {"kernel": sdom, "bound": "mfma", "achieved": round(sach, 1),
+                                  "peak": peak, "unit": "TFLOP/s", "frac": round(sach / peak, 4),
+                                  "traffic": traffic_for(sdom)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
