@@ -259,6 +259,73 @@ int64_t orc_topology(const int32_t* bin_offsets, int E, int F, int32_t* row_ptr,
     return nnz;
 }
 
+/*
+ * Gate backward: plain calculus on the gate defined above; the top-k
+ * selection is piecewise constant and passes no gradient.  For token t with
+ * picks e_j and the expert outputs yp_j the forward combined:
+ *   dg_j = sum_m dy[t, m] * yp_j[m]
+ *   g_j  = p[e_j]   (or p[e_j] / S with S = sum_i p[e_i] when renorm)
+ *   dL/dp[e]: the sum of dg_j over the picks j with e_j = e, or with renorm
+ *             dg_i / S - (sum_j dg_j p[e_j]) / S^2 at e = e_i, else 0
+ *   dlogits[t, e] = p[e] * (dL/dp[e] - sum_u p[u] dL/dp[u])    (softmax)
+ * yp holds the T*k rows in assignment order (row a = t*k + j), d values each.
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
+                       const int32_t* expert_idx, const float* dy, const double* yp, int d,
+                       double* dlogits) {
+    if (!logits || !expert_idx || !dy || !yp || !dlogits || T < 0 || E < 1 || k < 1 || k > E ||
+        d < 1)
+        return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * E);
+        double* dp = (double*)malloc(sizeof(double) * E);
+        double* dg = (double*)malloc(sizeof(double) * k);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const float* l = logits + t * E;
+            double mx = l[0];
+            for (int e = 1; e < E; ++e)
+                if (l[e] > mx) mx = l[e];
+            double z = 0.0;
+            for (int e = 0; e < E; ++e) z += exp((double)l[e] - mx);
+            for (int e = 0; e < E; ++e) p[e] = exp((double)l[e] - mx) / z;
+            for (int j = 0; j < k; ++j) {
+                const double* y = yp + (t * k + j) * (int64_t)d;
+                double s = 0.0;
+                for (int m = 0; m < d; ++m) s += (double)dy[t * d + m] * y[m];
+                dg[j] = s;
+            }
+            for (int e = 0; e < E; ++e) dp[e] = 0.0;
+            if (renorm) {
+                double S = 0.0, D = 0.0;
+                for (int j = 0; j < k; ++j) {
+                    const int e = expert_idx[t * k + j];
+                    if (e < 0 || e >= E) bad = 1;
+                    S += p[e];
+                }
+                for (int j = 0; j < k; ++j) D += dg[j] * p[expert_idx[t * k + j]];
+                for (int j = 0; j < k; ++j) dp[expert_idx[t * k + j]] += dg[j] / S - D / (S * S);
+            } else {
+                for (int j = 0; j < k; ++j) {
+                    const int e = expert_idx[t * k + j];
+                    if (e < 0 || e >= E) bad = 1;
+                    else dp[e] += dg[j];
+                }
+            }
+            double dot = 0.0;
+            for (int e = 0; e < E; ++e) dot += p[e] * dp[e];
+            for (int e = 0; e < E; ++e) dlogits[t * E + e] = p[e] * (dp[e] - dot);
+        }
+        free(p);
+        free(dp);
+        free(dg);
+    }
+    return bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------------ float layer */
 
 typedef struct {

@@ -74,6 +74,9 @@ def lib():
         L.orc_permute_pad.restype = C.c_int
         L.orc_permute_pad.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, _i32p, _f32p, C.c_int,
                                       C.c_int64, _f64p]
+        L.orc_route_backward.restype = C.c_int
+        L.orc_route_backward.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, C.c_int, _i32p,
+                                         _f32p, _f64p, C.c_int, _f64p]
         L.orc_topology.restype = C.c_int64
         L.orc_topology.argtypes = [_i32p, C.c_int, C.c_int, _i32p, _i32p, _i32p, _i32p, _i32p]
         lp = C.POINTER(_Layer)
@@ -142,6 +145,27 @@ def route(logits: np.ndarray, k: int, renorm: bool = False) -> dict:
     if rc != 0:
         raise ValueError("orc_route rejected its arguments")
     out["row_src"] = row_src[: int(out["bin_offsets"][E])].copy()
+    return out
+
+
+def route_backward(logits: np.ndarray, k: int, expert_idx: np.ndarray, dy: np.ndarray,
+                   yp_rows: np.ndarray, renorm: bool = False) -> np.ndarray:
+    """Gradient of <dy, y> with respect to the logits, [T, E] float64, given
+    the expert outputs yp_rows [T*k, d] (assignment order) the forward
+    combined; the selection is held fixed."""
+    logits = _f32(logits)
+    T, E = logits.shape
+    dy = _f32(dy)
+    yp_rows = np.ascontiguousarray(yp_rows, np.float64)
+    d = dy.shape[1]
+    if dy.shape != (T, d) or yp_rows.shape != (T * k, d):
+        raise ValueError("inconsistent shapes")
+    ei = np.ascontiguousarray(expert_idx, np.int32)
+    out = np.zeros((T, E), np.float64)
+    rc = lib().orc_route_backward(_p(logits, _f32p), T, E, k, int(bool(renorm)), _p(ei, _i32p),
+                                  _p(dy, _f32p), _p(yp_rows, _f64p), d, _p(out, _f64p))
+    if rc != 0:
+        raise ValueError("orc_route_backward rejected its arguments")
     return out
 
 
