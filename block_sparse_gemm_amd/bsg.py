@@ -28,7 +28,7 @@ EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
 
 # Every symbol include/bsg.h declares.
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
-           "bsg_permute_pad", "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dstd",
+           "bsg_route_backward", "bsg_permute_pad", "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_status_string", "bsg_last_error")
 
 
@@ -69,6 +69,9 @@ def lib():
         L.bsg_route_workspace_bytes.argtypes = [i64, i32, i32]
         L.bsg_route.restype = i32
         L.bsg_route.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.bsg_route_backward.restype = i32
+        L.bsg_route_backward.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32,
+                                         i64, vp, vp]
         L.bsg_permute_pad.restype = i32
         L.bsg_permute_pad.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp, i32, i64, vp, vp,
                                       vp]
@@ -173,6 +176,14 @@ def route(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets, wo
                                     _ptr(gate), _ptr(dest_row), _ptr(counts), _ptr(bin_offsets),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream()))
+
+
+def route_backward(logits, k, renorm, expert_idx, dest_row, dy, yp, dlogits):
+    T, E = logits.shape
+    _check("route_backward", lib().bsg_route_backward(
+        _ptr(logits), T, E, k, int(bool(renorm)), _ptr(expert_idx), _ptr(dest_row), _ptr(dy),
+        dtype_code(dy), dy.shape[1], _ptr(yp), dtype_code(yp), _ld(yp), _ptr(dlogits),
+        _stream()))
 
 
 def permute_pad(x, k, dest_row, scale, counts, bin_offsets, E, Tp_max, row_src, xp):

@@ -138,6 +138,32 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm,
                       "route");
 }
 
+bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
+                              const int32_t* expert_idx, const int32_t* dest_row, const void* dy,
+                              int dy_dtype, int d, const void* yp, int yp_dtype, int64_t ld_yp,
+                              float* dlogits, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dy_dtype) && dtype_ok(yp_dtype), "unknown dtype");
+    REQUIRE(T >= 1, "T must be positive");
+    REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
+    REQUIRE(k >= 1 && k <= E, "k must be in [1, E]");
+    if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
+    REQUIRE(T * k < INT32_MAX, "T*k must fit int32 assignment ids");
+    REQUIRE(d >= 1 && (d * elt_bytes(dy_dtype)) % 16 == 0 && (d * elt_bytes(yp_dtype)) % 16 == 0,
+            "d must keep rows 16-byte aligned");
+    REQUIRE(ld_yp >= d && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
+            "ld_yp must be >= d with 16-byte aligned rows");
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(expert_idx);
+    REQUIRE_PTR(dest_row);
+    REQUIRE_VEC_PTR(dy);
+    REQUIRE_VEC_PTR(yp);
+    REQUIRE_PTR(dlogits);
+    return hip_status(bsg::launch_route_backward(logits, T, E, k, renorm, expert_idx, dest_row, dy,
+                                                 dy_dtype, d, yp, yp_dtype, ld_yp, dlogits,
+                                                 (hipStream_t)stream),
+                      "route_backward");
+}
+
 bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                            const int32_t* dest_row, const float* scale, const int32_t* counts,
                            const int32_t* bin_offsets, int E, int64_t Tp_max, int32_t* row_src,

@@ -49,6 +49,11 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, hipStream_t stream);
 
+hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
+                                 const int32_t* expert_idx, const int32_t* dest_row,
+                                 const void* dy, int dy_dtype, int d, const void* yp,
+                                 int yp_dtype, int64_t ld_yp, float* dlogits, hipStream_t stream);
+
 hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               const int32_t* dest_row, const float* scale, const int32_t* counts,
                               const int32_t* bin_offsets, int E, int32_t* row_src, void* xp,

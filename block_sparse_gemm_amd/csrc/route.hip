@@ -214,6 +214,137 @@ __global__ __launch_bounds__(kRouteThreads) void route_place(
     }
 }
 
+// ------------------------------------------------------------ gate backward
+//
+// The gradient of <dy, y> with respect to the logits, the top-k selection
+// held fixed (plain calculus on the gate above).  One wavefront per token:
+//   dg_j   = <dy[t], yp[dest_row[t*k + j]]>        (fp32, lanes over d)
+//   dL/dp  = dg_j at e_j, or dg_j / S - (sum_i dg_i p[e_i]) / S^2 when the
+//            gates were renormalised (S = sum_i p[e_i])
+//   dlogits[t, e] = p[e] * (dL/dp[e] - sum_u p[u] dL/dp[u])
+template <int NV, int DY, int YP>
+__global__ __launch_bounds__(kRouteThreads) void route_backward_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
+    const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ dest_row,
+    const char* __restrict__ dy, int d, const char* __restrict__ yp, int64_t ld_yp_bytes,
+    float* __restrict__ dlogits) {
+    constexpr int DYE = DY == kBf16 ? 2 : 4, YPE = YP == kBf16 ? 2 : 4;
+    constexpr int V = 16 / (DYE > YPE ? DYE : YPE);  // values per lane and step
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t nwaves = (int64_t)gridDim.x * kRouteWaves;
+    for (int64_t t = (int64_t)blockIdx.x * kRouteWaves + threadIdx.x / kWave; t < T;
+         t += nwaves) {
+        // ---- dg_j, kept by lane j
+        float my_dg = 0.0f;
+        int my_e = 0;
+        for (int j = 0; j < k; ++j) {
+            const int64_t row = dest_row[t * k + j];
+            const char* yr = yp + row * ld_yp_bytes;
+            const char* dr = dy + t * (int64_t)d * DYE;
+            float s = 0.0f;
+            for (int c = lane * V; c < d; c += kWave * V) {
+#pragma unroll
+                for (int q = 0; q < V; ++q) {
+                    float a, b;
+                    if constexpr (DY == kBf16) a = bf16_to_f32(((const uint16_t*)dr)[c + q]);
+                    else a = ((const float*)dr)[c + q];
+                    if constexpr (YP == kBf16) b = bf16_to_f32(((const uint16_t*)yr)[c + q]);
+                    else b = ((const float*)yr)[c + q];
+                    s = fmaf(a, b, s);
+                }
+            }
+            s = wave_sum(s);
+            if (lane == j) {
+                my_dg = s;
+                my_e = expert_idx[t * k + j];
+            }
+        }
+        // ---- softmax of the logits (max-subtracted)
+        const float* l = logits + t * E;
+        float p[NV];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + kWave * i;
+            p[i] = e < E ? l[e] : -INFINITY;
+            mx = fmaxf(mx, p[i]);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+        float z = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + kWave * i;
+            p[i] = e < E ? expf(p[i] - mx) : 0.0f;
+            z += p[i];
+        }
+        z = wave_sum(z);
+        const float rz = 1.0f / z;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) p[i] *= rz;
+        // ---- dL/dp at the picks (lane j: expert e_j)
+        float pe = 0.0f;  // p[e_j] on lane j
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float x = __shfl(p[i], my_e & (kWave - 1), kWave);
+            if (i == (my_e >> 6)) pe = x;
+        }
+        float my_dp = my_dg;
+        if (renorm) {
+            const float S = wave_sum(lane < k ? pe : 0.0f);
+            const float D = wave_sum(lane < k ? my_dg * pe : 0.0f);
+            my_dp = my_dg / S - D / (S * S);
+        }
+        // ---- scatter to the experts' lanes, then the softmax Jacobian
+        float dp[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) dp[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int ej = __shfl(my_e, j, kWave);
+            const float dj = __shfl(my_dp, j, kWave);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (lane + kWave * i == ej) dp[i] += dj;
+        }
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) dot = fmaf(p[i], dp[i], dot);
+        dot = wave_sum(dot);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + kWave * i;
+            if (e < E) dlogits[t * E + e] = p[i] * (dp[i] - dot);
+        }
+    }
+}
+
+hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
+                                 const int32_t* expert_idx, const int32_t* dest_row,
+                                 const void* dy, int dy_dtype, int d, const void* yp,
+                                 int yp_dtype, int64_t ld_yp, float* dlogits,
+                                 hipStream_t stream) {
+    int64_t g = (T + kRouteWaves - 1) / kRouteWaves;
+    const int grid = (int)(g < 8192 ? g : 8192);
+    const int64_t ldb = ld_yp * (yp_dtype == kBf16 ? 2 : 4);
+#define BSG_RB(NV, DY, YP)                                                                      \
+    hipLaunchKernelGGL((route_backward_kernel<NV, DY, YP>), dim3(grid), dim3(kRouteThreads), 0,  \
+                       stream, logits, T, E, k, renorm, expert_idx, dest_row, (const char*)dy, d, \
+                       (const char*)yp, ldb, dlogits)
+#define BSG_RB_NV(DY, YP)                                                                       \
+    if (E <= 64) BSG_RB(1, DY, YP);                                                              \
+    else if (E <= 128) BSG_RB(2, DY, YP);                                                        \
+    else if (E <= 256) BSG_RB(4, DY, YP);                                                        \
+    else if (E <= 512) BSG_RB(8, DY, YP);                                                        \
+    else BSG_RB(16, DY, YP);
+    if (dy_dtype == kBf16 && yp_dtype == kBf16) { BSG_RB_NV(kBf16, kBf16) }
+    else if (dy_dtype == kBf16) { BSG_RB_NV(kBf16, kF32) }
+    else if (yp_dtype == kBf16) { BSG_RB_NV(kF32, kBf16) }
+    else { BSG_RB_NV(kF32, kF32) }
+#undef BSG_RB_NV
+#undef BSG_RB
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, hipStream_t stream) {

@@ -6,7 +6,8 @@ Forward (George Lin's Blog, MegaBlocks/FlexMoE post, sections 1.2-1.4):
 Backward (plain calculus on the same products, weight gradients through the
 transpose index as section 1.3 describes):
     permute_pad(dy, scale = gate) -> sdd(dYp, W2^T, GeLU') -> dsd(dH, W1^T)
-    -> unpermute_combine(gate = 1) ; dstd(A, dYp) = dW2 ; dstd(dH, Xp)^T = dW1
+    -> unpermute_combine(gate = 1) ; dstd(A, dYp) = dW2 ; dstd(dH, Xp)^T = dW1 ;
+    route_backward(dy, Yp) = dlogits (the gate's gradient, selection fixed)
 The two weight gradients run on a second stream, each as soon as its inputs
 exist (dW2 beside the GeLU' product, dW1 beside the input-gradient product),
 so the tail of one product's grid and the other's fill the GPU together.
@@ -89,6 +90,7 @@ class Layer:
             self.dx = torch.zeros(s.T, s.d, dtype=dt, device=dev)
             self.dW1 = torch.zeros(s.d, s.E * s.f, dtype=dt, device=dev)
             self.dW2 = torch.zeros(s.E * s.f, s.d, dtype=dt, device=dev)
+            self.dlogits = torch.zeros(s.T, s.E, dtype=torch.float32, device=dev)
             self.side = torch.cuda.Stream(device=dev)  # default priority
             self.ev_dyp = torch.cuda.Event()
             self.ev_dh = torch.cuda.Event()
@@ -107,6 +109,7 @@ class Layer:
     def forward(self, x, logits, W1, W2, W3=None):
         s, t = self.s, self.topo
         c = self._call
+        self.logits = logits  # the gate backward differentiates through it
         c("route", bsg.route, logits, s.k, s.renorm, self.expert_idx, self.gate, self.dest_row,
           self.counts, self.bin_offsets, self.route_ws)
         c("permute_pad", bsg.permute_pad, x, s.k, self.dest_row, None, self.counts,
@@ -128,6 +131,8 @@ class Layer:
         c("permute_pad_bwd", bsg.permute_pad, dy, s.k, self.dest_row, self.gate, self.counts,
           self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp)
         if not self.overlap:
+            c("route_backward", bsg.route_backward, self.logits, s.k, s.renorm, self.expert_idx,
+              self.dest_row, dy, self.yp, self.dlogits)
             c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
               aux_in=self.gp)
             c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
@@ -139,6 +144,8 @@ class Layer:
         self.ev_dyp.record(main)
         with torch.cuda.stream(self.side):
             self.side.wait_event(self.ev_dyp)
+            c("route_backward", bsg.route_backward, self.logits, s.k, s.renorm, self.expert_idx,
+              self.dest_row, dy, self.yp, self.dlogits)
             c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
         c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
           aux_in=self.gp)

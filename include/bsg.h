@@ -152,6 +152,24 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, i
                      void* workspace, size_t workspace_bytes, bsg_stream_t stream);
 
 /*
+ * route_backward - gradient of <dy, y> with respect to the router logits for
+ * the gate of bsg_route (plain calculus on it; the top-k selection is held
+ * fixed, it passes no gradient):
+ *   dg_j = sum_m dy[t][m] * yp[dest_row[t*k + j]][m]
+ *   dL/dp[e_j] = dg_j, or with renorm dg_j / S - (sum_i dg_i p[e_i]) / S^2
+ *                (S = sum_i p[e_i]); 0 for experts not picked
+ *   dlogits[t][e] = p[e] * (dL/dp[e] - sum_u p[u] dL/dp[u]),  p = softmax
+ *   logits [T, E] fp32 (as given to bsg_route); expert_idx, dest_row [T*k]
+ *   from bsg_route; dy [T, d] (dy_dtype) the gradient of the combined output
+ *   y; yp [Tp_max, ld_yp] (yp_dtype) the expert outputs the forward combined;
+ *   dlogits [T, E] fp32 out.  fp32 arithmetic.  Same limits as bsg_route.
+ */
+bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
+                              const int32_t* expert_idx, const int32_t* dest_row, const void* dy,
+                              int dy_dtype, int d, const void* yp, int yp_dtype, int64_t ld_yp,
+                              float* dlogits, bsg_stream_t stream);
+
+/*
  * permute_pad - fused permutation + padding (section 1.4 and the padding
  * paragraph of section 1.3): row dest_row[a] of xp receives row a/k of x,
  * times scale[a] when scale is not NULL (the product is rounded once to the

@@ -83,6 +83,28 @@ def test_route_validation(L):
     assert call(counts=C.c_void_p(0x10002)) == bsg.EINVAL
 
 
+def test_route_backward_validation(L):
+    ok = [P, 100, 8, 2, 0, P, P, P, bsg.BF16, 128, P, bsg.BF16, 128, P, None]
+    names = ["logits", "T", "E", "k", "renorm", "expert_idx", "dest_row", "dy", "dyt", "d", "yp",
+             "ypt", "ld", "dlogits", "stream"]
+
+    def call(**over):
+        a = list(ok)
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_route_backward(*a)
+
+    assert call(logits=None) == bsg.EINVAL
+    assert call(T=0) == bsg.EINVAL
+    assert call(k=9) == bsg.EINVAL
+    assert call(E=64, k=40) == bsg.EUNSUPPORTED
+    assert call(d=100) == bsg.EINVAL
+    assert call(ld=64) == bsg.EINVAL
+    assert call(dyt=7) == bsg.EINVAL
+    assert call(yp=MIS) == bsg.EINVAL
+    assert call(dlogits=None) == bsg.EINVAL
+
+
 def test_permute_pad_validation(L):
     T, d, k, E = 100, 128, 2, 8
     Tp = bsg.max_padded_rows(T, k, E)

@@ -190,6 +190,14 @@ def check_case(orc, case: Case, seed=0):
         # dW1 [d, E*f]: rows = model dims, cols = expert hidden units
         got1 = f64(L.dW1[torch.from_numpy(wc).cuda()][:, torch.from_numpy(wr).cuda()])
         check_float("dW1", got1, O.dW1_block(wc, wr), prec, report)
+        # gate backward on the sampled tokens: the oracle differentiates its
+        # own stored Yp, the GPU its own
+        # (Yp rows are in assignment order: token toks[i]'s k rows at i*k + j)
+        want_dl = orc.route_backward(inp["logits"][toks], cfg.k,
+                                     r["expert_idx"].reshape(cfg.T, cfg.k)[toks].reshape(-1),
+                                     inp["dy"].values[toks], Yp, cfg.renorm)
+        got_dl = L.dlogits[torch.from_numpy(toks).cuda()].cpu().numpy().astype(np.float64)
+        check_float("dlogits", got_dl, want_dl, prec, report)
         empty = np.nonzero(r["counts"] == 0)[0]
         for e in empty:  # experts without tokens: exactly zero weight gradients
             assert torch.count_nonzero(L.dW2[e * cfg.f:(e + 1) * cfg.f]).item() == 0
