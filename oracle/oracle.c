@@ -17,8 +17,8 @@
  *
  * Arithmetic: every sum is accumulated in fp64 in ascending index order and
  * never reassociated.  Values are rounded to the storage precision at the
- * points where the layer stores an intermediate (A, G, Yp, y, dYp, dH, dXp,
- * dx, dW); ORC_F64 disables every rounding (used by the finite-difference
+ * points where the layer stores an intermediate (A, the saved factors, Yp,
+ * y, dYp, dH, dXp, dx, dW); ORC_F64 disables every rounding (used by the finite-difference
  * and library cross-checks).
  *
  * Readings of points the pages leave open (each is listed with its reason in
@@ -31,8 +31,9 @@
  *     pad rows are zero;
  *   - exact erf GeLU; SwiGLU = silu(x W1) * (x W3);
  *   - the block-diagonal matrix is the first layer's output [Tp x E*f];
- *   - what the backward keeps of the forward is GeLU'(h), stored (rounded)
- *     next to A; the backward multiplies by it.
+ *   - what the backward keeps of the forward is GeLU'(h) (SwiGLU: silu(h)
+ *     and u * silu'(h)), stored (rounded) next to A; the backward multiplies
+ *     by it.
  *
  * Parity pins: none of the pages prints a worked numeric example, so every
  * function here is pinned by closed forms, invariants, library routines on
@@ -92,9 +93,16 @@ static double gelu_grad(double h) {
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* d/dz silu(z) = sigma(z) (1 + z (1 - sigma(z))),  sigma(z) = 1 / (1 + exp(-z)) */
+static double silu_grad(double z) {
+    const double sg = 1.0 / (1.0 + exp(-z));
+    return sg * (1.0 + z * (1.0 - sg));
+}
+
 double orc_gelu(double h) { return gelu(h); }
 double orc_gelu_grad(double h) { return gelu_grad(h); }
 double orc_silu(double z) { return silu(z); }
+double orc_silu_grad(double z) { return silu_grad(z); }
 
 /* ---------------------------------------------------------------- threads */
 
@@ -349,12 +357,17 @@ static int layer_ok(const orc_layer* L) {
 }
 
 /* First layer and activation for one assignment (section 1.2: layer one,
- * activation):  h[n] = sum_i x[t,i] W1[i, e*f+n];  A = act(h).
- * h gets the unrounded pre-activation (fp64); G_out (GeLU only) the stored
- * derivative act'(h), which is what the backward pass keeps of the forward
- * (its one rounding point between the passes). */
-static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, double* G_out,
-                        double* A_out) {
+ * then the activation):
+ *   h[n] = sum_i x[t,i] W1[i, e*f+n];  SwiGLU also u[n] = sum_i x[t,i] W3[i, e*f+n]
+ *   A[n] = rd(gelu(h[n]))  or  rd(silu(h[n]) * u[n])
+ * h and u stay unrounded (fp64).  S0 / S1 receive what the backward keeps of
+ * the forward, rounded where it is stored (the one rounding point between
+ * the passes):
+ *   GeLU    S0 = rd(gelu'(h))                       (dH = dA * S0)
+ *   SwiGLU  S0 = rd(silu(h)), S1 = rd(u * silu'(h)) (dH_up = dA * S0,
+ *                                                    dH_gate = dA * S1) */
+static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, double* S0,
+                        double* S1, double* A_out) {
     const int64_t t = a / L->k;
     const int e = L->expert_idx[a];
     const int64_t ldw = (int64_t)L->E * L->f;
@@ -373,13 +386,14 @@ static void first_layer(const orc_layer* L, int64_t a, double* h, double* hu, do
         }
     }
     for (int n = 0; n < L->f; ++n) {
-        double av;
-        if (L->act == ORC_ACT_SWIGLU)
-            av = silu(h[n]) * hu[n];
-        else
-            av = gelu(h[n]);
-        if (A_out) A_out[n] = rd(av, L->prec);
-        if (G_out) G_out[n] = rd(gelu_grad(h[n]), L->prec);
+        if (L->act == ORC_ACT_SWIGLU) {
+            if (A_out) A_out[n] = rd(silu(h[n]) * hu[n], L->prec);
+            if (S0) S0[n] = rd(silu(h[n]), L->prec);
+            if (S1) S1[n] = rd(hu[n] * silu_grad(h[n]), L->prec);
+        } else {
+            if (A_out) A_out[n] = rd(gelu(h[n]), L->prec);
+            if (S0) S0[n] = rd(gelu_grad(h[n]), L->prec);
+        }
     }
 }
 
@@ -395,20 +409,23 @@ static void second_layer(const orc_layer* L, int64_t a, const double* A, double*
     for (int m = 0; m < L->d; ++m) Yp[m] = rd(acc[m], L->prec_yp);
 }
 
+static double* dalloc(int64_t n) { return (double*)malloc(sizeof(double) * (size_t)n); }
+
 /*
- * Per-assignment forward: G (stored activation derivative, gelu only; may be
- * NULL), A (stored activation) [n, f], Yp (expert output) [n, d] for the
- * listed assignments.
+ * Per-assignment forward for the listed assignments, each array [n, f] or
+ * [n, d]: S0, S1 the saved factors of first_layer (S1 SwiGLU only; either
+ * may be NULL), A the stored activation, Yp the expert output.
  */
-int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, double* G,
-                       double* A, double* Yp) {
+int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, double* S0,
+                       double* S1, double* A, double* Yp) {
     if (!layer_ok(L) || !assigns || !A || !Yp) return -1;
+    const int swiglu = L->act == ORC_ACT_SWIGLU;
     int bad = 0;
 #pragma omp parallel
     {
-        double* h = (double*)malloc(sizeof(double) * L->f);
-        double* hu = L->act == ORC_ACT_SWIGLU ? (double*)malloc(sizeof(double) * L->f) : NULL;
-        double* acc = (double*)malloc(sizeof(double) * L->d);
+        double* h = dalloc(L->f);
+        double* hu = swiglu ? dalloc(L->f) : NULL;
+        double* acc = dalloc(L->d);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < n; ++q) {
             int64_t a = assigns[q];
@@ -416,7 +433,8 @@ int orc_assign_forward(const orc_layer* L, const int64_t* assigns, int64_t n, do
                 bad = 1;
                 continue;
             }
-            first_layer(L, a, h, hu, G ? G + q * L->f : NULL, A + q * L->f);
+            first_layer(L, a, h, hu, S0 ? S0 + q * L->f : NULL,
+                        S1 && swiglu ? S1 + q * L->f : NULL, A + q * L->f);
             second_layer(L, a, A + q * L->f, acc, Yp + q * L->d);
         }
         free(h);
@@ -436,12 +454,12 @@ int orc_forward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, dou
     int bad = 0;
 #pragma omp parallel
     {
-        double* h = (double*)malloc(sizeof(double) * L->f);
-        double* hu = L->act == ORC_ACT_SWIGLU ? (double*)malloc(sizeof(double) * L->f) : NULL;
-        double* A = (double*)malloc(sizeof(double) * L->f);
-        double* acc = (double*)malloc(sizeof(double) * L->d);
-        double* yp = (double*)malloc(sizeof(double) * L->d);
-        double* sum = (double*)malloc(sizeof(double) * L->d);
+        double* h = dalloc(L->f);
+        double* hu = L->act == ORC_ACT_SWIGLU ? dalloc(L->f) : NULL;
+        double* A = dalloc(L->f);
+        double* acc = dalloc(L->d);
+        double* yp = dalloc(L->d);
+        double* sum = dalloc(L->d);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < n; ++q) {
             int64_t t = tokens[q];
@@ -452,7 +470,7 @@ int orc_forward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, dou
             for (int m = 0; m < L->d; ++m) sum[m] = 0.0;
             for (int j = 0; j < L->k; ++j) {
                 int64_t a = t * L->k + j;
-                first_layer(L, a, h, hu, NULL, A);
+                first_layer(L, a, h, hu, NULL, NULL, A);
                 second_layer(L, a, A, acc, yp);
                 const double g = L->gate[a];
                 for (int m = 0; m < L->d; ++m) sum[m] += g * yp[m];
@@ -471,48 +489,90 @@ int orc_forward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, dou
 
 /* ---------------------------------------------------------------- backward */
 
+/* Scratch rows of one backward worker. */
+typedef struct {
+    double *h, *hu, *S0, *S1, *dYp, *dH, *dHu, *dXp;
+} bwd_scratch;
+
+static bwd_scratch bwd_alloc(const orc_layer* L) {
+    bwd_scratch w;
+    const int sw = L->act == ORC_ACT_SWIGLU;
+    w.h = dalloc(L->f);
+    w.hu = sw ? dalloc(L->f) : NULL;
+    w.S0 = dalloc(L->f);
+    w.S1 = sw ? dalloc(L->f) : NULL;
+    w.dYp = dalloc(L->d);
+    w.dH = dalloc(L->f);
+    w.dHu = sw ? dalloc(L->f) : NULL;
+    w.dXp = dalloc(L->d);
+    return w;
+}
+
+static void bwd_free(bwd_scratch* w) {
+    free(w->h);
+    free(w->hu);
+    free(w->S0);
+    free(w->S1);
+    free(w->dYp);
+    free(w->dH);
+    free(w->dHu);
+    free(w->dXp);
+}
+
 /*
  * Backward data path of one assignment (plain calculus on section 1.2's
- * SDD -> activation -> DSD; GeLU experts only):
+ * SDD -> activation -> DSD), into w->dYp, w->dH, w->dHu, w->dXp:
  *   dYp[m] = rd(gate * dy[t, m])
  *   da[n]  = sum_m dYp[m] W2[e*f+n, m]
- *   dH[n]  = rd(da[n] * G[n])             G = rd(gelu'(h)), stored by the forward
- *   dXp[i] = rd_yp(sum_n dH[n] W1[i, e*f+n])
+ *   GeLU    dH[n]  = rd(da[n] * S0[n])                 S0 = rd(gelu'(h))
+ *           dXp[i] = rd_yp(sum_n dH[n] W1[i, e*f+n])
+ *   SwiGLU  dH[n]  = rd(da[n] * S1[n])  gate projection, S1 = rd(u silu'(h))
+ *           dHu[n] = rd(da[n] * S0[n])  up projection,   S0 = rd(silu(h))
+ *           dXp[i] = rd_yp(sum_n dH[n] W1[i, e*f+n] + sum_n dHu[n] W3[i, e*f+n])
  */
-static void assign_backward(const orc_layer* L, int64_t a, double* h, double* G, double* dYp,
-                            double* dH, double* dXp) {
+static void assign_backward(const orc_layer* L, int64_t a, bwd_scratch* w) {
     const int64_t t = a / L->k;
     const int e = L->expert_idx[a];
     const int64_t ldw = (int64_t)L->E * L->f;
     const double g = L->gate[a];
-    first_layer(L, a, h, NULL, G, NULL);
-    for (int m = 0; m < L->d; ++m) dYp[m] = rd(g * (double)L->dy[t * L->d + m], L->prec);
+    const int sw = L->act == ORC_ACT_SWIGLU;
+    first_layer(L, a, w->h, w->hu, w->S0, w->S1, NULL);
+    for (int m = 0; m < L->d; ++m) w->dYp[m] = rd(g * (double)L->dy[t * L->d + m], L->prec);
     for (int n = 0; n < L->f; ++n) {
-        const float* w = L->W2 + ((int64_t)e * L->f + n) * L->d;
+        const float* w2 = L->W2 + ((int64_t)e * L->f + n) * L->d;
         double da = 0.0;
-        for (int m = 0; m < L->d; ++m) da += dYp[m] * (double)w[m];
-        dH[n] = rd(da * G[n], L->prec);
+        for (int m = 0; m < L->d; ++m) da += w->dYp[m] * (double)w2[m];
+        if (sw) {
+            w->dH[n] = rd(da * w->S1[n], L->prec);
+            w->dHu[n] = rd(da * w->S0[n], L->prec);
+        } else {
+            w->dH[n] = rd(da * w->S0[n], L->prec);
+        }
     }
     for (int i = 0; i < L->d; ++i) {
-        const float* w = L->W1 + i * ldw + (int64_t)e * L->f;
+        const float* w1 = L->W1 + i * ldw + (int64_t)e * L->f;
         double s = 0.0;
-        for (int n = 0; n < L->f; ++n) s += dH[n] * (double)w[n];
-        dXp[i] = rd(s, L->prec_yp);
+        for (int n = 0; n < L->f; ++n) s += w->dH[n] * (double)w1[n];
+        if (sw) {
+            const float* w3 = L->W3 + i * ldw + (int64_t)e * L->f;
+            double s3 = 0.0;
+            for (int n = 0; n < L->f; ++n) s3 += w->dHu[n] * (double)w3[n];
+            s += s3;
+        }
+        w->dXp[i] = rd(s, L->prec_yp);
     }
 }
 
-/* Per-assignment backward rows: dYp [n,d], dH [n,f], dXp [n,d]. */
+/* Per-assignment backward rows: dYp [n,d], dH [n,f], dHu [n,f] (SwiGLU
+ * only; may be NULL), dXp [n,d]. */
 int orc_assign_backward(const orc_layer* L, const int64_t* assigns, int64_t n, double* dYp,
-                        double* dH, double* dXp) {
-    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !assigns) return -1;
+                        double* dH, double* dHu, double* dXp) {
+    if (!layer_ok(L) || !L->dy || !assigns) return -1;
+    const int sw = L->act == ORC_ACT_SWIGLU;
     int bad = 0;
 #pragma omp parallel
     {
-        double* h = (double*)malloc(sizeof(double) * L->f);
-        double* G = (double*)malloc(sizeof(double) * L->f);
-        double* ldyp = (double*)malloc(sizeof(double) * L->d);
-        double* ldh = (double*)malloc(sizeof(double) * L->f);
-        double* ldxp = (double*)malloc(sizeof(double) * L->d);
+        bwd_scratch w = bwd_alloc(L);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < n; ++q) {
             int64_t a = assigns[q];
@@ -520,32 +580,25 @@ int orc_assign_backward(const orc_layer* L, const int64_t* assigns, int64_t n, d
                 bad = 1;
                 continue;
             }
-            assign_backward(L, a, h, G, ldyp, ldh, ldxp);
-            if (dYp) memcpy(dYp + q * L->d, ldyp, sizeof(double) * L->d);
-            if (dH) memcpy(dH + q * L->f, ldh, sizeof(double) * L->f);
-            if (dXp) memcpy(dXp + q * L->d, ldxp, sizeof(double) * L->d);
+            assign_backward(L, a, &w);
+            if (dYp) memcpy(dYp + q * L->d, w.dYp, sizeof(double) * L->d);
+            if (dH) memcpy(dH + q * L->f, w.dH, sizeof(double) * L->f);
+            if (dHu && sw) memcpy(dHu + q * L->f, w.dHu, sizeof(double) * L->f);
+            if (dXp) memcpy(dXp + q * L->d, w.dXp, sizeof(double) * L->d);
         }
-        free(h);
-        free(G);
-        free(ldyp);
-        free(ldh);
-        free(ldxp);
+        bwd_free(&w);
     }
     return bad ? -1 : 0;
 }
 
 /* Input gradient for the listed tokens: dx[t, i] = rd(sum_j dXp_{t,j}[i]). */
 int orc_backward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, double* dx) {
-    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !tokens || !dx) return -1;
+    if (!layer_ok(L) || !L->dy || !tokens || !dx) return -1;
     int bad = 0;
 #pragma omp parallel
     {
-        double* h = (double*)malloc(sizeof(double) * L->f);
-        double* G = (double*)malloc(sizeof(double) * L->f);
-        double* dYp = (double*)malloc(sizeof(double) * L->d);
-        double* dH = (double*)malloc(sizeof(double) * L->f);
-        double* dXp = (double*)malloc(sizeof(double) * L->d);
-        double* sum = (double*)malloc(sizeof(double) * L->d);
+        bwd_scratch w = bwd_alloc(L);
+        double* sum = dalloc(L->d);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < n; ++q) {
             int64_t t = tokens[q];
@@ -555,16 +608,12 @@ int orc_backward_tokens(const orc_layer* L, const int64_t* tokens, int64_t n, do
             }
             for (int i = 0; i < L->d; ++i) sum[i] = 0.0;
             for (int j = 0; j < L->k; ++j) {
-                assign_backward(L, t * L->k + j, h, G, dYp, dH, dXp);
-                for (int i = 0; i < L->d; ++i) sum[i] += dXp[i];
+                assign_backward(L, t * L->k + j, &w);
+                for (int i = 0; i < L->d; ++i) sum[i] += w.dXp[i];
             }
             for (int i = 0; i < L->d; ++i) dx[q * L->d + i] = rd(sum[i], L->prec);
         }
-        free(h);
-        free(G);
-        free(dYp);
-        free(dH);
-        free(dXp);
+        bwd_free(&w);
         free(sum);
     }
     return bad ? -1 : 0;
@@ -578,6 +627,19 @@ static int64_t expert_assignments(const orc_layer* L, int e, int64_t* out) {
     return c;
 }
 
+/* First-layer pre-activations of hidden unit col (= e*f + n) for one
+ * assignment: h through W1 and, for SwiGLU, u through W3 (fp64). */
+static void hidden_unit(const orc_layer* L, int64_t a, int64_t col, double* h, double* u) {
+    const int64_t ldw = (int64_t)L->E * L->f;
+    const float* xr = L->x + (a / L->k) * L->d;
+    double s = 0.0, s3 = 0.0;
+    for (int i = 0; i < L->d; ++i) s += (double)xr[i] * (double)L->W1[i * ldw + col];
+    if (L->act == ORC_ACT_SWIGLU)
+        for (int i = 0; i < L->d; ++i) s3 += (double)xr[i] * (double)L->W3[i * ldw + col];
+    *h = s;
+    *u = s3;
+}
+
 /*
  * Weight gradient of the second layer (section 1.3 "transpose indices": the
  * weight gradient is the product of the transposed sparse activation with
@@ -589,14 +651,13 @@ static int64_t expert_assignments(const orc_layer* L, int e, int64_t* out) {
  */
 int orc_dW2_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int64_t* cols,
                   int64_t nc, double* out) {
-    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !rows || !cols || !out) return -1;
+    if (!layer_ok(L) || !L->dy || !rows || !cols || !out) return -1;
     const int64_t ldw = (int64_t)L->E * L->f;
     int bad = 0;
 #pragma omp parallel
     {
         int64_t* as = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L->T * L->k));
-        double* an = (double*)malloc(sizeof(double) * (size_t)(L->T * L->k));
-        double* wcol = (double*)malloc(sizeof(double) * L->d);
+        double* an = dalloc(L->T * L->k);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t p = 0; p < nr; ++p) {
             int64_t row = rows[p];
@@ -606,13 +667,11 @@ int orc_dW2_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
             }
             int e = (int)(row / L->f);
             int64_t c = expert_assignments(L, e, as);
-            for (int i = 0; i < L->d; ++i) wcol[i] = L->W1[i * ldw + row];
             /* A_a[n] for every assignment of the expert */
             for (int64_t q = 0; q < c; ++q) {
-                const float* xr = L->x + (as[q] / L->k) * L->d;
-                double h = 0.0;
-                for (int i = 0; i < L->d; ++i) h += (double)xr[i] * wcol[i];
-                an[q] = rd(gelu(h), L->prec);
+                double h, u;
+                hidden_unit(L, as[q], row, &h, &u);
+                an[q] = rd(L->act == ORC_ACT_SWIGLU ? silu(h) * u : gelu(h), L->prec);
             }
             for (int64_t s = 0; s < nc; ++s) {
                 int64_t m = cols[s];
@@ -632,27 +691,30 @@ int orc_dW2_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
         }
         free(as);
         free(an);
-        free(wcol);
     }
     return bad ? -1 : 0;
 }
 
 /*
- * Weight gradient of the first layer:
- *   dW1[i, e*f+n] = rd(sum over assignments a of expert e, ascending,
- *                      of x[t_a, i] * dH_a[n])
- * for every (rows[p] = i, cols[q] = e*f+n) pair; out is [nr, nc].
+ * Weight gradient of a first-layer projection (proj 0: W1, proj 1: W3,
+ * SwiGLU only):
+ *   dW[i, e*f+n] = rd(sum over assignments a of expert e, ascending,
+ *                     of x[t_a, i] * dH_a[n])
+ * with dH the gradient of that projection's pre-activation as in
+ * assign_backward, for every (rows[p] = i, cols[q] = e*f+n) pair; out is
+ * [nr, nc].
  */
-int orc_dW1_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int64_t* cols,
-                  int64_t nc, double* out) {
-    if (!layer_ok(L) || !L->dy || L->act != ORC_ACT_GELU || !rows || !cols || !out) return -1;
+static int input_weight_grad(const orc_layer* L, int proj, const int64_t* rows, int64_t nr,
+                             const int64_t* cols, int64_t nc, double* out) {
+    if (!layer_ok(L) || !L->dy || !rows || !cols || !out) return -1;
+    if (proj == 1 && L->act != ORC_ACT_SWIGLU) return -1;
     const int64_t ldw = (int64_t)L->E * L->f;
+    const int sw = L->act == ORC_ACT_SWIGLU;
     int bad = 0;
 #pragma omp parallel
     {
         int64_t* as = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L->T * L->k));
-        double* dh = (double*)malloc(sizeof(double) * (size_t)(L->T * L->k));
-        double* wcol = (double*)malloc(sizeof(double) * L->d);
+        double* dh = dalloc(L->T * L->k);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t s = 0; s < nc; ++s) {
             int64_t col = cols[s];
@@ -662,20 +724,22 @@ int orc_dW1_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
             }
             int e = (int)(col / L->f);
             int64_t c = expert_assignments(L, e, as);
-            for (int i = 0; i < L->d; ++i) wcol[i] = L->W1[i * ldw + col];
             const float* w2 = L->W2 + col * L->d;
             for (int64_t q = 0; q < c; ++q) {
                 int64_t a = as[q];
                 const int64_t t = a / L->k;
-                const float* xr = L->x + t * L->d;
-                double h = 0.0;
-                for (int i = 0; i < L->d; ++i) h += (double)xr[i] * wcol[i];
+                double h, u;
+                hidden_unit(L, a, col, &h, &u);
                 double da = 0.0;
                 for (int m = 0; m < L->d; ++m) {
                     double dyp = rd((double)L->gate[a] * (double)L->dy[t * L->d + m], L->prec);
                     da += dyp * (double)w2[m];
                 }
-                dh[q] = rd(da * rd(gelu_grad(h), L->prec), L->prec);
+                double saved;
+                if (!sw) saved = gelu_grad(h);
+                else if (proj == 0) saved = u * silu_grad(h);
+                else saved = silu(h);
+                dh[q] = rd(da * rd(saved, L->prec), L->prec);
             }
             for (int64_t p = 0; p < nr; ++p) {
                 int64_t i = rows[p];
@@ -691,7 +755,16 @@ int orc_dW1_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
         }
         free(as);
         free(dh);
-        free(wcol);
     }
     return bad ? -1 : 0;
+}
+
+int orc_dW1_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int64_t* cols,
+                  int64_t nc, double* out) {
+    return input_weight_grad(L, 0, rows, nr, cols, nc, out);
+}
+
+int orc_dW3_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int64_t* cols,
+                  int64_t nc, double* out) {
+    return input_weight_grad(L, 1, rows, nr, cols, nc, out);
 }

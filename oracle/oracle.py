@@ -63,7 +63,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.orc_round.restype = C.c_double
         L.orc_round.argtypes = [C.c_double, C.c_int]
-        for name in ("orc_gelu", "orc_gelu_grad", "orc_silu"):
+        for name in ("orc_gelu", "orc_gelu_grad", "orc_silu", "orc_silu_grad"):
             getattr(L, name).restype = C.c_double
             getattr(L, name).argtypes = [C.c_double]
         L.orc_set_threads.argtypes = [C.c_int]
@@ -80,14 +80,14 @@ def lib():
         L.orc_topology.restype = C.c_int64
         L.orc_topology.argtypes = [_i32p, C.c_int, C.c_int, _i32p, _i32p, _i32p, _i32p, _i32p]
         lp = C.POINTER(_Layer)
-        L.orc_assign_forward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p]
+        L.orc_assign_forward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p, _f64p]
         L.orc_forward_tokens.argtypes = [lp, _i64p, C.c_int64, _f64p]
-        L.orc_assign_backward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p]
+        L.orc_assign_backward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p, _f64p]
         L.orc_backward_tokens.argtypes = [lp, _i64p, C.c_int64, _f64p]
-        L.orc_dW2_block.argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
-        L.orc_dW1_block.argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
+        for n in ("orc_dW2_block", "orc_dW1_block", "orc_dW3_block"):
+            getattr(L, n).argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
         for n in ("orc_assign_forward", "orc_forward_tokens", "orc_assign_backward",
-                  "orc_backward_tokens", "orc_dW2_block", "orc_dW1_block"):
+                  "orc_backward_tokens", "orc_dW2_block", "orc_dW1_block", "orc_dW3_block"):
             getattr(L, n).restype = C.c_int
         _lib = L
     return _lib
@@ -123,6 +123,10 @@ def gelu_grad(h: float) -> float:
 
 def silu(z: float) -> float:
     return lib().orc_silu(float(z))
+
+
+def silu_grad(z: float) -> float:
+    return lib().orc_silu_grad(float(z))
 
 
 def route(logits: np.ndarray, k: int, renorm: bool = False) -> dict:
@@ -206,9 +210,10 @@ def topology(bin_offsets: np.ndarray, E: int, F: int) -> dict:
 class Layer:
     """Float oracle of one layer call.
 
-    ``prec`` is the storage precision of A, G (= GeLU'(h), what the backward
-    keeps), dYp, dH, y, dx and the weight gradients; ``prec_yp`` that of Yp
-    and dXp ("f64" disables rounding)."""
+    ``prec`` is the storage precision of A, the saved factors (what the
+    backward keeps: GeLU'(h); SwiGLU silu(h) and u * silu'(h)), dYp, dH, y,
+    dx and the weight gradients; ``prec_yp`` that of Yp and dXp ("f64"
+    disables rounding)."""
 
     def __init__(self, x, W1, W2, expert_idx, gate, k, E, act="gelu", W3=None, dy=None,
                  prec="bf16", prec_yp=None):
@@ -242,16 +247,23 @@ class Layer:
         if rc != 0:
             raise ValueError(f"{name} rejected its arguments")
 
+    @property
+    def swiglu(self):
+        return self._s.act == ACT["swiglu"]
+
     def assign_forward(self, assigns):
-        """Per assignment: G = rd(GeLU'(h)) (GeLU only), A = rd(act(h)), Yp."""
+        """Per assignment: the saved factors G, A = rd(act(h)), Yp.
+
+        G is [n, f] = rd(GeLU'(h)) for GeLU; for SwiGLU it is [2, n, f]:
+        G[0] = rd(silu(h)), G[1] = rd(u * silu'(h))."""
         a = np.ascontiguousarray(assigns, np.int64)
         n = len(a)
-        G = np.zeros((n, self.f))
+        G = np.zeros((2, n, self.f) if self.swiglu else (1, n, self.f))
         A = np.zeros((n, self.f))
         Yp = np.zeros((n, self.d))
-        self._call("orc_assign_forward", _p(a, _i64p), n, _p(G, _f64p), _p(A, _f64p),
-                   _p(Yp, _f64p))
-        return G, A, Yp
+        self._call("orc_assign_forward", _p(a, _i64p), n, _p(G[0], _f64p),
+                   _p(G[1], _f64p) if self.swiglu else None, _p(A, _f64p), _p(Yp, _f64p))
+        return (G if self.swiglu else G[0]), A, Yp
 
     def forward_tokens(self, tokens):
         t = np.ascontiguousarray(tokens, np.int64)
@@ -260,14 +272,17 @@ class Layer:
         return y
 
     def assign_backward(self, assigns):
+        """Per assignment: dYp, dH, dXp.  dH is [n, f] for GeLU; for SwiGLU it
+        is [2, n, f]: dH[0] the gate projection's (pairs with W1), dH[1] the
+        up projection's (pairs with W3)."""
         a = np.ascontiguousarray(assigns, np.int64)
         n = len(a)
         dYp = np.zeros((n, self.d))
-        dH = np.zeros((n, self.f))
+        dH = np.zeros((2, n, self.f) if self.swiglu else (1, n, self.f))
         dXp = np.zeros((n, self.d))
-        self._call("orc_assign_backward", _p(a, _i64p), n, _p(dYp, _f64p), _p(dH, _f64p),
-                   _p(dXp, _f64p))
-        return dYp, dH, dXp
+        self._call("orc_assign_backward", _p(a, _i64p), n, _p(dYp, _f64p), _p(dH[0], _f64p),
+                   _p(dH[1], _f64p) if self.swiglu else None, _p(dXp, _f64p))
+        return dYp, (dH if self.swiglu else dH[0]), dXp
 
     def backward_tokens(self, tokens):
         t = np.ascontiguousarray(tokens, np.int64)
@@ -287,6 +302,15 @@ class Layer:
         c = np.ascontiguousarray(cols, np.int64)
         out = np.zeros((len(r), len(c)))
         self._call("orc_dW1_block", _p(r, _i64p), len(r), _p(c, _i64p), len(c), _p(out, _f64p))
+        return out
+
+    def dW3_block(self, rows, cols):
+        """Gradient of W3 (SwiGLU's up projection) at (rows = model dims,
+        cols = hidden units)."""
+        r = np.ascontiguousarray(rows, np.int64)
+        c = np.ascontiguousarray(cols, np.int64)
+        out = np.zeros((len(r), len(c)))
+        self._call("orc_dW3_block", _p(r, _i64p), len(r), _p(c, _i64p), len(c), _p(out, _f64p))
         return out
 
 
