@@ -5,13 +5,15 @@ Workload (default): the MoE-Small-shaped layer, T = 32768 tokens (32 x 1024),
 d = 768, E = 64 experts, f = 3072 per expert, top-1, GeLU, bf16 with fp32
 accumulation, per-expert logit bias N(0, 0.5); forward + backward:
 route, permute_pad, build_topology, SDD(+GeLU), DSD, unpermute_combine,
-then permute_pad(dy * gate), SDD(GeLU'), DSD, unpermute_combine,
-DSTD (dW2), DSTD (dW1).  Inputs are seeded synthetic draws resident in HBM
-before the timed region.
+then permute_pad(dy * gate), route_backward, SDD(GeLU'), DSD,
+unpermute_combine, DSTD (dW2), DSTD (dW1).  ``--config mixtral_train``
+runs the Mixtral-shaped SwiGLU layer (T = 8192, d = 4096, E = 8,
+f = 14336, top-2) forward + backward instead.  Inputs are seeded synthetic
+draws resident in HBM before the timed region.
 
 Prints ONE JSON line.  ``value`` is the useful TFLOP/s of the step
-(useful flops = 2 * T * k * d * f per product, 6 products; padded rows are
-excluded).  In the backward the weight gradients run on a second stream
+(useful flops = 2 * T * k * d * f per product; 6 products with GeLU
+experts, 9 with SwiGLU ones; padded rows are excluded).  In the backward the weight gradients run on a second stream
 beside the data-gradient chain.  ``roofline`` reports the step's dominant
 kernel (largest mean duration in the timed steps) against the bf16 dense
 MFMA peak, timed with HIP events on the stream each call runs on;
@@ -52,11 +54,22 @@ def parse():
     return ap.parse_args()
 
 
+def products_of(cfg, kernel):
+    """GEMM products (2 * T * k * d * f useful flops each) one call performs:
+    SwiGLU's forward SDD has two B operands and its input-gradient DSD two
+    block sets."""
+    sw = cfg.act == "swiglu"
+    if kernel in ("sdd", "dsd_bwd"):
+        return 2 if sw else 1
+    return 1
+
+
 def useful_flops(cfg):
     per = 2.0 * cfg.T * cfg.k * cfg.d * cfg.f
-    products = 3 if cfg.act == "swiglu" else 2
-    if cfg.backward:
-        products += 4
+    sw = cfg.act == "swiglu"
+    products = 3 if sw else 2
+    if cfg.backward:  # backward SDD, input-gradient DSD(s), one DSTD per weight
+        products += 6 if sw else 4
     return per, per * products
 
 
@@ -70,7 +83,9 @@ def cpu_baseline(cfg, inp, target_s):
                        act=cfg.act, W3=inp["W3"].values if "W3" in inp else None,
                        dy=inp["dy"].values if "dy" in inp else None, prec=cfg.dtype,
                        prec_yp=cfg.yp)
-    per_tok = 2.0 * cfg.k * cfg.d * cfg.f * (2 + (2 if cfg.backward else 0))
+    sw = cfg.act == "swiglu"
+    fwd_p, bwd_p = (3, 3) if sw else (2, 2)
+    per_tok = 2.0 * cfg.k * cfg.d * cfg.f * (fwd_p + (bwd_p if cfg.backward else 0))
 
     def run(n):
         toks = synth.sample_tokens(cfg.T, n, seed=7)
@@ -85,9 +100,11 @@ def cpu_baseline(cfg, inp, target_s):
     n, t = run(n)
     return {"value": per_tok * n / t / 1e12, "unit": "TFLOP/s", "cores": orc.get_threads(),
             "kind": "oracle",
-            "sample": f"{n} tokens of the {cfg.name} workload, forward + input-gradient path "
-                      f"(4 of the 6 products per token; weight gradients not sampled), "
-                      f"{t:.1f} s wall on {orc.get_threads()} OpenMP threads"}
+            "sample": f"{n} tokens of the {cfg.name} workload, forward"
+                      + (f" + input-gradient path ({fwd_p + bwd_p} of the "
+                         f"{fwd_p + bwd_p + (3 if sw else 2)} products per token; weight "
+                         f"gradients not sampled)" if cfg.backward else "")
+                      + f", {t:.1f} s wall on {orc.get_threads()} OpenMP threads"}
 
 
 def traffic_for(kernel_name):
@@ -180,7 +197,7 @@ def main():
     tflops = total / (step_ms * 1e-3) / 1e12
     gemms = [k for k in kern if k.startswith(("sdd", "dsd", "dstd"))]
     dom = max(gemms, key=lambda k: kern[k])
-    achieved = per_product / (kern[dom] * 1e-3) / 1e12
+    achieved = products_of(cfg, dom) * per_product / (kern[dom] * 1e-3) / 1e12
     peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
 
     kernels = {}
@@ -190,8 +207,9 @@ def main():
     for k, ms in kern.items():
         ent = {"ms": round(ms, 4)}
         if k in gemms:
-            ent["useful_tflops"] = round(per_product / (ms * 1e-3) / 1e12, 1)
-            ent["pct_bf16_peak"] = round(100 * per_product / (ms * 1e-3) / 1e12 / peak, 1)
+            fl = products_of(cfg, k) * per_product
+            ent["useful_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
+            ent["pct_bf16_peak"] = round(100 * fl / (ms * 1e-3) / 1e12 / peak, 1)
         elif k.startswith("permute_pad"):
             b = cfg.T * cfg.d * es + Tp * cfg.d * es + 4 * A_n + 4 * Tp
             ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
@@ -213,7 +231,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded N(0,1) logits + per-expert bias, N(0,1) x, N(0,0.02) weights)",
+        "data": "synthetic (seeded N(0,1) logits" + (", per-expert bias" if cfg.bias_std else "")
+                + (", hot/starved expert bias" if cfg.hot else "")
+                + f", N(0,{cfg.x_std:g}) x, N(0,{cfg.w_std:g}) weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T}, d={cfg.d}, E={cfg.E}, f={cfg.f}, "
                                f"k={cfg.k}, {cfg.act}, "
                                f"{'forward+backward' if cfg.backward else 'forward'}",
@@ -232,7 +252,7 @@ def main():
     sg = [k for k in kern_serial if k in gemms]
     if sg:
         sdom = max(sg, key=lambda k: kern_serial[k])
-        sach = per_product / (kern_serial[sdom] * 1e-3) / 1e12
+        sach = products_of(cfg, sdom) * per_product / (kern_serial[sdom] * 1e-3) / 1e12
         out["roofline_serial"] = {"kernel": sdom, "bound": "mfma", "achieved": round(sach, 1),
                                   "peak": peak, "unit": "TFLOP/s", "frac": round(sach / peak, 4),
                                   "traffic": traffic_for(sdom)}

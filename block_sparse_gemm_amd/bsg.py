@@ -18,13 +18,13 @@ LIB_PATH = os.path.join(HERE, "libbsg.so")
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 F32, BF16 = 0, 1
-EPI_NONE, EPI_GELU, EPI_SILU_MUL, EPI_GELU_BWD = 0, 1, 2, 3
+EPI_NONE, EPI_GELU, EPI_SILU_MUL, EPI_GELU_BWD, EPI_SILU_MUL_BWD = 0, 1, 2, 3, 4
 BLOCK = 128
 MAX_EXPERTS = 1024
 MAX_TOPK = 32
 
 EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
-             "gelu_bwd": EPI_GELU_BWD}
+             "gelu_bwd": EPI_GELU_BWD, "silu_mul_bwd": EPI_SILU_MUL_BWD}
 
 # Every symbol include/bsg.h declares.
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
@@ -81,8 +81,8 @@ def lib():
         L.bsg_sdd.argtypes = [vp, i64, vp, vp, i64, i32, i32, C.POINTER(TopologyStruct), i32, vp,
                               vp, vp, i32, vp]
         L.bsg_dsd.restype = i32
-        L.bsg_dsd.argtypes = [vp, C.POINTER(TopologyStruct), vp, i64, i32, i32, vp, i64, i32,
-                              i32, vp]
+        L.bsg_dsd.argtypes = [vp, vp, C.POINTER(TopologyStruct), vp, vp, i64, i32, i32, vp, i64,
+                              i32, i32, vp]
         L.bsg_dstd.restype = i32
         L.bsg_dstd.argtypes = [vp, C.POINTER(TopologyStruct), vp, i64, i32, vp, i64, i32, i32,
                                vp]
@@ -206,10 +206,10 @@ def sdd(a, b, K, topo: Topology, epilogue, out_blocks, b2=None, trans_b=False, a
                                 _ptr(aux_out), dtype_code(a), _stream()))
 
 
-def dsd(blocks, topo: Topology, b, N, c, trans_b=False):
-    _check("dsd", lib().bsg_dsd(_ptr(blocks), C.byref(topo.struct), _ptr(b), _ld(b),
-                                int(bool(trans_b)), N, _ptr(c), _ld(c), dtype_code(c),
-                                dtype_code(blocks), _stream()))
+def dsd(blocks, topo: Topology, b, N, c, trans_b=False, blocks2=None, b2=None):
+    _check("dsd", lib().bsg_dsd(_ptr(blocks), _ptr(blocks2), C.byref(topo.struct), _ptr(b),
+                                _ptr(b2), _ld(b), int(bool(trans_b)), N, _ptr(c), _ld(c),
+                                dtype_code(c), dtype_code(blocks), _stream()))
 
 
 def dstd(blocks, topo: Topology, dmat, N, c, trans_c=False):

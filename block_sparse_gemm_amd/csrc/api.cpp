@@ -223,7 +223,8 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
     bsg_status s = check_topology(topo);
     if (s != BSG_OK) return s;
-    REQUIRE(epilogue >= BSG_EPI_NONE && epilogue <= BSG_EPI_GELU_BWD, "unknown epilogue %d", epilogue);
+    REQUIRE(epilogue >= BSG_EPI_NONE && epilogue <= BSG_EPI_SILU_MUL_BWD, "unknown epilogue %d",
+            epilogue);
     const int es = elt_bytes(dtype);
     const int kt = dtype == BSG_BF16 ? 64 : 32;
     const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
@@ -241,9 +242,10 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     } else {
         REQUIRE(b2 == nullptr, "b2 is only used by BSG_EPI_SILU_MUL");
     }
-    if (epilogue == BSG_EPI_GELU_BWD) REQUIRE_VEC_PTR(aux_in);
-    else REQUIRE(aux_in == nullptr, "aux_in is only used by BSG_EPI_GELU_BWD");
-    if (epilogue != BSG_EPI_GELU) REQUIRE(aux_out == nullptr, "aux_out is only used by BSG_EPI_GELU");
+    if (epilogue == BSG_EPI_GELU_BWD || epilogue == BSG_EPI_SILU_MUL_BWD) REQUIRE_VEC_PTR(aux_in);
+    else REQUIRE(aux_in == nullptr, "aux_in is only used by the backward epilogues");
+    if (epilogue != BSG_EPI_GELU && epilogue != BSG_EPI_SILU_MUL)
+        REQUIRE(aux_out == nullptr, "aux_out is only used by BSG_EPI_GELU and BSG_EPI_SILU_MUL");
     else REQUIRE(aux_out == nullptr || aligned(aux_out, 16), "aux_out must be 16-byte aligned");
     bsg::GemmParams p = gemm_params(topo);
     p.a = a;
@@ -252,6 +254,7 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     p.aux_in = aux_in;
     p.out = out_blocks;
     p.aux_out = aux_out;
+    p.plane = (topo->Tp_max / BSG_BLOCK) * topo->F * BSG_BLOCK * BSG_BLOCK;
     p.lda = lda;
     p.ldb = ldb;
     p.K = K;
@@ -260,9 +263,9 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
                       "sdd");
 }
 
-bsg_status bsg_dsd(const void* blocks, const bsg_topology* topo, const void* b, int64_t ldb,
-                   int trans_b, int N, void* c, int64_t ldc, int c_dtype, int dtype,
-                   bsg_stream_t stream) {
+bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* topo,
+                   const void* b, const void* b2, int64_t ldb, int trans_b, int N, void* c,
+                   int64_t ldc, int c_dtype, int dtype, bsg_stream_t stream) {
     REQUIRE(dtype_ok(dtype) && dtype_ok(c_dtype), "unknown dtype");
     if (dtype == BSG_F32 && c_dtype != BSG_F32)
         return fail(BSG_EUNSUPPORTED, "fp32 operands need an fp32 output");
@@ -278,9 +281,17 @@ bsg_status bsg_dsd(const void* blocks, const bsg_topology* topo, const void* b, 
     REQUIRE_VEC_PTR(blocks);
     REQUIRE_VEC_PTR(b);
     REQUIRE_VEC_PTR(c);
+    REQUIRE((blocks2 == nullptr) == (b2 == nullptr), "blocks2 and b2 go together");
+    if (blocks2) {
+        REQUIRE_VEC_PTR(blocks2);
+        REQUIRE_VEC_PTR(b2);
+        REQUIRE((int64_t)topo->E * topo->F < bsg::kSecondSet, "too many column blocks");
+    }
     bsg::GemmParams p = gemm_params(topo);
     p.a = blocks;
+    p.a2 = blocks2;
     p.b = b;
+    p.b2 = b2;
     p.out = c;
     p.ldb = ldb;
     p.ldc = ldc;

@@ -119,4 +119,12 @@ __device__ __forceinline__ float silu_f(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
 }
 
+// silu and its derivative from one exponential: with sigma = 1 / (1 + exp(-g)),
+// silu(g) = g sigma and silu'(g) = sigma (1 + g (1 - sigma))
+__device__ __forceinline__ void silu_and_grad(float g, float& s, float& sp) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
+    s = g * sg;
+    sp = sg * fmaf(g, 1.0f - sg, 1.0f);
+}
+
 }  // namespace bsg

@@ -17,7 +17,10 @@
 //         their nonzero blocks; K = d.  Dual-B (SwiGLU): one block of W1 and
 //         the same block of W3 side by side, combined as silu(g) * u.
 //   DSD   a pair of block rows x 256 output columns; K walks the rows'
-//         blocks through row_ptr, their weight rows through col_idx.
+//         blocks through row_ptr, their weight rows through col_idx.  The
+//         two-set form (SwiGLU input gradient) walks them twice: the gate
+//         projection's blocks against W1, then the up projection's against
+//         W3, into one accumulator.
 //   DSTD  a pair of block columns x 256 output columns; K walks the
 //         columns' blocks through col_ptr / trans_idx, and their dense rows
 //         through row_idx.
@@ -232,7 +235,8 @@ struct KIdx {
 };
 
 // MODE: kModeSdd, kModeSddOne (dual-B SwiGLU: one block per tile),
-// kModeDsd, kModeDstd.  BK: B operand K-contiguous.
+// kModeDsd, kModeDsd2 (two block sets), kModeDstd.  BK: B operand
+// K-contiguous.
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     constexpr int ES = Elt<DT>::kBytes;
@@ -240,8 +244,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     constexpr int KPB = kBlock / KT;  // K-tiles per block
     constexpr int OES = OUT == kBf16 ? 2 : 4;
     constexpr bool AK = MODE != kModeDstd;
-    constexpr bool DUAL = EPI == kEpiSiluMul;
+    constexpr bool DUAL = EPI == kEpiSiluMul || EPI == kEpiSiluMulSave;
     constexpr bool SDD = MODE == kModeSdd || MODE == kModeSddOne;
+    constexpr bool DSD = MODE == kModeDsd || MODE == kModeDsd2;
     static_assert(KT / (DT == kBf16 ? 16 : 8) == 2, "two MFMA K-steps per K-tile");
 
     __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + 3 * kIdxCap * 4];
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     bool n1;
     int bcol0 = 0, bcol1 = 0;  // SDD: column blocks of B
     int rp0 = 0, rp1 = 0;      // SDD / DSD: row_ptr of the two rows
-    if constexpr (SDD || MODE == kModeDsd) {
+    if constexpr (SDD || DSD) {
         rp0 = P.row_ptr[mrow0];
         rp1 = P.row_ptr[mrow1];
     }
@@ -301,10 +306,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     const int64_t n0 = (int64_t)tq * 256;
     const int64_t n1off = n1 ? 128 : 0;  // an absent N half mirrors half 0
 
-    // ---- K extent in K-blocks (DSD / DSTD)
-    int nblk = 0, cp0 = 0, cp1 = 0;
-    if constexpr (MODE == kModeDsd) {
-        nblk = P.row_ptr[mrow0 + 1] - rp0;
+    // ---- K extent in K-blocks (DSD / DSTD); the two-set DSD walks the row's
+    // blocks twice, first in set one, then in set two
+    int nblk = 0, cp0 = 0, cp1 = 0, rowlen = 0;
+    if constexpr (DSD) {
+        rowlen = P.row_ptr[mrow0 + 1] - rp0;
+        nblk = MODE == kModeDsd2 ? 2 * rowlen : rowlen;
     } else if constexpr (MODE == kModeDstd) {
         cp0 = P.col_ptr[mrow0];
         cp1 = P.col_ptr[mrow1];
@@ -312,10 +319,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     }
     auto fetch = [&](int p) -> KIdx {
         KIdx r{0, 0, 0};
-        if constexpr (MODE == kModeDsd) {
+        if constexpr (DSD) {
+            int set = 0;
+            if (MODE == kModeDsd2 && p >= rowlen) {
+                p -= rowlen;
+                set = kSecondSet;
+            }
             r.b0 = rp0 + p;
             r.b1 = rp1 + p;
-            r.row = P.col_idx[r.b0];
+            r.row = P.col_idx[r.b0] | set;
         } else if constexpr (MODE == kModeDstd) {
             r.b0 = P.trans_idx[cp0 + p];
             r.b1 = P.trans_idx[cp1 + p];
@@ -377,16 +389,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         } else {
             const int blk0 = __builtin_amdgcn_readfirstlane(ti.b0);
             const int blk1 = __builtin_amdgcn_readfirstlane(ti.b1);
-            const int rowb = __builtin_amdgcn_readfirstlane(ti.row);
-            if constexpr (MODE == kModeDsd) {
-                r.a0 = (const char*)P.a + ((int64_t)blk0 * kBlock * kBlock + koff) * ES;
-                r.a1 = (const char*)P.a + ((int64_t)blk1 * kBlock * kBlock + koff) * ES;
+            int rowb = __builtin_amdgcn_readfirstlane(ti.row);
+            if constexpr (DSD) {
+                const char* As = (const char*)P.a;
+                const char* Bs = (const char*)P.b;
+                if constexpr (MODE == kModeDsd2) {
+                    if (rowb & kSecondSet) {  // uniform: the K-block is in set two
+                        As = (const char*)P.a2;
+                        Bs = (const char*)P.b2;
+                        rowb &= ~kSecondSet;
+                    }
+                }
+                r.a0 = As + ((int64_t)blk0 * kBlock * kBlock + koff) * ES;
+                r.a1 = As + ((int64_t)blk1 * kBlock * kBlock + koff) * ES;
                 const int64_t krow = (int64_t)kBlock * rowb + koff;
                 if constexpr (BK) {
-                    r.b0 = (const char*)P.b + (n0 * P.ldb + krow) * ES;
+                    r.b0 = Bs + (n0 * P.ldb + krow) * ES;
                     r.b1 = r.b0 + n1off * P.ldb * ES;
                 } else {
-                    r.b0 = (const char*)P.b + (krow * P.ldb + n0) * ES;
+                    r.b0 = Bs + (krow * P.ldb + n0) * ES;
                     r.b1 = r.b0 + n1off * ES;
                 }
             } else {  // DSTD: A = block^T (k-major as stored), B = dense rows
@@ -535,8 +556,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     // wave writes half of its 128 x 128 quarter (64 rows) at a time into a
     // private 32 KB region in the accumulator layout, then reads it back row
     // by row, so every store instruction writes 4 whole 256-byte rows
-    // (16 contiguous bytes a lane).  GeLU with the derivative kept stages
-    // both side by side (derivative, then activation).
+    // (16 contiguous bytes a lane).  Epilogues with two outputs stage them
+    // side by side: GeLU with the derivative kept (derivative, then
+    // activation) and the SwiGLU backward (gate, then up projection).
     constexpr bool STAGE = OUT == kBf16 && !DUAL;
     if constexpr (STAGE) __syncthreads();  // every wave is done with the operand ring
     const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
@@ -584,11 +606,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         orow = P.ldc * OES;
     }
 
-    // GeLU backward (bf16): the saved derivative, read one 32-row slab ahead
-    // of its use so the loads of slab mi + 1 overlap the work on slab mi
-    constexpr bool PRE = EPI == kEpiGeluBwd && OUT == kBf16;
+    // Backward epilogues (bf16): the saved factors, read one 32-row slab ahead
+    // of their use so the loads of slab mi + 1 overlap the work on slab mi.
+    // GeLU: one plane (the derivative); SwiGLU: two (silu(g), u * silu'(g)).
+    // (The two-plane prefetch does not fit beside the registers of a B
+    // operand read as stored; that variant reads the factors at use.)
+    constexpr bool TWO_IN = EPI == kEpiSiluMulBwd;
+    constexpr bool PRE = (EPI == kEpiGeluBwd || (TWO_IN && BK)) && OUT == kBf16;
     u32x2 hsave[2][NI][4];
-    auto hload = [&](int mi, u32x2 (&dst)[NI][4]) {
+    u32x2 qsave[TWO_IN ? 2 : 1][NI][4];
+    auto hload = [&](int mi, int buf) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -596,10 +623,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                 const int m = 32 * mi + l32;
                 const int nloc = 32 * ni + 8 * g + 4 * lh;
                 const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
-                dst[ni][g] = *(const u32x2*)((const char*)P.aux_in + off * 2);
+                hsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + off * 2);
+                if constexpr (TWO_IN)
+                    qsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + (P.plane + off) * 2);
             }
     };
-    if constexpr (PRE) hload(0, hsave[0]);
+    auto unpack = [](u32x2 u, float* f) {
+        f[0] = __uint_as_float(u[0] << 16);
+        f[1] = __uint_as_float(u[0] & 0xffff0000u);
+        f[2] = __uint_as_float(u[1] << 16);
+        f[3] = __uint_as_float(u[1] & 0xffff0000u);
+    };
+    if constexpr (PRE) hload(0, 0);
 
     // two halves of 64 staging rows: M slabs (mi) 2h, 2h + 1 with a
     // row-major output, N slabs (ni) 2h, 2h + 1 with the transposed one
@@ -612,7 +647,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                 const int mi = SWAP || !STAGE ? 2 * h + a : b;
                 const int ni = SWAP || !STAGE ? b : 2 * h + a;
                 if constexpr (PRE) {
-                    if (b == 0 && mi + 1 < 4) hload(mi + 1, hsave[(mi + 1) & 1]);
+                    if (b == 0 && mi + 1 < 4) hload(mi + 1, (mi + 1) & 1);
                 }
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -622,17 +657,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                     if constexpr (SDD) {
                         // block-major output: (m, n) of block b at b*16384 + m*128 + n
                         const int m = 32 * mi + l32;
-                        int nloc;
-                        if constexpr (DUAL) {
-                            nloc = wn * 64 + 32 * ni + 8 * g + 4 * lh;
+                        const int nloc = DUAL ? wn * 64 + 32 * ni + 8 * g + 4 * lh
+                                              : 32 * ni + 8 * g + 4 * lh;
+                        const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
+                        if constexpr (EPI == kEpiSiluMul) {
 #pragma unroll
                             for (int s = 0; s < 4; ++s)
                                 v[s] = silu_f(v[s]) * acc[mi][ni + 2][4 * g + s];
-                        } else {
-                            nloc = 32 * ni + 8 * g + 4 * lh;
-                        }
-                        const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
-                        if constexpr (EPI == kEpiGelu) {
+                        } else if constexpr (EPI == kEpiSiluMulSave) {
+                            // A = silu(g) u, and for the backward silu(g) and u silu'(g)
+                            float sv[4], qv[4];
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                const float u = acc[mi][ni + 2][4 * g + s];
+                                float sp;
+                                silu_and_grad(v[s], sv[s], sp);
+                                qv[s] = u * sp;
+                                v[s] = sv[s] * u;
+                            }
+                            store4<OUT>((char*)P.aux_out + off * OES, sv);
+                            store4<OUT>((char*)P.aux_out + (P.plane + off) * OES, qv);
+                        } else if constexpr (EPI == kEpiGelu) {
 #pragma unroll
                             for (int s = 0; s < 4; ++s) v[s] = gelu_f(v[s]);
                         } else if constexpr (EPI == kEpiGeluSave) {
@@ -645,17 +690,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                         } else if constexpr (EPI == kEpiGeluBwd) {
                             // dH = dA * GeLU'(h), the derivative saved by the forward
                             float gv[4];
-                            if constexpr (PRE) {
-                                const u32x2 u = hsave[mi & 1][ni][g];
-                                gv[0] = __uint_as_float(u[0] << 16);
-                                gv[1] = __uint_as_float(u[0] & 0xffff0000u);
-                                gv[2] = __uint_as_float(u[1] << 16);
-                                gv[3] = __uint_as_float(u[1] & 0xffff0000u);
-                            } else {
-                                load4<OUT>((const char*)P.aux_in + off * OES, gv);
-                            }
+                            if constexpr (PRE) unpack(hsave[mi & 1][ni][g], gv);
+                            else load4<OUT>((const char*)P.aux_in + off * OES, gv);
 #pragma unroll
                             for (int s = 0; s < 4; ++s) v[s] *= gv[s];
+                        } else if constexpr (EPI == kEpiSiluMulBwd) {
+                            // gate projection dA * u silu'(g) (plane 0 of the
+                            // output), up projection dA * silu(g) (plane 1)
+                            float sv[4], qv[4], up[4];
+                            if constexpr (PRE) {
+                                unpack(hsave[mi & 1][ni][g], sv);
+                                unpack(qsave[mi & 1][ni][g], qv);
+                            } else {
+                                load4<OUT>((const char*)P.aux_in + off * OES, sv);
+                                load4<OUT>((const char*)P.aux_in + (P.plane + off) * OES, qv);
+                            }
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                up[s] = v[s] * sv[s];
+                                v[s] *= qv[s];
+                            }
+                            if constexpr (STAGE) stage_put(region + 16384, mi, ni, g, up);
+                            else store4<OUT>((char*)P.out + (P.plane + off) * OES, up);
                         }
                         if constexpr (STAGE) {
                             stage_put(EPI == kEpiGeluSave ? region + 16384 : region, mi, ni, g, v);
@@ -686,6 +742,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                 stage_flush(region, (char*)P.aux_out + (int64_t)oblk * kBlock * kBlock * OES +
                                         h * 64 * orow, orow);
                 stage_flush(region + 16384, obase + h * 64 * orow, orow);
+            } else if constexpr (EPI == kEpiSiluMulBwd) {
+                stage_flush(region, obase + h * 64 * orow, orow);
+                stage_flush(region + 16384, obase + P.plane * OES + h * 64 * orow, orow);
             } else {
                 stage_flush(region, obase + h * 64 * orow, orow);
             }
@@ -719,6 +778,9 @@ static hipError_t dispatch_sdd(const GemmParams& p, int64_t grid, int trans_b, i
     case kEpiGeluBwd:
         return trans_b ? launch<DT, kModeSdd, true, kEpiGeluBwd, DT, true>(p, grid, s)
                        : launch<DT, kModeSdd, false, kEpiGeluBwd, DT, true>(p, grid, s);
+    case kEpiSiluMulBwd:
+        return trans_b ? launch<DT, kModeSdd, true, kEpiSiluMulBwd, DT, true>(p, grid, s)
+                       : launch<DT, kModeSdd, false, kEpiSiluMulBwd, DT, true>(p, grid, s);
     default:
         return hipErrorInvalidValue;
     }
@@ -729,6 +791,10 @@ hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, i
     if (epi == kEpiSiluMul) {  // dual B: one block per tile, B halves = W1 | W3
         if (trans_b) return hipErrorInvalidValue;
         const int64_t grid = row_pairs_max * p.F;
+        if (p.aux_out)
+            return dtype == kBf16
+                       ? launch<kBf16, kModeSddOne, false, kEpiSiluMulSave, kBf16, true>(p, grid, s)
+                       : launch<kF32, kModeSddOne, false, kEpiSiluMulSave, kF32, true>(p, grid, s);
         return dtype == kBf16
                    ? launch<kBf16, kModeSddOne, false, kEpiSiluMul, kBf16, true>(p, grid, s)
                    : launch<kF32, kModeSddOne, false, kEpiSiluMul, kF32, true>(p, grid, s);
@@ -738,17 +804,24 @@ hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, i
                           : dispatch_sdd<kF32>(p, grid, trans_b, epi, s);
 }
 
+template <int MODE>
+static hipError_t dispatch_dsd(const GemmParams& p, int64_t grid, int trans_b, int c_dtype,
+                               int dtype, hipStream_t s) {
+    if (dtype == kF32)
+        return trans_b ? launch<kF32, MODE, true, kEpiNone, kF32, true>(p, grid, s)
+                       : launch<kF32, MODE, false, kEpiNone, kF32, true>(p, grid, s);
+    if (c_dtype == kBf16)
+        return trans_b ? launch<kBf16, MODE, true, kEpiNone, kBf16, true>(p, grid, s)
+                       : launch<kBf16, MODE, false, kEpiNone, kBf16, true>(p, grid, s);
+    return trans_b ? launch<kBf16, MODE, true, kEpiNone, kF32, true>(p, grid, s)
+                   : launch<kBf16, MODE, false, kEpiNone, kF32, true>(p, grid, s);
+}
+
 hipError_t launch_dsd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int c_dtype,
                       int dtype, hipStream_t s) {
     const int64_t grid = row_pairs_max * p.ntn;
-    if (dtype == kF32)
-        return trans_b ? launch<kF32, kModeDsd, true, kEpiNone, kF32, true>(p, grid, s)
-                       : launch<kF32, kModeDsd, false, kEpiNone, kF32, true>(p, grid, s);
-    if (c_dtype == kBf16)
-        return trans_b ? launch<kBf16, kModeDsd, true, kEpiNone, kBf16, true>(p, grid, s)
-                       : launch<kBf16, kModeDsd, false, kEpiNone, kBf16, true>(p, grid, s);
-    return trans_b ? launch<kBf16, kModeDsd, true, kEpiNone, kF32, true>(p, grid, s)
-                   : launch<kBf16, kModeDsd, false, kEpiNone, kF32, true>(p, grid, s);
+    return p.a2 ? dispatch_dsd<kModeDsd2>(p, grid, trans_b, c_dtype, dtype, s)
+                : dispatch_dsd<kModeDsd>(p, grid, trans_b, c_dtype, dtype, s);
 }
 
 hipError_t launch_dstd(const GemmParams& p, int trans_c, int dtype, hipStream_t s) {

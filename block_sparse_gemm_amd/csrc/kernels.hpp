@@ -13,12 +13,19 @@ constexpr int kEpiNone = 0;
 constexpr int kEpiGelu = 1;
 constexpr int kEpiSiluMul = 2;
 constexpr int kEpiGeluBwd = 3;
-constexpr int kEpiGeluSave = 4;  // internal: GeLU that also stores its derivative
+constexpr int kEpiSiluMulBwd = 4;
+constexpr int kEpiGeluSave = 5;     // internal: GeLU that also stores its derivative
+constexpr int kEpiSiluMulSave = 6;  // internal: SiLU*mul that also stores silu, u*silu'
 
 constexpr int kModeSdd = 0;
 constexpr int kModeSddOne = 1;
 constexpr int kModeDsd = 2;
 constexpr int kModeDstd = 3;
+constexpr int kModeDsd2 = 4;  // DSD over two block sets, each with its own B
+
+// DSD over two block sets: the staged weight-row index of a K-block of the
+// second set carries this bit
+constexpr int kSecondSet = 1 << 30;
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
@@ -26,11 +33,16 @@ constexpr int kRouteChunk = 64;  // tokens per routing chunk
 
 struct GemmParams {
     const void* a;       // SDD: dense rows; DSD / DSTD: sparse blocks
+    const void* a2;      // two-set DSD: the second block set
     const void* b;       // SDD / DSD: dense B; DSTD: dense rows (dmat)
-    const void* b2;      // SDD dual-B second operand (SwiGLU up projection)
-    const void* aux_in;  // SDD GELU_BWD: saved GeLU derivative blocks
-    void* out;
-    void* aux_out;       // SDD GELU: optional saved GeLU derivative blocks
+    const void* b2;      // SDD dual-B second operand (SwiGLU up projection);
+                         // two-set DSD: the second set's B
+    const void* aux_in;  // SDD GELU_BWD: saved GeLU derivative blocks;
+                         // SILU_MUL_BWD: the two saved planes (silu, u*silu')
+    void* out;           // SILU_MUL_BWD: two planes (gate, up gradients)
+    void* aux_out;       // SDD GELU: optional saved derivative blocks;
+                         // SILU_MUL: optional two planes (silu, u*silu')
+    int64_t plane;       // elements between the planes of a two-plane block array
     int64_t lda, ldb, ldc;
     const int32_t* row_ptr;
     const int32_t* col_idx;

@@ -8,9 +8,14 @@ transpose index as section 1.3 describes):
     permute_pad(dy, scale = gate) -> sdd(dYp, W2^T, GeLU') -> dsd(dH, W1^T)
     -> unpermute_combine(gate = 1) ; dstd(A, dYp) = dW2 ; dstd(dH, Xp)^T = dW1 ;
     route_backward(dy, Yp) = dlogits (the gate's gradient, selection fixed)
-The two weight gradients run on a second stream, each as soon as its inputs
-exist (dW2 beside the GeLU' product, dW1 beside the input-gradient product),
-so the tail of one product's grid and the other's fill the GPU together.
+SwiGLU experts keep silu(g) and u * silu'(g) from the forward; their
+backward product gives the gate and the up projection's gradients (two
+planes of dH), the input gradient is one two-set dsd (dH_gate W1^T +
+dH_up W3^T), and dW1, dW3 are one dstd each.
+The weight gradients run on a second stream, each as soon as its inputs
+exist (dW2 beside the backward SDD product, dW1 (and dW3) beside the
+input-gradient product), so the tail of one product's grid and the other's
+fill the GPU together.
 
 torch only allocates device memory and provides the stream; every step runs
 in libbsg.so.  All buffers are sized once for the worst-case routing
@@ -76,20 +81,24 @@ class Layer:
         self.row_src = torch.zeros(self.Tp_max, **i32)
         self.xp = torch.zeros(self.Tp_max, s.d, dtype=dt, device=dev)
         self.act = torch.zeros(nnz_max * bsg.BLOCK, bsg.BLOCK, dtype=dt, device=dev)
-        # what the backward keeps of the forward: GeLU'(h), block-major like A
-        self.gp = torch.zeros_like(self.act) if s.backward else None
+        # what the backward keeps of the forward, block-major like A: GeLU'(h),
+        # or for SwiGLU two planes, silu(g) then u * silu'(g)
+        planes = 2 if s.act == "swiglu" else 1
+        self.gp = torch.zeros(planes * nnz_max * bsg.BLOCK, bsg.BLOCK, dtype=dt, device=dev) \
+            if s.backward else None
         self.yp = torch.zeros(self.Tp_max, s.d, dtype=ydt, device=dev)
         self.y = torch.zeros(s.T, s.d, dtype=dt, device=dev)
         if s.backward:
-            if s.act != "gelu":
-                raise NotImplementedError("backward is implemented for GeLU experts")
             self.dyp = torch.zeros(self.Tp_max, s.d, dtype=dt, device=dev)
             self.row_src_b = torch.zeros(self.Tp_max, **i32)
-            self.dh = torch.zeros_like(self.act)
+            # SwiGLU: plane 0 the gate projection's gradient, plane 1 the up's
+            self.dh = torch.zeros_like(self.gp)
             self.dxp = torch.zeros(self.Tp_max, s.d, dtype=ydt, device=dev)
             self.dx = torch.zeros(s.T, s.d, dtype=dt, device=dev)
             self.dW1 = torch.zeros(s.d, s.E * s.f, dtype=dt, device=dev)
             self.dW2 = torch.zeros(s.E * s.f, s.d, dtype=dt, device=dev)
+            self.dW3 = torch.zeros(s.d, s.E * s.f, dtype=dt, device=dev) \
+                if s.act == "swiglu" else None
             self.dlogits = torch.zeros(s.T, s.E, dtype=torch.float32, device=dev)
             self.side = torch.cuda.Stream(device=dev)  # default priority
             self.ev_dyp = torch.cuda.Event()
@@ -116,7 +125,7 @@ class Layer:
           self.bin_offsets, s.E, self.Tp_max, self.row_src, self.xp)
         c("build_topology", bsg.build_topology, self.bin_offsets, s.E, s.f, self.Tp_max, t)
         if s.act == "swiglu":
-            c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3)
+            c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3, aux_out=self.gp)
         else:
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.gp)
         c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp)
@@ -124,47 +133,78 @@ class Layer:
           s.k, s.d, self.y)
         return self.y
 
-    def backward(self, dy, W1, W2):
+    def plane(self, blocks, i):
+        """Plane i of a two-plane block array (a view)."""
+        n = self.topo.nnz_max * bsg.BLOCK
+        return blocks[i * n:(i + 1) * n]
+
+    def backward(self, dy, W1, W2, W3=None):
         s, t = self.s, self.topo
         c = self._call
         main = torch.cuda.current_stream()
+        sw = s.act == "swiglu"
+        dh0 = self.plane(self.dh, 0) if sw else self.dh
+
+        def route_backward():
+            c("route_backward", bsg.route_backward, self.logits, s.k, s.renorm, self.expert_idx,
+              self.dest_row, dy, self.yp, self.dlogits)
+
+        def sdd_bwd():
+            c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "silu_mul_bwd" if sw else "gelu_bwd",
+              self.dh, trans_b=True, aux_in=self.gp)
+
+        def dsd_bwd():
+            if sw:
+                c("dsd_bwd", bsg.dsd, dh0, t, W1, s.d, self.dxp, trans_b=True,
+                  blocks2=self.plane(self.dh, 1), b2=W3)
+            else:
+                c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
+            c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None,
+              s.T, s.k, s.d, self.dx)
+
+        def dw2():
+            c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
+
+        def dw1():
+            c("dstd_dw1", bsg.dstd, dh0, t, self.xp, s.d, self.dW1, trans_c=True)
+            if sw:
+                c("dstd_dw3", bsg.dstd, self.plane(self.dh, 1), t, self.xp, s.d, self.dW3,
+                  trans_c=True)
+
         c("permute_pad_bwd", bsg.permute_pad, dy, s.k, self.dest_row, self.gate, self.counts,
           self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp)
         if not self.overlap:
-            c("route_backward", bsg.route_backward, self.logits, s.k, s.renorm, self.expert_idx,
-              self.dest_row, dy, self.yp, self.dlogits)
-            c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
-              aux_in=self.gp)
-            c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
-            c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None,
-              s.T, s.k, s.d, self.dx)
-            c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
-            c("dstd_dw1", bsg.dstd, self.dh, t, self.xp, s.d, self.dW1, trans_c=True)
-            return self.dx, self.dW1, self.dW2
+            route_backward()
+            sdd_bwd()
+            dsd_bwd()
+            dw2()
+            dw1()
+            return self.grads()
         self.ev_dyp.record(main)
         with torch.cuda.stream(self.side):
             self.side.wait_event(self.ev_dyp)
-            c("route_backward", bsg.route_backward, self.logits, s.k, s.renorm, self.expert_idx,
-              self.dest_row, dy, self.yp, self.dlogits)
-            c("dstd_dw2", bsg.dstd, self.act, t, self.dyp, s.d, self.dW2)
-        c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "gelu_bwd", self.dh, trans_b=True,
-          aux_in=self.gp)
+            route_backward()
+            dw2()
+        sdd_bwd()
         self.ev_dh.record(main)
         with torch.cuda.stream(self.side):
             self.side.wait_event(self.ev_dh)
-            c("dstd_dw1", bsg.dstd, self.dh, t, self.xp, s.d, self.dW1, trans_c=True)
+            dw1()
             self.ev_wgrad.record(self.side)
-        c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
-        c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None, s.T,
-          s.k, s.d, self.dx)
+        dsd_bwd()
         main.wait_event(self.ev_wgrad)  # the step ends when both streams have
-        return self.dx, self.dW1, self.dW2
+        return self.grads()
+
+    def grads(self):
+        """(dx, dW1, dW2), plus dW3 for SwiGLU experts."""
+        g = (self.dx, self.dW1, self.dW2)
+        return g + (self.dW3,) if self.s.act == "swiglu" else g
 
     def step(self, x, logits, W1, W2, W3=None, dy=None):
         """One pass of the whole hot path: forward, plus backward when set."""
         self.forward(x, logits, W1, W2, W3)
         if self.s.backward:
-            self.backward(dy, W1, W2)
+            self.backward(dy, W1, W2, W3)
 
     # ---------------------------------------------------------- helpers
     def sparse_rows(self, blocks: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:

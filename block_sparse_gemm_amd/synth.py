@@ -92,6 +92,9 @@ CONFIGS = {
                              bias_std=0.5),
     "mixtral": LayerConfig("mixtral", T=8192, d=4096, E=8, f=14336, k=2, act="swiglu",
                            renorm=True, yp_dtype="f32"),
+    # the same layer trained: forward + backward of the SwiGLU experts
+    "mixtral_train": LayerConfig("mixtral_train", T=8192, d=4096, E=8, f=14336, k=2,
+                                 act="swiglu", renorm=True, yp_dtype="f32", backward=True),
     "skew": LayerConfig("skew", T=65536, d=1024, E=64, f=4096, k=2, backward=True,
                         hot=10, hot_bias=1.33, starved=6, starved_bias=-1.0),
 }

@@ -57,10 +57,12 @@ typedef enum {
 typedef enum { BSG_F32 = 0, BSG_BF16 = 1 } bsg_dtype;
 
 typedef enum {
-    BSG_EPI_NONE = 0,     /* out = acc */
-    BSG_EPI_GELU = 1,     /* out = gelu(acc) (exact erf form); optional aux_out = gelu'(acc) */
-    BSG_EPI_SILU_MUL = 2, /* dual B: out = silu(acc_b) * acc_b2 */
-    BSG_EPI_GELU_BWD = 3  /* out = acc * aux_in (aux_in = saved gelu') */
+    BSG_EPI_NONE = 0,        /* out = acc */
+    BSG_EPI_GELU = 1,        /* out = gelu(acc) (exact erf form); optional aux_out = gelu'(acc) */
+    BSG_EPI_SILU_MUL = 2,    /* dual B: out = silu(acc_b) * acc_b2; optional aux_out planes
+                                silu(acc_b), acc_b2 * silu'(acc_b) */
+    BSG_EPI_GELU_BWD = 3,    /* out = acc * aux_in (aux_in = saved gelu') */
+    BSG_EPI_SILU_MUL_BWD = 4 /* out planes acc * aux_in[1], acc * aux_in[0] */
 } bsg_epilogue;
 
 /* A hipStream_t passed as an opaque pointer (NULL = null stream). */
@@ -101,7 +103,9 @@ typedef struct {
  *                        writes nothing, or zeros for dstd
  * E, F and Tp_max are host values describing the capacity.
  * Sparse operands ("blocks") are stored block-major, [nnz_max][128][128],
- * each block row-major, in BCSR order.
+ * each block row-major, in BCSR order.  A two-plane block array is
+ * [2][nnz_max][128][128] with nnz_max = (Tp_max / 128) * F: plane 1 starts
+ * nnz_max blocks after plane 0.
  */
 typedef struct {
     int32_t* row_ptr;
@@ -205,8 +209,15 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
  *   NONE      acc
  *   GELU      gelu(acc); if aux_out != NULL also aux_out[b] = gelu'(acc), the
  *             derivative the backward needs (stored in dtype)
- *   SILU_MUL  silu(acc) * acc2 where acc2 uses b2 in place of b (SwiGLU)
+ *   SILU_MUL  silu(acc) * acc2 where acc2 uses b2 in place of b (SwiGLU);
+ *             if aux_out != NULL it is a two-plane block array that also
+ *             receives silu(acc) (plane 0) and acc2 * silu'(acc) (plane 1),
+ *             the factors the backward needs (stored in dtype)
  *   GELU_BWD  acc * aux_in[b]  (aux_in = the derivative blocks saved by GELU)
+ *   SILU_MUL_BWD  aux_in is the two-plane array saved by SILU_MUL and
+ *             out_blocks a two-plane array: plane 0 = acc * aux_in plane 1
+ *             (gradient of the gate projection, acc = dA), plane 1 =
+ *             acc * aux_in plane 0 (gradient of the up projection)
  * K must be a positive multiple of 64 (bf16) or 32 (fp32).
  */
 bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, int64_t ldb,
@@ -221,12 +232,16 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
  *                    B[128*col_idx[b] + j][n],  n < N,
  *   trans_b = 0: B[k][n] = b[k*ldb + n]  (b is [E*f, N], e.g. W2)
  *   trans_b = 1: B[k][n] = b[n*ldb + k]  (b is [N, E*f], e.g. W1 for dgrad)
+ * With blocks2 and b2 (both or neither; same topology, ldb and trans_b) the
+ * sum also runs over blocks2[b] against B2 taken from b2 (SwiGLU input
+ * gradient: gate projection with W1 plus up projection with W3), in one
+ * fp32 accumulation.
  * c is [Tp_max, N] with leading dimension ldc in c_dtype (bf16 or fp32);
  * rows >= Tp are untouched.  N must be a positive multiple of 128.
  */
-bsg_status bsg_dsd(const void* blocks, const bsg_topology* topo, const void* b, int64_t ldb,
-                   int trans_b, int N, void* c, int64_t ldc, int c_dtype, int dtype,
-                   bsg_stream_t stream);
+bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* topo,
+                   const void* b, const void* b2, int64_t ldb, int trans_b, int N, void* c,
+                   int64_t ldc, int c_dtype, int dtype, bsg_stream_t stream);
 
 /*
  * dstd - dense = sparse^T x dense, the weight gradient (section 1.3,

@@ -168,19 +168,31 @@ def test_sdd_validation(L):
     assert call(epi=bsg.EPI_NONE, aux_in=P) == bsg.EINVAL
     assert call(epi=bsg.EPI_NONE, aux_out=P) == bsg.EINVAL
     assert call(epi=bsg.EPI_GELU, b2=P) == bsg.EINVAL
+    assert call(epi=bsg.EPI_SILU_MUL_BWD) == bsg.EINVAL           # aux_in missing
+    assert call(epi=bsg.EPI_SILU_MUL_BWD, aux_in=P, b2=P) == bsg.EINVAL
+    assert call(epi=bsg.EPI_SILU_MUL_BWD, aux_in=P, aux_out=P) == bsg.EINVAL
+    assert call(epi=bsg.EPI_SILU_MUL, b2=P, aux_out=MIS) == bsg.EINVAL
+    assert call(epi=5) == bsg.EINVAL
 
 
 def test_dsd_dstd_validation(L):
     t = fake_topo(E=4, f=256)
     ncol = 4 * 256
-    assert L.bsg_dsd(P, C.byref(t), P, 256, 0, 200, P, 256, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
-    assert L.bsg_dsd(P, C.byref(t), P, 128, 0, 256, P, 256, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
-    assert L.bsg_dsd(P, C.byref(t), P, 256, 1, 256, P, 256, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
-    assert L.bsg_dsd(P, C.byref(t), P, 256, 0, 256, P, 128, bsg.BF16, bsg.BF16, None) == bsg.EINVAL
-    assert L.bsg_dsd(P, C.byref(t), P, 256, 0, 256, P, 256, bsg.BF16, bsg.F32,
-                     None) == bsg.EUNSUPPORTED
-    assert L.bsg_dsd(None, C.byref(t), P, 256, 0, 256, P, 256, bsg.BF16, bsg.BF16,
-                     None) == bsg.EINVAL
+
+    def dsd(blocks=P, blocks2=None, b=P, b2=None, ldb=256, trans_b=0, N=256, c=P, ldc=256,
+            c_dtype=bsg.BF16, dtype=bsg.BF16):
+        return L.bsg_dsd(blocks, blocks2, C.byref(t), b, b2, ldb, trans_b, N, c, ldc, c_dtype,
+                         dtype, None)
+
+    assert dsd(N=200) == bsg.EINVAL
+    assert dsd(ldb=128) == bsg.EINVAL
+    assert dsd(trans_b=1) == bsg.EINVAL          # ldb < E*f for B transposed
+    assert dsd(ldc=128) == bsg.EINVAL
+    assert dsd(dtype=bsg.F32) == bsg.EUNSUPPORTED
+    assert dsd(blocks=None) == bsg.EINVAL
+    assert dsd(blocks2=P) == bsg.EINVAL          # the second set needs its B
+    assert dsd(b2=P) == bsg.EINVAL               # ... and its blocks
+    assert dsd(blocks2=MIS, b2=P) == bsg.EINVAL
     assert L.bsg_dstd(P, C.byref(t), P, 256, 256, P, 256, 1, bsg.BF16, None) == bsg.EINVAL
     assert L.bsg_dstd(P, C.byref(t), P, 128, 256, P, 256, 0, bsg.BF16, None) == bsg.EINVAL
     assert L.bsg_dstd(P, C.byref(t), P, 256, 256, P, ncol, 2, bsg.BF16, None) == bsg.EINVAL

@@ -68,7 +68,7 @@ def run_gpu(cfg, inp):
     logits = torch.from_numpy(inp["logits"]).cuda()
     L.forward(x, logits, W1, W2, W3)
     if cfg.backward:
-        L.backward(dy, W1, W2)
+        L.backward(dy, W1, W2, W3)
     torch.cuda.synchronize()
     return L, dict(x=x, W1=W1, W2=W2, W3=W3, dy=dy, logits=logits)
 
@@ -159,7 +159,11 @@ def check_case(orc, case: Case, seed=0):
     G, A, Yp = O.assign_forward(assigns)
     rows = torch.from_numpy(r["dest_row"][assigns]).cuda()
     check_float("A", f64(L.sparse_rows(L.act, rows)), A, prec, report)
-    if cfg.backward:
+    sw = cfg.act == "swiglu"
+    if cfg.backward and sw:  # the saved factors silu(g), u * silu'(g)
+        check_float("S", f64(L.sparse_rows(L.plane(L.gp, 0), rows)), G[0], prec, report)
+        check_float("Q", f64(L.sparse_rows(L.plane(L.gp, 1), rows)), G[1], prec, report)
+    elif cfg.backward:
         check_float("G", f64(L.sparse_rows(L.gp, rows)), G, prec, report)
     # the bar follows the workload's arithmetic (bf16 operands, fp32
     # accumulation) even where Yp is stored in fp32
@@ -180,7 +184,11 @@ def check_case(orc, case: Case, seed=0):
         # itself is checked bit-exact with a shared scale in
         # test_permute_pad_scaled_exact
         check_float("dYp", f64(L.dyp[rows.long()]), dYp, prec, report)
-        check_float("dH", f64(L.sparse_rows(L.dh, rows)), dH, prec, report)
+        if sw:  # gate and up projections
+            check_float("dHg", f64(L.sparse_rows(L.plane(L.dh, 0), rows)), dH[0], prec, report)
+            check_float("dHu", f64(L.sparse_rows(L.plane(L.dh, 1), rows)), dH[1], prec, report)
+        else:
+            check_float("dH", f64(L.sparse_rows(L.dh, rows)), dH, prec, report)
         check_float("dXp", f64(L.dxp[rows.long()]), dXp, prec, report)
         check_float("dx", f64(L.dx[torch.from_numpy(toks).cuda()]), O.backward_tokens(toks),
                     prec, report)
@@ -190,6 +198,9 @@ def check_case(orc, case: Case, seed=0):
         # dW1 [d, E*f]: rows = model dims, cols = expert hidden units
         got1 = f64(L.dW1[torch.from_numpy(wc).cuda()][:, torch.from_numpy(wr).cuda()])
         check_float("dW1", got1, O.dW1_block(wc, wr), prec, report)
+        if sw:
+            got3 = f64(L.dW3[torch.from_numpy(wc).cuda()][:, torch.from_numpy(wr).cuda()])
+            check_float("dW3", got3, O.dW3_block(wc, wr), prec, report)
         # gate backward on the sampled tokens: the oracle differentiates its
         # own stored Yp, the GPU its own
         # (Yp rows are in assignment order: token toks[i]'s k rows at i*k + j)
@@ -202,6 +213,8 @@ def check_case(orc, case: Case, seed=0):
         for e in empty:  # experts without tokens: exactly zero weight gradients
             assert torch.count_nonzero(L.dW2[e * cfg.f:(e + 1) * cfg.f]).item() == 0
             assert torch.count_nonzero(L.dW1[:, e * cfg.f:(e + 1) * cfg.f]).item() == 0
+            if sw:
+                assert torch.count_nonzero(L.dW3[:, e * cfg.f:(e + 1) * cfg.f]).item() == 0
     _say(f"[parity] {cfg.name} ok; max|d|/max|o|: " +
          ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
     return L, dev, inp
@@ -234,6 +247,14 @@ SMALL = {
                                 renorm=True, yp_dtype="f32", backward=False)),
     "swiglu_f32": Case(_small("swiglu_f32", T=300, d=128, E=3, f=256, k=2, act="swiglu",
                               dtype="f32", renorm=True, backward=False, x_std=0.5)),
+    # SwiGLU training: F = 3 (a ragged column pair in the backward SDD), d = 384
+    # (an absent N half in the two-set DSD and the DSTDs)
+    "swiglu_train_bf16": Case(_small("swiglu_train_bf16", T=600, d=384, E=4, f=384, k=2,
+                                     act="swiglu", renorm=True, yp_dtype="f32")),
+    "swiglu_train_bf16_ypbf16": Case(_small("swiglu_train_bf16_ypbf16", T=500, d=256, E=3,
+                                            f=256, k=1, act="swiglu")),
+    "swiglu_train_f32": Case(_small("swiglu_train_f32", T=300, d=128, E=3, f=256, k=2,
+                                    act="swiglu", dtype="f32", renorm=True, x_std=0.5)),
 }
 
 
@@ -244,6 +265,8 @@ def _edge_cases():
     lg = np.random.default_rng(3).standard_normal((400, 6)).astype(np.float32)
     lg[:, 3] = -50.0
     cases["empty_expert"] = Case(cfg, logits=lg)
+    cfg = _small("empty_expert_swiglu", T=400, d=128, E=6, f=256, k=2, act="swiglu", renorm=True)
+    cases["empty_expert_swiglu"] = Case(cfg, logits=lg)
     # every token on one expert
     cfg = _small("one_expert", T=300, d=128, E=4, f=256, k=1)
     cases["one_expert"] = Case(cfg, logits=_assign_logits(300, 4, np.zeros(300, int)))
@@ -298,6 +321,7 @@ FULL = {
     "moe_xs": Case(synth.CONFIGS["moe_xs"], n_tokens=96),
     "moe_small": Case(synth.CONFIGS["moe_small"], n_tokens=64, n_wgrad=24),
     "mixtral": Case(synth.CONFIGS["mixtral"], n_tokens=12),
+    "mixtral_train": Case(synth.CONFIGS["mixtral_train"], n_tokens=8, n_wgrad=8),
     "skew": Case(synth.CONFIGS["skew"], n_tokens=32, n_wgrad=16),
 }
 
