@@ -13,13 +13,14 @@ draws resident in HBM before the timed region.
 
 Prints ONE JSON line.  ``value`` is the useful TFLOP/s of the step
 (useful flops = 2 * T * k * d * f per product; 6 products with GeLU
-experts, 9 with SwiGLU ones; padded rows are excluded).  In the backward the weight gradients run on a second stream
-beside the data-gradient chain.  ``roofline`` reports the step's dominant
-kernel (largest mean duration in the timed steps) against the bf16 dense
-MFMA peak, timed with HIP events on the stream each call runs on;
-``roofline_serial`` the same for a few steps after the timed region with
-every call alone.  ``traffic`` is HBM bytes per launch from the committed
-counter summary (null once the GEMM source has changed since).
+experts, 9 with SwiGLU ones; padded rows are excluded).  The calls run in order on one stream; ``--overlap`` runs the
+weight gradients on a second stream beside the data-gradient chain instead,
+and ``--compare-schedules`` also times the other schedule after the timed
+steps (context only).  ``roofline`` reports the step's dominant kernel (largest mean
+duration in the timed steps) against the bf16 dense MFMA peak, timed with
+HIP events on the stream each call runs on.  ``traffic`` is HBM bytes per
+launch from the committed counter summary (null once the GEMM source has
+changed since).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload on this host's cores.
 """
@@ -48,6 +49,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="moe_small")
+    ap.add_argument("--overlap", action="store_true",
+                    help="weight gradients on a second stream in the timed steps")
+    ap.add_argument("--compare-schedules", action="store_true",
+                    help="after the timed steps, also time the other backward schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -107,10 +112,11 @@ def cpu_baseline(cfg, inp, target_s):
                       + f", {t:.1f} s wall on {orc.get_threads()} OpenMP threads"}
 
 
-def traffic_for(kernel_name):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, valid
-    only while the kernel source is unchanged since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_for(config, kernel_name):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary of this
+    workload, valid only while the kernel source is unchanged since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -140,6 +146,7 @@ def main():
     s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
                     cfg.backward)
     L = layer.Layer(s)
+    L.overlap = args.overlap
     up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
     x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
     logits = torch.from_numpy(inp["logits"]).cuda()
@@ -177,21 +184,21 @@ def main():
             per.setdefault(name, []).append(open_ev.pop(name).elapsed_time(ev))
     kern = {k: float(np.mean(v)) for k, v in per.items()}
 
-    # context: each call alone (the weight gradients not overlapped), a few
-    # steps after the timed region
-    serial, ser = [], {}
-    L.overlap, L.mark = False, (lambda n, p, _m=serial: mark(n, p, _m))
-    for _ in range(3):
-        L.step(x, logits, W1, W2, W3, dy)
-    torch.cuda.synchronize()
-    L.overlap, L.mark = True, None
-    for name, phase, ev in serial:
-        if phase == "begin":
-            open_ev[name] = ev
-        else:
-            ser.setdefault(name, []).append(open_ev.pop(name).elapsed_time(ev))
-    kern_serial = {k: round(float(np.mean(v)), 4) for k, v in ser.items()}
     step_ms = wall * 1e3 / args.steps
+
+    # context: the other backward schedule, a few steps after the timed region
+    other = None
+    if cfg.backward and args.compare_schedules:
+        L.overlap = not args.overlap
+        for _ in range(args.warmup):
+            L.step(x, logits, W1, W2, W3, dy)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            L.step(x, logits, W1, W2, W3, dy)
+        torch.cuda.synchronize()
+        other = (time.perf_counter() - t1) * 1e3 / args.steps
+        L.overlap = args.overlap
 
     per_product, total = useful_flops(cfg)
     tflops = total / (step_ms * 1e-3) / 1e12
@@ -242,20 +249,13 @@ def main():
         "tokens_per_s": round(cfg.T / (step_ms * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(dom)},
+                     "traffic": traffic_for(cfg.name, dom)},
         "kernels": kernels,
-        "kernels_serial_ms": kern_serial,
+        "schedule": "two streams" if args.overlap else "one stream",
     }
-    # the same figure for the kernel that dominates when every call runs
-    # alone (context: in the timed steps the weight gradients share the GPU
-    # with the data-gradient chain, which stretches both durations)
-    sg = [k for k in kern_serial if k in gemms]
-    if sg:
-        sdom = max(sg, key=lambda k: kern_serial[k])
-        sach = products_of(cfg, sdom) * per_product / (kern_serial[sdom] * 1e-3) / 1e12
-        out["roofline_serial"] = {"kernel": sdom, "bound": "mfma", "achieved": round(sach, 1),
-                                  "peak": peak, "unit": "TFLOP/s", "frac": round(sach / peak, 4),
-                                  "traffic": traffic_for(sdom)}
+    if other is not None:
+        key = "ms_per_step_one_stream" if args.overlap else "ms_per_step_two_streams"
+        out[key] = round(other, 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -10,9 +10,9 @@ Two modes:
 ``python3 -m block_sparse_gemm_amd.traffic summarize --fetch F.csv --write W.csv``
     Reads the two ``*_counter_collection.csv`` files, scales each kernel's
     mean counter value per dispatch by what the copy kernel reads for its
-    known byte count, and writes ``profiles/traffic.json`` (bytes per launch,
-    keyed by the layer's call names, stamped with the hash of the GEMM
-    source so stale figures are ignored) and a Markdown table.
+    known byte count, and writes ``profiles/traffic_<config>.json`` (bytes
+    per launch, keyed by the layer's call names, stamped with the hash of the
+    GEMM source so stale figures are ignored) and a Markdown table.
 """
 from __future__ import annotations
 
@@ -35,18 +35,30 @@ def source_sha() -> str:
     return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
 
 
+def traffic_path(config: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+
+
 def call_name(kernel: str):
-    """Map a kernel symbol to the layer's call name (None if not a layer kernel)."""
+    """Map a kernel symbol to the layer's call name (None if not a layer kernel).
+
+    Template arguments: dtype, mode (0 SDD, 1 dual-B SDD, 2 DSD, 3 DSTD, 4
+    two-set DSD), B K-contiguous, epilogue (3 and 4: the backward ones), out
+    dtype, swap (false: transposed DSTD output).  dW1 and dW3 run the same
+    instantiation and share its figure."""
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)>", kernel)
     if m:
         _, mode, b_kc, epi, _, swap = m.groups()
         if mode in ("0", "1"):
-            return "sdd_bwd" if epi == "3" else "sdd"
+            return "sdd_bwd" if epi in ("3", "4") else "sdd"
         if mode == "2":
             return "dsd_bwd" if b_kc == "true" else "dsd"
+        if mode == "4":
+            return "dsd_bwd"
         if mode == "3":
             return "dstd_dw2" if swap == "true" else "dstd_dw1"
-    for k in ("route_topk", "route_scan", "route_place", "permute_pad", "build_topology", "combine"):
+    for k in ("route_backward", "route_topk", "route_scan", "route_place", "permute_pad",
+              "build_topology", "combine"):
         if k in kernel:
             return k
     return None
@@ -124,9 +136,13 @@ def summarize(args):
         if kern.find("gemm_kernel") >= 0:
             ent["source_sha"] = sha
         result[name] = ent
+        if name == "dstd_dw1":
+            result["dstd_dw3"] = ent
         rows.append((name, fb / 1e6, wb / 1e6, kern[:80]))
-    os.makedirs(os.path.dirname(args.out), exist_ok=True)
-    json.dump(result, open(args.out, "w"), indent=1)
+    out = args.out or traffic_path(args.config)
+    md = args.md or os.path.join(ROOT, "profiles", f"{args.config}_traffic.md")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    json.dump(result, open(out, "w"), indent=1)
     lines = [f"# HBM traffic per launch: {args.config} layer step", "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over L2 channels), each scaled",
              f"by the reading of a plain {COPY_BYTES >> 20} MiB copy: fetch factor {f_fac:.4f}, write factor "
@@ -134,7 +150,7 @@ def summarize(args):
              "| call | fetch MB | write MB | kernel |", "|---|---|---|---|"]
     for name, fm, wm, k in rows:
         lines.append(f"| {name} | {fm:.1f} | {wm:.1f} | `{k}` |")
-    open(args.md, "w").write("\n".join(lines) + "\n")
+    open(md, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -148,8 +164,8 @@ def main():
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
     s.add_argument("--config", default="moe_small")
-    s.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
-    s.add_argument("--md", default=os.path.join(ROOT, "profiles", "moe_small_traffic.md"))
+    s.add_argument("--out", default=None, help="default profiles/traffic_<config>.json")
+    s.add_argument("--md", default=None, help="default profiles/<config>_traffic.md")
     s.add_argument("--cmd", nargs="*", default=[])
     a = ap.parse_args()
     sys.path.insert(0, ROOT)
