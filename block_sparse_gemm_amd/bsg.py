@@ -46,7 +46,7 @@ class TopoSizes(C.Structure):
 class TopologyStruct(C.Structure):
     _fields_ = [("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("row_idx", C.c_void_p),
                 ("col_ptr", C.c_void_p), ("trans_idx", C.c_void_p), ("row_pairs", C.c_void_p),
-                ("meta", C.c_void_p),
+                ("expert_order", C.c_void_p), ("meta", C.c_void_p),
                 ("E", C.c_int32), ("F", C.c_int32), ("Tp_max", C.c_int64)]
 
 
@@ -161,11 +161,13 @@ class Topology:
         self.trans_idx = torch.zeros(self.nnz_max, **i32)
         self.row_pairs_max = int(sz.row_pairs_max)
         self.row_pairs = torch.zeros(self.row_pairs_max, **i32)
+        self.expert_order = torch.zeros(E, **i32)
         self.meta = torch.zeros(4, **i32)
         self.struct = TopologyStruct(self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
                                      self.row_idx.data_ptr(), self.col_ptr.data_ptr(),
                                      self.trans_idx.data_ptr(), self.row_pairs.data_ptr(),
-                                     self.meta.data_ptr(), E, self.F, Tp_max)
+                                     self.expert_order.data_ptr(), self.meta.data_ptr(), E,
+                                     self.F, Tp_max)
 
 
 # ------------------------------------------------------------------- calls

@@ -60,6 +60,7 @@ bsg_status check_topology(const bsg_topology* t) {
     REQUIRE_PTR(t->col_ptr);
     REQUIRE_PTR(t->trans_idx);
     REQUIRE_PTR(t->row_pairs);
+    REQUIRE_PTR(t->expert_order);
     REQUIRE_PTR(t->meta);
     return BSG_OK;
 }
@@ -199,7 +200,8 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
         bsg::launch_build_topology(bin_offsets, E, topo->F, Tp_max / BSG_BLOCK,
                                    row_pairs_max(Tp_max / BSG_BLOCK, E), topo->row_ptr,
                                    topo->col_idx, topo->row_idx, topo->col_ptr, topo->trans_idx,
-                                   topo->row_pairs, topo->meta, (hipStream_t)stream),
+                                   topo->row_pairs, topo->expert_order, topo->meta,
+                                   (hipStream_t)stream),
         "build_topology");
 }
 
@@ -211,9 +213,15 @@ static bsg::GemmParams gemm_params(const bsg_topology* t) {
     p.col_ptr = t->col_ptr;
     p.trans_idx = t->trans_idx;
     p.row_pairs = t->row_pairs;
+    p.expert_order = t->expert_order;
     p.meta = t->meta;
     p.E = t->E;
     p.F = t->F;
+    // Tiles go in groups of row pairs (see the kernel's tile order); a group
+    // pays off when its rows share an expert, so it follows the expected row
+    // pairs per expert, Tp_max / (256 E): 1, 2 or at most 4.
+    const int64_t rpe = t->Tp_max / (2 * BSG_BLOCK * (int64_t)t->E);
+    p.group = rpe >= 4 ? 4 : rpe >= 2 ? 2 : 1;
     return p;
 }
 

@@ -68,6 +68,31 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Chunked variant: chunks of C consecutive tiles are dealt to the XCDs in
+// turn, so tiles early in the order start first on every XCD (the order is
+// kept across the chip) while each chunk stays in one XCD's L2.  The tail
+// that does not fill a round falls back to xcd_remap.  Bijective on [0, n).
+__device__ __forceinline__ int xcd_chunked(int w, int n, int C) {
+    const int x = w % kXcds, i = w / kXcds;
+    const int full = n / (kXcds * C);
+    if (i < full * C) return ((i / C) * kXcds + x) * C + i % C;
+    const int base = full * kXcds * C;
+    return base + xcd_remap(w - base, n - base);
+}
+
+// Tile t of an nm x nn grid in groups of G rows: inside a group the tiles go
+// down the rows first, so the tiles that run at the same time cover a few
+// rows x a few columns and share the operand panels of both.  Bijective.
+__device__ __forceinline__ void grouped_tile(int t, int nm, int nn, int G, int& m, int& n) {
+    const int per = G * nn;
+    const int g = t / per;
+    const int first = g * G;
+    const int gs = min(G, nm - first);
+    const int local = t - g * per;
+    n = local / gs;
+    m = first + local % gs;
+}
+
 // ------------------------------------------------------------ activations
 //
 // GeLU in the exact form 0.5 h (1 + erf(h / sqrt 2)).  erf is evaluated with

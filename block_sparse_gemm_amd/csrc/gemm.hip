@@ -40,9 +40,13 @@
 // DSTD) are stored k-major and read with ds_read_b64_tr_b16, which hands
 // each lane 4 consecutive k of its row: no transpose pass anywhere.
 //
-// Workgroup ids are remapped so each XCD runs a contiguous range of tiles:
-// neighbouring tiles share the A panels (SDD, DSD) or the block columns
-// (DSTD), which then stay in that XCD's L2.
+// Tile order.  Workgroup ids are remapped so each XCD runs a contiguous
+// range of tiles, and the tiles of SDD and DSD go in groups of a few row
+// pairs, down the rows first: the tiles that run at the same time on one
+// XCD cover a few row pairs x a few column tiles and share both operands'
+// panels in that XCD's L2.  DSTD tiles, whose K is the expert's row count,
+// go expert by expert in descending size (longest first), in chunks dealt
+// to the XCDs in turn.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,6 +62,9 @@ constexpr int kLdsBytes = kStages * kStageBytes;
 constexpr int kSegsPerWave = kSegs / 4;          // per panel
 constexpr int kLoadsPerTile = 4 * kSegsPerWave;  // per wave and K-tile
 constexpr int kIdxCap = 2048;                    // K-blocks of one tile staged in LDS at a time
+
+// Tile order (see xcd_chunked): consecutive DSTD tiles kept on one XCD.
+constexpr int kDstdChunk = 8;
 
 template <int DT>
 struct Elt;
@@ -261,8 +268,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     if constexpr (MODE == kModeDstd) ntiles = P.E * ((F + 1) / 2) * tn;
     else ntiles = P.meta[3] * tn;
     if ((int)blockIdx.x >= ntiles) return;
-    const int tile = xcd_remap(blockIdx.x, ntiles);
-    const int tm = tile / tn, tq = tile % tn;
+    // tm: row pair (SDD / DSD) or expert column pair (DSTD); tq: N tile
+    int tm, tq;
+    if constexpr (MODE == kModeDstd) {
+        // a DSTD tile's K is its expert's rows: experts longest first, each
+        // expert's tiles in groups of column pairs x N tiles
+        const int cpe = (F + 1) / 2, per_e = cpe * tn;
+        const int tile = xcd_chunked(blockIdx.x, ntiles, kDstdChunk);
+        const int rank = tile / per_e;
+        int j;
+        grouped_tile(tile - rank * per_e, cpe, tn, P.group, j, tq);
+        tm = P.expert_order[rank] * cpe + j;
+    } else {
+        const int tile = xcd_remap(blockIdx.x, ntiles);
+        grouped_tile(tile, ntiles / tn, tn, P.group, tm, tq);
+    }
 
     // the wave index is uniform: keep it (and every LDS stage address derived
     // from it) in scalar registers

@@ -50,11 +50,13 @@ struct GemmParams {
     const int32_t* col_ptr;
     const int32_t* trans_idx;
     const int32_t* row_pairs;  // pairs of block rows sharing a column list
+    const int32_t* expert_order;  // experts by descending row count
     const int32_t* meta;  // {nnz, R, overflow, row pairs} written by build_topology
     int K;                // SDD reduction length
     int N;                // DSD / DSTD output width
     int ntn;              // 256-wide output tiles along N
     int E, F;             // experts, column blocks per expert
+    int group;            // rows per group of the tile order (>= 1)
 };
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
@@ -74,7 +76,8 @@ hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
 hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
                                  int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
                                  int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
-                                 int32_t* row_pairs, int32_t* meta, hipStream_t stream);
+                                 int32_t* row_pairs, int32_t* expert_order, int32_t* meta,
+                                 hipStream_t stream);
 
 hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int epi, int dtype,
                       hipStream_t s);

@@ -7,9 +7,12 @@
 // this metadata, mapping each (expert, token-row range) to its nonzero
 // blocks, together with the transpose metadata in a single kernel.
 //
-// It also emits the row-pair schedule the products run on: consecutive
-// block rows of one expert share their column list, so a 256-row tile of
-// two such rows reads one set of weight columns.
+// It also emits the schedules the products run on: the row pairs
+// (consecutive block rows of one expert share their column list, so a
+// 256-row tile of two such rows reads one set of weight columns), and the
+// experts in descending order of their row count, so the weight-gradient
+// product, whose tile cost grows with the expert's rows, starts its longest
+// tiles first.
 //
 // The first layer's output is block-diagonal: row block r belongs to the
 // expert whose bin holds row 128 r, and that expert owns the F column
@@ -40,7 +43,8 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     const int32_t* __restrict__ bin_offsets, int E, int F, int64_t row_blocks_max,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ row_idx,
     int32_t* __restrict__ col_ptr, int32_t* __restrict__ trans_idx,
-    int32_t* __restrict__ row_pairs, int32_t* __restrict__ meta) {
+    int32_t* __restrict__ row_pairs, int32_t* __restrict__ expert_order,
+    int32_t* __restrict__ meta) {
     __shared__ int s[kMaxExperts + 1];   // bin start in row blocks
     __shared__ int pp[kMaxExperts + 1];  // first row pair of each expert
     __shared__ int part[kTopoThreads];
@@ -70,6 +74,17 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     const int64_t R = s[E];
     const int64_t nnz = R * F;
     const int64_t g = (int64_t)blockIdx.x * kTopoThreads + threadIdx.x;
+
+    // expert g's place in descending row count (ties: lower id first)
+    if (g < E) {
+        const int rg = s[g + 1] - s[g];
+        int rank = 0;
+        for (int e = 0; e < E; ++e) {
+            const int re = s[e + 1] - s[e];
+            rank += (re > rg || (re == rg && e < g)) ? 1 : 0;
+        }
+        expert_order[rank] = (int32_t)g;
+    }
 
     if (R > row_blocks_max) {
         // the routing needs more rows than the topology holds: publish an
@@ -126,15 +141,17 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
 hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
                                  int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
                                  int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
-                                 int32_t* row_pairs, int32_t* meta, hipStream_t stream) {
+                                 int32_t* row_pairs, int32_t* expert_order, int32_t* meta,
+                                 hipStream_t stream) {
     int64_t n = row_blocks_max * F;
     if (row_pairs_max > n) n = row_pairs_max;
     if (row_blocks_max + 1 > n) n = row_blocks_max + 1;
     if ((int64_t)E * F + 1 > n) n = (int64_t)E * F + 1;
+    if (E > n) n = E;
     const int grid = (int)((n + kTopoThreads - 1) / kTopoThreads);
     hipLaunchKernelGGL(build_topology_kernel, dim3(grid), dim3(kTopoThreads), 0, stream,
                        bin_offsets, E, F, row_blocks_max, row_ptr, col_idx, row_idx, col_ptr,
-                       trans_idx, row_pairs, meta);
+                       trans_idx, row_pairs, expert_order, meta);
     return hipGetLastError();
 }
 

@@ -96,6 +96,9 @@ typedef struct {
  *                        block rows of one expert taken two at a time
  *                        (a last single row when the expert has an odd
  *                        number); entry = (first row << 1) | (pair ? 1 : 0)
+ *   expert_order [E]     the experts in descending order of their row
+ *                        blocks (ties: lower id first), the order in which
+ *                        dstd schedules its tiles (longest first)
  *   meta      [4]        written on the device: {nnz, R, overflow, pairs};
  *                        overflow = 1 when the routing needs more than
  *                        Tp_max rows: the topology is then published empty
@@ -114,6 +117,7 @@ typedef struct {
     int32_t* col_ptr;
     int32_t* trans_idx;
     int32_t* row_pairs;
+    int32_t* expert_order;
     int32_t* meta;
     int32_t E;
     int32_t F;

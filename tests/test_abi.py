@@ -123,8 +123,8 @@ def test_permute_pad_validation(L):
 
 
 def fake_topo(E=4, f=256, Tp=1024, **over):
-    t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x70000, 0x60000, E,
-                           f // 128, Tp)
+    t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x70000, 0x80000,
+                           0x60000, E, f // 128, Tp)
     for k, v in over.items():
         setattr(t, k, v)
     return t
@@ -139,6 +139,8 @@ def test_build_topology_validation(L):
     assert "capacity" in _err(L)
     t2 = fake_topo(row_idx=None)
     assert L.bsg_build_topology(P, 4, 256, 1024, C.byref(t2), None) == bsg.EINVAL
+    t4 = fake_topo(expert_order=None)
+    assert L.bsg_build_topology(P, 4, 256, 1024, C.byref(t4), None) == bsg.EINVAL
     t3 = fake_topo(Tp=1000)
     assert L.bsg_build_topology(P, 4, 256, 1000, C.byref(t3), None) == bsg.EINVAL
 

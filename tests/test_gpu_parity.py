@@ -144,6 +144,11 @@ def check_case(orc, case: Case, seed=0):
             want_pairs.append((r0 << 1) | (1 if r0 + 1 < s1 else 0))
     assert meta[3] == len(want_pairs)
     assert L.topo.row_pairs[:len(want_pairs)].cpu().numpy().tolist() == want_pairs
+    # the weight-gradient schedule: experts by descending row blocks, ties to
+    # the lower id
+    rb = np.diff(r["bin_offsets"]) // 128
+    want_order = sorted(range(cfg.E), key=lambda e: (-rb[e], e))
+    assert L.topo.expert_order.cpu().numpy().tolist() == want_order, "expert_order"
 
     # ---- permuted, padded copy: bit-exact
     prec = cfg.dtype
