@@ -130,7 +130,8 @@ int orc_get_threads(void) {
  * pick the k experts with the largest logits (ties: lower id first), in rank
  * order; gate = softmax probability over all E experts, renormalised over
  * the k picks when renorm != 0.  Then count tokens per expert, pad each
- * count up to a multiple of 128, lay the bins out in ascending expert order
+ * count up to a multiple of bin (128, the block of section 1.3; coarser
+ * bins for the block-size study), lay the bins out in ascending expert order
  * (exclusive scan), and give every assignment a = t*k + j the next free row
  * of its expert's bin, visiting assignments in ascending a.
  *
@@ -138,10 +139,10 @@ int orc_get_threads(void) {
  * assignment that fills each row, or -1 for a pad row.
  * Returns 0, or -1 on bad arguments.
  */
-int orc_route(const float* logits, int64_t T, int E, int k, int renorm,
+int orc_route(const float* logits, int64_t T, int E, int k, int renorm, int bin,
               int32_t* expert_idx, float* gate, int32_t* counts, int32_t* bin_offsets,
               int32_t* dest_row, int32_t* row_src, int64_t row_src_len) {
-    if (!logits || T < 0 || E < 1 || k < 1 || k > E) return -1;
+    if (!logits || T < 0 || E < 1 || k < 1 || k > E || bin < 1) return -1;
     for (int64_t t = 0; t < T; ++t) {
         const float* l = logits + t * E;
         /* selection: k passes of "largest not yet taken, lower id on ties" */
@@ -179,7 +180,7 @@ int orc_route(const float* logits, int64_t T, int E, int k, int renorm,
     /* padded bins, ascending expert id */
     bin_offsets[0] = 0;
     for (int e = 0; e < E; ++e) {
-        int64_t padded = ((int64_t)counts[e] + BLK - 1) / BLK * BLK;
+        int64_t padded = ((int64_t)counts[e] + bin - 1) / bin * bin;
         bin_offsets[e + 1] = (int32_t)(bin_offsets[e] + padded);
     }
     /* stable placement */

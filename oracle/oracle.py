@@ -69,8 +69,8 @@ def lib():
         L.orc_set_threads.argtypes = [C.c_int]
         L.orc_get_threads.restype = C.c_int
         L.orc_route.restype = C.c_int
-        L.orc_route.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, C.c_int, _i32p, _f32p, _i32p,
-                                _i32p, _i32p, _i32p, C.c_int64]
+        L.orc_route.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, C.c_int, C.c_int, _i32p, _f32p,
+                                _i32p, _i32p, _i32p, _i32p, C.c_int64]
         L.orc_permute_pad.restype = C.c_int
         L.orc_permute_pad.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, _i32p, _f32p, C.c_int,
                                       C.c_int64, _f64p]
@@ -129,8 +129,9 @@ def silu_grad(z: float) -> float:
     return lib().orc_silu_grad(float(z))
 
 
-def route(logits: np.ndarray, k: int, renorm: bool = False) -> dict:
-    """Top-k routing, gates, histogram, padded bins, stable placement."""
+def route(logits: np.ndarray, k: int, renorm: bool = False, bin_rows: int = 128) -> dict:
+    """Top-k routing, gates, histogram, bins padded to a multiple of
+    bin_rows, stable placement."""
     logits = _f32(logits)
     T, E = logits.shape
     out = {
@@ -140,9 +141,9 @@ def route(logits: np.ndarray, k: int, renorm: bool = False) -> dict:
         "bin_offsets": np.zeros(E + 1, np.int32),
         "dest_row": np.zeros(T * k, np.int32),
     }
-    bound = T * k + 127 * min(E, T * k) + 128
+    bound = T * k + (bin_rows - 1) * min(E, T * k) + bin_rows
     row_src = np.zeros(bound, np.int32)
-    rc = lib().orc_route(_p(logits, _f32p), T, E, k, int(bool(renorm)),
+    rc = lib().orc_route(_p(logits, _f32p), T, E, k, int(bool(renorm)), int(bin_rows),
                          _p(out["expert_idx"], _i32p), _p(out["gate"], _f32p),
                          _p(out["counts"], _i32p), _p(out["bin_offsets"], _i32p),
                          _p(out["dest_row"], _i32p), _p(row_src, _i32p), bound)

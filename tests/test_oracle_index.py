@@ -28,15 +28,15 @@ def brute_route(logits, k):
     return np.array(sel, dtype=np.int32).reshape(-1)
 
 
-def check_placement(r, T, E, k):
+def check_placement(r, T, E, k, bin_rows=128):
     ei, dest, counts, bo = r["expert_idx"], r["dest_row"], r["counts"], r["bin_offsets"]
     # histogram
     assert np.array_equal(counts, np.bincount(ei, minlength=E))
-    # padded bins: multiples of 128, 0..127 pad rows, empty expert -> 0 rows
+    # padded bins: multiples of the bin, 0..bin-1 pad rows, empty expert -> 0 rows
     P = np.diff(bo)
     assert bo[0] == 0
-    assert np.all(P % 128 == 0)
-    assert np.all((P - counts >= 0) & (P - counts <= 127))
+    assert np.all(P % bin_rows == 0)
+    assert np.all((P - counts >= 0) & (P - counts <= bin_rows - 1))
     assert np.all((P == 0) == (counts == 0))
     # stable placement == numpy stable argsort by expert id
     order = np.argsort(ei, kind="stable")
@@ -192,3 +192,20 @@ def test_permute_pad_invariants(orc):
     xps = orc.permute_pad(x, k, r["dest_row"], Tp, scale=sc, prec="f64")
     a = rs[rs >= 0]
     assert np.array_equal(xps[rs >= 0], x[a // k].astype(np.float64) * sc[a, None].astype(np.float64))
+
+
+@pytest.mark.parametrize("bin_rows", [256, 64])
+def test_route_coarser_and_finer_bins(orc, bin_rows):
+    """Bins padded to 256 (or 64) rows: the same selection and stable
+    placement, bins of ceil(count / bin) * bin rows."""
+    rng = np.random.default_rng(17)
+    T, E, k = 700, 9, 2
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 4] -= 3.0  # a small expert
+    r = orc.route(logits, k, False, bin_rows)
+    assert np.array_equal(r["expert_idx"], brute_route(logits, k))
+    check_placement(r, T, E, k, bin_rows)
+    c = np.bincount(brute_route(logits, k), minlength=E)
+    assert int(r["bin_offsets"][E]) == sum(-(-int(x) // bin_rows) * bin_rows for x in c)
+    r128 = orc.route(logits, k, False)
+    assert np.array_equal(r["gate"], r128["gate"])
