@@ -16,9 +16,12 @@ Prints ONE JSON line.  ``value`` is the useful TFLOP/s of the step
 experts, 9 with SwiGLU ones; padded rows are excluded).  The calls run in order on one stream; ``--overlap`` runs the
 weight gradients on a second stream beside the data-gradient chain instead,
 and ``--compare-schedules`` also times the other schedule after the timed
-steps (context only).  ``roofline`` reports the step's dominant kernel (largest mean
-duration in the timed steps) against the bf16 dense MFMA peak, timed with
-HIP events on the stream each call runs on.  ``traffic`` is HBM bytes per
+steps (context only).  ``roofline`` reports the step's dominant kernel against the bf16 dense MFMA
+peak, timed with HIP events on the stream it runs on over the timed steps.
+Which call dominates, and the per-call table ``kernels``, come from a probe
+pass of three steps before the timed ones with every call bracketed by
+events; the timed steps record events around the dominant call only, since
+each event costs GPU time (about 4 us a call pair here).  ``traffic`` is HBM bytes per
 launch from the committed counter summary (null once the GEMM source has
 changed since).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--config", default="moe_small")
     ap.add_argument("--overlap", action="store_true",
                     help="weight gradients on a second stream in the timed steps")
+    ap.add_argument("--bin-rows", type=int, default=128, choices=(128, 256),
+                    help="pad expert bins to a multiple of this many rows (block-size study)")
     ap.add_argument("--compare-schedules", action="store_true",
                     help="after the timed steps, also time the other backward schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,7 +88,7 @@ def cpu_baseline(cfg, inp, target_s):
     (2 products) and the input-gradient path (2 products) per token."""
     from oracle import oracle as orc
     from block_sparse_gemm_amd import synth
-    r = orc.route(inp["logits"], cfg.k, cfg.renorm)
+    r = orc.route(inp["logits"], cfg.k, cfg.renorm, cfg.bin_rows)
     O = orc.make_layer(inp["x"].values, inp["W1"].values, inp["W2"].values, r, cfg.k, cfg.E,
                        act=cfg.act, W3=inp["W3"].values if "W3" in inp else None,
                        dy=inp["dy"].values if "dy" in inp else None, prec=cfg.dtype,
@@ -141,10 +146,11 @@ def main():
     from block_sparse_gemm_amd import layer, synth
 
     cfg = synth.CONFIGS[args.config]
+    if args.bin_rows != cfg.bin_rows:
+        cfg = cfg.replace(name=f"{cfg.name}_bins{args.bin_rows}", bin_rows=args.bin_rows)
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, 0)
-    s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
-                    cfg.backward)
+    s = layer.Shape.of(cfg)
     L = layer.Layer(s)
     L.overlap = args.overlap
     up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
@@ -158,14 +164,37 @@ def main():
     torch.cuda.synchronize()
 
     # per-call event pairs, each recorded on the stream the call runs on
-    marks = []
+    def recorder(store, only=None):
+        def mark(name, phase):
+            if only is None or name == only:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record()
+                store.append((name, phase, ev))
+        return mark
 
-    def mark(name, phase, _m=marks):
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record()
-        _m.append((name, phase, ev))
+    def durations(store):
+        per, open_ev = {}, {}
+        for name, phase, ev in store:
+            if phase == "begin":
+                open_ev[name] = ev
+            else:
+                per.setdefault(name, []).append(open_ev.pop(name).elapsed_time(ev))
+        return {k: float(np.mean(v)) for k, v in per.items()}
 
-    L.mark = mark
+    # probe: every call timed alone for a few steps (the per-call table, and
+    # which product dominates).  Events cost a few microseconds of GPU time
+    # each, so the timed steps below record them around that product only.
+    probe = []
+    L.mark = recorder(probe)
+    for _ in range(3):
+        L.step(x, logits, W1, W2, W3, dy)
+    torch.cuda.synchronize()
+    kern = durations(probe)
+    gemms = [k for k in kern if k.startswith(("sdd", "dsd", "dstd"))]
+    dom = max(gemms, key=lambda k: kern[k])
+
+    timed = []
+    L.mark = recorder(timed, only=dom)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -174,16 +203,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     L.mark = None
-
-    # per-kernel averages from each call's begin/end events
-    per, open_ev = {}, {}
-    for name, phase, ev in marks:
-        if phase == "begin":
-            open_ev[name] = ev
-        else:
-            per.setdefault(name, []).append(open_ev.pop(name).elapsed_time(ev))
-    kern = {k: float(np.mean(v)) for k, v in per.items()}
-
+    dom_ms = durations(timed)[dom]
     step_ms = wall * 1e3 / args.steps
 
     # context: the other backward schedule, a few steps after the timed region
@@ -202,9 +222,7 @@ def main():
 
     per_product, total = useful_flops(cfg)
     tflops = total / (step_ms * 1e-3) / 1e12
-    gemms = [k for k in kern if k.startswith(("sdd", "dsd", "dstd"))]
-    dom = max(gemms, key=lambda k: kern[k])
-    achieved = products_of(cfg, dom) * per_product / (kern[dom] * 1e-3) / 1e12
+    achieved = products_of(cfg, dom) * per_product / (dom_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
 
     kernels = {}
@@ -223,6 +241,10 @@ def main():
         elif k.startswith("unpermute_combine"):
             ypes = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
             b = A_n * cfg.d * ypes + cfg.T * cfg.d * es + 8 * A_n
+            ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
+        elif k == "route_backward":
+            ypes = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
+            b = cfg.T * cfg.d * es + A_n * cfg.d * ypes + 8 * cfg.T * cfg.E + 8 * A_n
             ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
         kernels[k] = ent
 
@@ -243,13 +265,15 @@ def main():
                 + f", N(0,{cfg.x_std:g}) x, N(0,{cfg.w_std:g}) weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T}, d={cfg.d}, E={cfg.E}, f={cfg.f}, "
                                f"k={cfg.k}, {cfg.act}, "
-                               f"{'forward+backward' if cfg.backward else 'forward'}",
+                               f"{'forward+backward' if cfg.backward else 'forward'}, "
+                               f"bins of {cfg.bin_rows} rows",
                    "padded_rows": Tp, "padding_frac": round(1 - A_n / Tp, 4)},
         "pct_of_bf16_peak": round(100 * tflops / peak, 2),
         "tokens_per_s": round(cfg.T / (step_ms * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(cfg.name, dom)},
+                     "traffic": traffic_for(cfg.name, dom), "ms": round(dom_ms, 4)},
+        # every call timed alone in a probe pass before the timed steps
         "kernels": kernels,
         "schedule": "two streams" if args.overlap else "one stream",
     }

@@ -62,18 +62,18 @@ def lib():
         L = C.CDLL(LIB_PATH)
         vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
         L.bsg_max_padded_rows.restype = i64
-        L.bsg_max_padded_rows.argtypes = [i64, i32, i32]
+        L.bsg_max_padded_rows.argtypes = [i64, i32, i32, i32]
         L.bsg_topology_sizes.restype = i32
         L.bsg_topology_sizes.argtypes = [i64, i32, i32, C.POINTER(TopoSizes)]
         L.bsg_route_workspace_bytes.restype = sz
         L.bsg_route_workspace_bytes.argtypes = [i64, i32, i32]
         L.bsg_route.restype = i32
-        L.bsg_route.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.bsg_route.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.bsg_route_backward.restype = i32
         L.bsg_route_backward.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32,
                                          i64, vp, vp]
         L.bsg_permute_pad.restype = i32
-        L.bsg_permute_pad.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp, i32, i64, vp, vp,
+        L.bsg_permute_pad.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp, i32, i32, i64, vp, vp,
                                       vp]
         L.bsg_build_topology.restype = i32
         L.bsg_build_topology.argtypes = [vp, i32, i32, i64, C.POINTER(TopologyStruct), vp]
@@ -130,8 +130,8 @@ def _ld(t: torch.Tensor) -> int:
 
 # ------------------------------------------------------------- size queries
 
-def max_padded_rows(T: int, k: int, E: int) -> int:
-    return int(lib().bsg_max_padded_rows(T, k, E))
+def max_padded_rows(T: int, k: int, E: int, bin_rows: int = BLOCK) -> int:
+    return int(lib().bsg_max_padded_rows(T, k, E, bin_rows))
 
 
 def topology_sizes(Tp_max: int, E: int, f: int) -> TopoSizes:
@@ -172,9 +172,11 @@ class Topology:
 
 # ------------------------------------------------------------------- calls
 
-def route(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets, workspace):
+def route(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets, workspace,
+          bin_rows=BLOCK):
     T, E = logits.shape
-    _check("route", lib().bsg_route(_ptr(logits), T, E, k, int(bool(renorm)), _ptr(expert_idx),
+    _check("route", lib().bsg_route(_ptr(logits), T, E, k, int(bool(renorm)), bin_rows,
+                                    _ptr(expert_idx),
                                     _ptr(gate), _ptr(dest_row), _ptr(counts), _ptr(bin_offsets),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream()))
@@ -188,11 +190,13 @@ def route_backward(logits, k, renorm, expert_idx, dest_row, dy, yp, dlogits):
         _stream()))
 
 
-def permute_pad(x, k, dest_row, scale, counts, bin_offsets, E, Tp_max, row_src, xp):
+def permute_pad(x, k, dest_row, scale, counts, bin_offsets, E, Tp_max, row_src, xp,
+                bin_rows=BLOCK):
     T, d = x.shape
     _check("permute_pad", lib().bsg_permute_pad(_ptr(x), dtype_code(x), T, d, k, _ptr(dest_row),
                                                 _ptr(scale), _ptr(counts), _ptr(bin_offsets), E,
-                                                Tp_max, _ptr(row_src), _ptr(xp), _stream()))
+                                                bin_rows, Tp_max, _ptr(row_src), _ptr(xp),
+                                                _stream()))
 
 
 def build_topology(bin_offsets, E, f, Tp_max, topo: Topology):

@@ -86,11 +86,11 @@ const char* bsg_status_string(bsg_status s) {
 
 const char* bsg_last_error(void) { return g_err; }
 
-int64_t bsg_max_padded_rows(int64_t T, int k, int E) {
-    if (T < 1 || k < 1 || E < 1 || k > E) return -1;
+int64_t bsg_max_padded_rows(int64_t T, int k, int E, int bin_rows) {
+    if (T < 1 || k < 1 || E < 1 || k > E || (bin_rows != 128 && bin_rows != 256)) return -1;
     const int64_t A = T * k;
     const int64_t ne = A < E ? A : E;
-    return (A + 127 * ne) / BSG_BLOCK * BSG_BLOCK;
+    return (A + (bin_rows - 1) * ne) / bin_rows * bin_rows;
 }
 
 bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out) {
@@ -114,16 +114,26 @@ size_t bsg_route_workspace_bytes(int64_t T, int k, int E) {
     return (size_t)(nchunks * E * (int64_t)sizeof(int32_t));
 }
 
-bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm,
+// The bin granularity: 128 (the block) or 256; 64 would need product tiles
+// with 64-row halves, which are not built.
+static bsg_status check_bin(int bin_rows) {
+    if (bin_rows == 64) return fail(BSG_EUNSUPPORTED, "bin_rows 64 is not implemented");
+    REQUIRE(bin_rows == 128 || bin_rows == 256, "bin_rows must be 128 or 256");
+    return BSG_OK;
+}
+
+bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                      int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                      int32_t* bin_offsets, void* workspace, size_t workspace_bytes,
                      bsg_stream_t stream) {
+    const bsg_status bs = check_bin(bin_rows);
+    if (bs != BSG_OK) return bs;
     REQUIRE(T >= 1, "T must be positive");
     REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
     REQUIRE(k >= 1 && k <= E, "k must be in [1, E]");
     if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
     REQUIRE(T * k < INT32_MAX, "T*k must fit int32 assignment ids");
-    REQUIRE(bsg_max_padded_rows(T, k, E) < INT32_MAX, "padded rows must fit int32");
+    REQUIRE(bsg_max_padded_rows(T, k, E, bin_rows) < INT32_MAX, "padded rows must fit int32");
     REQUIRE_PTR(logits);
     REQUIRE_PTR(expert_idx);
     REQUIRE_PTR(gate);
@@ -133,7 +143,7 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm,
     REQUIRE_PTR(workspace);
     REQUIRE(workspace_bytes >= bsg_route_workspace_bytes(T, k, E), "workspace too small (%zu < %zu)",
             workspace_bytes, bsg_route_workspace_bytes(T, k, E));
-    return hip_status(bsg::launch_route(logits, T, E, k, renorm, expert_idx, gate, dest_row,
+    return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
                                         counts, bin_offsets, (int32_t*)workspace,
                                         (hipStream_t)stream),
                       "route");
@@ -167,14 +177,16 @@ bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int 
 
 bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                            const int32_t* dest_row, const float* scale, const int32_t* counts,
-                           const int32_t* bin_offsets, int E, int64_t Tp_max, int32_t* row_src,
-                           void* xp, bsg_stream_t stream) {
+                           const int32_t* bin_offsets, int E, int bin_rows, int64_t Tp_max,
+                           int32_t* row_src, void* xp, bsg_stream_t stream) {
     REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
+    const bsg_status bs = check_bin(bin_rows);
+    if (bs != BSG_OK) return bs;
     REQUIRE(T >= 1 && k >= 1 && E >= 1 && E <= BSG_MAX_EXPERTS && k <= E, "bad T, k or E");
     REQUIRE(k <= BSG_MAX_TOPK, "k > %d", BSG_MAX_TOPK);
     REQUIRE(T * k < INT32_MAX, "T*k must fit int32");
     REQUIRE(d >= 1 && (d * elt_bytes(dtype)) % 16 == 0, "d must keep rows 16-byte aligned");
-    REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E), "Tp_max below the padded-row bound");
+    REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E, bin_rows), "Tp_max below the padded-row bound");
     REQUIRE_VEC_PTR(x);
     REQUIRE_VEC_PTR(xp);
     REQUIRE_PTR(dest_row);
@@ -183,7 +195,8 @@ bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
     REQUIRE_PTR(row_src);
     REQUIRE(scale == nullptr || aligned(scale, 4), "scale must be 4-byte aligned");
     return hip_status(bsg::launch_permute_pad(x, dtype, T, d, k, dest_row, scale, counts,
-                                              bin_offsets, E, row_src, xp, (hipStream_t)stream),
+                                              bin_offsets, E, bin_rows, row_src, xp,
+                                              (hipStream_t)stream),
                       "permute_pad");
 }
 

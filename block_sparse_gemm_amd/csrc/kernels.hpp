@@ -59,7 +59,7 @@ struct GemmParams {
     int group;            // rows per group of the tile order (>= 1)
 };
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, hipStream_t stream);
 
@@ -70,8 +70,8 @@ hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, i
 
 hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               const int32_t* dest_row, const float* scale, const int32_t* counts,
-                              const int32_t* bin_offsets, int E, int32_t* row_src, void* xp,
-                              hipStream_t stream);
+                              const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
+                              void* xp, hipStream_t stream);
 
 hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
                                  int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,

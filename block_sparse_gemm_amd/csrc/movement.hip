@@ -105,11 +105,11 @@ template <int DT>
 __global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
     const u32x4* __restrict__ x, int64_t T, int chunks, int k, const int32_t* __restrict__ dest_row,
     const float* __restrict__ scale, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ bin_offsets, int E, int32_t* __restrict__ row_src,
+    const int32_t* __restrict__ bin_offsets, int E, int bin_rows, int32_t* __restrict__ row_src,
     u32x4* __restrict__ xp) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nwaves = (int64_t)gridDim.x * kMoveWaves;
-    const int64_t njobs = T + (int64_t)E * kBlock;
+    const int64_t njobs = T + (int64_t)E * bin_rows;  // a bin's tail is below bin_rows rows
     for (int64_t job = (int64_t)blockIdx.x * kMoveWaves + threadIdx.x / kWave; job < njobs;
          job += nwaves) {
         if (job < T) {
@@ -126,8 +126,8 @@ __global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
             if (lane < k) row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
         } else {
             const int64_t p = job - T;
-            const int e = (int)(p / kBlock);
-            const int64_t row = (int64_t)bin_offsets[e] + counts[e] + p % kBlock;
+            const int e = (int)(p / bin_rows);
+            const int64_t row = (int64_t)bin_offsets[e] + counts[e] + p % bin_rows;
             if (row >= bin_offsets[e + 1]) continue;
             u32x4* dst = xp + row * chunks;
             for (int c = lane; c < chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
@@ -181,19 +181,19 @@ static int move_grid(int64_t jobs) {
 
 hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               const int32_t* dest_row, const float* scale, const int32_t* counts,
-                              const int32_t* bin_offsets, int E, int32_t* row_src, void* xp,
-                              hipStream_t stream) {
+                              const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
+                              void* xp, hipStream_t stream) {
     const int es = dtype == kBf16 ? 2 : 4;
     const int chunks = d * es / 16;
-    const int grid = move_grid(T + (int64_t)E * kBlock);
+    const int grid = move_grid(T + (int64_t)E * bin_rows);
     if (dtype == kBf16)
         hipLaunchKernelGGL(permute_pad_kernel<kBf16>, dim3(grid), dim3(kMoveThreads), 0, stream,
                            (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
-                           row_src, (u32x4*)xp);
+                           bin_rows, row_src, (u32x4*)xp);
     else
         hipLaunchKernelGGL(permute_pad_kernel<kF32>, dim3(grid), dim3(kMoveThreads), 0, stream,
                            (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
-                           row_src, (u32x4*)xp);
+                           bin_rows, row_src, (u32x4*)xp);
     return hipGetLastError();
 }
 

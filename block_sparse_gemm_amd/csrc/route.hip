@@ -2,7 +2,8 @@
 //
 // George Lin's Blog (MegaBlocks/FlexMoE post), section 1.4: tokens are
 // routed to experts and regrouped from batch order into expert order, each
-// group padded to a multiple of the 128 block size (section 1.3).  The
+// group padded to a multiple of the 128 block size (section 1.3), or of a
+// coarser bin (256 rows) for the block-size study.  The
 // pages leave the gate's form open; this follows top-k on the logits with a
 // softmax gate.
 //
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(int32_t* __restrict_
 __global__ __launch_bounds__(kRouteThreads) void route_place(
     const int32_t* __restrict__ expert_idx, int64_t T, int E, int k,
     const int32_t* __restrict__ chunk_base, int nchunks, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ dest_row, int32_t* __restrict__ bin_offsets) {
+    int bin_rows, int32_t* __restrict__ dest_row, int32_t* __restrict__ bin_offsets) {
     __shared__ int bins[kMaxExperts + 1];
     __shared__ int part[kRouteThreads];
     __shared__ int running[kMaxExperts];
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_place(
     const int lo = threadIdx.x * per;
     const int hi = min(lo + per, E);
     int s = 0;
-    for (int e = lo; e < hi; ++e) s += (counts[e] + kBlock - 1) / kBlock * kBlock;
+    for (int e = lo; e < hi; ++e) s += (counts[e] + bin_rows - 1) / bin_rows * bin_rows;
     part[threadIdx.x] = s;
     for (int e = threadIdx.x; e < E; e += kRouteThreads) running[e] = 0;
     __syncthreads();
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_place(
     int run = part[threadIdx.x] - s;
     for (int e = lo; e < hi; ++e) {
         bins[e] = run;
-        run += (counts[e] + kBlock - 1) / kBlock * kBlock;
+        run += (counts[e] + bin_rows - 1) / bin_rows * bin_rows;
     }
     if (threadIdx.x == kRouteThreads - 1) bins[E] = part[kRouteThreads - 1];
     __syncthreads();
@@ -345,7 +346,7 @@ hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, i
     return hipGetLastError();
 }
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm,
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, hipStream_t stream) {
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
@@ -361,7 +362,7 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
     hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace, nchunks,
                        counts);
     hipLaunchKernelGGL(route_place, dim3(nchunks), dim3(kRouteThreads), 0, stream, expert_idx, T,
-                       E, k, workspace, nchunks, counts, dest_row, bin_offsets);
+                       E, k, workspace, nchunks, counts, bin_rows, dest_row, bin_offsets);
     return hipGetLastError();
 }
 

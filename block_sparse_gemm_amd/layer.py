@@ -42,6 +42,13 @@ class Shape:
     yp_dtype: str = "bf16"     # storage of Yp / dXp
     renorm: bool = False
     backward: bool = False
+    bin_rows: int = 128        # expert bins padded to a multiple of this (128 or 256)
+
+    @classmethod
+    def of(cls, cfg) -> "Shape":
+        """The shape of a workload description (synth.LayerConfig or alike)."""
+        return cls(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
+                   cfg.backward, getattr(cfg, "bin_rows", 128))
 
     @property
     def tdtype(self):
@@ -71,7 +78,7 @@ class Layer:
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         A = s.T * s.k
-        self.Tp_max = bsg.max_padded_rows(s.T, s.k, s.E)
+        self.Tp_max = bsg.max_padded_rows(s.T, s.k, s.E, s.bin_rows)
         self.topo = bsg.Topology(self.Tp_max, s.E, s.f, device=dev)
         nnz_max = self.topo.nnz_max
         dt, ydt = s.tdtype, s.yp_tdtype
@@ -124,9 +131,9 @@ class Layer:
         c = self._call
         self.logits = logits  # the gate backward differentiates through it
         c("route", bsg.route, logits, s.k, s.renorm, self.expert_idx, self.gate, self.dest_row,
-          self.counts, self.bin_offsets, self.route_ws)
+          self.counts, self.bin_offsets, self.route_ws, bin_rows=s.bin_rows)
         c("permute_pad", bsg.permute_pad, x, s.k, self.dest_row, None, self.counts,
-          self.bin_offsets, s.E, self.Tp_max, self.row_src, self.xp)
+          self.bin_offsets, s.E, self.Tp_max, self.row_src, self.xp, bin_rows=s.bin_rows)
         c("build_topology", bsg.build_topology, self.bin_offsets, s.E, s.f, self.Tp_max, t)
         if s.act == "swiglu":
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3, aux_out=self.gp)
@@ -176,7 +183,7 @@ class Layer:
                   trans_c=True)
 
         c("permute_pad_bwd", bsg.permute_pad, dy, s.k, self.dest_row, self.gate, self.counts,
-          self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp)
+          self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp, bin_rows=s.bin_rows)
         if not self.overlap:
             route_backward()
             sdd_bwd()

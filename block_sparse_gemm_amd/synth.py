@@ -65,6 +65,9 @@ class LayerConfig:
     starved_bias: float = 0.0
     # Yp / dXp storage dtype ("bf16" or "f32"); f32 configs keep f32.
     yp_dtype: Optional[str] = None
+    # expert bins padded to a multiple of bin_rows (128 = the block; 256 for
+    # the block-size study)
+    bin_rows: int = 128
 
     def __post_init__(self):
         assert self.dtype in DTYPES and self.act in ACTS

@@ -79,8 +79,7 @@ def run(args):
 
     cfg = synth.CONFIGS[args.config]
     inp = synth.make_inputs(cfg, 0)
-    s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
-                    cfg.backward)
+    s = layer.Shape.of(cfg)
     L = layer.Layer(s)
     up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
     x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")

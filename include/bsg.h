@@ -126,10 +126,12 @@ typedef struct {
 
 /* ------------------------------------------------------------ size queries */
 
-/* Upper bound on Tp for any routing: 128 * floor((A + 127*min(E, A)) / 128)
- * with A = T*k (each non-empty expert pads by at most 127 rows,
- * section 1.3 "block size").  Returns -1 on invalid sizes. */
-int64_t bsg_max_padded_rows(int64_t T, int k, int E);
+/* Upper bound on Tp for any routing with bins padded to a multiple of
+ * bin_rows (128, the block of section 1.3, or 256):
+ *   bin_rows * floor((A + (bin_rows - 1) * min(E, A)) / bin_rows),  A = T*k
+ * (each non-empty expert pads by at most bin_rows - 1 rows).  Returns -1 on
+ * invalid sizes or an unsupported bin_rows. */
+int64_t bsg_max_padded_rows(int64_t T, int k, int E, int bin_rows);
 
 /* Capacities of the topology arrays for Tp_max padded rows. */
 bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out /* host */);
@@ -148,16 +150,20 @@ size_t bsg_route_workspace_bytes(int64_t T, int k, int E);
  *   gate [T*k] fp32 = softmax over all E logits of the picked expert;
  *   renorm != 0 divides by the sum over the k picks.
  *   counts [E] int32 tokens per expert; bin_offsets [E+1] int32 exclusive
- *   scan of ceil(counts/128)*128 in ascending expert id (Tp = bin_offsets[E]).
+ *   scan of ceil(counts/bin_rows)*bin_rows in ascending expert id
+ *   (Tp = bin_offsets[E]).  bin_rows is 128 (section 1.3's padding to the
+ *   block) or 256 (coarser bins for the block-size study); 64 returns
+ *   BSG_EUNSUPPORTED (it needs product tiles with 64-row halves).
  *   dest_row [T*k] int32: row of the padded, expert-grouped layout that
  *   assignment a = t*k + j occupies; inside a bin, ascending a.
  *   workspace: bsg_route_workspace_bytes(T, k, E) device bytes.
  *   Requires 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 1.
  *   Deterministic: integer results are bit-identical on every run.
  */
-bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, int32_t* expert_idx,
-                     float* gate, int32_t* dest_row, int32_t* counts, int32_t* bin_offsets,
-                     void* workspace, size_t workspace_bytes, bsg_stream_t stream);
+bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
+                     int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
+                     int32_t* bin_offsets, void* workspace, size_t workspace_bytes,
+                     bsg_stream_t stream);
 
 /*
  * route_backward - gradient of <dy, y> with respect to the router logits for
@@ -184,13 +190,14 @@ bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int 
  * dtype); the rows of each bin past its count are zero-filled; row_src
  * receives, for every row below Tp, the assignment that fills it or -1.
  *   x [T, d] (dtype), xp [Tp_max, d] (dtype), row_src [Tp_max] int32,
- *   counts/bin_offsets as produced by bsg_route.  Rows >= Tp are untouched.
- *   d must be a positive multiple of 8 (bf16) or 4 (fp32).
+ *   counts/bin_offsets as produced by bsg_route with the same bin_rows.
+ *   Rows >= Tp are untouched.  d must be a positive multiple of 8 (bf16) or
+ *   4 (fp32); Tp_max at least bsg_max_padded_rows(T, k, E, bin_rows).
  */
 bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                            const int32_t* dest_row, const float* scale, const int32_t* counts,
-                           const int32_t* bin_offsets, int E, int64_t Tp_max, int32_t* row_src,
-                           void* xp, bsg_stream_t stream);
+                           const int32_t* bin_offsets, int E, int bin_rows, int64_t Tp_max,
+                           int32_t* row_src, void* xp, bsg_stream_t stream);
 
 /*
  * build_topology - the topology + transpose metadata in ONE launch

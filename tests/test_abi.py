@@ -40,8 +40,12 @@ def test_size_queries(L):
         A = T * k
         want = (A + 127 * min(E, A)) // 128 * 128
         assert bsg.max_padded_rows(T, k, E) == want
+        want = (A + 255 * min(E, A)) // 256 * 256
+        assert bsg.max_padded_rows(T, k, E, 256) == want
     assert bsg.max_padded_rows(0, 1, 1) == -1
     assert bsg.max_padded_rows(4, 3, 2) == -1
+    assert bsg.max_padded_rows(4, 1, 2, 64) == -1
+    assert bsg.max_padded_rows(4, 1, 2, 200) == -1
     s = bsg.topology_sizes(139136, 64, 4096)
     assert (s.row_blocks_max, s.nnz_max, s.n_cols) == (1087, 1087 * 32, 64 * 32)
     assert s.row_pairs_max == (1087 + 64 + 1) // 2
@@ -60,12 +64,12 @@ def _err(L):
 
 def test_route_validation(L):
     ws = 1 << 20
-    ok_args = [P, 100, 8, 2, 0, P, P, P, P, P, P, ws, None]
+    ok_args = [P, 100, 8, 2, 0, 128, P, P, P, P, P, P, ws, None]
 
     def call(**over):
         a = list(ok_args)
-        names = ["logits", "T", "E", "k", "renorm", "expert_idx", "gate", "dest_row", "counts",
-                 "bin_offsets", "ws", "wsb", "stream"]
+        names = ["logits", "T", "E", "k", "renorm", "bin", "expert_idx", "gate", "dest_row",
+                 "counts", "bin_offsets", "ws", "wsb", "stream"]
         for key, v in over.items():
             a[names.index(key)] = v
         return L.bsg_route(*a)
@@ -81,6 +85,8 @@ def test_route_validation(L):
     assert call(ws=None) == bsg.EINVAL
     assert call(wsb=4) == bsg.EINVAL and "workspace" in _err(L)
     assert call(counts=C.c_void_p(0x10002)) == bsg.EINVAL
+    assert call(bin=64) == bsg.EUNSUPPORTED
+    assert call(bin=100) == bsg.EINVAL
 
 
 def test_route_backward_validation(L):
@@ -108,15 +114,19 @@ def test_route_backward_validation(L):
 def test_permute_pad_validation(L):
     T, d, k, E = 100, 128, 2, 8
     Tp = bsg.max_padded_rows(T, k, E)
-    base = [P, bsg.BF16, T, d, k, P, None, P, P, E, Tp, P, P, None]
+    base = [P, bsg.BF16, T, d, k, P, None, P, P, E, 128, Tp, P, P, None]
     assert L.bsg_permute_pad(*[None if i == 0 else v for i, v in enumerate(base)]) == bsg.EINVAL
     b = list(base); b[1] = 7
     assert L.bsg_permute_pad(*b) == bsg.EINVAL
     b = list(base); b[3] = 100  # 200 bytes per row: not 16-byte aligned rows
     assert L.bsg_permute_pad(*b) == bsg.EINVAL
-    b = list(base); b[10] = Tp - 128
+    b = list(base); b[11] = Tp - 128
     assert L.bsg_permute_pad(*b) == bsg.EINVAL and "Tp_max" in _err(L)
-    b = list(base); b[12] = MIS
+    b = list(base); b[10] = 256  # the 256-row bins need a larger Tp_max
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL and "Tp_max" in _err(L)
+    b = list(base); b[10] = 64
+    assert L.bsg_permute_pad(*b) == bsg.EUNSUPPORTED
+    b = list(base); b[13] = MIS
     assert L.bsg_permute_pad(*b) == bsg.EINVAL
     b = list(base); b[4] = 9
     assert L.bsg_permute_pad(*b) == bsg.EINVAL

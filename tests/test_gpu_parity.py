@@ -60,8 +60,7 @@ def make_case_inputs(case: Case, seed=0):
 
 def run_gpu(cfg, inp):
     from block_sparse_gemm_amd import layer
-    s = layer.Shape(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, cfg.act, cfg.dtype, cfg.yp, cfg.renorm,
-                    cfg.backward)
+    s = layer.Shape.of(cfg)
     L = layer.Layer(s)
     up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
     x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
@@ -116,7 +115,7 @@ def check_case(orc, case: Case, seed=0):
     report = {}
 
     # ---- routing, bins, placement: bit-exact
-    r = orc.route(inp["logits"], cfg.k, cfg.renorm)
+    r = orc.route(inp["logits"], cfg.k, cfg.renorm, cfg.bin_rows)
     for key, t in (("expert_idx", L.expert_idx), ("dest_row", L.dest_row), ("counts", L.counts),
                    ("bin_offsets", L.bin_offsets)):
         assert np.array_equal(t.cpu().numpy(), r[key]), key
@@ -260,6 +259,10 @@ SMALL = {
                                             f=256, k=1, act="swiglu")),
     "swiglu_train_f32": Case(_small("swiglu_train_f32", T=300, d=128, E=3, f=256, k=2,
                                     act="swiglu", dtype="f32", renorm=True, x_std=0.5)),
+    # bins padded to 256 rows (every expert an even number of block rows)
+    "bins256_bf16": Case(_small("bins256_bf16", bin_rows=256)),
+    "bins256_swiglu": Case(_small("bins256_swiglu", T=500, d=256, E=4, f=256, k=2,
+                                  act="swiglu", renorm=True, yp_dtype="f32", bin_rows=256)),
 }
 
 
@@ -327,6 +330,9 @@ FULL = {
     "moe_small": Case(synth.CONFIGS["moe_small"], n_tokens=64, n_wgrad=24),
     "mixtral": Case(synth.CONFIGS["mixtral"], n_tokens=12),
     "mixtral_train": Case(synth.CONFIGS["mixtral_train"], n_tokens=8, n_wgrad=8),
+    "moe_small_bins256": Case(synth.CONFIGS["moe_small"].replace(name="moe_small_bins256",
+                                                                 bin_rows=256),
+                              n_tokens=48, n_wgrad=16),
     "skew": Case(synth.CONFIGS["skew"], n_tokens=32, n_wgrad=16),
 }
 
