@@ -235,6 +235,11 @@ def main():
             fl = products_of(cfg, k) * per_product
             ent["useful_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
             ent["pct_bf16_peak"] = round(100 * fl / (ms * 1e-3) / 1e12 / peak, 1)
+        elif k == "permute_pad_gate_bwd":  # + yp read, logits in, dlogits out
+            ypes = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
+            b = (cfg.T * cfg.d * es + A_n * cfg.d * ypes + Tp * cfg.d * es + 8 * cfg.T * cfg.E
+                 + 12 * A_n + 4 * Tp)
+            ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
         elif k.startswith("permute_pad"):
             b = cfg.T * cfg.d * es + Tp * cfg.d * es + 4 * A_n + 4 * Tp
             ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)

@@ -28,7 +28,8 @@ EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
 
 # Every symbol include/bsg.h declares.
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
-           "bsg_route_backward", "bsg_permute_pad", "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dstd",
+           "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
+           "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_status_string", "bsg_last_error")
 
 
@@ -75,6 +76,10 @@ def lib():
         L.bsg_permute_pad.restype = i32
         L.bsg_permute_pad.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp, i32, i32, i64, vp, vp,
                                       vp]
+        L.bsg_permute_pad_gate_backward.restype = i32
+        L.bsg_permute_pad_gate_backward.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, vp, i32,
+                                                    i32, i64, vp, vp, vp, i32, vp, vp, i32, i64,
+                                                    vp, vp]
         L.bsg_build_topology.restype = i32
         L.bsg_build_topology.argtypes = [vp, i32, i32, i64, C.POINTER(TopologyStruct), vp]
         L.bsg_sdd.restype = i32
@@ -197,6 +202,16 @@ def permute_pad(x, k, dest_row, scale, counts, bin_offsets, E, Tp_max, row_src, 
                                                 _ptr(scale), _ptr(counts), _ptr(bin_offsets), E,
                                                 bin_rows, Tp_max, _ptr(row_src), _ptr(xp),
                                                 _stream()))
+
+
+def permute_pad_gate_backward(dy, k, dest_row, gate, counts, bin_offsets, E, Tp_max, row_src,
+                              dyp, logits, renorm, expert_idx, yp, dlogits, bin_rows=BLOCK):
+    T, d = dy.shape
+    _check("permute_pad_gate_backward", lib().bsg_permute_pad_gate_backward(
+        _ptr(dy), dtype_code(dy), T, d, k, _ptr(dest_row), _ptr(gate), _ptr(counts),
+        _ptr(bin_offsets), E, bin_rows, Tp_max, _ptr(row_src), _ptr(dyp), _ptr(logits),
+        int(bool(renorm)), _ptr(expert_idx), _ptr(yp), dtype_code(yp), _ld(yp), _ptr(dlogits),
+        _stream()))
 
 
 def build_topology(bin_offsets, E, f, Tp_max, topo: Topology):

@@ -200,6 +200,43 @@ bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                       "permute_pad");
 }
 
+bsg_status bsg_permute_pad_gate_backward(const void* dy, int dtype, int64_t T, int d, int k,
+                                         const int32_t* dest_row, const float* gate,
+                                         const int32_t* counts, const int32_t* bin_offsets, int E,
+                                         int bin_rows, int64_t Tp_max, int32_t* row_src,
+                                         void* dyp, const float* logits, int renorm,
+                                         const int32_t* expert_idx, const void* yp, int yp_dtype,
+                                         int64_t ld_yp, float* dlogits, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dtype) && dtype_ok(yp_dtype), "unknown dtype");
+    if (dtype == BSG_F32 && yp_dtype == BSG_BF16)
+        return fail(BSG_EUNSUPPORTED, "fp32 dy with bf16 yp is not implemented");
+    const bsg_status bs = check_bin(bin_rows);
+    if (bs != BSG_OK) return bs;
+    REQUIRE(T >= 1 && k >= 1 && E >= 1 && E <= BSG_MAX_EXPERTS && k <= E, "bad T, k or E");
+    if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
+    REQUIRE(T * k < INT32_MAX, "T*k must fit int32");
+    REQUIRE(d >= 1 && (d * elt_bytes(dtype)) % 16 == 0, "d must keep rows 16-byte aligned");
+    REQUIRE(ld_yp >= d && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
+            "ld_yp must be >= d with 16-byte aligned rows");
+    REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E, bin_rows), "Tp_max below the padded-row bound");
+    REQUIRE_VEC_PTR(dy);
+    REQUIRE_VEC_PTR(dyp);
+    REQUIRE_VEC_PTR(yp);
+    REQUIRE_PTR(dest_row);
+    REQUIRE_PTR(gate);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(bin_offsets);
+    REQUIRE_PTR(row_src);
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(expert_idx);
+    REQUIRE_PTR(dlogits);
+    return hip_status(bsg::launch_permute_gate_backward(dy, dtype, T, d, k, dest_row, gate, counts,
+                                                        bin_offsets, E, bin_rows, row_src, dyp,
+                                                        logits, renorm, expert_idx, yp, yp_dtype,
+                                                        ld_yp, dlogits, (hipStream_t)stream),
+                      "permute_pad_gate_backward");
+}
+
 bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
                               const bsg_topology* topo, bsg_stream_t stream) {
     REQUIRE_PTR(bin_offsets);

@@ -152,4 +152,74 @@ __device__ __forceinline__ void silu_and_grad(float g, float& s, float& sp) {
     sp = sg * fmaf(g, 1.0f - sg, 1.0f);
 }
 
+
+// ------------------------------------------------------------ gate backward
+//
+// The router-logit gradient of one token, one wave: lane j < k holds dg_j =
+// <dy_t, yp_j> and the expert e_j of pick j.  Softmax p of the E logits
+// (NV per lane, max-subtracted); dL/dp at the picks (with renorm:
+// dg_j / S - (sum_i dg_i p_(e_i)) / S^2, S = sum of the picks' p); scattered
+// to the experts' lanes; out[e] = p_e (dL/dp_e - sum_u p_u dL/dp_u).
+template <int NV>
+__device__ __forceinline__ void gate_grad_token(const float* __restrict__ l, int E, int k,
+                                                int renorm, float my_dg, int my_e,
+                                                float* __restrict__ out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    // ---- softmax of the logits (max-subtracted)
+    float p[NV];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        p[i] = e < E ? l[e] : -INFINITY;
+        mx = fmaxf(mx, p[i]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        p[i] = e < E ? expf(p[i] - mx) : 0.0f;
+        z += p[i];
+    }
+    z = wave_sum(z);
+    const float rz = 1.0f / z;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) p[i] *= rz;
+    // ---- dL/dp at the picks (lane j: expert e_j)
+    float pe = 0.0f;  // p[e_j] on lane j
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const float x = __shfl(p[i], my_e & (kWave - 1), kWave);
+        if (i == (my_e >> 6)) pe = x;
+    }
+    float my_dp = my_dg;
+    if (renorm) {
+        const float S = wave_sum(lane < k ? pe : 0.0f);
+        const float D = wave_sum(lane < k ? my_dg * pe : 0.0f);
+        my_dp = my_dg / S - D / (S * S);
+    }
+    // ---- scatter to the experts' lanes, then the softmax Jacobian
+    float dp[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dp[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const int ej = __shfl(my_e, j, kWave);
+        const float dj = __shfl(my_dp, j, kWave);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (lane + kWave * i == ej) dp[i] += dj;
+    }
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) dot = fmaf(p[i], dp[i], dot);
+    dot = wave_sum(dot);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E) out[e] = p[i] * (dp[i] - dot);
+    }
+}
+
 }  // namespace bsg

@@ -73,6 +73,14 @@ hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
                               void* xp, hipStream_t stream);
 
+hipError_t launch_permute_gate_backward(const void* dy, int dtype, int64_t T, int d, int k,
+                                        const int32_t* dest_row, const float* gate,
+                                        const int32_t* counts, const int32_t* bin_offsets, int E,
+                                        int bin_rows, int32_t* row_src, void* dyp,
+                                        const float* logits, int renorm,
+                                        const int32_t* expert_idx, const void* yp, int yp_dtype,
+                                        int64_t ld_yp, float* dlogits, hipStream_t stream);
+
 hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
                                  int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
                                  int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,

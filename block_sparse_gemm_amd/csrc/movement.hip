@@ -1,5 +1,6 @@
-// Data movement: the fused permutation + padding gather, and the weighted
-// un-permute/combine.
+// Data movement: the fused permutation + padding gather, the weighted
+// un-permute/combine, and the backward's permutation of dy fused with the
+// gate backward.
 //
 // permute_pad follows George Lin's Blog (MegaBlocks/FlexMoE post),
 // section 1.4: one kernel reorders tokens from batch order into expert
@@ -136,6 +137,70 @@ __global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
     }
 }
 
+// The backward's first step in one pass over dy: dYp = permute_pad(dy,
+// scale = gate), exactly as permute_pad_kernel, and the gate backward of
+// each token: dg_j = <dy_t, yp_j> accumulated (fp32) while dy's chunks are
+// in registers, then the router-logit gradient (gate_grad_token).
+template <int DT, int YP, int NV>
+__global__ __launch_bounds__(kMoveThreads) void permute_gate_backward_kernel(
+    const u32x4* __restrict__ dy, int64_t T, int chunks, int k,
+    const int32_t* __restrict__ dest_row, const float* __restrict__ gate,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ bin_offsets, int E,
+    int bin_rows, int32_t* __restrict__ row_src, u32x4* __restrict__ dyp,
+    const float* __restrict__ logits, int renorm, const int32_t* __restrict__ expert_idx,
+    const char* __restrict__ yp, int64_t ld_yp_bytes, float* __restrict__ dlogits) {
+    constexpr int V = Row<DT>::kVec;                       // dy values per 16-byte chunk
+    constexpr int YCB = V * (YP == kBf16 ? 2 : 4);         // yp bytes of those values
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t nwaves = (int64_t)gridDim.x * kMoveWaves;
+    const int64_t njobs = T + (int64_t)E * bin_rows;
+    for (int64_t job = (int64_t)blockIdx.x * kMoveWaves + threadIdx.x / kWave; job < njobs;
+         job += nwaves) {
+        if (job < T) {
+            const int64_t t = job;
+            const u32x4* src = dy + t * chunks;
+            float my_dg = 0.0f;
+            int my_e = 0;
+            for (int j = 0; j < k; ++j) {
+                const int64_t a = t * k + j;
+                const int64_t row = dest_row[a];
+                const float g = gate[a];
+                const char* yr = yp + row * ld_yp_bytes;
+                float s = 0.0f;
+                for (int c = lane; c < chunks; c += kWave) {
+                    const u32x4 v = src[c];
+                    dyp[row * chunks + c] = scale_chunk<DT>(v, g);
+                    float x[V], y[V];
+                    Row<DT>::load_f32(&v, x);
+                    if constexpr (YCB == 16) {
+                        Row<YP>::load_f32(yr + (int64_t)c * 16, y);
+                    } else {  // bf16 dy, fp32 yp: two 16-byte chunks of yp
+                        Row<kF32>::load_f32(yr + (int64_t)c * 32, y);
+                        Row<kF32>::load_f32(yr + (int64_t)c * 32 + 16, y + 4);
+                    }
+#pragma unroll
+                    for (int q = 0; q < V; ++q) s = fmaf(x[q], y[q], s);
+                }
+                s = wave_sum(s);
+                if (lane == j) {
+                    my_dg = s;
+                    my_e = expert_idx[a];
+                }
+            }
+            if (lane < k) row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
+            gate_grad_token<NV>(logits + t * E, E, k, renorm, my_dg, my_e, dlogits + t * E);
+        } else {
+            const int64_t p = job - T;
+            const int e = (int)(p / bin_rows);
+            const int64_t row = (int64_t)bin_offsets[e] + counts[e] + p % bin_rows;
+            if (row >= bin_offsets[e + 1]) continue;
+            u32x4* dst = dyp + row * chunks;
+            for (int c = lane; c < chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
+            if (lane == 0) row_src[row] = -1;
+        }
+    }
+}
+
 // y[t] = sum_j g_j * yp[dest_row[t*k + j]], fp32 accumulation in ascending j.
 template <int DT_IN, int DT_OUT>
 __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
@@ -195,6 +260,52 @@ hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                            (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
                            bin_rows, row_src, (u32x4*)xp);
     return hipGetLastError();
+}
+
+template <int DT, int YP>
+static hipError_t launch_pgb(const void* dy, int64_t T, int d, int k, const int32_t* dest_row,
+                             const float* gate, const int32_t* counts,
+                             const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
+                             void* dyp, const float* logits, int renorm,
+                             const int32_t* expert_idx, const void* yp, int64_t ld_yp_bytes,
+                             float* dlogits, hipStream_t stream) {
+    const int chunks = d * (DT == kBf16 ? 2 : 4) / 16;
+    const int grid = move_grid(T + (int64_t)E * bin_rows);
+#define BSG_PGB(NV)                                                                              \
+    hipLaunchKernelGGL((permute_gate_backward_kernel<DT, YP, NV>), dim3(grid), dim3(kMoveThreads), \
+                       0, stream, (const u32x4*)dy, T, chunks, k, dest_row, gate, counts,        \
+                       bin_offsets, E, bin_rows, row_src, (u32x4*)dyp, logits, renorm, expert_idx, \
+                       (const char*)yp, ld_yp_bytes, dlogits)
+    if (E <= 64) BSG_PGB(1);
+    else if (E <= 128) BSG_PGB(2);
+    else if (E <= 256) BSG_PGB(4);
+    else if (E <= 512) BSG_PGB(8);
+    else BSG_PGB(16);
+#undef BSG_PGB
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_gate_backward(const void* dy, int dtype, int64_t T, int d, int k,
+                                        const int32_t* dest_row, const float* gate,
+                                        const int32_t* counts, const int32_t* bin_offsets, int E,
+                                        int bin_rows, int32_t* row_src, void* dyp,
+                                        const float* logits, int renorm,
+                                        const int32_t* expert_idx, const void* yp, int yp_dtype,
+                                        int64_t ld_yp, float* dlogits, hipStream_t stream) {
+    const int64_t ldb = ld_yp * (yp_dtype == kBf16 ? 2 : 4);
+    if (dtype == kBf16 && yp_dtype == kBf16)
+        return launch_pgb<kBf16, kBf16>(dy, T, d, k, dest_row, gate, counts, bin_offsets, E,
+                                        bin_rows, row_src, dyp, logits, renorm, expert_idx, yp,
+                                        ldb, dlogits, stream);
+    if (dtype == kBf16)
+        return launch_pgb<kBf16, kF32>(dy, T, d, k, dest_row, gate, counts, bin_offsets, E,
+                                       bin_rows, row_src, dyp, logits, renorm, expert_idx, yp,
+                                       ldb, dlogits, stream);
+    if (yp_dtype == kF32)
+        return launch_pgb<kF32, kF32>(dy, T, d, k, dest_row, gate, counts, bin_offsets, E,
+                                      bin_rows, row_src, dyp, logits, renorm, expert_idx, yp, ldb,
+                                      dlogits, stream);
+    return hipErrorInvalidValue;  // fp32 dy with bf16 yp: not a layout the layer produces
 }
 
 hipError_t launch_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,

@@ -260,62 +260,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_backward_kernel(
                 my_e = expert_idx[t * k + j];
             }
         }
-        // ---- softmax of the logits (max-subtracted)
-        const float* l = logits + t * E;
-        float p[NV];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = lane + kWave * i;
-            p[i] = e < E ? l[e] : -INFINITY;
-            mx = fmaxf(mx, p[i]);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-        float z = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = lane + kWave * i;
-            p[i] = e < E ? expf(p[i] - mx) : 0.0f;
-            z += p[i];
-        }
-        z = wave_sum(z);
-        const float rz = 1.0f / z;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) p[i] *= rz;
-        // ---- dL/dp at the picks (lane j: expert e_j)
-        float pe = 0.0f;  // p[e_j] on lane j
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const float x = __shfl(p[i], my_e & (kWave - 1), kWave);
-            if (i == (my_e >> 6)) pe = x;
-        }
-        float my_dp = my_dg;
-        if (renorm) {
-            const float S = wave_sum(lane < k ? pe : 0.0f);
-            const float D = wave_sum(lane < k ? my_dg * pe : 0.0f);
-            my_dp = my_dg / S - D / (S * S);
-        }
-        // ---- scatter to the experts' lanes, then the softmax Jacobian
-        float dp[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) dp[i] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int ej = __shfl(my_e, j, kWave);
-            const float dj = __shfl(my_dp, j, kWave);
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (lane + kWave * i == ej) dp[i] += dj;
-        }
-        float dot = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) dot = fmaf(p[i], dp[i], dot);
-        dot = wave_sum(dot);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = lane + kWave * i;
-            if (e < E) dlogits[t * E + e] = p[i] * (dp[i] - dot);
-        }
+        gate_grad_token<NV>(logits + t * E, E, k, renorm, my_dg, my_e, dlogits + t * E);
     }
 }
 

@@ -5,9 +5,10 @@ Forward (George Lin's Blog, MegaBlocks/FlexMoE post, sections 1.2-1.4):
     -> unpermute_combine
 Backward (plain calculus on the same products, weight gradients through the
 transpose index as section 1.3 describes):
-    permute_pad(dy, scale = gate) -> sdd(dYp, W2^T, GeLU') -> dsd(dH, W1^T)
-    -> unpermute_combine(gate = 1) ; dstd(A, dYp) = dW2 ; dstd(dH, Xp)^T = dW1 ;
-    route_backward(dy, Yp) = dlogits (the gate's gradient, selection fixed)
+    permute_pad(dy, scale = gate) + route_backward(dy, Yp) = dlogits (the
+    gate's gradient, selection fixed) in one pass over dy
+    -> sdd(dYp, W2^T, GeLU') -> dsd(dH, W1^T) -> unpermute_combine(gate = 1) ;
+    dstd(A, dYp) = dW2 ; dstd(dH, Xp)^T = dW1
 SwiGLU experts keep silu(g) and u * silu'(g) from the forward; their
 backward product gives the gate and the up projection's gradients (two
 planes of dH), the input gradient is one two-set dsd (dH_gate W1^T +
@@ -156,10 +157,6 @@ class Layer:
         sw = s.act == "swiglu"
         dh0 = self.plane(self.dh, 0) if sw else self.dh
 
-        def route_backward():
-            c("route_backward", bsg.route_backward, self.logits, s.k, s.renorm, self.expert_idx,
-              self.dest_row, dy, self.yp, self.dlogits)
-
         def sdd_bwd():
             c("sdd_bwd", bsg.sdd, self.dyp, W2, s.d, t, "silu_mul_bwd" if sw else "gelu_bwd",
               self.dh, trans_b=True, aux_in=self.gp)
@@ -182,10 +179,10 @@ class Layer:
                 c("dstd_dw3", bsg.dstd, self.plane(self.dh, 1), t, self.xp, s.d, self.dW3,
                   trans_c=True)
 
-        c("permute_pad_bwd", bsg.permute_pad, dy, s.k, self.dest_row, self.gate, self.counts,
-          self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp, bin_rows=s.bin_rows)
+        c("permute_pad_gate_bwd", bsg.permute_pad_gate_backward, dy, s.k, self.dest_row,
+          self.gate, self.counts, self.bin_offsets, s.E, self.Tp_max, self.row_src_b, self.dyp,
+          self.logits, s.renorm, self.expert_idx, self.yp, self.dlogits, bin_rows=s.bin_rows)
         if not self.overlap:
-            route_backward()
             sdd_bwd()
             dsd_bwd()
             dw2()
@@ -194,7 +191,6 @@ class Layer:
         self.ev_dyp.record(main)
         with torch.cuda.stream(self.side):
             self.side.wait_event(self.ev_dyp)
-            route_backward()
             dw2()
         sdd_bwd()
         self.ev_dh.record(main)

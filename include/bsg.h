@@ -200,6 +200,25 @@ bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                            int32_t* row_src, void* xp, bsg_stream_t stream);
 
 /*
+ * permute_pad_gate_backward - the backward's first step in one pass over
+ * dy: what bsg_permute_pad(dy, ..., scale = gate, ...) writes (dyp, row_src)
+ * and what bsg_route_backward writes (dlogits), the dot products
+ * <dy_t, yp_j> taken while dy's rows are read for the permutation
+ * (section 1.4's fused permutation kernel, here with the gate's gradient,
+ * plain calculus on the gate of bsg_route).  Arguments as in those two
+ * calls: dy [T, d] (dtype), gate [T*k] fp32 (the scale), yp [Tp_max, ld_yp]
+ * (yp_dtype) the forward's expert outputs, logits [T, E] fp32, dlogits
+ * [T, E] fp32 out.  fp32 dy needs fp32 yp (else BSG_EUNSUPPORTED).
+ */
+bsg_status bsg_permute_pad_gate_backward(const void* dy, int dtype, int64_t T, int d, int k,
+                                         const int32_t* dest_row, const float* gate,
+                                         const int32_t* counts, const int32_t* bin_offsets, int E,
+                                         int bin_rows, int64_t Tp_max, int32_t* row_src,
+                                         void* dyp, const float* logits, int renorm,
+                                         const int32_t* expert_idx, const void* yp, int yp_dtype,
+                                         int64_t ld_yp, float* dlogits, bsg_stream_t stream);
+
+/*
  * build_topology - the topology + transpose metadata in ONE launch
  * (section 1.4, last paragraph): maps each expert's token row range to its
  * nonzero blocks.  Fills every array of *topo (see bsg_topology) from

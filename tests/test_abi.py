@@ -132,6 +132,31 @@ def test_permute_pad_validation(L):
     assert L.bsg_permute_pad(*b) == bsg.EINVAL
 
 
+def test_permute_pad_gate_backward_validation(L):
+    T, d, k, E = 100, 128, 2, 8
+    Tp = bsg.max_padded_rows(T, k, E)
+    names = ["dy", "dt", "T", "d", "k", "dest", "gate", "counts", "bo", "E", "bin", "Tp", "rs",
+             "dyp", "logits", "renorm", "ei", "yp", "ypt", "ld", "dl", "stream"]
+    ok = [P, bsg.BF16, T, d, k, P, P, P, P, E, 128, Tp, P, P, P, 0, P, P, bsg.BF16, d, P, None]
+
+    def call(**over):
+        a = list(ok)
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_permute_pad_gate_backward(*a)
+
+    assert call(dy=None) == bsg.EINVAL
+    assert call(gate=None) == bsg.EINVAL
+    assert call(dl=None) == bsg.EINVAL
+    assert call(yp=MIS) == bsg.EINVAL
+    assert call(Tp=Tp - 128) == bsg.EINVAL and "Tp_max" in _err(L)
+    assert call(ld=64) == bsg.EINVAL
+    assert call(d=100) == bsg.EINVAL
+    assert call(dt=bsg.F32, ypt=bsg.BF16) == bsg.EUNSUPPORTED
+    assert call(bin=64) == bsg.EUNSUPPORTED
+    assert call(E=64, k=40) == bsg.EUNSUPPORTED
+
+
 def fake_topo(E=4, f=256, Tp=1024, **over):
     t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x70000, 0x80000,
                            0x60000, E, f // 128, Tp)

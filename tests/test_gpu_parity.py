@@ -366,3 +366,31 @@ def test_permute_pad_scaled_exact(orc, dtype):
     assert np.array_equal(row_src[:Tp].cpu().numpy(), r["row_src"])
     # rows at and beyond Tp are untouched
     assert torch.all(xp[Tp:] == 7.0).item() and torch.all(row_src[Tp:] == 99).item()
+
+
+def test_standalone_gate_backward_and_scaled_permute(orc):
+    """The layer runs the fused dy permutation + gate backward; the two
+    separate calls it replaces must give the same results: the scaled copy
+    bit for bit, dlogits against the oracle."""
+    from block_sparse_gemm_amd import bsg, layer
+    cfg = _small("standalone_bwd", T=700, d=384, E=6, f=256, k=2, renorm=True)
+    inp = synth.make_inputs(cfg, 13)
+    L, dev = run_gpu(cfg, inp)
+    dyp = torch.full_like(L.dyp, 3.0)
+    row_src = torch.full_like(L.row_src_b, 7)
+    dlogits = torch.full_like(L.dlogits, 5.0)
+    bsg.permute_pad(dev["dy"], cfg.k, L.dest_row, L.gate, L.counts, L.bin_offsets, cfg.E,
+                    L.Tp_max, row_src, dyp)
+    bsg.route_backward(dev["logits"], cfg.k, cfg.renorm, L.expert_idx, L.dest_row, dev["dy"],
+                       L.yp, dlogits)
+    torch.cuda.synchronize()
+    Tp = int(L.bin_offsets[-1].item())
+    assert torch.equal(dyp[:Tp], L.dyp[:Tp])
+    assert torch.equal(row_src[:Tp], L.row_src_b[:Tp])
+    r = orc.route(inp["logits"], cfg.k, cfg.renorm)
+    yp_rows = layer.to_numpy_f64(L.yp[torch.from_numpy(r["dest_row"]).cuda().long()])
+    want = orc.route_backward(inp["logits"], cfg.k, r["expert_idx"], inp["dy"].values, yp_rows,
+                              cfg.renorm)
+    report = {}
+    check_float("dlogits (standalone)", dlogits.cpu().numpy(), want, "bf16", report)
+    check_float("dlogits (fused)", L.dlogits.cpu().numpy(), want, "bf16", report)
