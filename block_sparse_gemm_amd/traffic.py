@@ -57,6 +57,8 @@ def call_name(kernel: str):
             return "dsd_bwd"
         if mode == "3":
             return "dstd_dw2" if swap == "true" else "dstd_dw1"
+    if "permute_gate_backward" in kernel:
+        return "permute_pad_gate_bwd"
     for k in ("route_backward", "route_topk", "route_scan", "route_place", "permute_pad",
               "build_topology", "combine"):
         if k in kernel:
