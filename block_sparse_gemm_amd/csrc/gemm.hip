@@ -453,6 +453,40 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         dma16(dst, base, pnl < 2 ? aoff[sg] : boff[sg]);
     };
 
+    // ---- this wave's output: does it exist, and its block (SDD)
+    const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
+    const int mrow = wm ? mrow1 : mrow0;  // this wave's block row / column
+    int oblk = 0;
+    if constexpr (MODE == kModeSdd) oblk = (wm ? rp1 : rp0) + 2 * tq + wn;
+    else if constexpr (MODE == kModeSddOne) oblk = (wm ? rp1 : rp0) + tq;
+    constexpr int NI = DUAL ? 2 : 4;
+
+    // Backward epilogues (bf16): the saved factors, read one 32-row slab ahead
+    // of their use so the loads of slab mi + 1 overlap the work on slab mi;
+    // with one plane, slab 0 is requested before the last K-tile (two planes
+    // in flight there would not fit the registers).
+    // GeLU: one plane (the derivative); SwiGLU: two (silu(g), u * silu'(g)).
+    // (The two-plane prefetch does not fit beside the registers of a B
+    // operand read as stored; that variant reads the factors at use.)
+    constexpr bool TWO_IN = EPI == kEpiSiluMulBwd;
+    constexpr bool PRE = (EPI == kEpiGeluBwd || (TWO_IN && BK)) && OUT == kBf16;
+    constexpr bool PRE_EARLY = PRE && !TWO_IN;
+    u32x2 hsave[2][NI][4];
+    u32x2 qsave[TWO_IN ? 2 : 1][NI][4];
+    auto hload = [&](int mi, int buf) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int m = 32 * mi + l32;
+                const int nloc = 32 * ni + 8 * g + 4 * lh;
+                const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
+                hsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + off * 2);
+                if constexpr (TWO_IN)
+                    qsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + (P.plane + off) * 2);
+            }
+    };
+
     f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -549,7 +583,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             __syncthreads();
             second_half(kt, true, false);
         }
-        // last K-tile
+        // last K-tile (every direct load has landed: the counter holds only
+        // what the epilogue's prefetch adds)
+        if constexpr (PRE_EARLY) {
+            if (active) hload(0, 0);
+        }
         first_half(kt, nk);
         second_half(kt, false, false);
     };
@@ -581,14 +619,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     // activation) and the SwiGLU backward (gate, then up projection).
     constexpr bool STAGE = OUT == kBf16 && !DUAL;
     if constexpr (STAGE) __syncthreads();  // every wave is done with the operand ring
-    const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
     if (!active) return;
-
-    const int mrow = wm ? mrow1 : mrow0;  // this wave's block row / column
-    int oblk = 0;
-    if constexpr (MODE == kModeSdd) oblk = (wm ? rp1 : rp0) + 2 * tq + wn;
-    else if constexpr (MODE == kModeSddOne) oblk = (wm ? rp1 : rp0) + tq;
-    constexpr int NI = DUAL ? 2 : 4;
+    if constexpr (PRE && !PRE_EARLY) hload(0, 0);
 
     // staging: row r (256 bytes) of a 64-row sub-region holds 16 chunks of
     // 16 bytes, chunk c at slot c ^ (r & 15), so the 16 lanes reading one row
@@ -626,35 +658,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         orow = P.ldc * OES;
     }
 
-    // Backward epilogues (bf16): the saved factors, read one 32-row slab ahead
-    // of their use so the loads of slab mi + 1 overlap the work on slab mi.
-    // GeLU: one plane (the derivative); SwiGLU: two (silu(g), u * silu'(g)).
-    // (The two-plane prefetch does not fit beside the registers of a B
-    // operand read as stored; that variant reads the factors at use.)
-    constexpr bool TWO_IN = EPI == kEpiSiluMulBwd;
-    constexpr bool PRE = (EPI == kEpiGeluBwd || (TWO_IN && BK)) && OUT == kBf16;
-    u32x2 hsave[2][NI][4];
-    u32x2 qsave[TWO_IN ? 2 : 1][NI][4];
-    auto hload = [&](int mi, int buf) {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int m = 32 * mi + l32;
-                const int nloc = 32 * ni + 8 * g + 4 * lh;
-                const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
-                hsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + off * 2);
-                if constexpr (TWO_IN)
-                    qsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + (P.plane + off) * 2);
-            }
-    };
     auto unpack = [](u32x2 u, float* f) {
         f[0] = __uint_as_float(u[0] << 16);
         f[1] = __uint_as_float(u[0] & 0xffff0000u);
         f[2] = __uint_as_float(u[1] << 16);
         f[3] = __uint_as_float(u[1] & 0xffff0000u);
     };
-    if constexpr (PRE) hload(0, 0);
 
     // two halves of 64 staging rows: M slabs (mi) 2h, 2h + 1 with a
     // row-major output, N slabs (ni) 2h, 2h + 1 with the transposed one
