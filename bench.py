@@ -56,6 +56,8 @@ def parse():
                     help="weight gradients on a second stream in the timed steps")
     ap.add_argument("--bin-rows", type=int, default=128, choices=(128, 256),
                     help="pad expert bins to a multiple of this many rows (block-size study)")
+    ap.add_argument("--context", action="store_true",
+                    help="also time dense bf16 GEMMs (torch.matmul) of the same (Tp, d, f)")
     ap.add_argument("--compare-schedules", action="store_true",
                     help="after the timed steps, also time the other backward schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -206,6 +208,40 @@ def main():
     dom_ms = durations(timed)[dom]
     step_ms = wall * 1e3 / args.steps
 
+    # spread of the step time: a few more steps, each between two events
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    ev[0].record()
+    for i in range(10):
+        L.step(x, logits, W1, W2, W3, dy)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    spread = np.percentile([ev[i].elapsed_time(ev[i + 1]) for i in range(10)], [10, 50, 90])
+
+    # context: dense bf16 GEMMs with the products' executed shapes (M = Tp)
+    dense = None
+    if args.context:
+        Tp0 = int(L.bin_offsets[-1].item())
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        a1 = torch.randn(Tp0, cfg.d, device="cuda").to(dt)
+        b1 = torch.randn(cfg.d, cfg.f, device="cuda").to(dt)
+        a2 = torch.randn(Tp0, cfg.f, device="cuda").to(dt)
+        b2 = torch.randn(cfg.f, cfg.d, device="cuda").to(dt)
+
+        def time_mm(a, b):
+            for _ in range(3):
+                torch.matmul(a, b)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                torch.matmul(a, b)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / 20
+
+        dense = {"sdd_shape_ms": round(time_mm(a1, b1), 4),
+                 "dsd_shape_ms": round(time_mm(a2, b2), 4)}
+        del a1, b1, a2, b2
+
     # context: the other backward schedule, a few steps after the timed region
     other = None
     if cfg.backward and args.compare_schedules:
@@ -282,9 +318,20 @@ def main():
         "kernels": kernels,
         "schedule": "two streams" if args.overlap else "one stream",
     }
+    out["step_ms_p10_p50_p90"] = [round(float(v), 4) for v in spread]
     if other is not None:
         key = "ms_per_step_one_stream" if args.overlap else "ms_per_step_two_streams"
         out[key] = round(other, 4)
+    if dense is not None:
+        # the block-sparse product's time against a dense GEMM of its executed
+        # shape (Tp x d x f): the block-sparse kernel runs at ratio x the
+        # dense GEMM's throughput on the same work
+        fl_exec = 2.0 * Tp * cfg.d * cfg.f
+        dense["sdd_ratio"] = round(dense["sdd_shape_ms"] * products_of(cfg, "sdd")
+                                   / kern["sdd"], 3)
+        dense["dsd_ratio"] = round(dense["dsd_shape_ms"] / kern["dsd"], 3)
+        dense["dense_tflops"] = round(fl_exec / (dense["sdd_shape_ms"] * 1e-3) / 1e12, 1)
+        out["context_dense_gemm"] = dense
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -195,7 +195,7 @@ bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
     REQUIRE_PTR(row_src);
     REQUIRE(scale == nullptr || aligned(scale, 4), "scale must be 4-byte aligned");
     return hip_status(bsg::launch_permute_pad(x, dtype, T, d, k, dest_row, scale, counts,
-                                              bin_offsets, E, bin_rows, row_src, xp,
+                                              bin_offsets, E, bin_rows, Tp_max, row_src, xp,
                                               (hipStream_t)stream),
                       "permute_pad");
 }
@@ -231,7 +231,8 @@ bsg_status bsg_permute_pad_gate_backward(const void* dy, int dtype, int64_t T, i
     REQUIRE_PTR(expert_idx);
     REQUIRE_PTR(dlogits);
     return hip_status(bsg::launch_permute_gate_backward(dy, dtype, T, d, k, dest_row, gate, counts,
-                                                        bin_offsets, E, bin_rows, row_src, dyp,
+                                                        bin_offsets, E, bin_rows, Tp_max, row_src,
+                                                        dyp,
                                                         logits, renorm, expert_idx, yp, yp_dtype,
                                                         ld_yp, dlogits, (hipStream_t)stream),
                       "permute_pad_gate_backward");

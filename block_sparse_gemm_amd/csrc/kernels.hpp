@@ -70,13 +70,14 @@ hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, i
 
 hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               const int32_t* dest_row, const float* scale, const int32_t* counts,
-                              const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
-                              void* xp, hipStream_t stream);
+                              const int32_t* bin_offsets, int E, int bin_rows, int64_t Tp_max,
+                              int32_t* row_src, void* xp, hipStream_t stream);
 
 hipError_t launch_permute_gate_backward(const void* dy, int dtype, int64_t T, int d, int k,
                                         const int32_t* dest_row, const float* gate,
                                         const int32_t* counts, const int32_t* bin_offsets, int E,
-                                        int bin_rows, int32_t* row_src, void* dyp,
+                                        int bin_rows, int64_t Tp_max, int32_t* row_src,
+                                        void* dyp,
                                         const float* logits, int renorm,
                                         const int32_t* expert_idx, const void* yp, int yp_dtype,
                                         int64_t ld_yp, float* dlogits, hipStream_t stream);

@@ -106,8 +106,8 @@ template <int DT>
 __global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
     const u32x4* __restrict__ x, int64_t T, int chunks, int k, const int32_t* __restrict__ dest_row,
     const float* __restrict__ scale, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ bin_offsets, int E, int bin_rows, int32_t* __restrict__ row_src,
-    u32x4* __restrict__ xp) {
+    const int32_t* __restrict__ bin_offsets, int E, int bin_rows, int64_t Tp_max,
+    int32_t* __restrict__ row_src, u32x4* __restrict__ xp) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nwaves = (int64_t)gridDim.x * kMoveWaves;
     const int64_t njobs = T + (int64_t)E * bin_rows;  // a bin's tail is below bin_rows rows
@@ -121,15 +121,17 @@ __global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
                 for (int j = 0; j < k; ++j) {
                     const int64_t a = t * k + j;
                     const int64_t row = dest_row[a];
-                    xp[row * chunks + c] = scale ? scale_chunk<DT>(v, scale[a]) : v;
+                    if (row < Tp_max)  // holds whenever the routing used this bin size
+                        xp[row * chunks + c] = scale ? scale_chunk<DT>(v, scale[a]) : v;
                 }
             }
-            if (lane < k) row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
+            if (lane < k && dest_row[t * k + lane] < Tp_max)
+                row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
         } else {
             const int64_t p = job - T;
             const int e = (int)(p / bin_rows);
             const int64_t row = (int64_t)bin_offsets[e] + counts[e] + p % bin_rows;
-            if (row >= bin_offsets[e + 1]) continue;
+            if (row >= bin_offsets[e + 1] || row >= Tp_max) continue;
             u32x4* dst = xp + row * chunks;
             for (int c = lane; c < chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
             if (lane == 0) row_src[row] = -1;
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kMoveThreads) void permute_gate_backward_kernel(
     const u32x4* __restrict__ dy, int64_t T, int chunks, int k,
     const int32_t* __restrict__ dest_row, const float* __restrict__ gate,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ bin_offsets, int E,
-    int bin_rows, int32_t* __restrict__ row_src, u32x4* __restrict__ dyp,
+    int bin_rows, int64_t Tp_max, int32_t* __restrict__ row_src, u32x4* __restrict__ dyp,
     const float* __restrict__ logits, int renorm, const int32_t* __restrict__ expert_idx,
     const char* __restrict__ yp, int64_t ld_yp_bytes, float* __restrict__ dlogits) {
     constexpr int V = Row<DT>::kVec;                       // dy values per 16-byte chunk
@@ -167,7 +169,8 @@ __global__ __launch_bounds__(kMoveThreads) void permute_gate_backward_kernel(
                 const float g = gate[a];
                 const char* yr = yp + row * ld_yp_bytes;
                 float s = 0.0f;
-                for (int c = lane; c < chunks; c += kWave) {
+                // row < Tp_max whenever the routing used this bin size
+                for (int c = lane; c < chunks && row < Tp_max; c += kWave) {
                     const u32x4 v = src[c];
                     dyp[row * chunks + c] = scale_chunk<DT>(v, g);
                     float x[V], y[V];
@@ -187,13 +190,14 @@ __global__ __launch_bounds__(kMoveThreads) void permute_gate_backward_kernel(
                     my_e = expert_idx[a];
                 }
             }
-            if (lane < k) row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
+            if (lane < k && dest_row[t * k + lane] < Tp_max)
+                row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
             gate_grad_token<NV>(logits + t * E, E, k, renorm, my_dg, my_e, dlogits + t * E);
         } else {
             const int64_t p = job - T;
             const int e = (int)(p / bin_rows);
             const int64_t row = (int64_t)bin_offsets[e] + counts[e] + p % bin_rows;
-            if (row >= bin_offsets[e + 1]) continue;
+            if (row >= bin_offsets[e + 1] || row >= Tp_max) continue;
             u32x4* dst = dyp + row * chunks;
             for (int c = lane; c < chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
             if (lane == 0) row_src[row] = -1;
@@ -246,27 +250,27 @@ static int move_grid(int64_t jobs) {
 
 hipError_t launch_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
                               const int32_t* dest_row, const float* scale, const int32_t* counts,
-                              const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
-                              void* xp, hipStream_t stream) {
+                              const int32_t* bin_offsets, int E, int bin_rows, int64_t Tp_max,
+                              int32_t* row_src, void* xp, hipStream_t stream) {
     const int es = dtype == kBf16 ? 2 : 4;
     const int chunks = d * es / 16;
     const int grid = move_grid(T + (int64_t)E * bin_rows);
     if (dtype == kBf16)
         hipLaunchKernelGGL(permute_pad_kernel<kBf16>, dim3(grid), dim3(kMoveThreads), 0, stream,
                            (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
-                           bin_rows, row_src, (u32x4*)xp);
+                           bin_rows, Tp_max, row_src, (u32x4*)xp);
     else
         hipLaunchKernelGGL(permute_pad_kernel<kF32>, dim3(grid), dim3(kMoveThreads), 0, stream,
                            (const u32x4*)x, T, chunks, k, dest_row, scale, counts, bin_offsets, E,
-                           bin_rows, row_src, (u32x4*)xp);
+                           bin_rows, Tp_max, row_src, (u32x4*)xp);
     return hipGetLastError();
 }
 
 template <int DT, int YP>
 static hipError_t launch_pgb(const void* dy, int64_t T, int d, int k, const int32_t* dest_row,
                              const float* gate, const int32_t* counts,
-                             const int32_t* bin_offsets, int E, int bin_rows, int32_t* row_src,
-                             void* dyp, const float* logits, int renorm,
+                             const int32_t* bin_offsets, int E, int bin_rows, int64_t Tp_max,
+                             int32_t* row_src, void* dyp, const float* logits, int renorm,
                              const int32_t* expert_idx, const void* yp, int64_t ld_yp_bytes,
                              float* dlogits, hipStream_t stream) {
     const int chunks = d * (DT == kBf16 ? 2 : 4) / 16;
@@ -274,7 +278,8 @@ static hipError_t launch_pgb(const void* dy, int64_t T, int d, int k, const int3
 #define BSG_PGB(NV)                                                                              \
     hipLaunchKernelGGL((permute_gate_backward_kernel<DT, YP, NV>), dim3(grid), dim3(kMoveThreads), \
                        0, stream, (const u32x4*)dy, T, chunks, k, dest_row, gate, counts,        \
-                       bin_offsets, E, bin_rows, row_src, (u32x4*)dyp, logits, renorm, expert_idx, \
+                       bin_offsets, E, bin_rows, Tp_max, row_src, (u32x4*)dyp, logits, renorm,  \
+                       expert_idx,                                                               \
                        (const char*)yp, ld_yp_bytes, dlogits)
     if (E <= 64) BSG_PGB(1);
     else if (E <= 128) BSG_PGB(2);
@@ -288,22 +293,23 @@ static hipError_t launch_pgb(const void* dy, int64_t T, int d, int k, const int3
 hipError_t launch_permute_gate_backward(const void* dy, int dtype, int64_t T, int d, int k,
                                         const int32_t* dest_row, const float* gate,
                                         const int32_t* counts, const int32_t* bin_offsets, int E,
-                                        int bin_rows, int32_t* row_src, void* dyp,
+                                        int bin_rows, int64_t Tp_max, int32_t* row_src,
+                                        void* dyp,
                                         const float* logits, int renorm,
                                         const int32_t* expert_idx, const void* yp, int yp_dtype,
                                         int64_t ld_yp, float* dlogits, hipStream_t stream) {
     const int64_t ldb = ld_yp * (yp_dtype == kBf16 ? 2 : 4);
     if (dtype == kBf16 && yp_dtype == kBf16)
         return launch_pgb<kBf16, kBf16>(dy, T, d, k, dest_row, gate, counts, bin_offsets, E,
-                                        bin_rows, row_src, dyp, logits, renorm, expert_idx, yp,
+                                        bin_rows, Tp_max, row_src, dyp, logits, renorm, expert_idx, yp,
                                         ldb, dlogits, stream);
     if (dtype == kBf16)
         return launch_pgb<kBf16, kF32>(dy, T, d, k, dest_row, gate, counts, bin_offsets, E,
-                                       bin_rows, row_src, dyp, logits, renorm, expert_idx, yp,
+                                       bin_rows, Tp_max, row_src, dyp, logits, renorm, expert_idx, yp,
                                        ldb, dlogits, stream);
     if (yp_dtype == kF32)
         return launch_pgb<kF32, kF32>(dy, T, d, k, dest_row, gate, counts, bin_offsets, E,
-                                      bin_rows, row_src, dyp, logits, renorm, expert_idx, yp, ldb,
+                                      bin_rows, Tp_max, row_src, dyp, logits, renorm, expert_idx, yp, ldb,
                                       dlogits, stream);
     return hipErrorInvalidValue;  // fp32 dy with bf16 yp: not a layout the layer produces
 }

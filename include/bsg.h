@@ -191,7 +191,8 @@ bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int 
  * receives, for every row below Tp, the assignment that fills it or -1.
  *   x [T, d] (dtype), xp [Tp_max, d] (dtype), row_src [Tp_max] int32,
  *   counts/bin_offsets as produced by bsg_route with the same bin_rows.
- *   Rows >= Tp are untouched.  d must be a positive multiple of 8 (bf16) or
+ *   Rows >= Tp are untouched, and no row at or beyond Tp_max is written
+ *   whatever bin_offsets holds.  d must be a positive multiple of 8 (bf16) or
  *   4 (fp32); Tp_max at least bsg_max_padded_rows(T, k, E, bin_rows).
  */
 bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
@@ -294,7 +295,9 @@ bsg_status bsg_dstd(const void* blocks, const bsg_topology* topo, const void* dm
  * section 1.4):  y[t][m] = sum_{j<k} gate[t*k+j] * yp[dest_row[t*k+j]][m],
  * accumulated in fp32 in ascending j and rounded once to y_dtype;
  * gate == NULL means every gate is 1 (input-gradient combine).
- *   yp [Tp_max, d] (yp_dtype, leading dimension ld_yp), y [T, d] (y_dtype).
+ *   yp [Tp_max, d] (yp_dtype, leading dimension ld_yp), y [T, d] (y_dtype);
+ *   every dest_row entry must be below yp's Tp_max (it is when yp was sized
+ *   with bsg_max_padded_rows for the bin size the routing used).
  */
 bsg_status bsg_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
                                  const int32_t* dest_row, const float* gate, int64_t T, int k,

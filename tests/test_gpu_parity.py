@@ -394,3 +394,24 @@ def test_standalone_gate_backward_and_scaled_permute(orc):
     report = {}
     check_float("dlogits (standalone)", dlogits.cpu().numpy(), want, "bf16", report)
     check_float("dlogits (fused)", L.dlogits.cpu().numpy(), want, "bf16", report)
+
+
+def test_permute_pad_never_writes_past_tp_max(orc):
+    """Bins from a 256-row routing given to a buffer sized for 128-row bins:
+    the copy writes nothing at or beyond Tp_max (sentinel rows inside the
+    same allocation stay untouched)."""
+    from block_sparse_gemm_amd import bsg, layer
+    cfg = _small("clamp", T=300, d=128, E=7, f=128, k=2)
+    inp = synth.make_inputs(cfg, 21, weights=False)
+    r = orc.route(inp["logits"], cfg.k, False, 256)
+    Tp128 = bsg.max_padded_rows(cfg.T, cfg.k, cfg.E, 128)
+    assert int(r["bin_offsets"][cfg.E]) > Tp128  # the routing overruns the buffer
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = layer.from_numpy(inp["x"], "bf16")
+    big = torch.full((Tp128 + 1024, cfg.d), 9.0, dtype=torch.bfloat16, device="cuda")
+    row_src = torch.full((Tp128 + 1024,), 77, dtype=torch.int32, device="cuda")
+    bsg.permute_pad(x, cfg.k, dev(r["dest_row"]), None, dev(r["counts"]),
+                    dev(r["bin_offsets"]), cfg.E, Tp128, row_src[:Tp128], big[:Tp128])
+    torch.cuda.synchronize()
+    assert torch.all(big[Tp128:] == 9.0)
+    assert torch.all(row_src[Tp128:] == 77)
