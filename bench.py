@@ -110,8 +110,16 @@ def cpu_baseline(cfg, inp, target_s):
     n0, t0 = run(32)
     n = int(min(cfg.T, max(32, n0 * target_s / max(t0, 1e-3))))
     n, t = run(n)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": per_tok * n / t / 1e12, "unit": "TFLOP/s", "cores": orc.get_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n} tokens of the {cfg.name} workload, forward"
                       + (f" + input-gradient path ({fwd_p + bwd_p} of the "
                          f"{fwd_p + bwd_p + (3 if sw else 2)} products per token; weight "
@@ -310,6 +318,8 @@ def main():
                                f"bins of {cfg.bin_rows} rows",
                    "padded_rows": Tp, "padding_frac": round(1 - A_n / Tp, 4)},
         "pct_of_bf16_peak": round(100 * tflops / peak, 2),
+        # the same step counted with the padded rows the products execute
+        "executed_tflops": round(total * Tp / A_n / (step_ms * 1e-3) / 1e12, 2),
         "tokens_per_s": round(cfg.T / (step_ms * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

@@ -285,6 +285,12 @@ def _edge_cases():
     ex = np.repeat(np.arange(4), [1, 127, 128, 129])
     cfg = _small("counts_1_127_128_129", T=385, d=128, E=4, f=128, k=1)
     cases["counts_1_127_128_129"] = Case(cfg, logits=_assign_logits(385, 4, ex))
+    # more experts than lanes (several logits per lane in routing and the gate
+    # backward), up to the 1024-expert limit, and the largest top-k
+    cases["many_experts"] = Case(_small("many_experts", T=1500, d=128, E=300, f=128, k=3))
+    cases["max_experts"] = Case(_small("max_experts", T=3000, d=128, E=1024, f=128, k=2,
+                                       renorm=True), n_tokens=200, n_wgrad=64)
+    cases["max_topk"] = Case(_small("max_topk", T=200, d=128, E=40, f=128, k=32, renorm=True))
     # ties in the logits (lower id wins)
     cfg = _small("ties", T=256, d=128, E=8, f=128, k=2)
     lg = np.random.default_rng(4).integers(-2, 3, size=(256, 8)).astype(np.float32)
