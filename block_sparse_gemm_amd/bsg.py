@@ -29,7 +29,7 @@ EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
 # Every symbol include/bsg.h declares.
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
            "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
-           "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dstd",
+           "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_status_string", "bsg_last_error")
 
 
@@ -88,6 +88,9 @@ def lib():
         L.bsg_dsd.restype = i32
         L.bsg_dsd.argtypes = [vp, vp, C.POINTER(TopologyStruct), vp, vp, i64, i32, i32, vp, i64,
                               i32, i32, vp]
+        L.bsg_dsd_combine_top1.restype = i32
+        L.bsg_dsd_combine_top1.argtypes = [vp, C.POINTER(TopologyStruct), vp, i64, i32, i32, vp,
+                                           i64, vp, vp, vp, i64, i32, vp]
         L.bsg_dstd.restype = i32
         L.bsg_dstd.argtypes = [vp, C.POINTER(TopologyStruct), vp, i64, i32, vp, i64, i32, i32,
                                vp]
@@ -231,6 +234,15 @@ def dsd(blocks, topo: Topology, b, N, c, trans_b=False, blocks2=None, b2=None):
     _check("dsd", lib().bsg_dsd(_ptr(blocks), _ptr(blocks2), C.byref(topo.struct), _ptr(b),
                                 _ptr(b2), _ld(b), int(bool(trans_b)), N, _ptr(c), _ld(c),
                                 dtype_code(c), dtype_code(blocks), _stream()))
+
+
+def dsd_combine_top1(blocks, topo: Topology, b, N, c, row_src, gate, y, trans_b=False):
+    """bsg_dsd + bsg_unpermute_combine for top-1 routing in one launch (c may
+    be None: only y is written)."""
+    _check("dsd_combine_top1", lib().bsg_dsd_combine_top1(
+        _ptr(blocks), C.byref(topo.struct), _ptr(b), _ld(b), int(bool(trans_b)), N, _ptr(c),
+        _ld(c) if c is not None else 0, _ptr(row_src), _ptr(gate), _ptr(y), _ld(y),
+        dtype_code(blocks), _stream()))
 
 
 def dstd(blocks, topo: Topology, dmat, N, c, trans_c=False):

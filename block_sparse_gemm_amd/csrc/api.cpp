@@ -361,6 +361,46 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
                       "dsd");
 }
 
+bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, const void* b,
+                                int64_t ldb, int trans_b, int N, void* c, int64_t ldc,
+                                const int32_t* row_src, const float* gate, void* y, int64_t ldy,
+                                int dtype, bsg_stream_t stream) {
+    REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
+    if (dtype != BSG_BF16) return fail(BSG_EUNSUPPORTED, "dsd_combine_top1 is implemented for bf16");
+    bsg_status s = check_topology(topo);
+    if (s != BSG_OK) return s;
+    const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
+    REQUIRE(N >= BSG_BLOCK && N % BSG_BLOCK == 0, "N must be a positive multiple of 128");
+    REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
+    REQUIRE(ldb >= (trans_b ? ncol : N) && (ldb * 2) % 16 == 0,
+            "ldb too small or rows not 16-byte aligned");
+    REQUIRE(ldy >= N && (ldy * 2) % 16 == 0, "ldy must be >= N with 16-byte aligned rows");
+    REQUIRE_VEC_PTR(blocks);
+    REQUIRE_VEC_PTR(b);
+    REQUIRE_VEC_PTR(y);
+    REQUIRE_PTR(row_src);
+    REQUIRE(gate == nullptr || aligned(gate, 4), "gate must be 4-byte aligned");
+    if (c) {
+        REQUIRE(aligned(c, 16), "c must be 16-byte aligned");
+        REQUIRE(ldc >= N && (ldc * 2) % 16 == 0, "ldc must be >= N with 16-byte aligned rows");
+    }
+    bsg::GemmParams p = gemm_params(topo);
+    p.a = blocks;
+    p.b = b;
+    p.out = c;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.N = N;
+    p.ntn = (N + 255) / 256;
+    p.scat_rows = row_src;
+    p.scat_gate = gate;
+    p.scat_out = y;
+    p.scat_ld = ldy;
+    return hip_status(bsg::launch_dsd(p, row_pairs_max(topo->Tp_max / BSG_BLOCK, topo->E), trans_b,
+                                      BSG_BF16, BSG_BF16, (hipStream_t)stream),
+                      "dsd_combine_top1");
+}
+
 bsg_status bsg_dstd(const void* blocks, const bsg_topology* topo, const void* dmat, int64_t ldd,
                     int N, void* c, int64_t ldc, int trans_c, int dtype, bsg_stream_t stream) {
     REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);

@@ -644,6 +644,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             *(u32x4*)(base + row * row_bytes + chunk * 16) = u;
         }
     };
+    // top-1 DSD: the staged rows also go to token order, y[t] = rd(g_t * v)
+    // with v the row as stored (the combine of one pick, bit for bit).  Lane
+    // l holds the assignment and gate of row l of each 64-row half, read once
+    // here; the flush takes them by lane shuffle.
+    int sc_a[2] = {-1, -1};
+    float sc_g[2] = {1.0f, 1.0f};
+    if constexpr (EPI == kEpiScatter) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sc_a[h] = P.scat_rows[(int64_t)kBlock * mrow + 64 * h + lane];
+        if (P.scat_gate) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) sc_g[h] = sc_a[h] >= 0 ? P.scat_gate[sc_a[h]] : 1.0f;
+        }
+    }
+    auto scatter_flush = [&](const lds_t* sub, int h) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int chunk = lane & 15;
+        const int64_t col = n0 + wn * 128 + chunk * 8;
+#pragma unroll 4
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 4 * rr + (lane >> 4);
+            const int a = __shfl(sc_a[h], row, kWave);
+            const float g = __shfl(sc_g[h], row, kWave);
+            const u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(
+                sub + row * 256 + ((chunk ^ (row & 15)) << 4));
+            if (a >= 0) {
+                u32x4 o = u;
+                if (P.scat_gate) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[i] = pack_bf16x2(g * __uint_as_float(u[i] << 16),
+                                           g * __uint_as_float(u[i] & 0xffff0000u));
+                }
+                *(u32x4*)((char*)P.scat_out + ((int64_t)a * P.scat_ld + col) * 2) = o;
+            }
+        }
+    };
     // origin and row pitch (bytes) of this wave's quarter in the output
     char* obase;
     int64_t orow;
@@ -774,6 +811,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             } else if constexpr (EPI == kEpiSiluMulBwd) {
                 stage_flush(region, obase + h * 64 * orow, orow);
                 stage_flush(region + 16384, obase + P.plane * OES + h * 64 * orow, orow);
+            } else if constexpr (EPI == kEpiScatter) {
+                if (P.out) stage_flush(region, obase + h * 64 * orow, orow);
+                scatter_flush(region, h);
             } else {
                 stage_flush(region, obase + h * 64 * orow, orow);
             }
@@ -849,6 +889,11 @@ static hipError_t dispatch_dsd(const GemmParams& p, int64_t grid, int trans_b, i
 hipError_t launch_dsd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int c_dtype,
                       int dtype, hipStream_t s) {
     const int64_t grid = row_pairs_max * p.ntn;
+    if (p.scat_out) {  // top-1 rows to token order: bf16 throughout, one block set
+        if (dtype != kBf16 || c_dtype != kBf16 || p.a2) return hipErrorInvalidValue;
+        return trans_b ? launch<kBf16, kModeDsd, true, kEpiScatter, kBf16, true>(p, grid, s)
+                       : launch<kBf16, kModeDsd, false, kEpiScatter, kBf16, true>(p, grid, s);
+    }
     return p.a2 ? dispatch_dsd<kModeDsd2>(p, grid, trans_b, c_dtype, dtype, s)
                 : dispatch_dsd<kModeDsd>(p, grid, trans_b, c_dtype, dtype, s);
 }

@@ -16,6 +16,7 @@ constexpr int kEpiGeluBwd = 3;
 constexpr int kEpiSiluMulBwd = 4;
 constexpr int kEpiGeluSave = 5;     // internal: GeLU that also stores its derivative
 constexpr int kEpiSiluMulSave = 6;  // internal: SiLU*mul that also stores silu, u*silu'
+constexpr int kEpiScatter = 7;      // internal: DSD rows also written in token order (top-1)
 
 constexpr int kModeSdd = 0;
 constexpr int kModeSddOne = 1;
@@ -43,6 +44,12 @@ struct GemmParams {
     void* aux_out;       // SDD GELU: optional saved derivative blocks;
                          // SILU_MUL: optional two planes (silu, u*silu')
     int64_t plane;       // elements between the planes of a two-plane block array
+    // DSD with top-1 routing: rows also go to token order, y[row_src[r]] =
+    // rd(gate[row_src[r]] * rd(c[r])) (gate NULL: 1); out may then be NULL
+    const int32_t* scat_rows;
+    const float* scat_gate;
+    void* scat_out;
+    int64_t scat_ld;
     int64_t lda, ldb, ldc;
     const int32_t* row_ptr;
     const int32_t* col_idx;

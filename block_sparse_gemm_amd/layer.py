@@ -76,6 +76,10 @@ class Layer:
         # includes its wait, so the default keeps every call in order on the
         # caller's stream.
         self.overlap = False
+        # top-1 bf16 layers: the combine runs in the DSD's epilogue (forward:
+        # Yp and y; backward with GeLU experts: dx straight from the product,
+        # no dXp)
+        self.fuse_top1 = s.k == 1 and s.dtype == "bf16" and s.yp_tdtype == torch.bfloat16
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         A = s.T * s.k
@@ -140,6 +144,10 @@ class Layer:
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3, aux_out=self.gp)
         else:
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.gp)
+        if self.fuse_top1:
+            c("dsd", bsg.dsd_combine_top1, self.act, t, W2, s.d, self.yp, self.row_src,
+              self.gate, self.y)
+            return self.y
         c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp)
         c("unpermute_combine", bsg.unpermute_combine, self.yp, self.dest_row, self.gate, s.T,
           s.k, s.d, self.y)
@@ -162,6 +170,10 @@ class Layer:
               self.dh, trans_b=True, aux_in=self.gp)
 
         def dsd_bwd():
+            if self.fuse_top1 and not sw:  # the fused form has one block set
+                c("dsd_bwd", bsg.dsd_combine_top1, self.dh, t, W1, s.d, None, self.row_src_b,
+                  None, self.dx, trans_b=True)
+                return
             if sw:
                 c("dsd_bwd", bsg.dsd, dh0, t, W1, s.d, self.dxp, trans_b=True,
                   blocks2=self.plane(self.dh, 1), b2=W3)

@@ -275,6 +275,23 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
                    int64_t ldc, int c_dtype, int dtype, bsg_stream_t stream);
 
 /*
+ * dsd_combine_top1 - bsg_dsd followed by bsg_unpermute_combine for top-1
+ * routing, in one launch: the product's rows leave the epilogue both to c
+ * (as bsg_dsd writes it; c may be NULL when only y is wanted) and straight
+ * to token order,
+ *   y[row_src[r]][n] = rd(gate[row_src[r]] * rd(C[r][n]))  (gate NULL: 1)
+ * for every row r below Tp with row_src[r] >= 0, which equals what
+ * bsg_unpermute_combine(c, ..., k = 1, ...) writes, bit for bit (the
+ * second layer and the reverse layout transform of section 1.4).  row_src
+ * comes from bsg_permute_pad of a top-1 routing (assignment id = token).
+ * bf16 only (blocks, b, c and y); y is [T, ldy].  One block set.
+ */
+bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, const void* b,
+                                int64_t ldb, int trans_b, int N, void* c, int64_t ldc,
+                                const int32_t* row_src, const float* gate, void* y, int64_t ldy,
+                                int dtype, bsg_stream_t stream);
+
+/*
  * dstd - dense = sparse^T x dense, the weight gradient (section 1.3,
  * "transpose indices": the blocks of each column are visited through
  * trans_idx, their rows found through row_idx):

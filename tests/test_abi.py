@@ -23,7 +23,7 @@ def L():
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(bsg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bsg_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(L):
@@ -155,6 +155,29 @@ def test_permute_pad_gate_backward_validation(L):
     assert call(dt=bsg.F32, ypt=bsg.BF16) == bsg.EUNSUPPORTED
     assert call(bin=64) == bsg.EUNSUPPORTED
     assert call(E=64, k=40) == bsg.EUNSUPPORTED
+
+
+def test_dsd_combine_top1_validation(L):
+    t = fake_topo(E=4, f=256)
+    names = ["blocks", "topo", "b", "ldb", "tb", "N", "c", "ldc", "rs", "gate", "y", "ldy", "dt",
+             "stream"]
+    ok = [P, C.byref(t), P, 256, 0, 256, P, 256, P, None, P, 256, bsg.BF16, None]
+
+    def call(**over):
+        a = list(ok)
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_dsd_combine_top1(*a)
+
+    assert call(blocks=None) == bsg.EINVAL
+    assert call(y=None) == bsg.EINVAL
+    assert call(rs=None) == bsg.EINVAL
+    assert call(ldy=128) == bsg.EINVAL
+    assert call(c=MIS) == bsg.EINVAL
+    assert call(ldc=128) == bsg.EINVAL
+    assert call(N=200) == bsg.EINVAL
+    assert call(dt=bsg.F32) == bsg.EUNSUPPORTED
+    assert call(gate=C.c_void_p(0x10002)) == bsg.EINVAL
 
 
 def fake_topo(E=4, f=256, Tp=1024, **over):
