@@ -149,8 +149,8 @@ def traffic_for(config, kernel_name):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's "
-              "multi-GPU sharding is described in DESIGN.md and not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the layer's "
+              "multi-GPU sharding (expert parallelism over RCCL) is not built.", file=sys.stderr)
         sys.exit(2)
     import torch
     from block_sparse_gemm_amd import layer, synth
