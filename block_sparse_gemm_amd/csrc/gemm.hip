@@ -610,14 +610,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         }
     }
 
-    // ---- epilogue.  bf16 results (except dual B) go out through LDS: each
+    // ---- epilogue.  bf16 results go out through LDS: each
     // wave writes half of its 128 x 128 quarter (64 rows) at a time into a
     // private 32 KB region in the accumulator layout, then reads it back row
     // by row, so every store instruction writes 4 whole 256-byte rows
     // (16 contiguous bytes a lane).  Epilogues with two outputs stage them
     // side by side: GeLU with the derivative kept (derivative, then
     // activation) and the SwiGLU backward (gate, then up projection).
-    constexpr bool STAGE = OUT == kBf16 && !DUAL;
+    constexpr bool STAGE = OUT == kBf16;
     if constexpr (STAGE) __syncthreads();  // every wave is done with the operand ring
     if (!active) return;
     if constexpr (PRE && !PRE_EARLY) hload(0, 0);
@@ -632,6 +632,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         *(__attribute__((address_space(3))) u32x2*)(sub + row * 256 +
                                                       ((chunk ^ (row & 15)) << 4) + lh * 8) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    // dual B (SwiGLU): a wave's slice is 64 columns, so a staged row is 128
+    // bytes (8 chunks, chunk c at slot c ^ (r & 7)), and a store instruction
+    // writes 8 rows of 128 contiguous bytes
+    auto stage_put_d = [&](lds_t* sub, int mi, int ni, int g, const float* v) {
+        const int row = (32 * mi) % 64 + l32;
+        const int chunk = 4 * ni + g;
+        *(__attribute__((address_space(3))) u32x2*)(sub + row * 128 +
+                                                      ((chunk ^ (row & 7)) << 4) + lh * 8) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    auto stage_flush_d = [&](const lds_t* sub, char* base) {  // base: the half's row 0
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int chunk = lane & 7;
+#pragma unroll 4
+        for (int rr = 0; rr < 8; ++rr) {
+            const int row = 8 * rr + (lane >> 3);
+            const u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(
+                sub + row * 128 + ((chunk ^ (row & 7)) << 4));
+            *(u32x4*)(base + row * (kBlock * 2) + chunk * 16) = u;
+        }
     };
     auto stage_flush = [&](const lds_t* sub, char* base, int64_t row_bytes) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -741,8 +762,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                                 qv[s] = u * sp;
                                 v[s] = sv[s] * u;
                             }
-                            store4<OUT>((char*)P.aux_out + off * OES, sv);
-                            store4<OUT>((char*)P.aux_out + (P.plane + off) * OES, qv);
+                            if constexpr (STAGE) {
+                                stage_put_d(region + 8192, mi, ni, g, sv);
+                                stage_put_d(region + 16384, mi, ni, g, qv);
+                            } else {
+                                store4<OUT>((char*)P.aux_out + off * OES, sv);
+                                store4<OUT>((char*)P.aux_out + (P.plane + off) * OES, qv);
+                            }
                         } else if constexpr (EPI == kEpiGelu) {
 #pragma unroll
                             for (int s = 0; s < 4; ++s) v[s] = gelu_f(v[s]);
@@ -779,7 +805,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                             if constexpr (STAGE) stage_put(region + 16384, mi, ni, g, up);
                             else store4<OUT>((char*)P.out + (P.plane + off) * OES, up);
                         }
-                        if constexpr (STAGE) {
+                        if constexpr (STAGE && DUAL) {
+                            stage_put_d(region, mi, ni, g, v);
+                        } else if constexpr (STAGE) {
                             stage_put(EPI == kEpiGeluSave ? region + 16384 : region, mi, ni, g, v);
                         } else {
                             store4<OUT>((char*)P.out + off * OES, v);
@@ -803,7 +831,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if constexpr (STAGE) {
+        if constexpr (STAGE && DUAL) {
+            const int64_t o = ((int64_t)oblk * kBlock * kBlock + 64 * h * kBlock + wn * 64) * OES;
+            stage_flush_d(region, (char*)P.out + o);
+            if constexpr (EPI == kEpiSiluMulSave) {
+                stage_flush_d(region + 8192, (char*)P.aux_out + o);
+                stage_flush_d(region + 16384, (char*)P.aux_out + P.plane * OES + o);
+            }
+        } else if constexpr (STAGE) {
             if constexpr (EPI == kEpiGeluSave) {
                 stage_flush(region, (char*)P.aux_out + (int64_t)oblk * kBlock * kBlock * OES +
                                         h * 64 * orow, orow);
