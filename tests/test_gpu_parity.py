@@ -447,3 +447,28 @@ def test_top1_fused_combine_is_bit_identical(bwd):
     assert torch.equal(outs[0][1], outs[1][1])
     if bwd:
         assert torch.equal(outs[0][2], outs[1][2])
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_two_stream_schedule_gives_the_same_bits(act):
+    """The backward with the weight gradients on a second stream gives the
+    same bits as the one-stream order (every kernel is deterministic), also
+    when it is run several times in a row."""
+    from block_sparse_gemm_amd import layer
+    kw = dict(act="swiglu", renorm=True, yp_dtype="f32") if act == "swiglu" else {}
+    cfg = _small("two_streams", T=800, d=256, E=5, f=256, k=2, **kw)
+    inp = synth.make_inputs(cfg, 23)
+    up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
+    x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    names = ("y", "dx", "dW1", "dW2", "dlogits") + (("dW3",) if act == "swiglu" else ())
+    results = []
+    for overlap in (False, True):
+        L = layer.Layer(layer.Shape.of(cfg))
+        L.overlap = overlap
+        for _ in range(3):
+            L.step(x, logits, W1, W2, W3, dy)
+        torch.cuda.synchronize()
+        results.append({n: getattr(L, n).clone() for n in names})
+    for n in names:
+        assert torch.equal(results[0][n], results[1][n]), n
