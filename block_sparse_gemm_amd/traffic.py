@@ -7,6 +7,12 @@ Two modes:
     calibration), then ``--steps`` steps of the layer.  Run it under
     ``rocprofv3 --pmc FETCH_SIZE`` and, separately, ``--pmc WRITE_SIZE``.
 
+``python3 -m block_sparse_gemm_amd.traffic counters --csv A.csv B.csv ... --md OUT.md``
+    Per call of the layer, the mean per dispatch of every counter in the given
+    ``*_counter_collection.csv`` files, and the busy fractions derived from
+    them on MI355X (8 XCDs, 256 CUs, 1024 SIMDs): MFMA busy, TA busy, TD busy,
+    TD stalled on the L2, LDS bank-conflict share, L2 hit rate.
+
 ``python3 -m block_sparse_gemm_amd.traffic summarize --fetch F.csv --write W.csv``
     Reads the two ``*_counter_collection.csv`` files, scales each kernel's
     mean counter value per dispatch by what the copy kernel reads for its
@@ -155,6 +161,62 @@ def summarize(args):
     print("\n".join(lines))
 
 
+XCDS, CUS, SIMDS = 8, 256, 1024   # MI355X
+
+
+def counters(args):
+    table = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in args.csv:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for disp, cs in per.items():
+            name = call_name(names[disp])
+            if name is None:
+                continue
+            cyc = cs.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+            for c, v in cs.items():
+                table[name][c].append(v)
+            if cyc <= 0:
+                continue
+            derived = {
+                "MFMA busy": ("SQ_VALU_MFMA_BUSY_CYCLES", SIMDS),
+                "TA busy": ("TA_BUSY_avr", 1),
+                "TD busy": ("TD_TD_BUSY", CUS),
+                "TD stalled on L2": ("TD_TC_STALL", CUS),
+                "TA stalled on L2": ("TA_ADDR_STALLED_BY_TC_CYCLES", CUS),
+            }
+            for label, (c, n) in derived.items():
+                if c in cs:
+                    table[name]["% " + label].append(100.0 * cs[c] / (n * cyc))
+            if cs.get("SQ_LDS_IDX_ACTIVE"):
+                table[name]["% LDS bank conflict"].append(
+                    100.0 * cs.get("SQ_LDS_BANK_CONFLICT", 0.0) / cs["SQ_LDS_IDX_ACTIVE"])
+            hit, miss = cs.get("TCC_HIT_sum"), cs.get("TCC_MISS_sum")
+            if hit is not None and miss is not None and hit + miss > 0:
+                table[name]["% L2 hit"].append(100.0 * hit / (hit + miss))
+    cols = sorted({c for cs in table.values() for c in cs if c.startswith("% ")})
+    order = ["sdd", "dsd", "sdd_bwd", "dsd_bwd", "dstd_dw2", "dstd_dw1", "permute_pad",
+             "permute_pad_gate_bwd", "combine"]
+    calls = [c for c in order if c in table] + sorted(c for c in table if c not in order)
+    lines = [f"# Counters per call: {args.config} layer step", "",
+             "Busy fractions of the kernel's active cycles (GRBM_GUI_ACTIVE per XCD), normalised by",
+             f"the unit count on MI355X ({SIMDS} SIMDs for MFMA, {CUS} CUs for TD, TA_BUSY_avr already",
+             "averaged); LDS bank conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; L2 hit =",
+             "TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum).  Means over the profiled dispatches.", "",
+             "Commands:", "", "```"] + args.cmd + ["```", "",
+             "| call | " + " | ".join(c[2:] + " %" for c in cols) + " |",
+             "|---|" + "---|" * len(cols)]
+    for name in calls:
+        vals = [table[name].get(c) for c in cols]
+        lines.append(f"| {name} | " + " | ".join(
+            "—" if not v else f"{sum(v) / len(v):.1f}" for v in vals) + " |")
+    open(args.md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -168,9 +230,14 @@ def main():
     s.add_argument("--out", default=None, help="default profiles/traffic_<config>.json")
     s.add_argument("--md", default=None, help="default profiles/<config>_traffic.md")
     s.add_argument("--cmd", nargs="*", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", nargs="+", required=True)
+    c.add_argument("--config", default="moe_small")
+    c.add_argument("--md", required=True)
+    c.add_argument("--cmd", nargs="*", default=[])
     a = ap.parse_args()
     sys.path.insert(0, ROOT)
-    run(a) if a.mode == "run" else summarize(a)
+    {"run": run, "summarize": summarize, "counters": counters}[a.mode](a)
 
 
 if __name__ == "__main__":
