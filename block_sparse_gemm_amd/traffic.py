@@ -1,6 +1,7 @@
-"""HBM traffic per kernel launch from rocprofv3 counters.
+"""HBM traffic per kernel launch from rocprofv3 counters, and the Markdown
+summaries of rocprofv3 output kept under profiles/.
 
-Two modes:
+Modes:
 
 ``python3 -m block_sparse_gemm_amd.traffic run [--config moe_small] [--steps 2]``
     The workload for a counter pass: a plain copy of a known size (the
@@ -19,6 +20,11 @@ Two modes:
     known byte count, and writes ``profiles/traffic_<config>.json`` (bytes
     per launch, keyed by the layer's call names, stamped with the hash of the
     GEMM source so stale figures are ignored) and a Markdown table.
+
+``python3 -m block_sparse_gemm_amd.traffic stats --csv run_kernel_stats.csv --md OUT.md``
+    The per-kernel table of a ``rocprofv3 --kernel-trace --stats`` run
+    (calls, mean / min / max duration, share of the traced time), with each
+    GEMM instantiation named by its product, epilogue and operand layout.
 """
 from __future__ import annotations
 
@@ -217,6 +223,36 @@ def counters(args):
     print("\n".join(lines))
 
 
+_MODES = {"0": "sdd", "1": "sdd_dual", "2": "dsd", "3": "dstd", "4": "dsd_two_sets"}
+_EPIS = {"0": "", "1": "+gelu", "2": "+silu_mul", "3": "+gelu_bwd", "4": "+silu_mul_bwd",
+         "5": "+gelu (saves gelu')", "6": "+silu_mul (saves silu, u*silu')", "7": "+top-1 combine"}
+
+
+def kernel_label(name: str) -> str:
+    """A readable name for a kernel of the stats table: GEMM instantiations
+    by product, epilogue, B operand layout and output type."""
+    m = re.match(r"void bsg::gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)>", name)
+    if m:
+        _, mode, bk, epi, out, swap = m.groups()
+        return (f"gemm {_MODES.get(mode, mode)}{_EPIS.get(epi, '+' + epi)} "
+                f"(B {'K' if bk == 'true' else 'MN'}-contig, out {'bf16' if out == '1' else 'f32'}"
+                f"{'' if swap == 'true' else ', transposed'})")
+    return re.sub(r"\(.*", "", name).replace("void ", "")[:70]
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    lines = [f"# {args.title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```"] + args.cmd + ["```", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {kernel_label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} "
+                     f"| {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} "
+                     f"| {float(r['Percentage']):.1f}% |")
+    open(args.md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -235,9 +271,14 @@ def main():
     c.add_argument("--config", default="moe_small")
     c.add_argument("--md", required=True)
     c.add_argument("--cmd", nargs="*", default=[])
+    k = sub.add_parser("stats")
+    k.add_argument("--csv", required=True, help="rocprofv3 run_kernel_stats.csv")
+    k.add_argument("--md", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--cmd", nargs="*", default=[])
     a = ap.parse_args()
     sys.path.insert(0, ROOT)
-    {"run": run, "summarize": summarize, "counters": counters}[a.mode](a)
+    {"run": run, "summarize": summarize, "counters": counters, "stats": stats}[a.mode](a)
 
 
 if __name__ == "__main__":
