@@ -4,9 +4,11 @@
 Workload (default): the MoE-Small-shaped layer, T = 32768 tokens (32 x 1024),
 d = 768, E = 64 experts, f = 3072 per expert, top-1, GeLU, bf16 with fp32
 accumulation, per-expert logit bias N(0, 0.5); forward + backward:
-route, permute_pad, build_topology, SDD(+GeLU), DSD, unpermute_combine,
-then permute_pad(dy * gate), route_backward, SDD(GeLU'), DSD,
-unpermute_combine, DSTD (dW2), DSTD (dW1).  ``--config mixtral_train``
+route, permute_pad, build_topology, SDD (+GeLU, keeping GeLU'), DSD, the
+combine, then the dy permutation fused with the gate backward, SDD (dA *
+GeLU'), DSD, the combine of dx, DSTD (dW2), DSTD (dW1).  With top-1 routing
+each combine runs inside its DSD's epilogue; with k > 1 it is a launch of
+its own.  ``--config mixtral_train``
 runs the Mixtral-shaped SwiGLU layer (T = 8192, d = 4096, E = 8,
 f = 14336, top-2) forward + backward instead.  Inputs are seeded synthetic
 draws resident in HBM before the timed region.
