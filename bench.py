@@ -23,7 +23,10 @@ peak, timed with HIP events on the stream it runs on over the timed steps.
 Which call dominates, and the per-call table ``kernels``, come from a probe
 pass of three steps before the timed ones with every call bracketed by
 events; the timed steps record events around the dominant call only, since
-each event costs GPU time (about 4 us a call pair here).  ``traffic`` is HBM bytes per
+each event costs GPU time (about 4 us a call pair here).  The data-movement
+calls' entries give HBM GB/s from their algorithmic bytes, as a share of the
+8 TB/s peak and of ``hbm_copy_ceiling``, a device copy of as many bytes as
+permute_pad moves, timed in the same run.  ``traffic`` is HBM bytes per
 launch from the committed counter summary (null once the GEMM source has
 changed since).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
@@ -32,7 +35,6 @@ workload on this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -137,11 +139,10 @@ def traffic_for(config, kernel_name):
     if not os.path.exists(path):
         return None
     try:
+        from block_sparse_gemm_amd.traffic import source_sha
         data = json.load(open(path))
-        src = os.path.join(ROOT, "block_sparse_gemm_amd", "csrc", "gemm.hip")
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
         ent = data.get(kernel_name)
-        if not ent or ent.get("source_sha") != h:
+        if not ent or ent.get("source_sha") != source_sha():
             return None
         return ent.get("bytes_per_launch")
     except Exception:
@@ -227,6 +228,26 @@ def main():
     torch.cuda.synchronize()
     spread = np.percentile([ev[i].elapsed_time(ev[i + 1]) for i in range(10)], [10, 50, 90])
 
+    # context: a device-to-device copy (torch copy_) moving as many bytes as
+    # permute_pad reads and writes, through four rotating buffer pairs so the
+    # 256 MB MALL cannot serve repeats: the practical HBM ceiling that the
+    # data-movement calls are compared with
+    es = 2 if cfg.dtype == "bf16" else 4
+    Tp = int(L.bin_offsets[-1].item())
+    half = (cfg.T + Tp) * cfg.d * es // 2
+    pairs = [(torch.empty(half // 2, dtype=torch.bfloat16, device="cuda"),
+              torch.empty(half // 2, dtype=torch.bfloat16, device="cuda")) for _ in range(4)]
+    for i in range(4):
+        pairs[i][1].copy_(pairs[i][0])
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for i in range(20):
+        pairs[i % 4][1].copy_(pairs[i % 4][0])
+    ce1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (half // 2) * 2 / (ce0.elapsed_time(ce1) / 20 * 1e-3) / 1e9
+    del pairs
+
     # context: dense bf16 GEMMs with the products' executed shapes (M = Tp)
     dense = None
     if args.context:
@@ -272,8 +293,6 @@ def main():
     peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
 
     kernels = {}
-    es = 2 if cfg.dtype == "bf16" else 4
-    Tp = int(L.bin_offsets[-1].item())
     A_n = cfg.T * cfg.k
     for k, ms in kern.items():
         ent = {"ms": round(ms, 4)}
@@ -297,6 +316,9 @@ def main():
             ypes = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
             b = cfg.T * cfg.d * es + A_n * cfg.d * ypes + 8 * cfg.T * cfg.E + 8 * A_n
             ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
+        if "gbps" in ent:
+            ent["pct_hbm_peak"] = round(100 * ent["gbps"] / HBM_PEAK, 1)
+            ent["frac_of_copy"] = round(ent["gbps"] / copy_gbps, 3)
         kernels[k] = ent
 
     out = {
@@ -328,6 +350,8 @@ def main():
                      "traffic": traffic_for(cfg.name, dom), "ms": round(dom_ms, 4)},
         # every call timed alone in a probe pass before the timed steps
         "kernels": kernels,
+        "hbm_copy_ceiling": {"bytes": 2 * (half // 2) * 2, "gbps": round(copy_gbps, 1),
+                             "pct_hbm_peak": round(100 * copy_gbps / HBM_PEAK, 1)},
         "schedule": "two streams" if args.overlap else "one stream",
     }
     out["step_ms_p10_p50_p90"] = [round(float(v), 4) for v in spread]

@@ -99,44 +99,49 @@ __device__ __forceinline__ void grouped_tile(int t, int nm, int nn, int G, int& 
 // the Abramowitz & Stegun 7.1.26 approximation
 //   erfc(z) ~ (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
 //   t = 1 / (1 + p z),  |error in erf| <= 1.5e-7  (z >= 0),
-// with the hardware reciprocal and exp2.  q below is 0.5 erfc(|h|/sqrt 2),
+// with the hardware reciprocal and exp2, at z = |h| / sqrt 2.  The constants
+// carry the scale factors: 1/sqrt 2 sits in p, and the exponential is taken
+// directly as the normal density phi(h) = exp(-h^2/2) / sqrt(2 pi), so the
+// coefficients a_i carry sqrt(2 pi) / 2.  q below is 0.5 erfc(|h|/sqrt 2),
 // i.e. Phi(-|h|).
 struct ErfcHalf {
-    float q;  // Phi(-|h|)
-    float e;  // exp(-h^2 / 2)
+    float q;    // Phi(-|h|)
+    float phi;  // exp(-h^2 / 2) / sqrt(2 pi)
 };
 
 __device__ __forceinline__ ErfcHalf erfc_half(float h) {
-    const float z = fabsf(h) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float p = fmaf(1.061405429f * 0.5f, t, -1.453152027f * 0.5f);
-    p = fmaf(p, t, 1.421413741f * 0.5f);
-    p = fmaf(p, t, -0.284496736f * 0.5f);
-    p = fmaf(p, t, 0.254829592f * 0.5f);
-    p *= t;
-    const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.44269504088896341f);
-    return {p * e, e};
+    constexpr float kP = 0.3275911f * 0.70710678118654752f;
+    constexpr float kS = 0.5f * 2.50662827463100050f;          // sqrt(2 pi) / 2
+    constexpr float kE = -0.5f * 1.44269504088896341f;         // -log2(e) / 2
+    constexpr float kL = -1.32574806473615971f;                // log2(1 / sqrt(2 pi))
+    const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(h), kP, 1.0f));
+    float p = fmaf(1.061405429f * kS, t, -1.453152027f * kS);
+    p = fmaf(p, t, 1.421413741f * kS);
+    p = fmaf(p, t, -0.284496736f * kS);
+    p = fmaf(p, t, 0.254829592f * kS);
+    const float phi = __builtin_amdgcn_exp2f(fmaf(h, h * kE, kL));
+    return {(p * t) * phi, phi};
 }
 
 __device__ __forceinline__ float gelu_f(float h) {
     const ErfcHalf r = erfc_half(h);
-    const float phi = h >= 0.0f ? 1.0f - r.q : r.q;
-    return h * phi;
+    const float cdf = h >= 0.0f ? 1.0f - r.q : r.q;
+    return h * cdf;
 }
 
-// d/dh gelu(h) = Phi(h) + h phi(h),  phi(h) = exp(-h^2/2) / sqrt(2 pi)
+// d/dh gelu(h) = Phi(h) + h phi(h)
 __device__ __forceinline__ float gelu_grad_f(float h) {
     const ErfcHalf r = erfc_half(h);
-    const float phi = h >= 0.0f ? 1.0f - r.q : r.q;
-    return fmaf(h * r.e, 0.398942280401432678f, phi);
+    const float cdf = h >= 0.0f ? 1.0f - r.q : r.q;
+    return fmaf(h, r.phi, cdf);
 }
 
 // Both at once (one erfc evaluation): what the training forward stores.
 __device__ __forceinline__ void gelu_and_grad(float h, float& g, float& gp) {
     const ErfcHalf r = erfc_half(h);
-    const float phi = h >= 0.0f ? 1.0f - r.q : r.q;
-    g = h * phi;
-    gp = fmaf(h * r.e, 0.398942280401432678f, phi);
+    const float cdf = h >= 0.0f ? 1.0f - r.q : r.q;
+    g = h * cdf;
+    gp = fmaf(h, r.phi, cdf);
 }
 
 // silu(g) = g / (1 + exp(-g))

@@ -38,13 +38,18 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SRC = os.path.join(ROOT, "block_sparse_gemm_amd", "csrc", "gemm.hip")
+# every source the GEMM kernels are compiled from
+GEMM_SRCS = [os.path.join(ROOT, "block_sparse_gemm_amd", "csrc", n)
+             for n in ("gemm.hip", "common.hpp", "kernels.hpp")]
 COPY_BYTES = 1 << 29           # 512 MiB read and 512 MiB written by the calibration copy
 COPY_NAMES = ("copyBuffer", "MulFunctor")   # the memcpy blit kernel, else x * 1
 
 
 def source_sha() -> str:
-    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(config: str) -> str:
