@@ -53,8 +53,8 @@ HBM_PEAK = 8000.0         # GB/s
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="moe_small")
     ap.add_argument("--overlap", action="store_true",
                     help="weight gradients on a second stream in the timed steps")
@@ -114,6 +114,14 @@ def cpu_baseline(cfg, inp, target_s):
     n0, t0 = run(32)
     n = int(min(cfg.T, max(32, n0 * target_s / max(t0, 1e-3))))
     n, t = run(n)
+    threads = orc.get_threads()
+    # the same oracle on one core, on a sample of about a tenth of the time
+    orc.set_threads(1)
+    try:
+        n1, t1 = run(8)
+        n1, t1 = run(int(min(cfg.T, max(8, n1 * target_s / 10 / max(t1, 1e-3)))))
+    finally:
+        orc.set_threads(threads)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -122,13 +130,15 @@ def cpu_baseline(cfg, inp, target_s):
                 break
     except OSError:
         pass
-    return {"value": per_tok * n / t / 1e12, "unit": "TFLOP/s", "cores": orc.get_threads(),
+    return {"value": per_tok * n / t / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "single_core_value": per_tok * n1 / t1 / 1e12,
+            "single_core_sample": f"{n1} tokens, {t1:.1f} s wall on 1 thread",
             "kind": "oracle", "cpu": cpu, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n} tokens of the {cfg.name} workload, forward"
                       + (f" + input-gradient path ({fwd_p + bwd_p} of the "
                          f"{fwd_p + bwd_p + (3 if sw else 2)} products per token; weight "
                          f"gradients not sampled)" if cfg.backward else "")
-                      + f", {t:.1f} s wall on {orc.get_threads()} OpenMP threads"}
+                      + f", {t:.1f} s wall on {threads} OpenMP threads"}
 
 
 def traffic_for(config, kernel_name):
@@ -220,13 +230,14 @@ def main():
     step_ms = wall * 1e3 / args.steps
 
     # spread of the step time: a few more steps, each between two events
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    NS = max(10, args.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(NS + 1)]
     ev[0].record()
-    for i in range(10):
+    for i in range(NS):
         L.step(x, logits, W1, W2, W3, dy)
         ev[i + 1].record()
     torch.cuda.synchronize()
-    spread = np.percentile([ev[i].elapsed_time(ev[i + 1]) for i in range(10)], [10, 50, 90])
+    spread = np.percentile([ev[i].elapsed_time(ev[i + 1]) for i in range(NS)], [10, 50, 90])
 
     # context: a device-to-device copy (torch copy_) moving as many bytes as
     # permute_pad reads and writes, through four rotating buffer pairs so the

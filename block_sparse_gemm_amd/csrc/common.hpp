@@ -165,20 +165,28 @@ __device__ __forceinline__ void silu_and_grad(float g, float& s, float& sp) {
 // (NV per lane, max-subtracted); dL/dp at the picks (with renorm:
 // dg_j / S - (sum_i dg_i p_(e_i)) / S^2, S = sum of the picks' p); scattered
 // to the experts' lanes; out[e] = p_e (dL/dp_e - sum_u p_u dL/dp_u).
+//
+// The logits are loaded apart (load_logits), so a caller can issue that load
+// before its other work on the token and hide its latency.
 template <int NV>
-__device__ __forceinline__ void gate_grad_token(const float* __restrict__ l, int E, int k,
-                                                int renorm, float my_dg, int my_e,
-                                                float* __restrict__ out) {
+__device__ __forceinline__ void load_logits(const float* __restrict__ l, int E, float* p) {
     const int lane = threadIdx.x & (kWave - 1);
-    // ---- softmax of the logits (max-subtracted)
-    float p[NV];
-    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = lane + kWave * i;
         p[i] = e < E ? l[e] : -INFINITY;
-        mx = fmaxf(mx, p[i]);
     }
+}
+
+template <int NV>
+__device__ __forceinline__ void gate_grad_token_loaded(float* p, int E, int k, int renorm,
+                                                       float my_dg, int my_e,
+                                                       float* __restrict__ out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    // ---- softmax of the logits (max-subtracted)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) mx = fmaxf(mx, p[i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
     float z = 0.0f;
@@ -225,6 +233,15 @@ __device__ __forceinline__ void gate_grad_token(const float* __restrict__ l, int
         const int e = lane + kWave * i;
         if (e < E) out[e] = p[i] * (dp[i] - dot);
     }
+}
+
+template <int NV>
+__device__ __forceinline__ void gate_grad_token(const float* __restrict__ l, int E, int k,
+                                                int renorm, float my_dg, int my_e,
+                                                float* __restrict__ out) {
+    float p[NV];
+    load_logits<NV>(l, E, p);
+    gate_grad_token_loaded<NV>(p, E, k, renorm, my_dg, my_e, out);
 }
 
 }  // namespace bsg

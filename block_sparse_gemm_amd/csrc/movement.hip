@@ -143,7 +143,11 @@ __global__ __launch_bounds__(kMoveThreads) void permute_pad_kernel(
 // scale = gate), exactly as permute_pad_kernel, and the gate backward of
 // each token: dg_j = <dy_t, yp_j> accumulated (fp32) while dy's chunks are
 // in registers, then the router-logit gradient (gate_grad_token).
-template <int DT, int YP, int NV>
+//
+// PAIR: rows of at least two wave-widths of chunks keep two chunks per lane
+// in flight; shorter rows take one chunk per step, which needs fewer
+// registers (more waves per SIMD).
+template <int DT, int YP, int NV, bool PAIR>
 __global__ __launch_bounds__(kMoveThreads) void permute_gate_backward_kernel(
     const u32x4* __restrict__ dy, int64_t T, int chunks, int k,
     const int32_t* __restrict__ dest_row, const float* __restrict__ gate,
@@ -161,38 +165,76 @@ __global__ __launch_bounds__(kMoveThreads) void permute_gate_backward_kernel(
         if (job < T) {
             const int64_t t = job;
             const u32x4* src = dy + t * chunks;
+            // the token's picks (and, for long rows, its logits) are
+            // requested first, so the softmax at the end waits on nothing
+            float lg[NV];
+            if constexpr (PAIR) load_logits<NV>(logits + t * E, E, lg);
+            const int my_e = lane < k ? expert_idx[t * k + lane] : 0;
             float my_dg = 0.0f;
-            int my_e = 0;
             for (int j = 0; j < k; ++j) {
                 const int64_t a = t * k + j;
                 const int64_t row = dest_row[a];
                 const float g = gate[a];
                 const char* yr = yp + row * ld_yp_bytes;
                 float s = 0.0f;
-                // row < Tp_max whenever the routing used this bin size
-                for (int c = lane; c < chunks && row < Tp_max; c += kWave) {
-                    const u32x4 v = src[c];
-                    dyp[row * chunks + c] = scale_chunk<DT>(v, g);
-                    float x[V], y[V];
-                    Row<DT>::load_f32(&v, x);
-                    if constexpr (YCB == 16) {
-                        Row<YP>::load_f32(yr + (int64_t)c * 16, y);
-                    } else {  // bf16 dy, fp32 yp: two 16-byte chunks of yp
-                        Row<kF32>::load_f32(yr + (int64_t)c * 32, y);
-                        Row<kF32>::load_f32(yr + (int64_t)c * 32 + 16, y + 4);
-                    }
+                if constexpr (PAIR) {
+                    // two chunks per lane in flight; row < Tp_max whenever
+                    // the routing used this bin size
+                    for (int c0 = lane; c0 < chunks && row < Tp_max; c0 += 2 * kWave) {
+                        const int c1 = c0 + kWave;
+                        const bool two = c1 < chunks;
+                        // raw 16-byte words in flight (yp: YCB / 16 words a chunk)
+                        u32x4 v[2], w[2][YCB / 16];
+                        v[0] = src[c0];
+                        if (two) v[1] = src[c1];
 #pragma unroll
-                    for (int q = 0; q < V; ++q) s = fmaf(x[q], y[q], s);
+                        for (int h = 0; h < 2; ++h) {
+                            if (h == 1 && !two) break;
+                            const int c = h == 0 ? c0 : c1;
+#pragma unroll
+                            for (int u = 0; u < YCB / 16; ++u)
+                                w[h][u] = *(const u32x4*)(yr + (int64_t)c * YCB + 16 * u);
+                        }
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            if (h == 1 && !two) break;
+                            const int c = h == 0 ? c0 : c1;
+                            dyp[row * chunks + c] = scale_chunk<DT>(v[h], g);
+                            float x[V], y[V];
+                            Row<DT>::load_f32(&v[h], x);
+                            if constexpr (YCB == 16) {
+                                Row<YP>::load_f32(&w[h][0], y);
+                            } else {  // bf16 dy, fp32 yp: two 16-byte words of yp
+                                Row<kF32>::load_f32(&w[h][0], y);
+                                Row<kF32>::load_f32(&w[h][1], y + 4);
+                            }
+#pragma unroll
+                            for (int q = 0; q < V; ++q) s = fmaf(x[q], y[q], s);
+                        }
+                    }
+                } else {
+                    for (int c = lane; c < chunks && row < Tp_max; c += kWave) {
+                        const u32x4 v = src[c];
+                        dyp[row * chunks + c] = scale_chunk<DT>(v, g);
+                        float x[V], y[V];
+                        Row<DT>::load_f32(&v, x);
+                        if constexpr (YCB == 16) {
+                            Row<YP>::load_f32(yr + (int64_t)c * 16, y);
+                        } else {  // bf16 dy, fp32 yp: two 16-byte chunks of yp
+                            Row<kF32>::load_f32(yr + (int64_t)c * 32, y);
+                            Row<kF32>::load_f32(yr + (int64_t)c * 32 + 16, y + 4);
+                        }
+#pragma unroll
+                        for (int q = 0; q < V; ++q) s = fmaf(x[q], y[q], s);
+                    }
                 }
                 s = wave_sum(s);
-                if (lane == j) {
-                    my_dg = s;
-                    my_e = expert_idx[a];
-                }
+                if (lane == j) my_dg = s;
             }
             if (lane < k && dest_row[t * k + lane] < Tp_max)
                 row_src[dest_row[t * k + lane]] = (int32_t)(t * k + lane);
-            gate_grad_token<NV>(logits + t * E, E, k, renorm, my_dg, my_e, dlogits + t * E);
+            if constexpr (!PAIR) load_logits<NV>(logits + t * E, E, lg);
+            gate_grad_token_loaded<NV>(lg, E, k, renorm, my_dg, my_e, dlogits + t * E);
         } else {
             const int64_t p = job - T;
             const int e = (int)(p / bin_rows);
@@ -275,17 +317,23 @@ static hipError_t launch_pgb(const void* dy, int64_t T, int d, int k, const int3
                              float* dlogits, hipStream_t stream) {
     const int chunks = d * (DT == kBf16 ? 2 : 4) / 16;
     const int grid = move_grid(T + (int64_t)E * bin_rows);
-#define BSG_PGB(NV)                                                                              \
-    hipLaunchKernelGGL((permute_gate_backward_kernel<DT, YP, NV>), dim3(grid), dim3(kMoveThreads), \
-                       0, stream, (const u32x4*)dy, T, chunks, k, dest_row, gate, counts,        \
-                       bin_offsets, E, bin_rows, Tp_max, row_src, (u32x4*)dyp, logits, renorm,  \
-                       expert_idx,                                                               \
-                       (const char*)yp, ld_yp_bytes, dlogits)
-    if (E <= 64) BSG_PGB(1);
-    else if (E <= 128) BSG_PGB(2);
-    else if (E <= 256) BSG_PGB(4);
-    else if (E <= 512) BSG_PGB(8);
-    else BSG_PGB(16);
+#define BSG_PGB(NV, PAIR)                                                                        \
+    hipLaunchKernelGGL((permute_gate_backward_kernel<DT, YP, NV, PAIR>), dim3(grid),             \
+                       dim3(kMoveThreads), 0, stream, (const u32x4*)dy, T, chunks, k, dest_row,  \
+                       gate, counts, bin_offsets, E, bin_rows, Tp_max, row_src, (u32x4*)dyp,     \
+                       logits, renorm, expert_idx, (const char*)yp, ld_yp_bytes, dlogits)
+#define BSG_PGB_E(PAIR)                   \
+    if (E <= 64) BSG_PGB(1, PAIR);        \
+    else if (E <= 128) BSG_PGB(2, PAIR);  \
+    else if (E <= 256) BSG_PGB(4, PAIR);  \
+    else if (E <= 512) BSG_PGB(8, PAIR);  \
+    else BSG_PGB(16, PAIR);
+    if (chunks >= 2 * kWave) {
+        BSG_PGB_E(true)
+    } else {
+        BSG_PGB_E(false)
+    }
+#undef BSG_PGB_E
 #undef BSG_PGB
     return hipGetLastError();
 }
