@@ -260,6 +260,14 @@ SMALL = {
                                             f=256, k=1, act="swiglu")),
     "swiglu_train_f32": Case(_small("swiglu_train_f32", T=300, d=128, E=3, f=256, k=2,
                                     act="swiglu", dtype="f32", renorm=True, x_std=0.5)),
+    # rows of 128 or more 16-byte chunks, not a multiple of 128: the backward's
+    # dy permutation keeps two chunks per lane in flight, with some lanes
+    # holding one (bf16 d = 1152: 144 chunks; fp32 d = 640: 160 chunks)
+    "long_rows_bf16": Case(_small("long_rows_bf16", T=300, d=1152, E=4, f=256, k=2)),
+    "long_rows_yp_f32": Case(_small("long_rows_yp_f32", T=300, d=1152, E=3, f=128, k=2,
+                                    renorm=True, yp_dtype="f32")),
+    "long_rows_f32": Case(_small("long_rows_f32", T=200, d=640, E=3, f=128, k=1, dtype="f32",
+                                 x_std=0.5)),
     # bins padded to 256 rows (every expert an even number of block rows)
     "bins256_bf16": Case(_small("bins256_bf16", bin_rows=256)),
     "bins256_swiglu": Case(_small("bins256_swiglu", T=500, d=256, E=4, f=256, k=2,
