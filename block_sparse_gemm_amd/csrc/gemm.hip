@@ -199,13 +199,16 @@ __device__ __forceinline__ void mma<kF32>(f32x16& acc, u32x4 x, u32x4 y) {
 }
 
 // Wait until at most `tiles` K-tiles of this wave's direct loads are still
-// in flight (they retire in issue order); kLoadsPerTile loads per K-tile.
+// in flight (they retire in issue order); LPT loads per K-tile: 8, or 6 in
+// a half tile, which skips the absent M half's panel.
+template <int LPT>
 __device__ __forceinline__ void wait_tiles(int tiles) {
+    static_assert(LPT == 8 || LPT == 6, "8 or 6 loads per K-tile");
     switch (tiles) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPT) : "memory"); break;
     }
 }
 static_assert(kLoadsPerTile == 8, "wait_tiles encodes 8 loads per K-tile");
@@ -244,8 +247,13 @@ struct KIdx {
 // MODE: kModeSdd, kModeSddOne (dual-B SwiGLU: one block per tile),
 // kModeDsd, kModeDsd2 (two block sets), kModeDstd.  BK: B operand
 // K-contiguous.
-template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
+// HALF: a half tile of SDD / DSD, one block row (the expert's last, when it
+// has an odd number of them) instead of a pair.  Its four waves split that
+// block row: wave (wm, wn) takes rows 64 wm .. 64 wm + 63 x the 128 columns
+// of N half wn, as 2 x 4 accumulators, and the absent half's panel is not
+// loaded (6 direct loads per K-tile instead of 8).
+template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP, bool HALF>
+__device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
     constexpr int ES = Elt<DT>::kBytes;
     constexpr int KT = Elt<DT>::kKt;
     constexpr int KPB = kBlock / KT;  // K-tiles per block
@@ -256,8 +264,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     constexpr bool DSD = MODE == kModeDsd || MODE == kModeDsd2;
     constexpr bool SPLIT = MODE != kModeDstd;  // loads of a K-tile over two half-steps
     static_assert(KT / (DT == kBf16 ? 16 : 8) == 2, "two MFMA K-steps per K-tile");
-
-    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + 3 * kIdxCap * 4];
+    static_assert(!HALF || ((SDD && !DUAL) || DSD) && SWAP, "half tiles: SDD / DSD, row-major C");
+    constexpr int LPT = HALF ? kLoadsPerTile - 2 : kLoadsPerTile;  // direct loads per K-tile
+    constexpr int NH = HALF ? 1 : 2;      // 64-row output halves per wave
+    constexpr int NMI = HALF ? 2 : 4;     // 32-row A fragments per wave
     lds_t* lds = (lds_t*)smem;
 
     // ---- tile count (device-side sizes) and XCD-aware remap
@@ -290,6 +300,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int l32 = lane & 31, lh = lane >> 5;
+    // first row of this wave's output inside its block row (half tiles)
+    const int roff = HALF ? 64 * wm : 0;
 
     // ---- the tile's two M halves (block rows, or block columns for DSTD)
     int mrow0, mrow1;
@@ -449,13 +461,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     const uint32_t lds0 = lds_u32(lds) + wave * kSegsPerWave * 1024;
     auto dma = [&](int t, const Bases& b, int j) {
         const int pnl = j & 3, sg = j >> 2;
+        if (HALF && pnl == 1) return;  // the absent M half
         const uint32_t dst = lds0 + (t % kStages) * kStageBytes + pnl * kPanelBytes + sg * 1024;
         const char* base = pnl == 0 ? b.a0 : pnl == 1 ? b.a1 : pnl == 2 ? b.b0 : b.b1;
         dma16(dst, base, pnl < 2 ? aoff[sg] : boff[sg]);
     };
 
     // ---- this wave's output: does it exist, and its block (SDD)
-    const bool active = (wm == 0 || m1) && (DUAL || wn == 0 || n1);
+    const bool active = (HALF || wm == 0 || m1) && (DUAL || wn == 0 || n1);
     const int mrow = wm ? mrow1 : mrow0;  // this wave's block row / column
     int oblk = 0;
     if constexpr (MODE == kModeSdd) oblk = (wm ? rp1 : rp0) + 2 * tq + wn;
@@ -479,7 +492,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int m = 32 * mi + l32;
+                const int m = roff + 32 * mi + l32;
                 const int nloc = 32 * ni + 8 * g + 4 * lh;
                 const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
                 hsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + off * 2);
@@ -511,10 +524,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     // fragment g of K-step c of K-tile t: g < 4 -> A row tile g, else B tile g - 4
     auto read1 = [&](int t, int c, int g, u32x4* af, u32x4* bf) {
         const lds_t* st = lds + (t % kStages) * kStageBytes;
-        if (g < 4) af[g] = frag<DT, AK>(st + wm * kPanelBytes, 32 * g, c);
-        else bf[g - 4] = frag<DT, BK>(st + bpanel[g - 4] * kPanelBytes, brow[g - 4], c);
+        if (HALF && g < 4) {  // rows 64 wm .. + 63 of the one A panel
+            if (g < NMI) af[g] = frag<DT, AK>(st, roff + 32 * g, c);
+        } else if (g < 4) {
+            af[g] = frag<DT, AK>(st + wm * kPanelBytes, 32 * g, c);
+        } else {
+            bf[g - 4] = frag<DT, BK>(st + bpanel[g - 4] * kPanelBytes, brow[g - 4], c);
+        }
     };
     auto mma2 = [&](int g, const u32x4* af, const u32x4* bf) {
+        if (2 * g >= 4 * NMI) return;  // half tiles: A fragments 0, 1 only
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int mi = (2 * g + h) >> 2, ni = (2 * g + h) & 3;
@@ -574,7 +593,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
 #pragma unroll
             for (int j = 0; j < kLoadsPerTile; ++j) dma(t, b, j);
         }
-        wait_tiles(min(kStages - 1, nk - 1));
+        wait_tiles<LPT>(min(kStages - 1, nk - 1));
         __syncthreads();
 #pragma unroll
         for (int g = 0; g < 8; ++g) read1(0, 0, g, a0f, b0f);
@@ -582,14 +601,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         // steady state: publish K-tile kt + 1, load K-tile kt + kStages
         for (; kt + kStages < nk; ++kt) {
             first_half(kt, nk);
-            wait_tiles(kStages - 2);
+            wait_tiles<LPT>(kStages - 2);
             __syncthreads();
             second_half(kt, true, true);
         }
         // tail: publish without new loads
         for (; kt + 1 < nk; ++kt) {
             first_half(kt, nk);
-            wait_tiles(min(kStages - 2, nk - 2 - kt));
+            wait_tiles<LPT>(min(kStages - 2, nk - 2 - kt));
             __syncthreads();
             second_half(kt, true, false);
         }
@@ -685,10 +704,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     float sc_g[2] = {1.0f, 1.0f};
     if constexpr (EPI == kEpiScatter) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sc_a[h] = P.scat_rows[(int64_t)kBlock * mrow + 64 * h + lane];
+        for (int h = 0; h < NH; ++h) sc_a[h] = P.scat_rows[(int64_t)kBlock * mrow + roff + 64 * h + lane];
         if (P.scat_gate) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) sc_g[h] = sc_a[h] >= 0 ? P.scat_gate[sc_a[h]] : 1.0f;
+            for (int h = 0; h < NH; ++h) sc_g[h] = sc_a[h] >= 0 ? P.scat_gate[sc_a[h]] : 1.0f;
         }
     }
     auto scatter_flush = [&](const lds_t* sub, int h) {
@@ -718,10 +737,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     char* obase;
     int64_t orow;
     if constexpr (SDD) {
-        obase = (char*)P.out + (int64_t)oblk * kBlock * kBlock * OES;
+        obase = (char*)P.out + ((int64_t)oblk * kBlock * kBlock + roff * kBlock) * OES;
         orow = kBlock * OES;
     } else if constexpr (SWAP) {
-        obase = (char*)P.out + (((int64_t)kBlock * mrow) * P.ldc + n0 + wn * 128) * OES;
+        obase = (char*)P.out + (((int64_t)kBlock * mrow + roff) * P.ldc + n0 + wn * 128) * OES;
         orow = P.ldc * OES;
     } else {
         obase = (char*)P.out + ((n0 + wn * 128) * P.ldc + (int64_t)kBlock * mrow) * OES;
@@ -738,7 +757,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     // two halves of 64 staging rows: M slabs (mi) 2h, 2h + 1 with a
     // row-major output, N slabs (ni) 2h, 2h + 1 with the transposed one
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
 #pragma unroll
@@ -746,7 +765,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                 const int mi = SWAP || !STAGE ? 2 * h + a : b;
                 const int ni = SWAP || !STAGE ? b : 2 * h + a;
                 if constexpr (PRE) {
-                    if (b == 0 && mi + 1 < 4) hload(mi + 1, (mi + 1) & 1);
+                    if (b == 0 && mi + 1 < NMI) hload(mi + 1, (mi + 1) & 1);
                 }
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -755,7 +774,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                     for (int s = 0; s < 4; ++s) v[s] = acc[mi][ni][4 * g + s];
                     if constexpr (SDD) {
                         // block-major output: (m, n) of block b at b*16384 + m*128 + n
-                        const int m = 32 * mi + l32;
+                        const int m = roff + 32 * mi + l32;
                         const int nloc = DUAL ? wn * 64 + 32 * ni + 8 * g + 4 * lh
                                               : 32 * ni + 8 * g + 4 * lh;
                         const int64_t off = (int64_t)oblk * kBlock * kBlock + m * kBlock + nloc;
@@ -827,7 +846,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
                     } else if constexpr (STAGE) {
                         stage_put(region, mi, ni, g, v);
                     } else if constexpr (SWAP) {  // DSD, or DSTD with row-major C
-                        const int m = 32 * mi + l32;
+                        const int m = roff + 32 * mi + l32;
                         const int64_t col = n0 + wn * 128 + 32 * ni + 8 * g + 4 * lh;
                         const int64_t off = ((int64_t)kBlock * mrow + m) * P.ldc + col;
                         store4<OUT>((char*)P.out + off * OES, v);
@@ -852,7 +871,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             }
         } else if constexpr (STAGE) {
             if constexpr (EPI == kEpiGeluSave) {
-                stage_flush(region, (char*)P.aux_out + (int64_t)oblk * kBlock * kBlock * OES +
+                stage_flush(region, (char*)P.aux_out +
+                                        ((int64_t)oblk * kBlock * kBlock + roff * kBlock) * OES +
                                         h * 64 * orow, orow);
                 stage_flush(region + 16384, obase + h * 64 * orow, orow);
             } else if constexpr (EPI == kEpiSiluMulBwd) {
@@ -866,6 +886,31 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             }
         }
     }
+}
+
+// Whether this workgroup's SDD / DSD tile is a half tile: the same tile
+// order as gemm_tile's, then bit 0 of the row pair (second block row
+// present).  Workgroups beyond the live tile count say no (gemm_tile exits).
+template <int MODE>
+__device__ __forceinline__ bool half_tile(const GemmParams& P) {
+    const int tn = MODE == kModeSdd ? (P.F + 1) / 2 : P.ntn;
+    const int ntiles = P.meta[3] * tn;
+    if ((int)blockIdx.x >= ntiles) return false;
+    int tm, tq;
+    grouped_tile(xcd_remap(blockIdx.x, ntiles), ntiles / tn, tn, P.group, tm, tq);
+    return __builtin_amdgcn_readfirstlane(P.row_pairs[tm] & 1) == 0;
+}
+
+template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + 3 * kIdxCap * 4];
+    if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
+        if (half_tile<MODE>(P)) {
+            gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true>(P, smem);
+            return;
+        }
+    }
+    gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, false>(P, smem);
 }
 
 // ----------------------------------------------------------------- launch
