@@ -11,7 +11,9 @@
 // identical on every run:
 //   1. route_topk     one workgroup per 64-token chunk, one wavefront per
 //                     token at a time (4 each, loaded up front): top-k by
-//                     wave reductions, softmax gate; an LDS histogram.
+//                     wave reductions, softmax gate; an LDS histogram.  Up
+//                     to 64 experts and top-16 (route_topk_seg): the 4
+//                     tokens of a wave side by side, 16 lanes each.
 //   2. route_scan     one workgroup per expert: exclusive scan of that
 //                     expert's per-chunk counts (in place) and its total.
 //   3. route_place    one workgroup per chunk: padded bin offsets, then the
@@ -108,6 +110,94 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
             gate[t * k + lane] = p / denom;
             atomicAdd(&hist[my_sel], 1);  // LDS only: the count is order-free
         }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kTopkThreads)
+        chunk_counts[(int64_t)e * nchunks + blockIdx.x] = hist[e];
+}
+
+// E <= 64, k <= 16: a wave's 4 tokens side by side, 16 lanes each (lane s of
+// a token's segment holds experts s, s + 16, ...), so the top-k and softmax
+// reductions are 4-step butterflies within 16 lanes that serve all 4 tokens
+// at once.  Same selection order (larger logit, then lower id) as route_topk.
+template <int NV>
+__global__ __launch_bounds__(kTopkThreads) void route_topk_seg(
+    const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
+    int32_t* __restrict__ expert_idx, float* __restrict__ gate,
+    int32_t* __restrict__ chunk_counts, int nchunks) {
+    constexpr int kSeg = 16;
+    static_assert(kTokPerWave * kSeg == kWave, "the wave's tokens fill its lanes");
+    __shared__ int hist[kSeg * NV];
+    for (int e = threadIdx.x; e < E; e += kTopkThreads) hist[e] = 0;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int sl = lane & (kSeg - 1);
+    const int64_t t = (int64_t)blockIdx.x * kRouteChunk + wave * kTokPerWave + lane / kSeg;
+    const bool live = t < T;
+
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = sl + kSeg * i;
+        v[i] = (live && e < E) ? logits[t * E + e] : 0.0f;
+    }
+    __syncthreads();  // histogram cleared
+
+    uint32_t taken = 0;  // bit i: expert sl + 16 i already picked
+    int my_sel = -1;
+    float my_val = 0.0f;
+    float top_val = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        // lane-local best among untaken experts: larger logit, then lower id
+        int bi = -1;
+        float bv = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = sl + kSeg * i;
+            if (e < E && !((taken >> i) & 1u) && (bi < 0 || v[i] > bv)) {
+                bi = e;
+                bv = v[i];
+            }
+        }
+        // butterfly within the segment: a total order, every lane ends with the winner
+#pragma unroll
+        for (int off = kSeg / 2; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, kSeg);
+            const int oi = __shfl_xor(bi, off, kSeg);
+            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+                bi = oi;
+                bv = ov;
+            }
+        }
+        if ((bi & (kSeg - 1)) == sl) taken |= 1u << (bi / kSeg);
+        if (sl == j) {
+            my_sel = bi;
+            my_val = bv;
+        }
+        if (j == 0) top_val = bv;
+    }
+    // softmax over all experts, max-subtracted (the first pick is the max)
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = sl + kSeg * i;
+        if (e < E) z += expf(v[i] - top_val);
+    }
+#pragma unroll
+    for (int off = kSeg / 2; off >= 1; off >>= 1) z += __shfl_xor(z, off, kSeg);
+    const float p = sl < k ? expf(my_val - top_val) : 0.0f;
+    float denom = z;
+    if (renorm) {
+        float ps = p;
+#pragma unroll
+        for (int off = kSeg / 2; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, kSeg);
+        denom = ps;
+    }
+    if (live && sl < k) {
+        expert_idx[t * k + sl] = my_sel;
+        gate[t * k + sl] = p / denom;
+        atomicAdd(&hist[my_sel], 1);  // LDS only: the count is order-free
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kTopkThreads)
@@ -298,11 +388,18 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
 #define BSG_TOPK(NV)                                                                         \
     hipLaunchKernelGGL(route_topk<NV>, dim3(nchunks), dim3(kTopkThreads), 0, stream, logits, T, \
                        E, k, renorm, expert_idx, gate, workspace, nchunks)
-    if (E <= 64) BSG_TOPK(1);
+#define BSG_TOPK_SEG(NV)                                                                     \
+    hipLaunchKernelGGL(route_topk_seg<NV>, dim3(nchunks), dim3(kTopkThreads), 0, stream, logits, \
+                       T, E, k, renorm, expert_idx, gate, workspace, nchunks)
+    if (E <= 16 && k <= 16) BSG_TOPK_SEG(1);
+    else if (E <= 32 && k <= 16) BSG_TOPK_SEG(2);
+    else if (E <= 64 && k <= 16) BSG_TOPK_SEG(4);
+    else if (E <= 64) BSG_TOPK(1);
     else if (E <= 128) BSG_TOPK(2);
     else if (E <= 256) BSG_TOPK(4);
     else if (E <= 512) BSG_TOPK(8);
     else BSG_TOPK(16);
+#undef BSG_TOPK_SEG
 #undef BSG_TOPK
     hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace, nchunks,
                        counts);
