@@ -15,13 +15,15 @@
 //                     to 64 experts and top-16 (route_topk_seg): the 4
 //                     tokens of a wave side by side, 16 lanes each.
 //   2. route_scan     one workgroup per expert: exclusive scan of that
-//                     expert's per-chunk counts (in place) and its total.
+//                     expert's per-chunk counts (in place) and its total,
+//                     by wave shuffles and one barrier.
 //   3. route_place    one workgroup per chunk: padded bin offsets, then the
 //                     rank of each assignment among the chunk's earlier
 //                     assignments to the same expert, found with wave64
 //                     ballots on the expert id bits.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "scan.hpp"
 
 namespace bsg {
 
@@ -208,29 +210,21 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_seg(
 __global__ __launch_bounds__(kRouteThreads) void route_scan(int32_t* __restrict__ chunk_counts,
                                                             int nchunks,
                                                             int32_t* __restrict__ counts) {
-    __shared__ int part[kRouteThreads];
+    __shared__ int wsum[kRouteWaves];
     int32_t* row = chunk_counts + (int64_t)blockIdx.x * nchunks;
     const int per = (nchunks + kRouteThreads - 1) / kRouteThreads;
     const int lo = threadIdx.x * per;
     const int hi = min(lo + per, nchunks);
     int s = 0;
     for (int c = lo; c < hi; ++c) s += row[c];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    // Hillis-Steele inclusive scan of the 256 partial sums
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-        const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-        __syncthreads();
-        part[threadIdx.x] += add;
-        __syncthreads();
-    }
-    int run = part[threadIdx.x] - s;  // exclusive prefix of this segment
+    int total;
+    int run = block_excl_scan<kRouteWaves>(s, wsum, total);  // exclusive prefix of this segment
     for (int c = lo; c < hi; ++c) {
         const int v = row[c];
         row[c] = run;
         run += v;
     }
-    if (threadIdx.x == kRouteThreads - 1) counts[blockIdx.x] = part[kRouteThreads - 1];
+    if (threadIdx.x == kRouteThreads - 1) counts[blockIdx.x] = total;
 }
 
 // Bin offsets + stable in-chunk ranks -> dest_row.
@@ -239,7 +233,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_place(
     const int32_t* __restrict__ chunk_base, int nchunks, const int32_t* __restrict__ counts,
     int bin_rows, int32_t* __restrict__ dest_row, int32_t* __restrict__ bin_offsets) {
     __shared__ int bins[kMaxExperts + 1];
-    __shared__ int part[kRouteThreads];
+    __shared__ int wsum[kRouteWaves];
     __shared__ int running[kMaxExperts];
     __shared__ int wcnt[kRouteWaves][kMaxExperts];
 
@@ -249,21 +243,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_place(
     const int hi = min(lo + per, E);
     int s = 0;
     for (int e = lo; e < hi; ++e) s += (counts[e] + bin_rows - 1) / bin_rows * bin_rows;
-    part[threadIdx.x] = s;
     for (int e = threadIdx.x; e < E; e += kRouteThreads) running[e] = 0;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-        const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-        __syncthreads();
-        part[threadIdx.x] += add;
-        __syncthreads();
-    }
-    int run = part[threadIdx.x] - s;
+    int total;
+    int run = block_excl_scan<kRouteWaves>(s, wsum, total);
     for (int e = lo; e < hi; ++e) {
         bins[e] = run;
         run += (counts[e] + bin_rows - 1) / bin_rows * bin_rows;
     }
-    if (threadIdx.x == kRouteThreads - 1) bins[E] = part[kRouteThreads - 1];
+    if (threadIdx.x == kRouteThreads - 1) bins[E] = total;
     __syncthreads();
     if (blockIdx.x == 0)
         for (int e = threadIdx.x; e <= E; e += kRouteThreads) bin_offsets[e] = bins[e];

@@ -22,6 +22,7 @@
 // and finds the owner of a row block by binary search.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "scan.hpp"
 
 namespace bsg {
 
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     int32_t* __restrict__ meta) {
     __shared__ int s[kMaxExperts + 1];   // bin start in row blocks
     __shared__ int pp[kMaxExperts + 1];  // first row pair of each expert
-    __shared__ int part[kTopoThreads];
+    __shared__ int wsum[kTopoThreads / kWave];
     for (int e = threadIdx.x; e <= E; e += kTopoThreads) s[e] = bin_offsets[e] / kBlock;
     __syncthreads();
     // row pairs: expert e's R_e row blocks form ceil(R_e / 2) pairs of
@@ -56,20 +57,13 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     const int lo = threadIdx.x * per, hi = min(lo + per, E);
     int sum = 0;
     for (int e = lo; e < hi; ++e) sum += (s[e + 1] - s[e] + 1) / 2;
-    part[threadIdx.x] = sum;
-    __syncthreads();
-    for (int off = 1; off < kTopoThreads; off <<= 1) {
-        const int add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-        __syncthreads();
-        part[threadIdx.x] += add;
-        __syncthreads();
-    }
-    int run = part[threadIdx.x] - sum;
+    int total;
+    int run = block_excl_scan<kTopoThreads / kWave>(sum, wsum, total);
     for (int e = lo; e < hi; ++e) {
         pp[e] = run;
         run += (s[e + 1] - s[e] + 1) / 2;
     }
-    if (threadIdx.x == kTopoThreads - 1) pp[E] = part[kTopoThreads - 1];
+    if (threadIdx.x == kTopoThreads - 1) pp[E] = total;
     __syncthreads();
     const int64_t R = s[E];
     const int64_t nnz = R * F;
