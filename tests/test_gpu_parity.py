@@ -480,3 +480,42 @@ def test_two_stream_schedule_gives_the_same_bits(act):
         results.append({n: getattr(L, n).clone() for n in names})
     for n in names:
         assert torch.equal(results[0][n], results[1][n]), n
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_layer_reuse_across_routings(act):
+    """One Layer called on two different routings in turn (A, B, A: other bin
+    sizes, padded row counts and half tiles) gives, call by call, the same bits
+    as a freshly allocated Layer on the same inputs: nothing a previous call
+    left in the reused buffers reaches a result."""
+    from block_sparse_gemm_amd import layer
+    if act == "gelu":
+        cfg = _small("reuse_gelu", T=900, d=256, E=6, f=256, k=2)
+    else:
+        cfg = _small("reuse_swiglu", T=700, d=256, E=4, f=256, k=2, act="swiglu", renorm=True,
+                     yp_dtype="f32")
+    ins = [synth.make_inputs(cfg, seed) for seed in (11, 12)]
+    ins[1]["logits"] = ins[1]["logits"].copy()
+    ins[1]["logits"][:, 0] += 2.0  # expert 0 takes most picks: other bins than routing A
+    s = layer.Shape.of(cfg)
+    names = ["y", "dx", "dW1", "dW2", "dlogits", "dest_row", "bin_offsets"]
+    if act == "swiglu":
+        names.append("dW3")
+
+    def call(L, inp):
+        up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
+        x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
+        L.forward(x, torch.from_numpy(inp["logits"]).cuda(), W1, W2, W3)
+        L.backward(dy, W1, W2, W3)
+        torch.cuda.synchronize()
+        return {n: getattr(L, n).clone() for n in names}
+
+    _say(f"[parity] layer reuse across routings, {act}")
+    shared = layer.Layer(s)
+    order = (0, 1, 0)
+    got = [call(shared, ins[i]) for i in order]
+    want = [call(layer.Layer(s), ins[i]) for i in order]
+    assert not torch.equal(got[0]["bin_offsets"], got[1]["bin_offsets"]), "routings A and B differ"
+    for c, (g, w) in enumerate(zip(got, want)):
+        for n in names:
+            assert torch.equal(g[n], w[n]), f"call {c}: {n}"
