@@ -80,6 +80,32 @@ def products_of(cfg, kernel):
     return 1
 
 
+def algorithmic_bytes(cfg, kernel, Tp, fuse_top1):
+    """HBM bytes one call of a product must move at the least: each operand
+    read once, each result written once (padded rows included, since they are
+    stored).  Sparse planes are (Tp / 128) * F blocks of 128 x 128."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    byp = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
+    sw = cfg.act == "swiglu"
+    plane = (Tp // 128) * (cfg.f // 128) * 128 * 128 * b  # A, a saved factor or dH
+    weight = cfg.d * cfg.E * cfg.f * b                     # W1, W2 or W3
+    rows = Tp * cfg.d * b                                  # Xp or dYp
+    tokens = cfg.T * cfg.d * b                             # y or dx
+    if kernel == "sdd":      # rows, W1 (and W3) in; A (and the saved factors) out
+        saved = (2 if sw else 1) if cfg.backward else 0
+        return rows + weight * (2 if sw else 1) + plane * (1 + saved)
+    if kernel == "dsd":      # A, W2 in; Yp out (and y with the top-1 combine)
+        return plane + weight + Tp * cfg.d * byp + (tokens if fuse_top1 else 0)
+    if kernel == "sdd_bwd":  # dYp, W2, the saved factors in; dH out
+        return rows + weight + 2 * plane * (2 if sw else 1)
+    if kernel == "dsd_bwd":  # dH, W1 (and W3) in; dXp out, or dx with the top-1 combine
+        out = tokens if (fuse_top1 and not sw) else Tp * cfg.d * byp
+        return (plane + weight) * (2 if sw else 1) + out
+    if kernel.startswith("dstd"):  # blocks, dense rows in; a weight gradient out
+        return plane + rows + weight
+    return None
+
+
 def useful_flops(cfg):
     per = 2.0 * cfg.T * cfg.k * cfg.d * cfg.f
     sw = cfg.act == "swiglu"
@@ -302,6 +328,9 @@ def main():
     tflops = total / (step_ms * 1e-3) / 1e12
     achieved = products_of(cfg, dom) * per_product / (dom_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
+    dom_bytes = algorithmic_bytes(cfg, dom, int(L.bin_offsets[-1].item()), L.fuse_top1)
+    intensity = products_of(cfg, dom) * per_product / dom_bytes
+    attainable = min(peak, intensity * HBM_PEAK / 1e3)  # flop/B x GB/s -> TFLOP/s
 
     kernels = {}
     A_n = cfg.T * cfg.k
@@ -358,7 +387,15 @@ def main():
         "tokens_per_s": round(cfg.T / (step_ms * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(cfg.name, dom), "ms": round(dom_ms, 4)},
+                     "traffic": traffic_for(cfg.name, dom), "ms": round(dom_ms, 4),
+                     # the same product against min(peak, intensity x 8 TB/s):
+                     # useful flops per algorithmic HBM byte decide whether
+                     # matrix cores or HBM bound it at this shape
+                     "algorithmic_bytes": dom_bytes,
+                     "intensity_flop_per_byte": round(intensity, 1),
+                     "attainable": round(attainable, 1),
+                     "attainable_bound": "mfma" if attainable >= peak else "hbm",
+                     "frac_of_attainable": round(achieved / attainable, 4)},
         # every call timed alone in a probe pass before the timed steps
         "kernels": kernels,
         "hbm_copy_ceiling": {"bytes": 2 * (half // 2) * 2, "gbps": round(copy_gbps, 1),
