@@ -270,9 +270,13 @@ static bsg::GemmParams gemm_params(const bsg_topology* t) {
     p.F = t->F;
     // Tiles go in groups of row pairs (see the kernel's tile order); a group
     // pays off when its rows share an expert, so it follows the expected row
-    // pairs per expert, Tp_max / (256 E): 1, 2 or at most 4.
+    // pairs per expert, Tp_max / (256 E): 1, 2 or 4, and 8 when the experts
+    // are also few (at most 16), so that long bins are the rule rather than
+    // the few hot experts of a skewed routing: a group of 8 row pairs then
+    // stays inside one expert, and the tiles an XCD runs at once share each
+    // weight panel eight ways instead of four.
     const int64_t rpe = t->Tp_max / (2 * BSG_BLOCK * (int64_t)t->E);
-    p.group = rpe >= 4 ? 4 : rpe >= 2 ? 2 : 1;
+    p.group = (rpe >= 8 && t->E <= 16) ? 8 : rpe >= 4 ? 4 : rpe >= 2 ? 2 : 1;
     return p;
 }
 
