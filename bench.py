@@ -15,13 +15,15 @@ draws resident in HBM before the timed region.
 
 Prints ONE JSON line.  ``value`` is the useful TFLOP/s of the step
 (useful flops = 2 * T * k * d * f per product; 6 products with GeLU
-experts, 9 with SwiGLU ones; padded rows are excluded).  The calls run in order on one stream; ``--overlap`` runs the
-weight gradients on a second stream beside the data-gradient chain instead,
-and ``--compare-schedules`` also times the other schedule after the timed
-steps (context only).  ``roofline`` reports the step's dominant kernel against the bf16 dense MFMA
+experts, 9 with SwiGLU ones; padded rows are excluded).  The backward runs
+the layer's schedule: the weight gradients on a second stream beside the
+data-gradient chain when the products are short (MoE-Small), every call in
+order on one stream otherwise; ``--overlap`` and ``--one-stream`` force
+either, and ``--compare-schedules`` also times the other schedule after the
+timed steps (context only).  ``roofline`` reports the step's dominant kernel against the bf16 dense MFMA
 peak, timed with HIP events on the stream it runs on over the timed steps.
 Which call dominates, and the per-call table ``kernels``, come from a probe
-pass of three steps before the timed ones with every call bracketed by
+pass of three steps on one stream before the timed ones with every call bracketed by
 events; the timed steps record events around the dominant call only, since
 each event costs GPU time (about 4 us a call pair here).  The data-movement
 calls' entries give HBM GB/s from their algorithmic bytes, as a share of the
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="moe_small")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="every call in order on one stream (the layer's choice otherwise)")
     ap.add_argument("--overlap", action="store_true",
                     help="weight gradients on a second stream in the timed steps")
     ap.add_argument("--bin-rows", type=int, default=128, choices=(128, 256),
@@ -201,7 +205,9 @@ def main():
     inp = synth.make_inputs(cfg, 0)
     s = layer.Shape.of(cfg)
     L = layer.Layer(s)
-    L.overlap = args.overlap
+    if args.overlap or args.one_stream:
+        L.overlap = args.overlap
+    two = L.overlap  # the schedule of the timed steps
     up = lambda key: layer.from_numpy(inp[key], cfg.dtype) if key in inp else None
     x, W1, W2, W3, dy = up("x"), up("W1"), up("W2"), up("W3"), up("dy")
     logits = torch.from_numpy(inp["logits"]).cuda()
@@ -231,13 +237,17 @@ def main():
         return {k: float(np.mean(v)) for k, v in per.items()}
 
     # probe: every call timed alone for a few steps (the per-call table, and
-    # which product dominates).  Events cost a few microseconds of GPU time
-    # each, so the timed steps below record them around that product only.
+    # which product dominates), every call in order on one stream so that each
+    # time is the call's own, not shared with a call on the other stream.
+    # Events cost a few microseconds of GPU time each, so the timed steps
+    # below (in the layer's schedule) record them around that product only.
     probe = []
     L.mark = recorder(probe)
+    L.overlap = False
     for _ in range(3):
         L.step(x, logits, W1, W2, W3, dy)
     torch.cuda.synchronize()
+    L.overlap = two
     kern = durations(probe)
     gemms = [k for k in kern if k.startswith(("sdd", "dsd", "dstd"))]
     dom = max(gemms, key=lambda k: kern[k])
@@ -313,7 +323,7 @@ def main():
     # context: the other backward schedule, a few steps after the timed region
     other = None
     if cfg.backward and args.compare_schedules:
-        L.overlap = not args.overlap
+        L.overlap = not two
         for _ in range(args.warmup):
             L.step(x, logits, W1, W2, W3, dy)
         torch.cuda.synchronize()
@@ -322,7 +332,7 @@ def main():
             L.step(x, logits, W1, W2, W3, dy)
         torch.cuda.synchronize()
         other = (time.perf_counter() - t1) * 1e3 / args.steps
-        L.overlap = args.overlap
+        L.overlap = two
 
     per_product, total = useful_flops(cfg)
     tflops = total / (step_ms * 1e-3) / 1e12
@@ -400,11 +410,11 @@ def main():
         "kernels": kernels,
         "hbm_copy_ceiling": {"bytes": 2 * (half // 2) * 2, "gbps": round(copy_gbps, 1),
                              "pct_hbm_peak": round(100 * copy_gbps / HBM_PEAK, 1)},
-        "schedule": "two streams" if args.overlap else "one stream",
+        "schedule": "two streams" if two else "one stream",
     }
     out["step_ms_p10_p50_p90"] = [round(float(v), 4) for v in spread]
     if other is not None:
-        key = "ms_per_step_one_stream" if args.overlap else "ms_per_step_two_streams"
+        key = "ms_per_step_one_stream" if two else "ms_per_step_two_streams"
         out[key] = round(other, 4)
     if dense is not None:
         # the block-sparse product's time against a dense GEMM of its executed

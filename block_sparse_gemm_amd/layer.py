@@ -13,8 +13,8 @@ SwiGLU experts keep silu(g) and u * silu'(g) from the forward; their
 backward product gives the gate and the up projection's gradients (two
 planes of dH), the input gradient is one two-set dsd (dH_gate W1^T +
 dH_up W3^T), and dW1, dW3 are one dstd each.
-With ``overlap`` set the weight gradients run on a second stream, each as
-soon as its inputs exist (dW2 beside the backward SDD product, dW1 (and dW3)
+With ``overlap`` set (the default when the products are short) the weight
+gradients run on a second stream, each as soon as its inputs exist (dW2 beside the backward SDD product, dW1 (and dW3)
 beside the input-gradient product), so the tail of one product's grid and
 the other's fill the GPU together.
 
@@ -71,11 +71,14 @@ class Layer:
         self.mark = None
         # True: the weight gradients run on a second stream beside the
         # data-gradient chain.  Each product's grid covers every CU (one
-        # workgroup per CU), so the second stream only fills grid tails; the
-        # step measured under 1 % shorter and each call's duration then
-        # includes its wait, so the default keeps every call in order on the
-        # caller's stream.
-        self.overlap = False
+        # workgroup per CU), so the second stream only fills grid tails.
+        # That pays when the products are short (at most about 0.4 TFLOP
+        # each, a few hundred microseconds, where the tails are a large
+        # share): the MoE-Small-shaped step measured 1.52 -> 1.49 ms.  With
+        # longer products (the skewed and Mixtral-shaped layers) it measured
+        # no faster, so there every call stays in order on the caller's
+        # stream.  Set it to choose the schedule.
+        self.overlap = s.backward and 2.0 * s.T * s.k * s.d * s.f <= 4e11
         # top-1 bf16 layers: the combine runs in the DSD's epilogue (forward:
         # Yp and y; backward with GeLU experts: dx straight from the product,
         # no dXp)
