@@ -238,6 +238,19 @@ bsg_status bsg_permute_pad_gate_backward(const void* dy, int dtype, int64_t T, i
                       "permute_pad_gate_backward");
 }
 
+// Tiles go in groups of row pairs (see the kernel's tile order); a group
+// pays off when its rows share an expert, so it follows the expected row
+// pairs per expert, Tp_max / (256 E): 1, 2 or 4, and 8 when the experts are
+// also few (at most 16), so that long bins are the rule rather than the few
+// hot experts of a skewed routing: a group of 8 row pairs then stays inside
+// one expert, and the tiles an XCD runs at once share each weight panel
+// eight ways instead of four.  The topology builder cuts each expert's row
+// pairs into groups of at most this many.
+static int tile_group(int64_t Tp_max, int E) {
+    const int64_t rpe = Tp_max / (2 * BSG_BLOCK * (int64_t)E);
+    return (rpe >= 8 && E <= 16) ? 8 : rpe >= 4 ? 4 : rpe >= 2 ? 2 : 1;
+}
+
 bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
                               const bsg_topology* topo, bsg_stream_t stream) {
     REQUIRE_PTR(bin_offsets);
@@ -252,7 +265,7 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
                                    row_pairs_max(Tp_max / BSG_BLOCK, E), topo->row_ptr,
                                    topo->col_idx, topo->row_idx, topo->col_ptr, topo->trans_idx,
                                    topo->row_pairs, topo->expert_order, topo->meta,
-                                   (hipStream_t)stream),
+                                   tile_group(Tp_max, E), (hipStream_t)stream),
         "build_topology");
 }
 
@@ -268,15 +281,7 @@ static bsg::GemmParams gemm_params(const bsg_topology* t) {
     p.meta = t->meta;
     p.E = t->E;
     p.F = t->F;
-    // Tiles go in groups of row pairs (see the kernel's tile order); a group
-    // pays off when its rows share an expert, so it follows the expected row
-    // pairs per expert, Tp_max / (256 E): 1, 2 or 4, and 8 when the experts
-    // are also few (at most 16), so that long bins are the rule rather than
-    // the few hot experts of a skewed routing: a group of 8 row pairs then
-    // stays inside one expert, and the tiles an XCD runs at once share each
-    // weight panel eight ways instead of four.
-    const int64_t rpe = t->Tp_max / (2 * BSG_BLOCK * (int64_t)t->E);
-    p.group = (rpe >= 8 && t->E <= 16) ? 8 : rpe >= 4 ? 4 : rpe >= 2 ? 2 : 1;
+    p.group = tile_group(t->Tp_max, t->E);
     return p;
 }
 

@@ -238,6 +238,25 @@ __device__ __forceinline__ void load4(const char* src, float* v) {
     }
 }
 
+// SDD / DSD tile order.  The topology cuts each expert's row pairs into
+// groups of a few (row_pairs entry bits 1-3: the row pair's place in its
+// group, bits 4-6: the group's size - 1), so a group never spans two
+// experts.  A group's tiles have consecutive ids, down its row pairs first:
+// the tiles an XCD runs at once cover a few row pairs of one expert x a few
+// column tiles and share both operands' panels.  Tile t lies in the group of
+// row pair t / tn, since the groups before it hold exactly its first row
+// pair's count of row pairs.
+__device__ __forceinline__ void row_pair_tile(const int32_t* __restrict__ row_pairs, int tile,
+                                              int tn, int& tm, int& tq) {
+    const int p0 = tile / tn;
+    const int ent = row_pairs[p0];
+    const int first = p0 - ((ent >> 1) & 7);
+    const int size = ((ent >> 4) & 7) + 1;
+    const int local = tile - first * tn;
+    tq = local / size;
+    tm = first + local % size;
+}
+
 // Indices of one K-block for both M halves.
 struct KIdx {
     int b0, b1;  // block of M half 0 / 1
@@ -291,8 +310,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
         grouped_tile(tile - rank * per_e, cpe, tn, P.group, j, tq);
         tm = P.expert_order[rank] * cpe + j;
     } else {
-        const int tile = xcd_remap(blockIdx.x, ntiles);
-        grouped_tile(tile, ntiles / tn, tn, P.group, tm, tq);
+        row_pair_tile(P.row_pairs, xcd_remap(blockIdx.x, ntiles), tn, tm, tq);
     }
 
     // the wave index is uniform: keep it (and every LDS stage address derived
@@ -313,7 +331,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
         m1 = 2 * j + 1 < F;
     } else {
         const int ent = P.row_pairs[tm];
-        mrow0 = ent >> 1;
+        mrow0 = ent >> 7;
         m1 = (ent & 1) != 0;
     }
     mrow1 = m1 ? mrow0 + 1 : mrow0;  // an absent half mirrors half 0 (loaded, never stored)
@@ -897,7 +915,7 @@ __device__ __forceinline__ bool half_tile(const GemmParams& P) {
     const int ntiles = P.meta[3] * tn;
     if ((int)blockIdx.x >= ntiles) return false;
     int tm, tq;
-    grouped_tile(xcd_remap(blockIdx.x, ntiles), ntiles / tn, tn, P.group, tm, tq);
+    row_pair_tile(P.row_pairs, xcd_remap(blockIdx.x, ntiles), tn, tm, tq);
     return __builtin_amdgcn_readfirstlane(P.row_pairs[tm] & 1) == 0;
 }
 

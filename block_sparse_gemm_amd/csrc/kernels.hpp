@@ -93,7 +93,7 @@ hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64
                                  int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
                                  int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
                                  int32_t* row_pairs, int32_t* expert_order, int32_t* meta,
-                                 hipStream_t stream);
+                                 int group, hipStream_t stream);
 
 hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int epi, int dtype,
                       hipStream_t s);

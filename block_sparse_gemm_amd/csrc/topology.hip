@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ row_idx,
     int32_t* __restrict__ col_ptr, int32_t* __restrict__ trans_idx,
     int32_t* __restrict__ row_pairs, int32_t* __restrict__ expert_order,
-    int32_t* __restrict__ meta) {
+    int32_t* __restrict__ meta, int group) {
     __shared__ int s[kMaxExperts + 1];   // bin start in row blocks
     __shared__ int pp[kMaxExperts + 1];  // first row pair of each expert
     __shared__ int wsum[kTopoThreads / kWave];
@@ -101,11 +101,16 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
         meta[3] = pp[E];
     }
     if (g < pp[E]) {
+        // the expert's row pairs go in groups of `group` (the last one
+        // shorter): the products take a group's tiles together
         const int e = owner_of(pp, E, g);
         const int j = (int)(g - pp[e]);
         const int Re = s[e + 1] - s[e];
         const int r0 = s[e] + 2 * j;
-        row_pairs[g] = (r0 << 1) | (2 * j + 1 < Re ? 1 : 0);
+        const int npairs = pp[e + 1] - pp[e];
+        const int off = j % group;
+        const int size = min(group, npairs - (j - off));
+        row_pairs[g] = (r0 << 7) | ((size - 1) << 4) | (off << 1) | (2 * j + 1 < Re ? 1 : 0);
     }
     // BCSR block pointer: every non-empty row block holds F blocks
     if (g <= row_blocks_max) row_ptr[g] = (int32_t)((g < R ? g : R) * F);
@@ -136,7 +141,7 @@ hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64
                                  int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
                                  int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
                                  int32_t* row_pairs, int32_t* expert_order, int32_t* meta,
-                                 hipStream_t stream) {
+                                 int group, hipStream_t stream) {
     int64_t n = row_blocks_max * F;
     if (row_pairs_max > n) n = row_pairs_max;
     if (row_blocks_max + 1 > n) n = row_blocks_max + 1;
@@ -145,7 +150,7 @@ hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64
     const int grid = (int)((n + kTopoThreads - 1) / kTopoThreads);
     hipLaunchKernelGGL(build_topology_kernel, dim3(grid), dim3(kTopoThreads), 0, stream,
                        bin_offsets, E, F, row_blocks_max, row_ptr, col_idx, row_idx, col_ptr,
-                       trans_idx, row_pairs, expert_order, meta);
+                       trans_idx, row_pairs, expert_order, meta, group);
     return hipGetLastError();
 }
 

@@ -95,7 +95,11 @@ typedef struct {
  *   row_pairs [row_pairs_max] the schedule of the products: consecutive
  *                        block rows of one expert taken two at a time
  *                        (a last single row when the expert has an odd
- *                        number); entry = (first row << 1) | (pair ? 1 : 0)
+ *                        number), each expert's pairs cut into groups of
+ *                        G = 1, 2, 4 or 8 (the last one shorter), G set
+ *                        from Tp_max and E; entry = (first row << 7) |
+ *                        ((group size - 1) << 4) | (place in the group
+ *                        << 1) | (pair ? 1 : 0)
  *   expert_order [E]     the experts in descending order of their row
  *                        blocks (ties: lower id first), the order in which
  *                        dstd schedules its tiles (longest first)

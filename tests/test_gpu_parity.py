@@ -135,12 +135,20 @@ def check_case(orc, case: Case, seed=0):
     for key in ("col_idx", "row_idx", "trans_idx"):
         assert np.array_equal(getattr(L.topo, key)[:nnz].cpu().numpy(), t[key]), key
     assert np.array_equal(L.topo.col_ptr.cpu().numpy(), t["col_ptr"]), "col_ptr"
-    # the products' schedule: each expert's block rows two at a time
+    # the products' schedule: each expert's block rows two at a time, the
+    # pairs in groups of G (from Tp_max and E), each entry with its place in
+    # its group and the group's size
+    rpe = L.Tp_max // (256 * cfg.E)
+    G = 8 if (rpe >= 8 and cfg.E <= 16) else 4 if rpe >= 4 else 2 if rpe >= 2 else 1
     want_pairs = []
     for e in range(cfg.E):
         s0, s1 = r["bin_offsets"][e] // 128, r["bin_offsets"][e + 1] // 128
-        for r0 in range(s0, s1, 2):
-            want_pairs.append((r0 << 1) | (1 if r0 + 1 < s1 else 0))
+        starts = list(range(s0, s1, 2))
+        for j, r0 in enumerate(starts):
+            off = j % G
+            size = min(G, len(starts) - (j - off))
+            want_pairs.append((r0 << 7) | ((size - 1) << 4) | (off << 1)
+                              | (1 if r0 + 1 < s1 else 0))
     assert meta[3] == len(want_pairs)
     assert L.topo.row_pairs[:len(want_pairs)].cpu().numpy().tolist() == want_pairs
     # the weight-gradient schedule: experts by descending row blocks, ties to
