@@ -63,7 +63,8 @@ struct GemmParams {
     int N;                // DSD / DSTD output width
     int ntn;              // 256-wide output tiles along N
     int E, F;             // experts, column blocks per expert
-    int group;            // rows per group of the tile order (>= 1)
+    int group;            // DSTD: column pairs per group of an expert's tiles (>= 1); SDD and
+                          // DSD take their groups from row_pairs
 };
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
