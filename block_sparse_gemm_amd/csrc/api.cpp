@@ -65,6 +65,24 @@ bsg_status check_topology(const bsg_topology* t) {
     return BSG_OK;
 }
 
+// The products address an operand panel's rows through 32-bit per-lane
+// byte offsets from the panel's origin (the largest: row 127 of a panel
+// whose rows are contiguous along K, or K-row 31 (bf16) / 15 (fp32) of a
+// panel whose rows are contiguous along M or N).  A leading dimension whose
+// largest offset does not fit is refused rather than wrapped.
+bool panel_ld_fits(int64_t ld, int es, bool k_contiguous) {
+    const int64_t last_row = k_contiguous ? 127 : (es == 2 ? 31 : 15);
+    const int64_t row_bytes = k_contiguous ? 64 : 256 * (es == 2 ? 1 : 2);
+    return last_row * ld * es + row_bytes <= (int64_t)UINT32_MAX;
+}
+
+#define REQUIRE_PANEL_LD(ld, es, kc)                                                       \
+    do {                                                                                   \
+        if (!panel_ld_fits((ld), (es), (kc)))                                              \
+            return fail(BSG_EUNSUPPORTED, #ld " = %lld is too large for the products' "    \
+                        "32-bit panel offsets", (long long)(ld));                          \
+    } while (0)
+
 int64_t row_pairs_max(int64_t row_blocks_max, int E) {
     const int64_t ne = E < row_blocks_max ? E : row_blocks_max;
     return (row_blocks_max + ne + 1) / 2;
@@ -301,6 +319,8 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
     REQUIRE(ldb >= (trans_b ? K : ncol) && (ldb * es) % 16 == 0,
             "ldb too small or rows not 16-byte aligned");
+    REQUIRE_PANEL_LD(lda, es, true);
+    REQUIRE_PANEL_LD(ldb, es, trans_b == 1);
     REQUIRE_VEC_PTR(a);
     REQUIRE_VEC_PTR(b);
     REQUIRE_VEC_PTR(out_blocks);
@@ -346,6 +366,7 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
     REQUIRE(ldb >= (trans_b ? ncol : N) && (ldb * es) % 16 == 0,
             "ldb too small or rows not 16-byte aligned");
     REQUIRE(ldc >= N && (ldc * ces) % 16 == 0, "ldc must be >= N with 16-byte aligned rows");
+    REQUIRE_PANEL_LD(ldb, es, trans_b == 1);
     REQUIRE_VEC_PTR(blocks);
     REQUIRE_VEC_PTR(b);
     REQUIRE_VEC_PTR(c);
@@ -384,6 +405,7 @@ bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, co
     REQUIRE(ldb >= (trans_b ? ncol : N) && (ldb * 2) % 16 == 0,
             "ldb too small or rows not 16-byte aligned");
     REQUIRE(ldy >= N && (ldy * 2) % 16 == 0, "ldy must be >= N with 16-byte aligned rows");
+    REQUIRE_PANEL_LD(ldb, 2, trans_b == 1);
     REQUIRE_VEC_PTR(blocks);
     REQUIRE_VEC_PTR(b);
     REQUIRE_VEC_PTR(y);
@@ -422,6 +444,7 @@ bsg_status bsg_dstd(const void* blocks, const bsg_topology* topo, const void* dm
     REQUIRE(ldd >= N && (ldd * es) % 16 == 0, "ldd must be >= N with 16-byte aligned rows");
     REQUIRE(ldc >= (trans_c ? ncol : N) && (ldc * es) % 16 == 0,
             "ldc too small or rows not 16-byte aligned");
+    REQUIRE_PANEL_LD(ldd, es, false);
     REQUIRE_VEC_PTR(blocks);
     REQUIRE_VEC_PTR(dmat);
     REQUIRE_VEC_PTR(c);

@@ -20,7 +20,12 @@
  *  - Arrays of activations, weights and blocks are moved with 16-byte
  *    vectors and must be 16-byte aligned; index, count and gate arrays
  *    must be 4-byte aligned.  Leading dimensions are in elements and must
- *    keep every row 16-byte aligned.
+ *    keep every row 16-byte aligned.  The products (sdd, dsd, dstd) reach
+ *    the rows of an operand panel through 32-bit byte offsets from the
+ *    panel's first row: a dense operand's leading dimension must keep
+ *    127 * ld * elt + 64 (rows contiguous along K) or 31 * ld * 2 + 256
+ *    (bf16) / 15 * ld * 4 + 512 (fp32) (rows contiguous along M or N)
+ *    below 2^32, else BSG_EUNSUPPORTED.
  *  - Arguments are validated BEFORE any HIP call.  An invalid argument
  *    returns BSG_EINVAL, a valid but unimplemented combination
  *    BSG_EUNSUPPORTED, a failed launch BSG_EHIP; bsg_last_error() then
@@ -137,10 +142,15 @@ typedef struct {
  * invalid sizes or an unsupported bin_rows. */
 int64_t bsg_max_padded_rows(int64_t T, int k, int E, int bin_rows);
 
-/* Capacities of the topology arrays for Tp_max padded rows. */
+/* Capacities of the topology arrays for Tp_max padded rows.  A host-side
+ * helper for sizing the caller's buffers; the pages define no such call
+ * (the capacities follow from the block grid of section 1.3: Tp_max/128
+ * row blocks of F blocks each, E*F column blocks). */
 bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out /* host */);
 
-/* Bytes of device workspace bsg_route needs (0 on invalid sizes). */
+/* Bytes of device workspace bsg_route needs (0 on invalid sizes): per-chunk
+ * expert counts of the deterministic placement (64 tokens a chunk).  A
+ * host-side helper the pages do not define. */
 size_t bsg_route_workspace_bytes(int64_t T, int k, int E);
 
 /* ------------------------------------------------------------------ calls */

@@ -279,3 +279,33 @@ def test_status_strings(L):
     assert L.bsg_status_string(-2) == b"unsupported combination"
     assert L.bsg_status_string(-3) == b"HIP runtime error"
     assert L.bsg_status_string(7) == b"unknown status"
+
+
+def test_leading_dimensions_beyond_32bit_panel_offsets(L):
+    """The products reach a panel's rows through 32-bit byte offsets: a
+    leading dimension whose last panel row lies 4 GiB or more past the
+    panel's origin is refused, not wrapped (bf16: row 127 of a K-contiguous
+    panel, K-row 31 of a panel contiguous along M or N)."""
+    t = fake_topo(E=4, f=256)
+    kc = 16909320    # 127 * kc * 2 + 64 > 2^32 - 1 (the largest accepted is 16909312)
+    km = 69273664    # 31 * km * 2 + 256 > 2^32 - 1 (the largest accepted is 69273656)
+    assert 127 * (kc - 8) * 2 + 64 <= 2**32 - 1 < 127 * kc * 2 + 64
+    assert 31 * (km - 8) * 2 + 256 <= 2**32 - 1 < 31 * km * 2 + 256
+
+    def sdd(lda=256, ldb=1024, trans_b=0):
+        return L.bsg_sdd(P, lda, P, None, ldb, trans_b, 256, C.byref(t), bsg.EPI_GELU, None, P,
+                         None, bsg.BF16, None)
+
+    assert sdd(lda=kc) == bsg.EUNSUPPORTED and "32-bit" in _err(L)
+    assert sdd(ldb=km) == bsg.EUNSUPPORTED
+    assert sdd(ldb=kc, trans_b=1) == bsg.EUNSUPPORTED
+
+    def dsd(ldb, trans_b):
+        return L.bsg_dsd(P, None, C.byref(t), P, None, ldb, trans_b, 256, P, 256, bsg.BF16,
+                         bsg.BF16, None)
+
+    assert dsd(km, 0) == bsg.EUNSUPPORTED
+    assert dsd(kc, 1) == bsg.EUNSUPPORTED
+    assert L.bsg_dsd_combine_top1(P, C.byref(t), P, kc, 1, 256, P, 256, P, None, P, 256,
+                                  bsg.BF16, None) == bsg.EUNSUPPORTED
+    assert L.bsg_dstd(P, C.byref(t), P, km, 256, P, 256, 0, bsg.BF16, None) == bsg.EUNSUPPORTED
