@@ -655,11 +655,22 @@ int orc_dW2_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
     if (!layer_ok(L) || !L->dy || !rows || !cols || !out) return -1;
     const int64_t ldw = (int64_t)L->E * L->f;
     int bad = 0;
+    for (int64_t s = 0; s < nc; ++s)
+        if (cols[s] < 0 || cols[s] >= L->d) bad = 1;
+    if (bad) return -1;
+    /* Each thread takes a contiguous range of rows, so consecutive rows of
+     * one expert share its assignment list and its rounded dYp values
+     * (computed once per expert when they fit the cache budget below); the
+     * sums themselves are the same, term for term, as per entry. */
 #pragma omp parallel
     {
         int64_t* as = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L->T * L->k));
         double* an = dalloc(L->T * L->k);
-#pragma omp for schedule(dynamic, 1)
+        double* acc = dalloc(nc);
+        double* dyp = NULL;
+        int cur_e = -1;
+        int64_t c = 0;
+#pragma omp for schedule(static)
         for (int64_t p = 0; p < nr; ++p) {
             int64_t row = rows[p];
             if (row < 0 || row >= ldw) {
@@ -667,29 +678,41 @@ int orc_dW2_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
                 continue;
             }
             int e = (int)(row / L->f);
-            int64_t c = expert_assignments(L, e, as);
+            if (e != cur_e) {
+                cur_e = e;
+                c = expert_assignments(L, e, as);
+                free(dyp);
+                dyp = c * nc <= ((int64_t)1 << 24) ? dalloc(c * nc) : NULL;
+                if (dyp)
+                    for (int64_t q = 0; q < c; ++q)
+                        for (int64_t s = 0; s < nc; ++s)
+                            dyp[q * nc + s] = rd((double)L->gate[as[q]] *
+                                                     (double)L->dy[(as[q] / L->k) * L->d + cols[s]],
+                                                 L->prec);
+            }
             /* A_a[n] for every assignment of the expert */
             for (int64_t q = 0; q < c; ++q) {
                 double h, u;
                 hidden_unit(L, as[q], row, &h, &u);
                 an[q] = rd(L->act == ORC_ACT_SWIGLU ? silu(h) * u : gelu(h), L->prec);
             }
-            for (int64_t s = 0; s < nc; ++s) {
-                int64_t m = cols[s];
-                if (m < 0 || m >= L->d) {
-                    bad = 1;
-                    continue;
+            /* every entry's sum runs over q ascending; the entries of the
+             * row are accumulated side by side */
+            for (int64_t s = 0; s < nc; ++s) acc[s] = 0.0;
+            for (int64_t q = 0; q < c; ++q) {
+                const int64_t a = as[q];
+                for (int64_t s = 0; s < nc; ++s) {
+                    const double g = dyp ? dyp[q * nc + s]
+                                         : rd((double)L->gate[a] *
+                                                  (double)L->dy[(a / L->k) * L->d + cols[s]],
+                                              L->prec);
+                    acc[s] += an[q] * g;
                 }
-                double acc = 0.0;
-                for (int64_t q = 0; q < c; ++q) {
-                    int64_t a = as[q];
-                    double dyp = rd((double)L->gate[a] * (double)L->dy[(a / L->k) * L->d + m],
-                                    L->prec);
-                    acc += an[q] * dyp;
-                }
-                out[p * nc + s] = rd(acc, L->prec);
             }
+            for (int64_t s = 0; s < nc; ++s) out[p * nc + s] = rd(acc[s], L->prec);
         }
+        free(acc);
+        free(dyp);
         free(as);
         free(an);
     }
@@ -712,11 +735,22 @@ static int input_weight_grad(const orc_layer* L, int proj, const int64_t* rows, 
     const int64_t ldw = (int64_t)L->E * L->f;
     const int sw = L->act == ORC_ACT_SWIGLU;
     int bad = 0;
+    for (int64_t p = 0; p < nr; ++p)
+        if (rows[p] < 0 || rows[p] >= L->d) bad = 1;
+    if (bad) return -1;
+    /* Contiguous column ranges per thread: consecutive hidden units of one
+     * expert share its assignment list and its rounded dYp rows (kept once
+     * per expert when they fit the cache budget below); every sum is the
+     * same, term for term, as per entry. */
 #pragma omp parallel
     {
         int64_t* as = (int64_t*)malloc(sizeof(int64_t) * (size_t)(L->T * L->k));
         double* dh = dalloc(L->T * L->k);
-#pragma omp for schedule(dynamic, 1)
+        double* acc = dalloc(nr);
+        double* dyp = NULL;
+        int cur_e = -1;
+        int64_t c = 0;
+#pragma omp for schedule(static)
         for (int64_t s = 0; s < nc; ++s) {
             int64_t col = cols[s];
             if (col < 0 || col >= ldw) {
@@ -724,7 +758,18 @@ static int input_weight_grad(const orc_layer* L, int proj, const int64_t* rows, 
                 continue;
             }
             int e = (int)(col / L->f);
-            int64_t c = expert_assignments(L, e, as);
+            if (e != cur_e) {
+                cur_e = e;
+                c = expert_assignments(L, e, as);
+                free(dyp);
+                dyp = c * L->d <= ((int64_t)1 << 24) ? dalloc(c * L->d) : NULL;
+                if (dyp)
+                    for (int64_t q = 0; q < c; ++q)
+                        for (int m = 0; m < L->d; ++m)
+                            dyp[q * L->d + m] = rd((double)L->gate[as[q]] *
+                                                       (double)L->dy[(as[q] / L->k) * L->d + m],
+                                                   L->prec);
+            }
             const float* w2 = L->W2 + col * L->d;
             for (int64_t q = 0; q < c; ++q) {
                 int64_t a = as[q];
@@ -733,8 +778,9 @@ static int input_weight_grad(const orc_layer* L, int proj, const int64_t* rows, 
                 hidden_unit(L, a, col, &h, &u);
                 double da = 0.0;
                 for (int m = 0; m < L->d; ++m) {
-                    double dyp = rd((double)L->gate[a] * (double)L->dy[t * L->d + m], L->prec);
-                    da += dyp * (double)w2[m];
+                    const double g = dyp ? dyp[q * L->d + m]
+                                         : rd((double)L->gate[a] * (double)L->dy[t * L->d + m], L->prec);
+                    da += g * (double)w2[m];
                 }
                 double saved;
                 if (!sw) saved = gelu_grad(h);
@@ -742,18 +788,17 @@ static int input_weight_grad(const orc_layer* L, int proj, const int64_t* rows, 
                 else saved = silu(h);
                 dh[q] = rd(da * rd(saved, L->prec), L->prec);
             }
-            for (int64_t p = 0; p < nr; ++p) {
-                int64_t i = rows[p];
-                if (i < 0 || i >= L->d) {
-                    bad = 1;
-                    continue;
-                }
-                double acc = 0.0;
-                for (int64_t q = 0; q < c; ++q)
-                    acc += (double)L->x[(as[q] / L->k) * L->d + i] * dh[q];
-                out[p * nc + s] = rd(acc, L->prec);
+            /* every entry's sum runs over q ascending; the entries of the
+             * column are accumulated side by side */
+            for (int64_t p = 0; p < nr; ++p) acc[p] = 0.0;
+            for (int64_t q = 0; q < c; ++q) {
+                const float* xr = L->x + (as[q] / L->k) * L->d;
+                for (int64_t p = 0; p < nr; ++p) acc[p] += (double)xr[rows[p]] * dh[q];
             }
+            for (int64_t p = 0; p < nr; ++p) out[p * nc + s] = rd(acc[p], L->prec);
         }
+        free(acc);
+        free(dyp);
         free(as);
         free(dh);
     }
