@@ -325,6 +325,62 @@ def _edge_cases():
 EDGE = _edge_cases()
 
 
+def _picks_logits(T, E, k, counts, seed):
+    """Logits under which expert e receives exactly counts[e] of the T*k
+    picks (every count at most T), each token k distinct experts, tokens in
+    a seeded random order; the picks' logits are 8 - 2 j (+ noise) for slot
+    j, every other logit lies in [-1, 1)."""
+    counts = np.asarray(counts)
+    assert counts.sum() == T * k and counts.max() <= T
+    rng = np.random.default_rng(seed)
+    flat = np.repeat(np.arange(E), counts)          # runs of at most T entries
+    picks = flat.reshape(k, T).T                    # token t: flat[t], flat[t + T], ...
+    picks = picks[rng.permutation(T)]
+    lg = rng.uniform(-1.0, 1.0, size=(T, E)).astype(np.float32)
+    for j in range(k):
+        lg[np.arange(T), picks[:, j]] = 8.0 - 2.0 * j + rng.uniform(0, 0.5, T)
+    return np.ascontiguousarray(lg)
+
+
+# Tile groups of 4 and 8 row pairs (set from Tp_max and E), compared element
+# by element: every expert ends in a half tile or a short last group (or
+# both), and the DSTD column-pair groups hold fewer pairs than G at the end.
+GROUPS = {
+    # Tp_max 4480, E 4: G = 4.  Block rows 15, 11, 6, 3: groups 4+4 (half at
+    # the end), 4+2 (half), 3, 2 (half); F = 9 (column-pair groups 4+1, a
+    # single last column); d = 384 (an absent N half)
+    "group4_gelu": (_small("group4_gelu", T=4096, d=384, E=4, f=1152, k=1),
+                    [1800, 1300, 700, 296], 4),
+    # Tp_max 8576, E 4: G = 8.  Block rows 27, 19, 13, 7 (all odd): groups
+    # 8+6, 8+2, 7, 4, each ending in a half tile; F = 17
+    "group8_gelu": (_small("group8_gelu", T=8192, d=256, E=4, f=2176, k=1),
+                    [3400, 2400, 1600, 792], 8),
+    # SwiGLU trained, top-2: Tp_max 16768, E 4: G = 8.  Block rows 47, 35,
+    # 28, 20: groups 8+8+8 (half), 8+8+2 (half), 8+6, 8+2; the two-set DSD
+    # and three DSTDs; F = 9
+    "group8_swiglu_train": (_small("group8_swiglu_train", T=8192, d=128, E=4, f=1152, k=2,
+                                   act="swiglu", renorm=True, yp_dtype="f32"),
+                            [6000, 4400, 3500, 2484], 8),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUPS))
+def test_tile_groups_full(orc, name):
+    """The products' tile schedule at groups of 4 and 8 row pairs, every
+    output element against the oracle (forward and backward)."""
+    from block_sparse_gemm_amd import bsg
+    cfg, counts, G = GROUPS[name]
+    Tp_max = bsg.max_padded_rows(cfg.T, cfg.k, cfg.E)
+    rpe = Tp_max // (256 * cfg.E)
+    assert (8 if (rpe >= 8 and cfg.E <= 16) else 4 if rpe >= 4 else 2) == G
+    blocks = [-(-c // 128) for c in counts]
+    assert any(b % 2 for b in blocks)                       # half tiles
+    assert any(((b + 1) // 2) % G for b in blocks)          # short last groups
+    lg = _picks_logits(cfg.T, cfg.E, cfg.k, counts, seed=31)
+    L, _, _ = check_case(orc, Case(cfg, logits=lg))
+    assert L.counts.cpu().numpy().tolist() == list(counts)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small(orc, name):
     check_case(orc, SMALL[name])
