@@ -22,12 +22,14 @@ EPI_NONE, EPI_GELU, EPI_SILU_MUL, EPI_GELU_BWD, EPI_SILU_MUL_BWD = 0, 1, 2, 3, 4
 BLOCK = 128
 MAX_EXPERTS = 1024
 MAX_TOPK = 32
+ROUTE_SCRATCH_BYTES = 4 << 20   # BSG_ROUTE_SCRATCH_BYTES
 
 EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
              "gelu_bwd": EPI_GELU_BWD, "silu_mul_bwd": EPI_SILU_MUL_BWD}
 
 # Every symbol include/bsg.h declares.
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
+           "bsg_route_noalloc",
            "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
            "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_status_string", "bsg_last_error")
@@ -70,6 +72,8 @@ def lib():
         L.bsg_route_workspace_bytes.argtypes = [i64, i32, i32]
         L.bsg_route.restype = i32
         L.bsg_route.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.bsg_route_noalloc.restype = i32
+        L.bsg_route_noalloc.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.bsg_route_backward.restype = i32
         L.bsg_route_backward.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32,
                                          i64, vp, vp]
@@ -188,6 +192,14 @@ def route(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets, wo
                                     _ptr(gate), _ptr(dest_row), _ptr(counts), _ptr(bin_offsets),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream()))
+
+
+def route_noalloc(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets,
+                  bin_rows=BLOCK):
+    T, E = logits.shape
+    _check("route_noalloc", lib().bsg_route_noalloc(
+        _ptr(logits), T, E, k, int(bool(renorm)), bin_rows, _ptr(expert_idx), _ptr(gate),
+        _ptr(dest_row), _ptr(counts), _ptr(bin_offsets), _stream()))
 
 
 def route_backward(logits, k, renorm, expert_idx, dest_row, dy, yp, dlogits):

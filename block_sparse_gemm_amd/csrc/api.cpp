@@ -9,6 +9,8 @@
 
 #include "kernels.hpp"
 
+static_assert(bsg::kRouteScratchBytes == BSG_ROUTE_SCRATCH_BYTES, "one scratch size");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -140,10 +142,9 @@ static bsg_status check_bin(int bin_rows) {
     return BSG_OK;
 }
 
-bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
-                     int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
-                     int32_t* bin_offsets, void* workspace, size_t workspace_bytes,
-                     bsg_stream_t stream) {
+static bsg_status check_route(const float* logits, int64_t T, int E, int k, int bin_rows,
+                              int32_t* expert_idx, float* gate, int32_t* dest_row,
+                              int32_t* counts, int32_t* bin_offsets) {
     const bsg_status bs = check_bin(bin_rows);
     if (bs != BSG_OK) return bs;
     REQUIRE(T >= 1, "T must be positive");
@@ -158,6 +159,16 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, i
     REQUIRE_PTR(dest_row);
     REQUIRE_PTR(counts);
     REQUIRE_PTR(bin_offsets);
+    return BSG_OK;
+}
+
+bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
+                     int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
+                     int32_t* bin_offsets, void* workspace, size_t workspace_bytes,
+                     bsg_stream_t stream) {
+    const bsg_status s =
+        check_route(logits, T, E, k, bin_rows, expert_idx, gate, dest_row, counts, bin_offsets);
+    if (s != BSG_OK) return s;
     REQUIRE_PTR(workspace);
     REQUIRE(workspace_bytes >= bsg_route_workspace_bytes(T, k, E), "workspace too small (%zu < %zu)",
             workspace_bytes, bsg_route_workspace_bytes(T, k, E));
@@ -165,6 +176,26 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, i
                                         counts, bin_offsets, (int32_t*)workspace,
                                         (hipStream_t)stream),
                       "route");
+}
+
+bsg_status bsg_route_noalloc(const float* logits, int64_t T, int E, int k, int renorm,
+                             int bin_rows, int32_t* expert_idx, float* gate, int32_t* dest_row,
+                             int32_t* counts, int32_t* bin_offsets, bsg_stream_t stream) {
+    const bsg_status s =
+        check_route(logits, T, E, k, bin_rows, expert_idx, gate, dest_row, counts, bin_offsets);
+    if (s != BSG_OK) return s;
+    const size_t need = bsg_route_workspace_bytes(T, k, E);
+    if (need > BSG_ROUTE_SCRATCH_BYTES)
+        return fail(BSG_EUNSUPPORTED,
+                    "route_noalloc needs %zu bytes of scratch (ceil(T/64) * E * 4), above its "
+                    "static %zu bytes; call bsg_route with a workspace",
+                    need, (size_t)BSG_ROUTE_SCRATCH_BYTES);
+    int32_t* scratch = nullptr;
+    const hipError_t e = bsg::route_scratch((hipStream_t)stream, &scratch);
+    if (e != hipSuccess) return hip_status(e, "route_noalloc scratch");
+    return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
+                                        counts, bin_offsets, scratch, (hipStream_t)stream),
+                      "route_noalloc");
 }
 
 bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int renorm,

@@ -67,6 +67,13 @@ struct GemmParams {
                           // DSD take their groups from row_pairs
 };
 
+// Bytes of the file-scope device array behind the allocation-free routing
+// entry point (per GPU): 4 MiB, one count per (64-token chunk, expert).
+constexpr size_t kRouteScratchBytes = size_t(4) << 20;
+
+// That array's address on the device of `stream` (looked up once per device).
+hipError_t route_scratch(hipStream_t stream, int32_t** out);
+
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, hipStream_t stream);

@@ -21,11 +21,46 @@
 //                     rank of each assignment among the chunk's earlier
 //                     assignments to the same expert, found with wave64
 //                     ballots on the expert id bits.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "scan.hpp"
 
 namespace bsg {
+
+// Device memory of the allocation-free routing entry point: the per-chunk
+// expert counts that bsg_route keeps in the caller's workspace.  One copy
+// per GPU, held until the process ends; its host-side name is no device
+// address, so host code uses only the address hipGetSymbolAddress returns
+// for the device (route_scratch below).
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+hipError_t route_scratch(hipStream_t stream, int32_t** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    // the null stream runs on the current device
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // once per device, with that device current
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (back != hipSuccess) return back;
+        addr[dev] = p;
+    }
+    *out = (int32_t*)addr[dev];
+    return hipSuccess;
+}
 
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / kWave;

@@ -13,7 +13,8 @@
  * --------------------------------
  *  - Every array argument is a DEVICE pointer unless stated otherwise,
  *    allocated and freed by the caller; the library never allocates, frees,
- *    synchronises the host or keeps global mutable state.
+ *    synchronises the host or keeps global mutable state (one exception:
+ *    the static device array of bsg_route_noalloc).
  *  - Every kernel is enqueued on `stream` (a hipStream_t; NULL means the
  *    null stream) and runs asynchronously; results are valid once the
  *    stream has reached them.
@@ -178,6 +179,27 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, i
                      int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                      int32_t* bin_offsets, void* workspace, size_t workspace_bytes,
                      bsg_stream_t stream);
+
+/*
+ * route_noalloc - bsg_route for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, with the
+ * per-chunk expert counts kept in a file-scope device array of the library
+ * (BSG_ROUTE_SCRATCH_BYTES per GPU, held until the process ends) instead
+ * of a caller workspace.  The call allocates and frees nothing.  Arguments,
+ * outputs and limits as bsg_route; in addition
+ * bsg_route_workspace_bytes(T, k, E) must not exceed BSG_ROUTE_SCRATCH_BYTES
+ * (ceil(T/64) * E <= 1M, e.g. T = 65536 with E = 1024), else
+ * BSG_EUNSUPPORTED.  The array's address on the stream's device is looked
+ * up on the first call there (BSG_EHIP if that fails).  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  Nothing
+ * in the array needs clearing: each call writes every count it reads.
+ */
+#define BSG_ROUTE_SCRATCH_BYTES (4u << 20)
+bsg_status bsg_route_noalloc(const float* logits, int64_t T, int E, int k, int renorm,
+                             int bin_rows, int32_t* expert_idx, float* gate, int32_t* dest_row,
+                             int32_t* counts, int32_t* bin_offsets, bsg_stream_t stream);
 
 /*
  * route_backward - gradient of <dy, y> with respect to the router logits for

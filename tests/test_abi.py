@@ -309,3 +309,29 @@ def test_leading_dimensions_beyond_32bit_panel_offsets(L):
     assert L.bsg_dsd_combine_top1(P, C.byref(t), P, kc, 1, 256, P, 256, P, None, P, 256,
                                   bsg.BF16, None) == bsg.EUNSUPPORTED
     assert L.bsg_dstd(P, C.byref(t), P, km, 256, P, 256, 0, bsg.BF16, None) == bsg.EUNSUPPORTED
+
+
+def test_route_noalloc_validation(L):
+    """The allocation-free routing call validates like bsg_route, and refuses
+    a request whose per-chunk counts exceed its static device array, all
+    before any HIP call."""
+    ok = [P, 100, 8, 2, 0, 128, P, P, P, P, P, None]
+    names = ["logits", "T", "E", "k", "renorm", "bin", "expert_idx", "gate", "dest_row",
+             "counts", "bin_offsets", "stream"]
+
+    def call(**over):
+        a = list(ok)
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_route_noalloc(*a)
+
+    assert call(logits=None) == bsg.EINVAL
+    assert call(gate=None) == bsg.EINVAL
+    assert call(T=0) == bsg.EINVAL
+    assert call(k=9) == bsg.EINVAL
+    assert call(E=64, k=40) == bsg.EUNSUPPORTED
+    assert call(bin=64) == bsg.EUNSUPPORTED
+    assert call(counts=C.c_void_p(0x10002)) == bsg.EINVAL
+    # ceil(T / 64) * E * 4 bytes of counts: 1025 chunks x 1024 experts > 4 MiB
+    assert bsg.route_workspace_bytes(64 * 1025, 1, 1024) > bsg.ROUTE_SCRATCH_BYTES
+    assert call(T=64 * 1025, E=1024, k=1) == bsg.EUNSUPPORTED and "scratch" in _err(L)
