@@ -35,6 +35,12 @@ bsg_status hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Bounds checked before any size is multiplied, so that validation itself
+// never overflows: tokens and block rows fit int32 ids, leading dimensions
+// and widths stay far below the point where a byte count would wrap.
+constexpr int64_t kMaxLd = int64_t(1) << 40;
+constexpr int kMaxWidth = 1 << 24;
+
 int elt_bytes(int dtype) { return dtype == BSG_BF16 ? 2 : 4; }
 
 bool dtype_ok(int dtype) { return dtype == BSG_F32 || dtype == BSG_BF16; }
@@ -55,7 +61,9 @@ bsg_status check_topology(const bsg_topology* t) {
     REQUIRE(t->F >= 1, "topo->F must be positive");
     REQUIRE(t->Tp_max >= BSG_BLOCK && t->Tp_max % BSG_BLOCK == 0,
             "topo->Tp_max must be a positive multiple of 128");
-    REQUIRE((t->Tp_max / BSG_BLOCK) * (int64_t)t->F < INT32_MAX, "too many blocks for int32 ids");
+    REQUIRE(t->Tp_max / BSG_BLOCK <= INT32_MAX &&
+                (t->Tp_max / BSG_BLOCK) * (int64_t)t->F < INT32_MAX,
+            "too many blocks for int32 ids");
     REQUIRE_PTR(t->row_ptr);
     REQUIRE_PTR(t->col_idx);
     REQUIRE_PTR(t->row_idx);
@@ -107,7 +115,8 @@ const char* bsg_status_string(bsg_status s) {
 const char* bsg_last_error(void) { return g_err; }
 
 int64_t bsg_max_padded_rows(int64_t T, int k, int E, int bin_rows) {
-    if (T < 1 || k < 1 || E < 1 || k > E || (bin_rows != 128 && bin_rows != 256)) return -1;
+    if (T < 1 || T > INT32_MAX || k < 1 || E < 1 || k > E || (bin_rows != 128 && bin_rows != 256))
+        return -1;
     const int64_t A = T * k;
     const int64_t ne = A < E ? A : E;
     return (A + (bin_rows - 1) * ne) / bin_rows * bin_rows;
@@ -119,6 +128,7 @@ bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out)
             "Tp_max must be a positive multiple of 128");
     REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
     REQUIRE(f >= BSG_BLOCK && f % BSG_BLOCK == 0, "f must be a positive multiple of 128");
+    REQUIRE(Tp_max / BSG_BLOCK <= INT32_MAX, "too many block rows for int32 ids");
     const int64_t F = f / BSG_BLOCK;
     out->row_blocks_max = Tp_max / BSG_BLOCK;
     out->nnz_max = out->row_blocks_max * F;
@@ -129,7 +139,7 @@ bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out)
 }
 
 size_t bsg_route_workspace_bytes(int64_t T, int k, int E) {
-    if (T < 1 || k < 1 || E < 1 || k > E) return 0;
+    if (T < 1 || T > INT32_MAX || k < 1 || E < 1 || k > E) return 0;
     const int64_t nchunks = (T + bsg::kRouteChunk - 1) / bsg::kRouteChunk;
     return (size_t)(nchunks * E * (int64_t)sizeof(int32_t));
 }
@@ -151,7 +161,7 @@ static bsg_status check_route(const float* logits, int64_t T, int E, int k, int 
     REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
     REQUIRE(k >= 1 && k <= E, "k must be in [1, E]");
     if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
-    REQUIRE(T * k < INT32_MAX, "T*k must fit int32 assignment ids");
+    REQUIRE(T <= INT32_MAX && T * k < INT32_MAX, "T*k must fit int32 assignment ids");
     REQUIRE(bsg_max_padded_rows(T, k, E, bin_rows) < INT32_MAX, "padded rows must fit int32");
     REQUIRE_PTR(logits);
     REQUIRE_PTR(expert_idx);
@@ -207,10 +217,11 @@ bsg_status bsg_route_backward(const float* logits, int64_t T, int E, int k, int 
     REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
     REQUIRE(k >= 1 && k <= E, "k must be in [1, E]");
     if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
-    REQUIRE(T * k < INT32_MAX, "T*k must fit int32 assignment ids");
-    REQUIRE(d >= 1 && (d * elt_bytes(dy_dtype)) % 16 == 0 && (d * elt_bytes(yp_dtype)) % 16 == 0,
+    REQUIRE(T <= INT32_MAX && T * k < INT32_MAX, "T*k must fit int32 assignment ids");
+    REQUIRE(d >= 1 && d <= kMaxWidth && (d * elt_bytes(dy_dtype)) % 16 == 0 &&
+                (d * elt_bytes(yp_dtype)) % 16 == 0,
             "d must keep rows 16-byte aligned");
-    REQUIRE(ld_yp >= d && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
+    REQUIRE(ld_yp >= d && ld_yp <= kMaxLd && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
             "ld_yp must be >= d with 16-byte aligned rows");
     REQUIRE_PTR(logits);
     REQUIRE_PTR(expert_idx);
@@ -233,8 +244,9 @@ bsg_status bsg_permute_pad(const void* x, int dtype, int64_t T, int d, int k,
     if (bs != BSG_OK) return bs;
     REQUIRE(T >= 1 && k >= 1 && E >= 1 && E <= BSG_MAX_EXPERTS && k <= E, "bad T, k or E");
     REQUIRE(k <= BSG_MAX_TOPK, "k > %d", BSG_MAX_TOPK);
-    REQUIRE(T * k < INT32_MAX, "T*k must fit int32");
-    REQUIRE(d >= 1 && (d * elt_bytes(dtype)) % 16 == 0, "d must keep rows 16-byte aligned");
+    REQUIRE(T <= INT32_MAX && T * k < INT32_MAX, "T*k must fit int32");
+    REQUIRE(d >= 1 && d <= kMaxWidth && (d * elt_bytes(dtype)) % 16 == 0,
+            "d must keep rows 16-byte aligned");
     REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E, bin_rows), "Tp_max below the padded-row bound");
     REQUIRE_VEC_PTR(x);
     REQUIRE_VEC_PTR(xp);
@@ -263,9 +275,10 @@ bsg_status bsg_permute_pad_gate_backward(const void* dy, int dtype, int64_t T, i
     if (bs != BSG_OK) return bs;
     REQUIRE(T >= 1 && k >= 1 && E >= 1 && E <= BSG_MAX_EXPERTS && k <= E, "bad T, k or E");
     if (k > BSG_MAX_TOPK) return fail(BSG_EUNSUPPORTED, "k > %d is not implemented", BSG_MAX_TOPK);
-    REQUIRE(T * k < INT32_MAX, "T*k must fit int32");
-    REQUIRE(d >= 1 && (d * elt_bytes(dtype)) % 16 == 0, "d must keep rows 16-byte aligned");
-    REQUIRE(ld_yp >= d && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
+    REQUIRE(T <= INT32_MAX && T * k < INT32_MAX, "T*k must fit int32");
+    REQUIRE(d >= 1 && d <= kMaxWidth && (d * elt_bytes(dtype)) % 16 == 0,
+            "d must keep rows 16-byte aligned");
+    REQUIRE(ld_yp >= d && ld_yp <= kMaxLd && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
             "ld_yp must be >= d with 16-byte aligned rows");
     REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E, bin_rows), "Tp_max below the padded-row bound");
     REQUIRE_VEC_PTR(dy);
@@ -346,9 +359,10 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     const int kt = dtype == BSG_BF16 ? 64 : 32;
     const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
     REQUIRE(K >= kt && K % kt == 0, "K must be a positive multiple of %d", kt);
-    REQUIRE(lda >= K && (lda * es) % 16 == 0, "lda must be >= K with 16-byte aligned rows");
+    REQUIRE(lda >= K && lda <= kMaxLd && (lda * es) % 16 == 0,
+            "lda must be >= K with 16-byte aligned rows");
     REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
-    REQUIRE(ldb >= (trans_b ? K : ncol) && (ldb * es) % 16 == 0,
+    REQUIRE(ldb >= (trans_b ? K : ncol) && ldb <= kMaxLd && (ldb * es) % 16 == 0,
             "ldb too small or rows not 16-byte aligned");
     REQUIRE_PANEL_LD(lda, es, true);
     REQUIRE_PANEL_LD(ldb, es, trans_b == 1);
@@ -392,11 +406,13 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
     if (s != BSG_OK) return s;
     const int es = elt_bytes(dtype), ces = elt_bytes(c_dtype);
     const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
-    REQUIRE(N >= BSG_BLOCK && N % BSG_BLOCK == 0, "N must be a positive multiple of 128");
+    REQUIRE(N >= BSG_BLOCK && N <= kMaxWidth && N % BSG_BLOCK == 0,
+            "N must be a positive multiple of 128");
     REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
-    REQUIRE(ldb >= (trans_b ? ncol : N) && (ldb * es) % 16 == 0,
+    REQUIRE(ldb >= (trans_b ? ncol : N) && ldb <= kMaxLd && (ldb * es) % 16 == 0,
             "ldb too small or rows not 16-byte aligned");
-    REQUIRE(ldc >= N && (ldc * ces) % 16 == 0, "ldc must be >= N with 16-byte aligned rows");
+    REQUIRE(ldc >= N && ldc <= kMaxLd && (ldc * ces) % 16 == 0,
+            "ldc must be >= N with 16-byte aligned rows");
     REQUIRE_PANEL_LD(ldb, es, trans_b == 1);
     REQUIRE_VEC_PTR(blocks);
     REQUIRE_VEC_PTR(b);
@@ -431,11 +447,13 @@ bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, co
     bsg_status s = check_topology(topo);
     if (s != BSG_OK) return s;
     const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
-    REQUIRE(N >= BSG_BLOCK && N % BSG_BLOCK == 0, "N must be a positive multiple of 128");
+    REQUIRE(N >= BSG_BLOCK && N <= kMaxWidth && N % BSG_BLOCK == 0,
+            "N must be a positive multiple of 128");
     REQUIRE(trans_b == 0 || trans_b == 1, "trans_b must be 0 or 1");
-    REQUIRE(ldb >= (trans_b ? ncol : N) && (ldb * 2) % 16 == 0,
+    REQUIRE(ldb >= (trans_b ? ncol : N) && ldb <= kMaxLd && (ldb * 2) % 16 == 0,
             "ldb too small or rows not 16-byte aligned");
-    REQUIRE(ldy >= N && (ldy * 2) % 16 == 0, "ldy must be >= N with 16-byte aligned rows");
+    REQUIRE(ldy >= N && ldy <= kMaxLd && (ldy * 2) % 16 == 0,
+            "ldy must be >= N with 16-byte aligned rows");
     REQUIRE_PANEL_LD(ldb, 2, trans_b == 1);
     REQUIRE_VEC_PTR(blocks);
     REQUIRE_VEC_PTR(b);
@@ -444,7 +462,8 @@ bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, co
     REQUIRE(gate == nullptr || aligned(gate, 4), "gate must be 4-byte aligned");
     if (c) {
         REQUIRE(aligned(c, 16), "c must be 16-byte aligned");
-        REQUIRE(ldc >= N && (ldc * 2) % 16 == 0, "ldc must be >= N with 16-byte aligned rows");
+        REQUIRE(ldc >= N && ldc <= kMaxLd && (ldc * 2) % 16 == 0,
+                "ldc must be >= N with 16-byte aligned rows");
     }
     bsg::GemmParams p = gemm_params(topo);
     p.a = blocks;
@@ -470,10 +489,12 @@ bsg_status bsg_dstd(const void* blocks, const bsg_topology* topo, const void* dm
     if (s != BSG_OK) return s;
     const int es = elt_bytes(dtype);
     const int64_t ncol = (int64_t)topo->E * topo->F * BSG_BLOCK;
-    REQUIRE(N >= BSG_BLOCK && N % BSG_BLOCK == 0, "N must be a positive multiple of 128");
+    REQUIRE(N >= BSG_BLOCK && N <= kMaxWidth && N % BSG_BLOCK == 0,
+            "N must be a positive multiple of 128");
     REQUIRE(trans_c == 0 || trans_c == 1, "trans_c must be 0 or 1");
-    REQUIRE(ldd >= N && (ldd * es) % 16 == 0, "ldd must be >= N with 16-byte aligned rows");
-    REQUIRE(ldc >= (trans_c ? ncol : N) && (ldc * es) % 16 == 0,
+    REQUIRE(ldd >= N && ldd <= kMaxLd && (ldd * es) % 16 == 0,
+            "ldd must be >= N with 16-byte aligned rows");
+    REQUIRE(ldc >= (trans_c ? ncol : N) && ldc <= kMaxLd && (ldc * es) % 16 == 0,
             "ldc too small or rows not 16-byte aligned");
     REQUIRE_PANEL_LD(ldd, es, false);
     REQUIRE_VEC_PTR(blocks);
@@ -494,9 +515,10 @@ bsg_status bsg_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
                                  const int32_t* dest_row, const float* gate, int64_t T, int k,
                                  int d, void* y, int y_dtype, bsg_stream_t stream) {
     REQUIRE(dtype_ok(yp_dtype) && dtype_ok(y_dtype), "unknown dtype");
-    REQUIRE(T >= 1 && k >= 1 && k <= BSG_MAX_TOPK && T * k < INT32_MAX, "bad T or k");
-    REQUIRE(d >= 8 && d % 8 == 0, "d must be a positive multiple of 8");
-    REQUIRE(ld_yp >= d && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
+    REQUIRE(T >= 1 && T <= INT32_MAX && k >= 1 && k <= BSG_MAX_TOPK && T * k < INT32_MAX,
+            "bad T or k");
+    REQUIRE(d >= 8 && d <= kMaxWidth && d % 8 == 0, "d must be a positive multiple of 8");
+    REQUIRE(ld_yp >= d && ld_yp <= kMaxLd && (ld_yp * elt_bytes(yp_dtype)) % 16 == 0,
             "ld_yp must be >= d with 16-byte aligned rows");
     REQUIRE_VEC_PTR(yp);
     REQUIRE_VEC_PTR(y);

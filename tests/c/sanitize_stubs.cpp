@@ -1,0 +1,80 @@
+// Host-only stand-ins for the kernel launchers of the C ABI, so that the
+// argument validation in api.cpp can be built and run under AddressSanitizer
+// and UndefinedBehaviorSanitizer on a machine without a GPU.  Each stand-in
+// records the call and reports success; no device code exists in this
+// build.
+#include <hip/hip_runtime.h>
+
+#include "../../block_sparse_gemm_amd/csrc/kernels.hpp"
+
+int g_launches = 0;  // read by the driver
+
+extern "C" const char* hipGetErrorString(hipError_t) { return "host-only build"; }
+
+namespace bsg {
+
+static int32_t g_scratch[16];
+
+hipError_t route_scratch(hipStream_t, int32_t** out) {
+    *out = g_scratch;
+    return hipSuccess;
+}
+
+hipError_t launch_route(const float*, int64_t, int, int, int, int, int32_t*, float*, int32_t*,
+                        int32_t*, int32_t*, int32_t*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_route_backward(const float*, int64_t, int, int, int, const int32_t*,
+                                 const int32_t*, const void*, int, int, const void*, int, int64_t,
+                                 float*, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_permute_pad(const void*, int, int64_t, int, int, const int32_t*, const float*,
+                              const int32_t*, const int32_t*, int, int, int64_t, int32_t*, void*,
+                              hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_permute_gate_backward(const void*, int, int64_t, int, int, const int32_t*,
+                                        const float*, const int32_t*, const int32_t*, int, int,
+                                        int64_t, int32_t*, void*, const float*, int,
+                                        const int32_t*, const void*, int, int64_t, float*,
+                                        hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_build_topology(const int32_t*, int, int, int64_t, int64_t, int32_t*, int32_t*,
+                                 int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, int,
+                                 hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_sdd(const GemmParams&, int64_t, int, int, int, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_dsd(const GemmParams&, int64_t, int, int, int, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_dstd(const GemmParams&, int, int, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_unpermute_combine(const void*, int, int64_t, const int32_t*, const float*,
+                                    int64_t, int, int, void*, int, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+
+}  // namespace bsg
