@@ -814,3 +814,169 @@ int orc_dW3_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
                   int64_t nc, double* out) {
     return input_weight_grad(L, 1, rows, nr, cols, nc, out);
 }
+
+/* ------------------------------------------------------- block products */
+
+/*
+ * The three block-sparse products on given operands (section 1.2: SDD, the
+ * first layer kept only at the nonzero blocks, then DSD, sparse x dense;
+ * section 1.3: DSTD, the transposed sparse operand times a dense one, one
+ * block column at a time through the transpose index), for the MoE
+ * topology the bins define: row block r belongs to the expert e whose bin
+ * holds row 128 r, and expert e owns column blocks e*F .. e*F + F - 1, so
+ * nonzero block b = r*F + j sits at (r, e*F + j).  Operands hold the stored
+ * values (bf16 widened to fp32); sums run in fp64 over k ascending and are
+ * rounded once to prec, after the epilogue.  Block arrays are block-major,
+ * [nnz][128][128], a second plane nnz blocks after the first.
+ */
+
+/* expert of each row block, from the bins; returns the row-block count */
+static int64_t row_owners(const int32_t* bin_offsets, int E, int32_t** owner) {
+    const int64_t R = bin_offsets[E] / BLK;
+    int32_t* o = (int32_t*)malloc(sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
+    for (int64_t r = 0; r < R; ++r) {
+        o[r] = -1;
+        for (int e = 0; e < E; ++e)
+            if (r * BLK >= bin_offsets[e] && r * BLK < bin_offsets[e + 1]) o[r] = e;
+    }
+    *owner = o;
+    return R;
+}
+
+/* B[k][n] of a dense operand stored as given (trans = 0: b[k*ld + n]) or
+ * transposed (trans = 1: b[n*ld + k]) */
+static double elem(const float* b, int64_t ld, int trans, int64_t k, int64_t n) {
+    return (double)(trans ? b[n * ld + k] : b[k * ld + n]);
+}
+
+/*
+ * SDD: acc_b[m][n] = sum_k a[128 r + m][k] * B[k][128 c + n], k < K, then
+ *   epi 0  acc
+ *   epi 1  gelu(acc); aux_out (if not NULL) gelu'(acc)
+ *   epi 2  silu(acc) * acc2 (acc2 from b2); aux_out (if not NULL) two planes:
+ *          silu(acc), acc2 * silu'(acc)
+ *   epi 3  acc * aux_in[b]
+ *   epi 4  out two planes: acc * aux_in plane 1, acc * aux_in plane 0
+ * Returns nnz, or -1 on bad arguments.
+ */
+int64_t orc_sdd(const float* a, int64_t lda, const float* b, const float* b2, int64_t ldb,
+                int trans_b, int K, const int32_t* bin_offsets, int E, int F, int epi,
+                const float* aux_in, int prec, double* out, double* aux_out) {
+    if (!a || !b || !bin_offsets || !out || K < 1 || E < 1 || F < 1 || epi < 0 || epi > 4)
+        return -1;
+    if ((epi == 2 && !b2) || ((epi == 3 || epi == 4) && !aux_in)) return -1;
+    int32_t* owner;
+    const int64_t R = row_owners(bin_offsets, E, &owner);
+    const int64_t nnz = R * F;
+    const int64_t bs = (int64_t)BLK * BLK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t blk = 0; blk < nnz; ++blk) {
+        const int64_t r = blk / F, c = (int64_t)owner[r] * F + blk % F;
+        double* acc = dalloc(BLK * BLK);
+        double* acc2 = dalloc(BLK * BLK);
+        for (int64_t i = 0; i < bs; ++i) acc[i] = acc2[i] = 0.0;
+        for (int64_t m = 0; m < BLK; ++m) {
+            const float* ar = a + (r * BLK + m) * lda;
+            for (int64_t k = 0; k < K; ++k) {
+                const double av = ar[k];
+                for (int64_t n = 0; n < BLK; ++n) {
+                    acc[m * BLK + n] += av * elem(b, ldb, trans_b, k, c * BLK + n);
+                    if (epi == 2) acc2[m * BLK + n] += av * elem(b2, ldb, trans_b, k, c * BLK + n);
+                }
+            }
+        }
+        for (int64_t i = 0; i < bs; ++i) {
+            const double h = acc[i];
+            const int64_t o = blk * bs + i;
+            switch (epi) {
+            case 0: out[o] = rd(h, prec); break;
+            case 1:
+                out[o] = rd(gelu(h), prec);
+                if (aux_out) aux_out[o] = rd(gelu_grad(h), prec);
+                break;
+            case 2:
+                out[o] = rd(silu(h) * acc2[i], prec);
+                if (aux_out) {
+                    aux_out[o] = rd(silu(h), prec);
+                    aux_out[nnz * bs + o] = rd(acc2[i] * silu_grad(h), prec);
+                }
+                break;
+            case 3: out[o] = rd(h * (double)aux_in[o], prec); break;
+            default:
+                out[o] = rd(h * (double)aux_in[nnz * bs + o], prec);
+                out[nnz * bs + o] = rd(h * (double)aux_in[o], prec);
+            }
+        }
+        free(acc);
+        free(acc2);
+    }
+    free(owner);
+    return nnz;
+}
+
+/*
+ * DSD: c[128 r + m][n] = sum over the blocks b of row r (ascending), sum_j
+ * blocks[b][m][j] * B[128 col(b) + j][n], then the same over blocks2 with
+ * B2 from b2 when blocks2 is not NULL; c is [Tp][N] (row-major, N columns).
+ * Returns the row count Tp, or -1 on bad arguments.
+ */
+int64_t orc_dsd(const float* blocks, const float* blocks2, const int32_t* bin_offsets, int E,
+                int F, const float* b, const float* b2, int64_t ldb, int trans_b, int N, int prec,
+                double* c) {
+    if (!blocks || !bin_offsets || !b || !c || E < 1 || F < 1 || N < 1 || (blocks2 && !b2))
+        return -1;
+    int32_t* owner;
+    const int64_t R = row_owners(bin_offsets, E, &owner);
+    const int64_t bs = (int64_t)BLK * BLK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < R * BLK; ++row) {
+        const int64_t r = row / BLK, m = row % BLK;
+        double* acc = dalloc(N);
+        for (int n = 0; n < N; ++n) acc[n] = 0.0;
+        for (int set = 0; set < (blocks2 ? 2 : 1); ++set) {
+            const float* bl = set ? blocks2 : blocks;
+            const float* bb = set ? b2 : b;
+            for (int j = 0; j < F; ++j) {
+                const int64_t blk = r * F + j, col = (int64_t)owner[r] * F + j;
+                for (int64_t q = 0; q < BLK; ++q) {
+                    const double v = bl[blk * bs + m * BLK + q];
+                    for (int n = 0; n < N; ++n) acc[n] += v * elem(bb, ldb, trans_b, col * BLK + q, n);
+                }
+            }
+        }
+        for (int n = 0; n < N; ++n) c[row * N + n] = rd(acc[n], prec);
+        free(acc);
+    }
+    free(owner);
+    return R * BLK;
+}
+
+/*
+ * DSTD: C[128 c + m][n] = sum over the blocks b of block column c, in
+ * ascending row (the transpose index's order), sum_j blocks[b][j][m] *
+ * dmat[128 row(b) + j][n]; C is [E*F*128][N]; a column without blocks (an
+ * expert without rows) is zero.  Returns 0, or -1 on bad arguments.
+ */
+int orc_dstd(const float* blocks, const int32_t* bin_offsets, int E, int F, const float* dmat,
+             int64_t ldd, int N, int prec, double* C) {
+    if (!blocks || !bin_offsets || !dmat || !C || E < 1 || F < 1 || N < 1) return -1;
+    const int64_t bs = (int64_t)BLK * BLK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t out_row = 0; out_row < (int64_t)E * F * BLK; ++out_row) {
+        const int64_t c = out_row / BLK, m = out_row % BLK;
+        const int e = (int)(c / F), j = (int)(c % F);
+        double* acc = dalloc(N);
+        for (int n = 0; n < N; ++n) acc[n] = 0.0;
+        for (int64_t r = bin_offsets[e] / BLK; r < bin_offsets[e + 1] / BLK; ++r) {
+            const int64_t blk = r * F + j;
+            for (int64_t q = 0; q < BLK; ++q) {
+                const double v = blocks[blk * bs + q * BLK + m];
+                const float* dr = dmat + (r * BLK + q) * ldd;
+                for (int n = 0; n < N; ++n) acc[n] += v * (double)dr[n];
+            }
+        }
+        for (int n = 0; n < N; ++n) C[out_row * N + n] = rd(acc[n], prec);
+        free(acc);
+    }
+    return 0;
+}

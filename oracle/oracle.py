@@ -86,6 +86,15 @@ def lib():
         L.orc_backward_tokens.argtypes = [lp, _i64p, C.c_int64, _f64p]
         for n in ("orc_dW2_block", "orc_dW1_block", "orc_dW3_block"):
             getattr(L, n).argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
+        L.orc_sdd.restype = C.c_int64
+        L.orc_sdd.argtypes = [_f32p, C.c_int64, _f32p, _f32p, C.c_int64, C.c_int, C.c_int, _i32p,
+                              C.c_int, C.c_int, C.c_int, _f32p, C.c_int, _f64p, _f64p]
+        L.orc_dsd.restype = C.c_int64
+        L.orc_dsd.argtypes = [_f32p, _f32p, _i32p, C.c_int, C.c_int, _f32p, _f32p, C.c_int64,
+                              C.c_int, C.c_int, C.c_int, _f64p]
+        L.orc_dstd.restype = C.c_int
+        L.orc_dstd.argtypes = [_f32p, _i32p, C.c_int, C.c_int, _f32p, C.c_int64, C.c_int,
+                               C.c_int, _f64p]
         for n in ("orc_assign_forward", "orc_forward_tokens", "orc_assign_backward",
                   "orc_backward_tokens", "orc_dW2_block", "orc_dW1_block", "orc_dW3_block"):
             getattr(L, n).restype = C.c_int
@@ -320,3 +329,67 @@ def make_layer(x, W1, W2, route_out, k, E, act="gelu", W3=None, dy=None, prec="b
     """Convenience: a :class:`Layer` over the oracle's own routing."""
     return Layer(x, W1, W2, route_out["expert_idx"], route_out["gate"], k, E, act=act, W3=W3,
                  dy=dy, prec=prec, prec_yp=prec_yp)
+
+
+# ------------------------------------------------------------ block products
+#
+# The three products on given operands for the MoE topology the bins define
+# (orc_sdd, orc_dsd, orc_dstd in oracle.c: section 1.2's SDD and DSD, section
+# 1.3's DSTD through the transpose index).  Dense operands are 2-D fp32 arrays
+# of the stored values; block arrays are [planes * nnz, 128, 128] or flat.
+
+SDD_EPI = {"none": 0, "gelu": 1, "silu_mul": 2, "gelu_bwd": 3, "silu_mul_bwd": 4}
+
+
+def _nnz(bin_offsets, E, F):
+    return int(bin_offsets[E]) // 128 * F
+
+
+def sdd(a, b, K, bin_offsets, E, F, epilogue="none", prec="bf16", b2=None, trans_b=False,
+        aux_in=None, want_aux=False):
+    """Blocks [planes * nnz, 128, 128] of the first-layer product (and the
+    saved factors when want_aux, for gelu / silu_mul)."""
+    a, b, b2 = _f32(a), _f32(b), _f32(b2)
+    bo = np.ascontiguousarray(bin_offsets, np.int32)
+    nnz = _nnz(bo, E, F)
+    epi = SDD_EPI[epilogue]
+    planes = 2 if epi == 4 else 1
+    out = np.zeros((planes * nnz, 128, 128))
+    aux = np.zeros(((2 if epi == 2 else 1) * nnz, 128, 128)) if want_aux else None
+    ai = None if aux_in is None else _f32(aux_in).reshape(-1)
+    if b2 is not None and b2.shape != b.shape:
+        raise ValueError("b2 must have b's shape")
+    rc = lib().orc_sdd(_p(a, _f32p), a.shape[1], _p(b, _f32p), _p(b2, _f32p), b.shape[1],
+                       int(bool(trans_b)), int(K), _p(bo, _i32p), E, F, epi, _p(ai, _f32p),
+                       PREC[prec], _p(out, _f64p), _p(aux, _f64p))
+    if rc != nnz:
+        raise ValueError("orc_sdd rejected its arguments")
+    return (out, aux) if want_aux else out
+
+
+def dsd(blocks, bin_offsets, E, F, b, N, prec="bf16", trans_b=False, blocks2=None, b2=None):
+    """Rows [Tp, N] of the sparse x dense product (two block sets summed
+    when blocks2 / b2 are given)."""
+    bl, bl2 = _f32(blocks).reshape(-1), None if blocks2 is None else _f32(blocks2).reshape(-1)
+    b, b2 = _f32(b), _f32(b2)
+    bo = np.ascontiguousarray(bin_offsets, np.int32)
+    Tp = int(bo[E])
+    c = np.zeros((Tp, N))
+    rc = lib().orc_dsd(_p(bl, _f32p), _p(bl2, _f32p), _p(bo, _i32p), E, F, _p(b, _f32p),
+                       _p(b2, _f32p), b.shape[1], int(bool(trans_b)), int(N), PREC[prec],
+                       _p(c, _f64p))
+    if rc != Tp:
+        raise ValueError("orc_dsd rejected its arguments")
+    return c
+
+
+def dstd(blocks, bin_offsets, E, F, dmat, N, prec="bf16"):
+    """The weight-gradient product [E * F * 128, N] (untransposed)."""
+    bl, dm = _f32(blocks).reshape(-1), _f32(dmat)
+    bo = np.ascontiguousarray(bin_offsets, np.int32)
+    C_ = np.zeros((E * F * 128, N))
+    rc = lib().orc_dstd(_p(bl, _f32p), _p(bo, _i32p), E, F, _p(dm, _f32p), dm.shape[1], int(N),
+                        PREC[prec], _p(C_, _f64p))
+    if rc != 0:
+        raise ValueError("orc_dstd rejected its arguments")
+    return C_
