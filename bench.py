@@ -20,17 +20,26 @@ the layer's schedule: the weight gradients on a second stream beside the
 data-gradient chain when the products are short (MoE-Small), every call in
 order on one stream otherwise; ``--overlap`` and ``--one-stream`` force
 either, and ``--compare-schedules`` also times the other schedule after the
-timed steps (context only).  ``roofline`` reports the step's dominant kernel against the bf16 dense MFMA
-peak, timed with HIP events on the stream it runs on over the timed steps.
+timed steps (context only).  ``roofline`` reports the step's dominant kernel
+against the roof that binds it: HBM (8 TB/s) when its useful flops per
+algorithmic byte fall below the ridge (2.5 PFLOP/s / 8 TB/s = 312.5), the
+bf16 dense MFMA peak otherwise; its flop rate and fraction of the MFMA peak
+come beside it.  The kernel's time is taken with HIP events on the stream it
+runs on over the timed steps.
 Which call dominates, and the per-call table ``kernels``, come from a probe
-pass of three steps on one stream before the timed ones with every call bracketed by
-events; the timed steps record events around the dominant call only, since
-each event costs GPU time (about 4 us a call pair here).  The data-movement
-calls' entries give HBM GB/s from their algorithmic bytes, as a share of the
-8 TB/s peak and of ``hbm_copy_ceiling``, a device copy of as many bytes as
-permute_pad moves, timed in the same run.  ``traffic`` is HBM bytes per
-launch from the committed counter summary (null once the GEMM source has
-changed since).
+pass of three steps on one stream before the timed ones with every call
+bracketed by events; the timed steps record events around the dominant call
+only, since each event costs GPU time (about 4 us a call pair here).
+``forward_products`` times the forward products alone (SDD + GeLU writing A
+only, DSD writing Yp) with their rooflines and the ratio to a dense
+hipBLASLt GEMM (torch.matmul) of the same executed shape.
+``data_movement`` times permute_pad, the backward's dy permutation with the
+gate backward and unpermute_combine alone (for top-1 layers also on a top-2
+routing of the same tokens), each after a 512 MiB write that flushes the
+256 MB last-level cache, as GB/s of algorithmic bytes against the 8 TB/s
+peak and against ``hbm_copy_ceiling``, the library's streaming copy of as
+many bytes timed the same way.  ``traffic`` is HBM bytes per launch from the
+committed counter summary (null once the GEMM source has changed since).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload on this host's cores.
 """
@@ -64,8 +73,6 @@ def parse():
                     help="weight gradients on a second stream in the timed steps")
     ap.add_argument("--bin-rows", type=int, default=128, choices=(128, 256),
                     help="pad expert bins to a multiple of this many rows (block-size study)")
-    ap.add_argument("--context", action="store_true",
-                    help="also time dense bf16 GEMMs (torch.matmul) of the same (Tp, d, f)")
     ap.add_argument("--compare-schedules", action="store_true",
                     help="after the timed steps, also time the other backward schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,7 +203,7 @@ def main():
               "multi-GPU sharding (expert parallelism over RCCL) is not built.", file=sys.stderr)
         sys.exit(2)
     import torch
-    from block_sparse_gemm_amd import layer, synth
+    from block_sparse_gemm_amd import bsg, layer, synth
 
     cfg = synth.CONFIGS[args.config]
     if args.bin_rows != cfg.bin_rows:
@@ -275,50 +282,137 @@ def main():
     torch.cuda.synchronize()
     spread = np.percentile([ev[i].elapsed_time(ev[i + 1]) for i in range(NS)], [10, 50, 90])
 
-    # context: a device-to-device copy (torch copy_) moving as many bytes as
-    # permute_pad reads and writes, through four rotating buffer pairs so the
-    # 256 MB MALL cannot serve repeats: the practical HBM ceiling that the
-    # data-movement calls are compared with
     es = 2 if cfg.dtype == "bf16" else 4
     Tp = int(L.bin_offsets[-1].item())
-    half = (cfg.T + Tp) * cfg.d * es // 2
-    pairs = [(torch.empty(half // 2, dtype=torch.bfloat16, device="cuda"),
-              torch.empty(half // 2, dtype=torch.bfloat16, device="cuda")) for _ in range(4)]
-    for i in range(4):
-        pairs[i][1].copy_(pairs[i][0])
-    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ce0.record()
-    for i in range(20):
-        pairs[i % 4][1].copy_(pairs[i % 4][0])
-    ce1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * (half // 2) * 2 / (ce0.elapsed_time(ce1) / 20 * 1e-3) / 1e9
-    del pairs
+    t = L.topo
+    A_n = cfg.T * cfg.k
+    ypes = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
 
-    # context: dense bf16 GEMMs with the products' executed shapes (M = Tp)
-    dense = None
-    if args.context:
-        Tp0 = int(L.bin_offsets[-1].item())
-        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-        a1 = torch.randn(Tp0, cfg.d, device="cuda").to(dt)
-        b1 = torch.randn(cfg.d, cfg.f, device="cuda").to(dt)
-        a2 = torch.randn(Tp0, cfg.f, device="cuda").to(dt)
-        b2 = torch.randn(cfg.f, cfg.d, device="cuda").to(dt)
-
-        def time_mm(a, b):
-            for _ in range(3):
-                torch.matmul(a, b)
+    def event_ms(fn, iters, before=None):
+        """Median ms of fn over iters runs, each between two events on the
+        current stream; before() runs untimed ahead of each."""
+        ms = []
+        for _ in range(iters):
+            if before is not None:
+                before()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(20):
-                torch.matmul(a, b)
+            fn()
             e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / 20
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
 
-        dense = {"sdd_shape_ms": round(time_mm(a1, b1), 4),
-                 "dsd_shape_ms": round(time_mm(a2, b2), 4)}
-        del a1, b1, a2, b2
+    # last-level cache flush: the library's streaming copy writes (and reads)
+    # 512 MiB, twice the 256 MB MALL, before each timed data-movement call
+    fl_a = torch.empty(256 << 20, dtype=torch.bfloat16, device="cuda")
+    fl_b = torch.empty_like(fl_a)
+    flush = lambda: bsg.stream_copy(fl_a, fl_b)
+
+    def copy_gbps(moved):
+        """The library's streaming copy moving `moved` bytes (half read, half
+        written), MALL flushed before each run: the HBM ceiling."""
+        n = max(16, moved // 2 // 16 * 16)
+        a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        bsg.stream_copy(a, b)
+        ms = event_ms(lambda: bsg.stream_copy(a, b), 10, flush)
+        del a, b
+        return 2 * n / (ms * 1e-3) / 1e9
+
+    # data-movement calls alone, MALL flushed before each run
+    dm = {}
+    perm_bytes = cfg.T * cfg.d * es + Tp * cfg.d * es + 4 * A_n + 4 * Tp
+    ceiling = copy_gbps(perm_bytes)
+    big_ceiling = copy_gbps(2 << 30)
+    logits_t = logits
+
+    def entry(ms, nbytes):
+        g = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "bytes": int(nbytes), "gbps": round(g, 1),
+                "pct_hbm_peak": round(100 * g / HBM_PEAK, 1),
+                "frac_of_copy": round(g / ceiling, 3)}
+
+    dm["permute_pad"] = entry(event_ms(lambda: bsg.permute_pad(
+        x, cfg.k, L.dest_row, None, L.counts, L.bin_offsets, cfg.E, L.Tp_max, L.row_src, L.xp,
+        bin_rows=cfg.bin_rows), 10, flush), perm_bytes)
+    if cfg.backward:
+        gb_bytes = (cfg.T * cfg.d * es + A_n * cfg.d * ypes + Tp * cfg.d * es
+                    + 8 * cfg.T * cfg.E + 12 * A_n + 4 * Tp)
+        dm["permute_pad_gate_bwd"] = entry(event_ms(lambda: bsg.permute_pad_gate_backward(
+            dy, cfg.k, L.dest_row, L.gate, L.counts, L.bin_offsets, cfg.E, L.Tp_max,
+            L.row_src_b, L.dyp, logits_t, cfg.renorm, L.expert_idx, L.yp, L.dlogits,
+            bin_rows=cfg.bin_rows), 10, flush), gb_bytes)
+    dm["unpermute_combine"] = entry(event_ms(lambda: bsg.unpermute_combine(
+        L.yp, L.dest_row, L.gate, cfg.T, cfg.k, cfg.d, L.y), 10, flush),
+        A_n * cfg.d * ypes + cfg.T * cfg.d * es + 8 * A_n)
+    if cfg.k == 1:
+        # the layer runs its top-1 combine inside the DSD; the standalone call
+        # is also measured on a top-2 routing of the same tokens and logits
+        k2 = 2
+        i32 = dict(dtype=torch.int32, device="cuda")
+        ei2, de2 = torch.zeros(cfg.T * k2, **i32), torch.zeros(cfg.T * k2, **i32)
+        g2 = torch.zeros(cfg.T * k2, device="cuda")
+        c2, b2 = torch.zeros(cfg.E, **i32), torch.zeros(cfg.E + 1, **i32)
+        ws2 = torch.zeros(bsg.route_workspace_bytes(cfg.T, k2, cfg.E), dtype=torch.uint8,
+                          device="cuda")
+        bsg.route(logits_t, k2, False, ei2, g2, de2, c2, b2, ws2)
+        Tp2 = bsg.max_padded_rows(cfg.T, k2, cfg.E)
+        yp2 = torch.randn(Tp2, cfg.d, device="cuda").to(L.yp.dtype)
+        dm["unpermute_combine_top2"] = entry(event_ms(lambda: bsg.unpermute_combine(
+            yp2, de2, g2, cfg.T, k2, cfg.d, L.y), 10, flush),
+            cfg.T * k2 * cfg.d * ypes + cfg.T * cfg.d * es + 8 * cfg.T * k2)
+        del ei2, de2, g2, c2, b2, ws2, yp2
+    copy_ceiling = {"kernel": "bsg_stream_copy", "same_bytes_as_permute_pad": {
+        "bytes": perm_bytes, "gbps": round(ceiling, 1),
+        "pct_hbm_peak": round(100 * ceiling / HBM_PEAK, 1)},
+        "2GiB": {"bytes": 2 << 30, "gbps": round(big_ceiling, 1),
+                 "pct_hbm_peak": round(100 * big_ceiling / HBM_PEAK, 1)},
+        "flush": "512 MiB streaming copy before each timed run"}
+    del fl_a, fl_b
+
+    # forward-only products at this shape (what the layer runs without a
+    # backward): SDD + GeLU writing A only, and DSD writing Yp, each against
+    # its rooflines and a dense hipBLASLt GEMM (torch.matmul) of the same
+    # executed shape (Tp x d x f)
+    per_product = 2.0 * cfg.T * cfg.k * cfg.d * cfg.f
+    peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
+    plane = (Tp // 128) * (cfg.f // 128) * 128 * 128 * es
+    weight = cfg.d * cfg.E * cfg.f * es
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dense_ms(M, K, N):
+        a = torch.randn(M, K, device="cuda").to(dt)
+        b = torch.randn(K, N, device="cuda").to(dt)
+        torch.matmul(a, b)
+        ms = event_ms(lambda: torch.matmul(a, b), 20)
+        del a, b
+        return ms
+
+    fwd = {}
+    if cfg.act == "gelu":
+        W1f, W2f = W1, W2
+        prods = {
+            "sdd_gelu": (lambda: bsg.sdd(L.xp, W1f, cfg.d, t, "gelu", L.act),
+                         Tp * cfg.d * es + weight + plane, dense_ms(Tp, cfg.d, cfg.f)),
+            "dsd": (lambda: bsg.dsd(L.act, t, W2f, cfg.d, L.yp),
+                    plane + weight + Tp * cfg.d * ypes, dense_ms(Tp, cfg.f, cfg.d)),
+        }
+        for name, (fn, nbytes, dms) in prods.items():
+            fn()
+            ms = event_ms(fn, 20)
+            tf = per_product / (ms * 1e-3) / 1e12
+            inten = per_product / nbytes
+            att = min(peak, inten * HBM_PEAK / 1e3)
+            fwd[name] = {"ms": round(ms, 4), "useful_tflops": round(tf, 1),
+                         "frac_of_mfma_peak": round(tf / peak, 4),
+                         "algorithmic_bytes": int(nbytes),
+                         "intensity_flop_per_byte": round(inten, 1),
+                         "attainable_tflops": round(att, 1),
+                         "attainable_bound": "mfma" if att >= peak else "hbm",
+                         "frac_of_attainable": round(tf / att, 4),
+                         "dense_gemm_same_shape_ms": round(dms, 4),
+                         "dense_ratio": round(dms / ms, 3)}
 
     # context: the other backward schedule, a few steps after the timed region
     other = None
@@ -337,13 +431,16 @@ def main():
     per_product, total = useful_flops(cfg)
     tflops = total / (step_ms * 1e-3) / 1e12
     achieved = products_of(cfg, dom) * per_product / (dom_ms * 1e-3) / 1e12
-    peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
-    dom_bytes = algorithmic_bytes(cfg, dom, int(L.bin_offsets[-1].item()), L.fuse_top1)
+    dom_bytes = algorithmic_bytes(cfg, dom, Tp, L.fuse_top1)
     intensity = products_of(cfg, dom) * per_product / dom_bytes
     attainable = min(peak, intensity * HBM_PEAK / 1e3)  # flop/B x GB/s -> TFLOP/s
+    # the roof that binds this kernel: HBM when its useful flops per
+    # algorithmic byte fall below the ridge (peak / 8 TB/s), else MFMA
+    ridge = peak * 1e3 / HBM_PEAK
+    hbm_bound = intensity < ridge
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     kernels = {}
-    A_n = cfg.T * cfg.k
     for k, ms in kern.items():
         ent = {"ms": round(ms, 4)}
         if k in gemms:
@@ -368,7 +465,6 @@ def main():
             ent["gbps"] = round(b / (ms * 1e-3) / 1e9, 1)
         if "gbps" in ent:
             ent["pct_hbm_peak"] = round(100 * ent["gbps"] / HBM_PEAK, 1)
-            ent["frac_of_copy"] = round(ent["gbps"] / copy_gbps, 3)
         kernels[k] = ent
 
     out = {
@@ -395,37 +491,32 @@ def main():
         # the same step counted with the padded rows the products execute
         "executed_tflops": round(total * Tp / A_n / (step_ms * 1e-3) / 1e12, 2),
         "tokens_per_s": round(cfg.T / (step_ms * 1e-3), 1),
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "roofline": {"kernel": dom, "bound": "hbm" if hbm_bound else "mfma",
+                     "achieved": round(dom_gbps if hbm_bound else achieved, 1),
+                     "peak": HBM_PEAK if hbm_bound else peak,
+                     "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                     "frac": round(dom_gbps / HBM_PEAK if hbm_bound else achieved / peak, 4),
                      "traffic": traffic_for(cfg.name, dom), "ms": round(dom_ms, 4),
-                     # the same product against min(peak, intensity x 8 TB/s):
-                     # useful flops per algorithmic HBM byte decide whether
-                     # matrix cores or HBM bound it at this shape
+                     # the same kernel in flops, against the dense MFMA peak and
+                     # against min(peak, intensity x 8 TB/s)
+                     "useful_tflops": round(achieved, 1),
+                     "frac_of_mfma_peak": round(achieved / peak, 4),
                      "algorithmic_bytes": dom_bytes,
                      "intensity_flop_per_byte": round(intensity, 1),
-                     "attainable": round(attainable, 1),
-                     "attainable_bound": "mfma" if attainable >= peak else "hbm",
+                     "ridge_flop_per_byte": round(ridge, 1),
+                     "attainable_tflops": round(attainable, 1),
                      "frac_of_attainable": round(achieved / attainable, 4)},
         # every call timed alone in a probe pass before the timed steps
         "kernels": kernels,
-        "hbm_copy_ceiling": {"bytes": 2 * (half // 2) * 2, "gbps": round(copy_gbps, 1),
-                             "pct_hbm_peak": round(100 * copy_gbps / HBM_PEAK, 1)},
+        "forward_products": fwd or None,
+        "data_movement": dm,
+        "hbm_copy_ceiling": copy_ceiling,
         "schedule": "two streams" if two else "one stream",
     }
     out["step_ms_p10_p50_p90"] = [round(float(v), 4) for v in spread]
     if other is not None:
         key = "ms_per_step_one_stream" if two else "ms_per_step_two_streams"
         out[key] = round(other, 4)
-    if dense is not None:
-        # the block-sparse product's time against a dense GEMM of its executed
-        # shape (Tp x d x f): the block-sparse kernel runs at ratio x the
-        # dense GEMM's throughput on the same work
-        fl_exec = 2.0 * Tp * cfg.d * cfg.f
-        dense["sdd_ratio"] = round(dense["sdd_shape_ms"] * products_of(cfg, "sdd")
-                                   / kern["sdd"], 3)
-        dense["dsd_ratio"] = round(dense["dsd_shape_ms"] / kern["dsd"], 3)
-        dense["dense_tflops"] = round(fl_exec / (dense["sdd_shape_ms"] * 1e-3) / 1e12, 1)
-        out["context_dense_gemm"] = dense
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -32,7 +32,7 @@ SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_byt
            "bsg_route_noalloc",
            "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
            "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
-           "bsg_unpermute_combine", "bsg_status_string", "bsg_last_error")
+           "bsg_unpermute_combine", "bsg_stream_copy", "bsg_status_string", "bsg_last_error")
 
 
 class BsgError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
         L.bsg_route_workspace_bytes.argtypes = [i64, i32, i32]
         L.bsg_route.restype = i32
         L.bsg_route.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.bsg_stream_copy.restype = i32
+        L.bsg_stream_copy.argtypes = [vp, vp, sz, vp]
         L.bsg_route_noalloc.restype = i32
         L.bsg_route_noalloc.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.bsg_route_backward.restype = i32
@@ -267,3 +269,10 @@ def unpermute_combine(yp, dest_row, gate, T, k, d, y):
     _check("unpermute_combine", lib().bsg_unpermute_combine(
         _ptr(yp), dtype_code(yp), _ld(yp), _ptr(dest_row), _ptr(gate), T, k, d, _ptr(y),
         dtype_code(y), _stream()))
+
+
+def stream_copy(src, dst, nbytes=None):
+    """Copy nbytes (default: all of src) from src to dst with the library's
+    streaming copy (a measurement ceiling, not a step of the layer)."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check("stream_copy", lib().bsg_stream_copy(_ptr(src), _ptr(dst), n, _stream()))

@@ -529,4 +529,15 @@ bsg_status bsg_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
                       "unpermute_combine");
 }
 
+bsg_status bsg_stream_copy(const void* src, void* dst, size_t bytes, bsg_stream_t stream) {
+    REQUIRE_VEC_PTR(src);
+    REQUIRE_VEC_PTR(dst);
+    REQUIRE(bytes % 16 == 0 && bytes <= ((size_t)1 << 46), "bytes must be a multiple of 16");
+    const char* s = (const char*)src;
+    const char* d = (const char*)dst;
+    REQUIRE(s + bytes <= d || d + bytes <= s, "src and dst overlap");
+    return hip_status(bsg::launch_stream_copy(src, dst, (int64_t)(bytes / 16), (hipStream_t)stream),
+                      "stream_copy");
+}
+
 }  // extern "C"

@@ -113,4 +113,6 @@ hipError_t launch_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
                                     const int32_t* dest_row, const float* gate, int64_t T, int k,
                                     int d, void* y, int y_dtype, hipStream_t stream);
 
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t words, hipStream_t stream);
+
 }  // namespace bsg

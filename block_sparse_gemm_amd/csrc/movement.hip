@@ -285,6 +285,68 @@ __global__ __launch_bounds__(kMoveThreads) void combine_kernel(
     }
 }
 
+// A plain streaming copy of n 16-byte words, the HBM ceiling the
+// data-movement calls are measured against: every word read once and
+// written once.  Two forms, the faster of a sweep on the MI355X (grid sizes
+// 1K-64K workgroups, 2-16 words in flight per thread, temporal and
+// non-temporal accesses): up to 512 MiB, a grid-stride loop over up to
+// 16384 workgroups with eight loads of each thread in flight (4.1 TB/s at
+// 53 MB, 5.25 TB/s at 200 MB);
+// beyond it, each workgroup copies 16 KB blocks, four words per thread
+// (5.6 TB/s at 1 GiB).
+__global__ __launch_bounds__(kMoveThreads) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                                   u32x4* __restrict__ dst,
+                                                                   int64_t n) {
+    constexpr int U = 8;
+    const int64_t stride = (int64_t)gridDim.x * kMoveThreads;
+    int64_t i = (int64_t)blockIdx.x * kMoveThreads + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) dst[i + u * stride] = v[u];
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(kMoveThreads) void stream_copy_blocks_kernel(
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n) {
+    constexpr int U = 4;
+    constexpr int64_t kChunk = (int64_t)kMoveThreads * U;
+    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < n; base += (int64_t)gridDim.x * kChunk) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base + u * kMoveThreads + threadIdx.x;
+            if (j < n) v[u] = src[j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base + u * kMoveThreads + threadIdx.x;
+            if (j < n) dst[j] = v[u];
+        }
+    }
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t words, hipStream_t stream) {
+    if (words <= 0) return hipSuccess;
+    if (words * 16 > (int64_t(512) << 20)) {
+        const int64_t chunks = (words + kMoveThreads * 4 - 1) / (kMoveThreads * 4);
+        const int grid = (int)(chunks < 65536 ? chunks : 65536);
+        hipLaunchKernelGGL(stream_copy_blocks_kernel, dim3(grid), dim3(kMoveThreads), 0, stream,
+                           (const u32x4*)src, (u32x4*)dst, words);
+    } else {
+        // as many workgroups as the sweep found best: up to 16384, never more
+        // than one word per thread
+        const int64_t g = (words + kMoveThreads - 1) / kMoveThreads;
+        const int grid = (int)(g < 16384 ? g : 16384);
+        hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(kMoveThreads), 0, stream,
+                           (const u32x4*)src, (u32x4*)dst, words);
+    }
+    return hipGetLastError();
+}
+
 static int move_grid(int64_t jobs) {
     int64_t g = (jobs + kMoveWaves - 1) / kMoveWaves;
     return (int)(g < 8192 ? (g < 1 ? 1 : g) : 8192);

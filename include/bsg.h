@@ -356,6 +356,16 @@ bsg_status bsg_unpermute_combine(const void* yp, int yp_dtype, int64_t ld_yp,
                                  const int32_t* dest_row, const float* gate, int64_t T, int k,
                                  int d, void* y, int y_dtype, bsg_stream_t stream);
 
+/*
+ * stream_copy - a plain device-to-device copy of `bytes` bytes (a multiple of
+ * 16; src and dst 16-byte aligned, not overlapping), every byte read once
+ * and written once.  Not a step of the method: the HBM ceiling that the
+ * data-movement calls (permute_pad, unpermute_combine) are measured against,
+ * and a way to write enough memory to evict the last-level cache between
+ * timed runs.
+ */
+bsg_status bsg_stream_copy(const void* src, void* dst, size_t bytes, bsg_stream_t stream);
+
 /* Static description of a status code. */
 const char* bsg_status_string(bsg_status s);
 

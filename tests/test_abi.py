@@ -335,3 +335,12 @@ def test_route_noalloc_validation(L):
     # ceil(T / 64) * E * 4 bytes of counts: 1025 chunks x 1024 experts > 4 MiB
     assert bsg.route_workspace_bytes(64 * 1025, 1, 1024) > bsg.ROUTE_SCRATCH_BYTES
     assert call(T=64 * 1025, E=1024, k=1) == bsg.EUNSUPPORTED and "scratch" in _err(L)
+
+
+def test_stream_copy_validation(L):
+    Q = C.c_void_p(0x100000)
+    assert L.bsg_stream_copy(None, P, 64, None) == bsg.EINVAL
+    assert L.bsg_stream_copy(P, MIS, 64, None) == bsg.EINVAL
+    assert L.bsg_stream_copy(P, Q, 40, None) == bsg.EINVAL        # not a multiple of 16
+    assert L.bsg_stream_copy(P, C.c_void_p(0x10010), 64, None) == bsg.EINVAL  # overlap
+    assert "overlap" in _err(L)
