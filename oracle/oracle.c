@@ -234,21 +234,25 @@ int orc_permute_pad(const float* x, int64_t T, int d, int k, const int32_t* dest
  * col_idx; the COO half: row_idx per block), then a stable counting sort of
  * the blocks by column gives col_ptr and trans_idx (BCSR block ids listed in
  * column order, ascending block id inside a column).
- * Output sizes: row_ptr [Tp/128 + 1], col_ptr [E*F + 1], the others [nnz].
+ * Row blocks are br rows high (128, the block of section 1.3, or 64 for the
+ * block-size study) and 128 columns wide; every bin offset must be a
+ * multiple of br.
+ * Output sizes: row_ptr [Tp/br + 1], col_ptr [E*F + 1], the others [nnz].
  * Returns nnz, or -1 on bad arguments.
  */
-int64_t orc_topology(const int32_t* bin_offsets, int E, int F, int32_t* row_ptr, int32_t* col_idx,
-                     int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx) {
-    if (!bin_offsets || E < 1 || F < 1) return -1;
+int64_t orc_topology(const int32_t* bin_offsets, int E, int F, int br, int32_t* row_ptr,
+                     int32_t* col_idx, int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx) {
+    if (!bin_offsets || E < 1 || F < 1 || br < 1) return -1;
     int64_t Tp = bin_offsets[E];
-    if (Tp % BLK) return -1;
-    int64_t R = Tp / BLK, C = (int64_t)E * F;
+    for (int e = 0; e <= E; ++e)
+        if (bin_offsets[e] % br) return -1;
+    int64_t R = Tp / br, C = (int64_t)E * F;
     int64_t nnz = 0;
     for (int64_t r = 0; r < R; ++r) {
         row_ptr[r] = (int32_t)nnz;
         int owner = -1;
         for (int e = 0; e < E; ++e)
-            if (r * BLK >= bin_offsets[e] && r * BLK < bin_offsets[e + 1]) owner = e;
+            if (r * br >= bin_offsets[e] && r * br < bin_offsets[e + 1]) owner = e;
         for (int64_t c = 0; c < C; ++c) {
             if (c / F == owner) {
                 col_idx[nnz] = (int32_t)c;
@@ -822,22 +826,23 @@ int orc_dW3_block(const orc_layer* L, const int64_t* rows, int64_t nr, const int
  * first layer kept only at the nonzero blocks, then DSD, sparse x dense;
  * section 1.3: DSTD, the transposed sparse operand times a dense one, one
  * block column at a time through the transpose index), for the MoE
- * topology the bins define: row block r belongs to the expert e whose bin
- * holds row 128 r, and expert e owns column blocks e*F .. e*F + F - 1, so
- * nonzero block b = r*F + j sits at (r, e*F + j).  Operands hold the stored
+ * topology the bins define: blocks are br rows (128, or 64 for the
+ * block-size study) by 128 columns, row block r belongs to the expert e
+ * whose bin holds row br * r, and expert e owns column blocks
+ * e*F .. e*F + F - 1, so nonzero block b = r*F + j sits at (r, e*F + j).  Operands hold the stored
  * values (bf16 widened to fp32); sums run in fp64 over k ascending and are
  * rounded once to prec, after the epilogue.  Block arrays are block-major,
- * [nnz][128][128], a second plane nnz blocks after the first.
+ * [nnz][br][128], a second plane nnz blocks after the first.
  */
 
 /* expert of each row block, from the bins; returns the row-block count */
-static int64_t row_owners(const int32_t* bin_offsets, int E, int32_t** owner) {
-    const int64_t R = bin_offsets[E] / BLK;
+static int64_t row_owners(const int32_t* bin_offsets, int E, int br, int32_t** owner) {
+    const int64_t R = bin_offsets[E] / br;
     int32_t* o = (int32_t*)malloc(sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
     for (int64_t r = 0; r < R; ++r) {
         o[r] = -1;
         for (int e = 0; e < E; ++e)
-            if (r * BLK >= bin_offsets[e] && r * BLK < bin_offsets[e + 1]) o[r] = e;
+            if (r * br >= bin_offsets[e] && r * br < bin_offsets[e + 1]) o[r] = e;
     }
     *owner = o;
     return R;
@@ -850,7 +855,7 @@ static double elem(const float* b, int64_t ld, int trans, int64_t k, int64_t n) 
 }
 
 /*
- * SDD: acc_b[m][n] = sum_k a[128 r + m][k] * B[k][128 c + n], k < K, then
+ * SDD: acc_b[m][n] = sum_k a[br r + m][k] * B[k][128 c + n], k < K, then
  *   epi 0  acc
  *   epi 1  gelu(acc); aux_out (if not NULL) gelu'(acc)
  *   epi 2  silu(acc) * acc2 (acc2 from b2); aux_out (if not NULL) two planes:
@@ -860,23 +865,24 @@ static double elem(const float* b, int64_t ld, int trans, int64_t k, int64_t n) 
  * Returns nnz, or -1 on bad arguments.
  */
 int64_t orc_sdd(const float* a, int64_t lda, const float* b, const float* b2, int64_t ldb,
-                int trans_b, int K, const int32_t* bin_offsets, int E, int F, int epi,
+                int trans_b, int K, const int32_t* bin_offsets, int E, int F, int br, int epi,
                 const float* aux_in, int prec, double* out, double* aux_out) {
-    if (!a || !b || !bin_offsets || !out || K < 1 || E < 1 || F < 1 || epi < 0 || epi > 4)
+    if (!a || !b || !bin_offsets || !out || K < 1 || E < 1 || F < 1 || br < 1 || epi < 0 ||
+        epi > 4)
         return -1;
     if ((epi == 2 && !b2) || ((epi == 3 || epi == 4) && !aux_in)) return -1;
     int32_t* owner;
-    const int64_t R = row_owners(bin_offsets, E, &owner);
+    const int64_t R = row_owners(bin_offsets, E, br, &owner);
     const int64_t nnz = R * F;
-    const int64_t bs = (int64_t)BLK * BLK;
+    const int64_t bs = (int64_t)br * BLK;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t blk = 0; blk < nnz; ++blk) {
         const int64_t r = blk / F, c = (int64_t)owner[r] * F + blk % F;
-        double* acc = dalloc(BLK * BLK);
-        double* acc2 = dalloc(BLK * BLK);
+        double* acc = dalloc(bs);
+        double* acc2 = dalloc(bs);
         for (int64_t i = 0; i < bs; ++i) acc[i] = acc2[i] = 0.0;
-        for (int64_t m = 0; m < BLK; ++m) {
-            const float* ar = a + (r * BLK + m) * lda;
+        for (int64_t m = 0; m < br; ++m) {
+            const float* ar = a + (r * br + m) * lda;
             for (int64_t k = 0; k < K; ++k) {
                 const double av = ar[k];
                 for (int64_t n = 0; n < BLK; ++n) {
@@ -915,22 +921,23 @@ int64_t orc_sdd(const float* a, int64_t lda, const float* b, const float* b2, in
 }
 
 /*
- * DSD: c[128 r + m][n] = sum over the blocks b of row r (ascending), sum_j
+ * DSD: c[br r + m][n] = sum over the blocks b of row r (ascending), sum_j
  * blocks[b][m][j] * B[128 col(b) + j][n], then the same over blocks2 with
  * B2 from b2 when blocks2 is not NULL; c is [Tp][N] (row-major, N columns).
  * Returns the row count Tp, or -1 on bad arguments.
  */
 int64_t orc_dsd(const float* blocks, const float* blocks2, const int32_t* bin_offsets, int E,
-                int F, const float* b, const float* b2, int64_t ldb, int trans_b, int N, int prec,
-                double* c) {
-    if (!blocks || !bin_offsets || !b || !c || E < 1 || F < 1 || N < 1 || (blocks2 && !b2))
+                int F, int br, const float* b, const float* b2, int64_t ldb, int trans_b, int N,
+                int prec, double* c) {
+    if (!blocks || !bin_offsets || !b || !c || E < 1 || F < 1 || br < 1 || N < 1 ||
+        (blocks2 && !b2))
         return -1;
     int32_t* owner;
-    const int64_t R = row_owners(bin_offsets, E, &owner);
-    const int64_t bs = (int64_t)BLK * BLK;
+    const int64_t R = row_owners(bin_offsets, E, br, &owner);
+    const int64_t bs = (int64_t)br * BLK;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t row = 0; row < R * BLK; ++row) {
-        const int64_t r = row / BLK, m = row % BLK;
+    for (int64_t row = 0; row < R * br; ++row) {
+        const int64_t r = row / br, m = row % br;
         double* acc = dalloc(N);
         for (int n = 0; n < N; ++n) acc[n] = 0.0;
         for (int set = 0; set < (blocks2 ? 2 : 1); ++set) {
@@ -948,30 +955,30 @@ int64_t orc_dsd(const float* blocks, const float* blocks2, const int32_t* bin_of
         free(acc);
     }
     free(owner);
-    return R * BLK;
+    return R * br;
 }
 
 /*
  * DSTD: C[128 c + m][n] = sum over the blocks b of block column c, in
  * ascending row (the transpose index's order), sum_j blocks[b][j][m] *
- * dmat[128 row(b) + j][n]; C is [E*F*128][N]; a column without blocks (an
+ * dmat[br row(b) + j][n]; C is [E*F*128][N]; a column without blocks (an
  * expert without rows) is zero.  Returns 0, or -1 on bad arguments.
  */
-int orc_dstd(const float* blocks, const int32_t* bin_offsets, int E, int F, const float* dmat,
-             int64_t ldd, int N, int prec, double* C) {
-    if (!blocks || !bin_offsets || !dmat || !C || E < 1 || F < 1 || N < 1) return -1;
-    const int64_t bs = (int64_t)BLK * BLK;
+int orc_dstd(const float* blocks, const int32_t* bin_offsets, int E, int F, int br,
+             const float* dmat, int64_t ldd, int N, int prec, double* C) {
+    if (!blocks || !bin_offsets || !dmat || !C || E < 1 || F < 1 || br < 1 || N < 1) return -1;
+    const int64_t bs = (int64_t)br * BLK;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t out_row = 0; out_row < (int64_t)E * F * BLK; ++out_row) {
         const int64_t c = out_row / BLK, m = out_row % BLK;
         const int e = (int)(c / F), j = (int)(c % F);
         double* acc = dalloc(N);
         for (int n = 0; n < N; ++n) acc[n] = 0.0;
-        for (int64_t r = bin_offsets[e] / BLK; r < bin_offsets[e + 1] / BLK; ++r) {
+        for (int64_t r = bin_offsets[e] / br; r < bin_offsets[e + 1] / br; ++r) {
             const int64_t blk = r * F + j;
-            for (int64_t q = 0; q < BLK; ++q) {
+            for (int64_t q = 0; q < br; ++q) {
                 const double v = blocks[blk * bs + q * BLK + m];
-                const float* dr = dmat + (r * BLK + q) * ldd;
+                const float* dr = dmat + (r * br + q) * ldd;
                 for (int n = 0; n < N; ++n) acc[n] += v * (double)dr[n];
             }
         }

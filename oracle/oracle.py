@@ -78,7 +78,8 @@ def lib():
         L.orc_route_backward.argtypes = [_f32p, C.c_int64, C.c_int, C.c_int, C.c_int, _i32p,
                                          _f32p, _f64p, C.c_int, _f64p]
         L.orc_topology.restype = C.c_int64
-        L.orc_topology.argtypes = [_i32p, C.c_int, C.c_int, _i32p, _i32p, _i32p, _i32p, _i32p]
+        L.orc_topology.argtypes = [_i32p, C.c_int, C.c_int, C.c_int, _i32p, _i32p, _i32p, _i32p,
+                                   _i32p]
         lp = C.POINTER(_Layer)
         L.orc_assign_forward.argtypes = [lp, _i64p, C.c_int64, _f64p, _f64p, _f64p, _f64p]
         L.orc_forward_tokens.argtypes = [lp, _i64p, C.c_int64, _f64p]
@@ -88,13 +89,13 @@ def lib():
             getattr(L, n).argtypes = [lp, _i64p, C.c_int64, _i64p, C.c_int64, _f64p]
         L.orc_sdd.restype = C.c_int64
         L.orc_sdd.argtypes = [_f32p, C.c_int64, _f32p, _f32p, C.c_int64, C.c_int, C.c_int, _i32p,
-                              C.c_int, C.c_int, C.c_int, _f32p, C.c_int, _f64p, _f64p]
+                              C.c_int, C.c_int, C.c_int, C.c_int, _f32p, C.c_int, _f64p, _f64p]
         L.orc_dsd.restype = C.c_int64
-        L.orc_dsd.argtypes = [_f32p, _f32p, _i32p, C.c_int, C.c_int, _f32p, _f32p, C.c_int64,
-                              C.c_int, C.c_int, C.c_int, _f64p]
+        L.orc_dsd.argtypes = [_f32p, _f32p, _i32p, C.c_int, C.c_int, C.c_int, _f32p, _f32p,
+                              C.c_int64, C.c_int, C.c_int, C.c_int, _f64p]
         L.orc_dstd.restype = C.c_int
-        L.orc_dstd.argtypes = [_f32p, _i32p, C.c_int, C.c_int, _f32p, C.c_int64, C.c_int,
-                               C.c_int, _f64p]
+        L.orc_dstd.argtypes = [_f32p, _i32p, C.c_int, C.c_int, C.c_int, _f32p, C.c_int64,
+                               C.c_int, C.c_int, _f64p]
         for n in ("orc_assign_forward", "orc_forward_tokens", "orc_assign_backward",
                   "orc_backward_tokens", "orc_dW2_block", "orc_dW1_block", "orc_dW3_block"):
             getattr(L, n).restype = C.c_int
@@ -198,18 +199,19 @@ def permute_pad(x: np.ndarray, k: int, dest_row: np.ndarray, Tp: int, scale=None
     return xp
 
 
-def topology(bin_offsets: np.ndarray, E: int, F: int) -> dict:
+def topology(bin_offsets: np.ndarray, E: int, F: int, block_rows: int = 128) -> dict:
     """Hybrid BCSR-COO topology and transpose index of the block-diagonal
-    first-layer output."""
+    first-layer output, in blocks of block_rows x 128."""
     bo = np.ascontiguousarray(bin_offsets, np.int32)
-    R = int(bo[E]) // 128
+    R = int(bo[E]) // block_rows
     cap = R * F
     row_ptr = np.zeros(R + 1, np.int32)
     col_idx = np.zeros(cap, np.int32)
     row_idx = np.zeros(cap, np.int32)
     col_ptr = np.zeros(E * F + 1, np.int32)
     trans_idx = np.zeros(cap, np.int32)
-    nnz = lib().orc_topology(_p(bo, _i32p), E, F, _p(row_ptr, _i32p), _p(col_idx, _i32p),
+    nnz = lib().orc_topology(_p(bo, _i32p), E, F, block_rows, _p(row_ptr, _i32p),
+                             _p(col_idx, _i32p),
                              _p(row_idx, _i32p), _p(col_ptr, _i32p), _p(trans_idx, _i32p))
     if nnz < 0:
         raise ValueError("orc_topology rejected its arguments")
@@ -341,33 +343,35 @@ def make_layer(x, W1, W2, route_out, k, E, act="gelu", W3=None, dy=None, prec="b
 SDD_EPI = {"none": 0, "gelu": 1, "silu_mul": 2, "gelu_bwd": 3, "silu_mul_bwd": 4}
 
 
-def _nnz(bin_offsets, E, F):
-    return int(bin_offsets[E]) // 128 * F
+def _nnz(bin_offsets, E, F, br):
+    return int(bin_offsets[E]) // br * F
 
 
 def sdd(a, b, K, bin_offsets, E, F, epilogue="none", prec="bf16", b2=None, trans_b=False,
-        aux_in=None, want_aux=False):
-    """Blocks [planes * nnz, 128, 128] of the first-layer product (and the
-    saved factors when want_aux, for gelu / silu_mul)."""
+        aux_in=None, want_aux=False, block_rows=128):
+    """Blocks [planes * nnz, block_rows, 128] of the first-layer product (and
+    the saved factors when want_aux, for gelu / silu_mul)."""
     a, b, b2 = _f32(a), _f32(b), _f32(b2)
     bo = np.ascontiguousarray(bin_offsets, np.int32)
-    nnz = _nnz(bo, E, F)
+    br = int(block_rows)
+    nnz = _nnz(bo, E, F, br)
     epi = SDD_EPI[epilogue]
     planes = 2 if epi == 4 else 1
-    out = np.zeros((planes * nnz, 128, 128))
-    aux = np.zeros(((2 if epi == 2 else 1) * nnz, 128, 128)) if want_aux else None
+    out = np.zeros((planes * nnz, br, 128))
+    aux = np.zeros(((2 if epi == 2 else 1) * nnz, br, 128)) if want_aux else None
     ai = None if aux_in is None else _f32(aux_in).reshape(-1)
     if b2 is not None and b2.shape != b.shape:
         raise ValueError("b2 must have b's shape")
     rc = lib().orc_sdd(_p(a, _f32p), a.shape[1], _p(b, _f32p), _p(b2, _f32p), b.shape[1],
-                       int(bool(trans_b)), int(K), _p(bo, _i32p), E, F, epi, _p(ai, _f32p),
+                       int(bool(trans_b)), int(K), _p(bo, _i32p), E, F, br, epi, _p(ai, _f32p),
                        PREC[prec], _p(out, _f64p), _p(aux, _f64p))
     if rc != nnz:
         raise ValueError("orc_sdd rejected its arguments")
     return (out, aux) if want_aux else out
 
 
-def dsd(blocks, bin_offsets, E, F, b, N, prec="bf16", trans_b=False, blocks2=None, b2=None):
+def dsd(blocks, bin_offsets, E, F, b, N, prec="bf16", trans_b=False, blocks2=None, b2=None,
+        block_rows=128):
     """Rows [Tp, N] of the sparse x dense product (two block sets summed
     when blocks2 / b2 are given)."""
     bl, bl2 = _f32(blocks).reshape(-1), None if blocks2 is None else _f32(blocks2).reshape(-1)
@@ -375,21 +379,21 @@ def dsd(blocks, bin_offsets, E, F, b, N, prec="bf16", trans_b=False, blocks2=Non
     bo = np.ascontiguousarray(bin_offsets, np.int32)
     Tp = int(bo[E])
     c = np.zeros((Tp, N))
-    rc = lib().orc_dsd(_p(bl, _f32p), _p(bl2, _f32p), _p(bo, _i32p), E, F, _p(b, _f32p),
-                       _p(b2, _f32p), b.shape[1], int(bool(trans_b)), int(N), PREC[prec],
-                       _p(c, _f64p))
+    rc = lib().orc_dsd(_p(bl, _f32p), _p(bl2, _f32p), _p(bo, _i32p), E, F, int(block_rows),
+                       _p(b, _f32p), _p(b2, _f32p), b.shape[1], int(bool(trans_b)), int(N),
+                       PREC[prec], _p(c, _f64p))
     if rc != Tp:
         raise ValueError("orc_dsd rejected its arguments")
     return c
 
 
-def dstd(blocks, bin_offsets, E, F, dmat, N, prec="bf16"):
+def dstd(blocks, bin_offsets, E, F, dmat, N, prec="bf16", block_rows=128):
     """The weight-gradient product [E * F * 128, N] (untransposed)."""
     bl, dm = _f32(blocks).reshape(-1), _f32(dmat)
     bo = np.ascontiguousarray(bin_offsets, np.int32)
     C_ = np.zeros((E * F * 128, N))
-    rc = lib().orc_dstd(_p(bl, _f32p), _p(bo, _i32p), E, F, _p(dm, _f32p), dm.shape[1], int(N),
-                        PREC[prec], _p(C_, _f64p))
+    rc = lib().orc_dstd(_p(bl, _f32p), _p(bo, _i32p), E, F, int(block_rows), _p(dm, _f32p),
+                        dm.shape[1], int(N), PREC[prec], _p(C_, _f64p))
     if rc != 0:
         raise ValueError("orc_dstd rejected its arguments")
     return C_

@@ -35,7 +35,7 @@ int orc_route(const float* logits, int64_t T, int E, int k, int renorm, int bin,
               int32_t* dest_row, int32_t* row_src, int64_t row_src_len);
 int orc_permute_pad(const float* x, int64_t T, int d, int k, const int32_t* dest_row,
                     const float* scale, int prec, int64_t Tp, double* xp);
-int64_t orc_topology(const int32_t* bin_offsets, int E, int F, int32_t* row_ptr,
+int64_t orc_topology(const int32_t* bin_offsets, int E, int F, int br, int32_t* row_ptr,
                      int32_t* col_idx, int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx);
 int orc_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
                        const int32_t* expert_idx, const float* dy, const double* yp, int d,
@@ -167,6 +167,9 @@ static void abi_checks() {
                                 nullptr) == BSG_OK);
     EXPECT(bsg_dstd(P, &t, P, 256, 256, P, 1024, 1, BSG_BF16, nullptr) == BSG_OK);
     EXPECT(bsg_dstd(P, &t, P, INT64_MAX, 256, P, 1024, 1, BSG_BF16, nullptr) == BSG_EINVAL);
+    EXPECT(bsg_stream_copy(P, (void*)0x100000, 4096, nullptr) == BSG_OK);
+    EXPECT(bsg_stream_copy(P, (void*)0x10010, 4096, nullptr) == BSG_EINVAL);
+    EXPECT(bsg_stream_copy(P, (void*)0x100000, SIZE_MAX - 15, nullptr) == BSG_EINVAL);
     EXPECT(strcmp(bsg_status_string(BSG_EHIP), "HIP runtime error") == 0);
     EXPECT(strcmp(bsg_status_string((bsg_status)7), "unknown status") == 0);
 }
@@ -197,8 +200,8 @@ static void oracle_checks() {
     const int F = 2;
     std::vector<int32_t> rp(Tp / 128 + 1), ci(Tp / 128 * F), ri(Tp / 128 * F), cp(E * F + 1),
         tr(Tp / 128 * F);
-    EXPECT(orc_topology(bo.data(), E, F, rp.data(), ci.data(), ri.data(), cp.data(), tr.data()) ==
-           Tp / 128 * F);
+    EXPECT(orc_topology(bo.data(), E, F, 128, rp.data(), ci.data(), ri.data(), cp.data(),
+                        tr.data()) == Tp / 128 * F);
     for (int act = 0; act < 2; ++act)
         for (int prec = 0; prec < 3; ++prec) {
             orc_layer L = {T, d, E, f, k, act, prec, prec, x.data(), W1.data(), W3.data(),

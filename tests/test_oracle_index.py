@@ -120,11 +120,12 @@ def test_route_workloads(orc, name):
         assert counts[-1] > 0 and np.sum(counts < 128) >= 6
 
 
-def closed_form_topology(bo, E, F):
-    """The block-diagonal MoE topology written out directly."""
-    R_e = np.diff(bo) // 128
-    s_e = bo[:-1] // 128
-    R = int(bo[E]) // 128
+def closed_form_topology(bo, E, F, br=128):
+    """The block-diagonal MoE topology written out directly (blocks of br
+    rows)."""
+    R_e = np.diff(bo) // br
+    s_e = bo[:-1] // br
+    R = int(bo[E]) // br
     owner = np.repeat(np.arange(E), R_e)
     row_ptr = np.arange(R + 1) * F
     col_idx = (owner[:, None] * F + np.arange(F)[None, :]).reshape(-1)
@@ -148,18 +149,20 @@ def test_topology_golden(orc):
         assert t[key].tolist() == g[key], key
 
 
+@pytest.mark.parametrize("br", [128, 64])
 @pytest.mark.parametrize("counts,F", [([3, 4, 3], 2), ([0, 300, 0, 129, 1], 3), ([128], 1),
-                                      ([0, 0, 5], 4), ([1000, 0, 256, 17, 128, 129], 5)])
-def test_topology_closed_form_and_invariants(orc, counts, F):
+                                      ([0, 0, 5], 4), ([1000, 0, 256, 17, 128, 129], 5),
+                                      ([64, 65, 0, 191, 192, 193], 2)])
+def test_topology_closed_form_and_invariants(orc, counts, F, br):
     E = len(counts)
-    P = [(c + 127) // 128 * 128 for c in counts]
+    P = [(c + br - 1) // br * br for c in counts]
     bo = np.concatenate([[0], np.cumsum(P)]).astype(np.int32)
-    t = orc.topology(bo, E, F)
-    cf = closed_form_topology(bo, E, F)
+    t = orc.topology(bo, E, F, br)
+    cf = closed_form_topology(bo, E, F, br)
     for key, want in zip(("row_ptr", "col_idx", "row_idx", "col_ptr", "trans_idx"), cf):
         assert np.array_equal(t[key], want), key
     nnz = t["nnz"]
-    assert nnz == (bo[E] // 128) * F
+    assert nnz == (bo[E] // br) * F
     # one materialised row index per block, consistent with the row pointer
     assert len(t["row_idx"]) == nnz
     for r in range(len(t["row_ptr"]) - 1):
@@ -209,3 +212,13 @@ def test_route_coarser_and_finer_bins(orc, bin_rows):
     assert int(r["bin_offsets"][E]) == sum(-(-int(x) // bin_rows) * bin_rows for x in c)
     r128 = orc.route(logits, k, False)
     assert np.array_equal(r["gate"], r128["gate"])
+
+
+def test_topology_refuses_bins_off_the_block_grid(orc):
+    """Bins of 64 rows need blocks of 64 rows: a bin offset that is not a
+    multiple of the block height is refused."""
+    bo = np.array([0, 64, 192], np.int32)
+    with pytest.raises(ValueError):
+        orc.topology(bo, 2, 2, 128)
+    t = orc.topology(bo, 2, 2, 64)
+    assert t["nnz"] == 3 * 2

@@ -16,7 +16,7 @@ def _layer(orc, cfg, seed, empty=None):
     inp = synth.make_inputs(cfg, seed)
     if empty is not None:
         inp["logits"][:, empty] = -50.0
-    r = orc.route(inp["logits"], cfg.k, cfg.renorm)
+    r = orc.route(inp["logits"], cfg.k, cfg.renorm, cfg.bin_rows)
     O = orc.make_layer(inp["x"].values, inp["W1"].values, inp["W2"].values, r, cfg.k, cfg.E,
                        act=cfg.act, W3=inp["W3"].values if "W3" in inp else None,
                        dy=inp["dy"].values, prec=cfg.dtype, prec_yp=cfg.yp)
@@ -24,20 +24,27 @@ def _layer(orc, cfg, seed, empty=None):
 
 
 def _rows(blocks, F, rows):
-    """Full rows [len(rows), F*128] of a block-major array."""
-    b = blocks.reshape(-1, 128, 128)
-    base = (rows // 128) * F
-    return np.concatenate([b[base + j, rows % 128] for j in range(F)], axis=1)
+    """Full rows [len(rows), F*128] of a block-major array (block height
+    from the array's shape)."""
+    br = blocks.shape[1]
+    b = blocks.reshape(-1, br, 128)
+    base = (rows // br) * F
+    return np.concatenate([b[base + j, rows % br] for j in range(F)], axis=1)
 
 
+@pytest.mark.parametrize("br", [128, 64])
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
-def test_products_reproduce_the_per_token_oracle(orc, act):
+def test_products_reproduce_the_per_token_oracle(orc, act, br):
+    """Blocks of 128 rows over bins of 128, and blocks of 64 rows over bins
+    of 64 (the block-size study)."""
     kw = dict(renorm=True) if act == "swiglu" else {}
     cfg = synth.LayerConfig("prod_pin", T=300, d=128, E=4, f=256, k=2, act=act, backward=True,
-                            **kw)
+                            bin_rows=br, **kw)
     inp, r, O = _layer(orc, cfg, 3, empty=2)       # expert 2 gets no token
     E, F, d, f = cfg.E, cfg.f // 128, cfg.d, cfg.f
     bo = r["bin_offsets"]
+    assert np.all(bo % br == 0)
+    P = dict(block_rows=br)
     Tp = int(bo[E])
     assert r["counts"][2] == 0
     xp = orc.permute_pad(inp["x"].values, cfg.k, r["dest_row"], Tp, prec="bf16")
@@ -50,11 +57,11 @@ def test_products_reproduce_the_per_token_oracle(orc, act):
 
     # first layer + activation (and the saved factors)
     if act == "gelu":
-        A, G = orc.sdd(xp, inp["W1"].values, d, bo, E, F, "gelu", want_aux=True)
+        A, G = orc.sdd(xp, inp["W1"].values, d, bo, E, F, "gelu", want_aux=True, **P)
         assert np.array_equal(_rows(G, F, rows), S)
     else:
         A, SQ = orc.sdd(xp, inp["W1"].values, d, bo, E, F, "silu_mul", b2=inp["W3"].values,
-                        want_aux=True)
+                        want_aux=True, **P)
         nnz = A.shape[0]
         assert np.array_equal(_rows(SQ[:nnz], F, rows), S[0])
         assert np.array_equal(_rows(SQ[nnz:], F, rows), S[1])
@@ -65,33 +72,34 @@ def test_products_reproduce_the_per_token_oracle(orc, act):
     assert not np.any(_rows(A, F, pad))
 
     # second layer
-    Yp = orc.dsd(A, bo, E, F, inp["W2"].values, d)
+    Yp = orc.dsd(A, bo, E, F, inp["W2"].values, d, **P)
     assert np.array_equal(Yp[rows], Yp_tok)
     assert np.array_equal(dyp[rows], dYp_tok)
 
     # backward first product: dA = dYp W2^T, times the saved factor(s)
     if act == "gelu":
-        dH = orc.sdd(dyp, inp["W2"].values, d, bo, E, F, "gelu_bwd", trans_b=True, aux_in=G)
+        dH = orc.sdd(dyp, inp["W2"].values, d, bo, E, F, "gelu_bwd", trans_b=True, aux_in=G,
+                     **P)
         assert np.array_equal(_rows(dH, F, rows), dH_tok)
-        dXp = orc.dsd(dH, bo, E, F, inp["W1"].values, d, trans_b=True)
+        dXp = orc.dsd(dH, bo, E, F, inp["W1"].values, d, trans_b=True, **P)
         assert np.array_equal(dXp[rows], dXp_tok)
     else:
         dH = orc.sdd(dyp, inp["W2"].values, d, bo, E, F, "silu_mul_bwd", trans_b=True,
-                     aux_in=G)
+                     aux_in=G, **P)
         nnz = dH.shape[0] // 2
         assert np.array_equal(_rows(dH[:nnz], F, rows), dH_tok[0])   # gate projection
         assert np.array_equal(_rows(dH[nnz:], F, rows), dH_tok[1])   # up projection
         dXp = orc.dsd(dH[:nnz], bo, E, F, inp["W1"].values, d, trans_b=True, blocks2=dH[nnz:],
-                      b2=inp["W3"].values)
+                      b2=inp["W3"].values, **P)
         # the two projections' sums may interleave differently: equal up to
         # one rounding of nearly equal fp64 sums
         np.testing.assert_allclose(dXp[rows], dXp_tok, rtol=2 ** -7, atol=1e-12)
 
     # weight gradients through the transpose index; the empty expert's are zero
-    dW2 = orc.dstd(A, bo, E, F, dyp, d)
+    dW2 = orc.dstd(A, bo, E, F, dyp, d, **P)
     all_rows, all_cols = np.arange(E * f), np.arange(d)
     assert np.array_equal(dW2, O.dW2_block(all_rows, all_cols))
-    dW1t = orc.dstd(dH if act == "gelu" else dH[:dH.shape[0] // 2], bo, E, F, xp, d)
+    dW1t = orc.dstd(dH if act == "gelu" else dH[:dH.shape[0] // 2], bo, E, F, xp, d, **P)
     assert np.array_equal(dW1t.T, O.dW1_block(all_cols, all_rows))
     assert not np.any(dW2[2 * f:3 * f]) and not np.any(dW1t[2 * f:3 * f])
 
