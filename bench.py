@@ -71,7 +71,7 @@ def parse():
                     help="every call in order on one stream (the layer's choice otherwise)")
     ap.add_argument("--overlap", action="store_true",
                     help="weight gradients on a second stream in the timed steps")
-    ap.add_argument("--bin-rows", type=int, default=128, choices=(128, 256),
+    ap.add_argument("--bin-rows", type=int, default=128, choices=(64, 128, 256),
                     help="pad expert bins to a multiple of this many rows (block-size study)")
     ap.add_argument("--compare-schedules", action="store_true",
                     help="after the timed steps, also time the other backward schedule")
@@ -98,7 +98,7 @@ def algorithmic_bytes(cfg, kernel, Tp, fuse_top1):
     b = 2 if cfg.dtype == "bf16" else 4
     byp = 4 if (cfg.yp == "f32" or cfg.dtype == "f32") else 2
     sw = cfg.act == "swiglu"
-    plane = (Tp // 128) * (cfg.f // 128) * 128 * 128 * b  # A, a saved factor or dH
+    plane = Tp * cfg.f * b                                 # A, a saved factor or dH
     weight = cfg.d * cfg.E * cfg.f * b                     # W1, W2 or W3
     rows = Tp * cfg.d * b                                  # Xp or dYp
     tokens = cfg.T * cfg.d * b                             # y or dx
@@ -377,7 +377,7 @@ def main():
     # executed shape (Tp x d x f)
     per_product = 2.0 * cfg.T * cfg.k * cfg.d * cfg.f
     peak = MFMA_PEAK_BF16 if cfg.dtype == "bf16" else MFMA_PEAK_F32
-    plane = (Tp // 128) * (cfg.f // 128) * 128 * 128 * es
+    plane = Tp * cfg.f * es
     weight = cfg.d * cfg.E * cfg.f * es
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 

@@ -43,14 +43,15 @@ class BsgError(RuntimeError):
 
 class TopoSizes(C.Structure):
     _fields_ = [("row_blocks_max", C.c_int64), ("nnz_max", C.c_int64), ("n_cols", C.c_int64),
-                ("row_pairs_max", C.c_int64)]
+                ("row_tiles_max", C.c_int64)]
 
 
 class TopologyStruct(C.Structure):
     _fields_ = [("row_ptr", C.c_void_p), ("col_idx", C.c_void_p), ("row_idx", C.c_void_p),
-                ("col_ptr", C.c_void_p), ("trans_idx", C.c_void_p), ("row_pairs", C.c_void_p),
+                ("col_ptr", C.c_void_p), ("trans_idx", C.c_void_p), ("row_tiles", C.c_void_p),
                 ("expert_order", C.c_void_p), ("meta", C.c_void_p),
-                ("E", C.c_int32), ("F", C.c_int32), ("Tp_max", C.c_int64)]
+                ("E", C.c_int32), ("F", C.c_int32), ("block_rows", C.c_int32),
+                ("Tp_max", C.c_int64)]
 
 
 _lib = None
@@ -67,7 +68,7 @@ def lib():
         L.bsg_max_padded_rows.restype = i64
         L.bsg_max_padded_rows.argtypes = [i64, i32, i32, i32]
         L.bsg_topology_sizes.restype = i32
-        L.bsg_topology_sizes.argtypes = [i64, i32, i32, C.POINTER(TopoSizes)]
+        L.bsg_topology_sizes.argtypes = [i64, i32, i32, i32, C.POINTER(TopoSizes)]
         L.bsg_route_workspace_bytes.restype = sz
         L.bsg_route_workspace_bytes.argtypes = [i64, i32, i32]
         L.bsg_route.restype = i32
@@ -148,9 +149,9 @@ def max_padded_rows(T: int, k: int, E: int, bin_rows: int = BLOCK) -> int:
     return int(lib().bsg_max_padded_rows(T, k, E, bin_rows))
 
 
-def topology_sizes(Tp_max: int, E: int, f: int) -> TopoSizes:
+def topology_sizes(Tp_max: int, E: int, f: int, block_rows: int = BLOCK) -> TopoSizes:
     out = TopoSizes()
-    _check("topology_sizes", lib().bsg_topology_sizes(Tp_max, E, f, C.byref(out)))
+    _check("topology_sizes", lib().bsg_topology_sizes(Tp_max, E, f, block_rows, C.byref(out)))
     return out
 
 
@@ -161,27 +162,29 @@ def route_workspace_bytes(T: int, k: int, E: int) -> int:
 # ------------------------------------------------------------------ topology
 
 class Topology:
-    """Device buffers of one hybrid BCSR-COO topology (capacity for Tp_max)."""
+    """Device buffers of one hybrid BCSR-COO topology (capacity for Tp_max),
+    in blocks of block_rows (128, or 64 for bins of 64 rows) x 128."""
 
-    def __init__(self, Tp_max: int, E: int, f: int, device="cuda"):
-        sz = topology_sizes(Tp_max, E, f)
+    def __init__(self, Tp_max: int, E: int, f: int, device="cuda", block_rows: int = BLOCK):
+        sz = topology_sizes(Tp_max, E, f, block_rows)
         i32 = dict(dtype=torch.int32, device=device)
         self.E, self.F, self.f, self.Tp_max = E, f // BLOCK, f, Tp_max
+        self.block_rows = block_rows
         self.row_blocks_max, self.nnz_max = int(sz.row_blocks_max), int(sz.nnz_max)
         self.row_ptr = torch.zeros(self.row_blocks_max + 1, **i32)
         self.col_idx = torch.zeros(self.nnz_max, **i32)
         self.row_idx = torch.zeros(self.nnz_max, **i32)
         self.col_ptr = torch.zeros(E * self.F + 1, **i32)
         self.trans_idx = torch.zeros(self.nnz_max, **i32)
-        self.row_pairs_max = int(sz.row_pairs_max)
-        self.row_pairs = torch.zeros(self.row_pairs_max, **i32)
+        self.row_tiles_max = int(sz.row_tiles_max)
+        self.row_tiles = torch.zeros(self.row_tiles_max, **i32)
         self.expert_order = torch.zeros(E, **i32)
         self.meta = torch.zeros(4, **i32)
         self.struct = TopologyStruct(self.row_ptr.data_ptr(), self.col_idx.data_ptr(),
                                      self.row_idx.data_ptr(), self.col_ptr.data_ptr(),
-                                     self.trans_idx.data_ptr(), self.row_pairs.data_ptr(),
+                                     self.trans_idx.data_ptr(), self.row_tiles.data_ptr(),
                                      self.expert_order.data_ptr(), self.meta.data_ptr(), E,
-                                     self.F, Tp_max)
+                                     self.F, block_rows, Tp_max)
 
 
 # ------------------------------------------------------------------- calls

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbsg.so")
 
-SOURCES = ["route.hip", "movement.hip", "topology.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["gemm_br128.hip", "gemm_br64.hip", "route.hip", "movement.hip", "topology.hip",
+           "gemm.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -59,17 +59,20 @@ bsg_status check_topology(const bsg_topology* t) {
     REQUIRE(t != nullptr, "topo is NULL");
     REQUIRE(t->E >= 1 && t->E <= BSG_MAX_EXPERTS, "topo->E out of range");
     REQUIRE(t->F >= 1, "topo->F must be positive");
-    REQUIRE(t->Tp_max >= BSG_BLOCK && t->Tp_max % BSG_BLOCK == 0,
-            "topo->Tp_max must be a positive multiple of 128");
-    REQUIRE(t->Tp_max / BSG_BLOCK <= INT32_MAX &&
-                (t->Tp_max / BSG_BLOCK) * (int64_t)t->F < INT32_MAX,
+    REQUIRE(t->block_rows == 128 || t->block_rows == 64, "topo->block_rows must be 128 or 64");
+    REQUIRE(t->Tp_max >= t->block_rows && t->Tp_max % t->block_rows == 0,
+            "topo->Tp_max must be a positive multiple of topo->block_rows");
+    // row_tiles entries keep the first block row in 23 bits
+    REQUIRE(t->Tp_max / t->block_rows < (int64_t(1) << 23), "too many block rows for row tiles");
+    REQUIRE(t->Tp_max / t->block_rows <= INT32_MAX &&
+                (t->Tp_max / t->block_rows) * (int64_t)t->F < INT32_MAX,
             "too many blocks for int32 ids");
     REQUIRE_PTR(t->row_ptr);
     REQUIRE_PTR(t->col_idx);
     REQUIRE_PTR(t->row_idx);
     REQUIRE_PTR(t->col_ptr);
     REQUIRE_PTR(t->trans_idx);
-    REQUIRE_PTR(t->row_pairs);
+    REQUIRE_PTR(t->row_tiles);
     REQUIRE_PTR(t->expert_order);
     REQUIRE_PTR(t->meta);
     return BSG_OK;
@@ -93,9 +96,13 @@ bool panel_ld_fits(int64_t ld, int es, bool k_contiguous) {
                         "32-bit panel offsets", (long long)(ld));                          \
     } while (0)
 
-int64_t row_pairs_max(int64_t row_blocks_max, int E) {
+// Product tiles of 256 rows: each expert's R_e block rows of br rows make
+// ceil(R_e / Q) tiles (Q = 256 / br), so their sum is at most
+// (R + (Q - 1) * ne) / Q over the ne <= min(E, R) non-empty experts.
+int64_t row_tiles_max(int64_t row_blocks_max, int E, int br) {
+    const int64_t q = 256 / br;
     const int64_t ne = E < row_blocks_max ? E : row_blocks_max;
-    return (row_blocks_max + ne + 1) / 2;
+    return (row_blocks_max + (q - 1) * (ne + 1)) / q;
 }
 
 }  // namespace
@@ -115,25 +122,28 @@ const char* bsg_status_string(bsg_status s) {
 const char* bsg_last_error(void) { return g_err; }
 
 int64_t bsg_max_padded_rows(int64_t T, int k, int E, int bin_rows) {
-    if (T < 1 || T > INT32_MAX || k < 1 || E < 1 || k > E || (bin_rows != 128 && bin_rows != 256))
+    if (T < 1 || T > INT32_MAX || k < 1 || E < 1 || k > E ||
+        (bin_rows != 64 && bin_rows != 128 && bin_rows != 256))
         return -1;
     const int64_t A = T * k;
     const int64_t ne = A < E ? A : E;
     return (A + (bin_rows - 1) * ne) / bin_rows * bin_rows;
 }
 
-bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out) {
+bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, int block_rows,
+                              bsg_topo_sizes* out) {
     REQUIRE(out != nullptr, "out is NULL");
-    REQUIRE(Tp_max >= BSG_BLOCK && Tp_max % BSG_BLOCK == 0,
-            "Tp_max must be a positive multiple of 128");
+    REQUIRE(block_rows == 128 || block_rows == 64, "block_rows must be 128 or 64");
+    REQUIRE(Tp_max >= block_rows && Tp_max % block_rows == 0,
+            "Tp_max must be a positive multiple of block_rows");
     REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
     REQUIRE(f >= BSG_BLOCK && f % BSG_BLOCK == 0, "f must be a positive multiple of 128");
-    REQUIRE(Tp_max / BSG_BLOCK <= INT32_MAX, "too many block rows for int32 ids");
+    REQUIRE(Tp_max / block_rows <= INT32_MAX, "too many block rows for int32 ids");
     const int64_t F = f / BSG_BLOCK;
-    out->row_blocks_max = Tp_max / BSG_BLOCK;
+    out->row_blocks_max = Tp_max / block_rows;
     out->nnz_max = out->row_blocks_max * F;
     out->n_cols = (int64_t)E * F;
-    out->row_pairs_max = row_pairs_max(out->row_blocks_max, E);
+    out->row_tiles_max = row_tiles_max(out->row_blocks_max, E, block_rows);
     REQUIRE(out->nnz_max < INT32_MAX && out->n_cols < INT32_MAX, "too many blocks for int32 ids");
     return ok();
 }
@@ -144,11 +154,11 @@ size_t bsg_route_workspace_bytes(int64_t T, int k, int E) {
     return (size_t)(nchunks * E * (int64_t)sizeof(int32_t));
 }
 
-// The bin granularity: 128 (the block) or 256; 64 would need product tiles
-// with 64-row halves, which are not built.
+// The bin granularity: 128 (the block), or 64 or 256 for the block-size
+// study (bins of 64 rows go with a topology of 64-row blocks).
 static bsg_status check_bin(int bin_rows) {
-    if (bin_rows == 64) return fail(BSG_EUNSUPPORTED, "bin_rows 64 is not implemented");
-    REQUIRE(bin_rows == 128 || bin_rows == 256, "bin_rows must be 128 or 256");
+    REQUIRE(bin_rows == 64 || bin_rows == 128 || bin_rows == 256,
+            "bin_rows must be 64, 128 or 256");
     return BSG_OK;
 }
 
@@ -323,11 +333,12 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
     REQUIRE(topo->E == E && topo->F == f / BSG_BLOCK && topo->Tp_max == Tp_max,
             "topo capacity does not match E, f, Tp_max");
     return hip_status(
-        bsg::launch_build_topology(bin_offsets, E, topo->F, Tp_max / BSG_BLOCK,
-                                   row_pairs_max(Tp_max / BSG_BLOCK, E), topo->row_ptr,
-                                   topo->col_idx, topo->row_idx, topo->col_ptr, topo->trans_idx,
-                                   topo->row_pairs, topo->expert_order, topo->meta,
-                                   tile_group(Tp_max, E), (hipStream_t)stream),
+        bsg::launch_build_topology(bin_offsets, E, topo->F, topo->block_rows,
+                                   Tp_max / topo->block_rows,
+                                   row_tiles_max(Tp_max / topo->block_rows, E, topo->block_rows),
+                                   topo->row_ptr, topo->col_idx, topo->row_idx, topo->col_ptr,
+                                   topo->trans_idx, topo->row_tiles, topo->expert_order,
+                                   topo->meta, tile_group(Tp_max, E), (hipStream_t)stream),
         "build_topology");
 }
 
@@ -338,13 +349,18 @@ static bsg::GemmParams gemm_params(const bsg_topology* t) {
     p.row_idx = t->row_idx;
     p.col_ptr = t->col_ptr;
     p.trans_idx = t->trans_idx;
-    p.row_pairs = t->row_pairs;
+    p.row_tiles = t->row_tiles;
     p.expert_order = t->expert_order;
     p.meta = t->meta;
     p.E = t->E;
     p.F = t->F;
+    p.br = t->block_rows;
     p.group = tile_group(t->Tp_max, t->E);
     return p;
+}
+
+static int64_t tiles_max(const bsg_topology* t) {
+    return row_tiles_max(t->Tp_max / t->block_rows, t->E, t->block_rows);
 }
 
 bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, int64_t ldb,
@@ -387,11 +403,11 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     p.aux_in = aux_in;
     p.out = out_blocks;
     p.aux_out = aux_out;
-    p.plane = (topo->Tp_max / BSG_BLOCK) * topo->F * BSG_BLOCK * BSG_BLOCK;
+    p.plane = (topo->Tp_max / topo->block_rows) * topo->F * topo->block_rows * BSG_BLOCK;
     p.lda = lda;
     p.ldb = ldb;
     p.K = K;
-    return hip_status(bsg::launch_sdd(p, row_pairs_max(topo->Tp_max / BSG_BLOCK, topo->E), trans_b,
+    return hip_status(bsg::launch_sdd(p, tiles_max(topo), trans_b,
                                       epilogue, dtype, (hipStream_t)stream),
                       "sdd");
 }
@@ -433,7 +449,7 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
     p.ldc = ldc;
     p.N = N;
     p.ntn = (N + 255) / 256;
-    return hip_status(bsg::launch_dsd(p, row_pairs_max(topo->Tp_max / BSG_BLOCK, topo->E), trans_b,
+    return hip_status(bsg::launch_dsd(p, tiles_max(topo), trans_b,
                                       c_dtype, dtype, (hipStream_t)stream),
                       "dsd");
 }
@@ -477,7 +493,7 @@ bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, co
     p.scat_gate = gate;
     p.scat_out = y;
     p.scat_ld = ldy;
-    return hip_status(bsg::launch_dsd(p, row_pairs_max(topo->Tp_max / BSG_BLOCK, topo->E), trans_b,
+    return hip_status(bsg::launch_dsd(p, tiles_max(topo), trans_b,
                                       BSG_BF16, BSG_BF16, (hipStream_t)stream),
                       "dsd_combine_top1");
 }

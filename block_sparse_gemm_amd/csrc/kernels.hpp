@@ -56,15 +56,17 @@ struct GemmParams {
     const int32_t* row_idx;
     const int32_t* col_ptr;
     const int32_t* trans_idx;
-    const int32_t* row_pairs;  // pairs of block rows sharing a column list
+    const int32_t* row_tiles;  // tiles of up to 256 rows of one expert (block rows sharing a
+                               // column list)
     const int32_t* expert_order;  // experts by descending row count
     const int32_t* meta;  // {nnz, R, overflow, row pairs} written by build_topology
     int K;                // SDD reduction length
     int N;                // DSD / DSTD output width
     int ntn;              // 256-wide output tiles along N
     int E, F;             // experts, column blocks per expert
+    int br;               // rows of a block: 128, or 64 for bins of 64 rows
     int group;            // DSTD: column pairs per group of an expert's tiles (>= 1); SDD and
-                          // DSD take their groups from row_pairs
+                          // DSD take their groups from row_tiles
 };
 
 // Bytes of the file-scope device array behind the allocation-free routing
@@ -97,15 +99,15 @@ hipError_t launch_permute_gate_backward(const void* dy, int dtype, int64_t T, in
                                         const int32_t* expert_idx, const void* yp, int yp_dtype,
                                         int64_t ld_yp, float* dlogits, hipStream_t stream);
 
-hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
-                                 int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
-                                 int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
-                                 int32_t* row_pairs, int32_t* expert_order, int32_t* meta,
-                                 int group, hipStream_t stream);
+hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int br,
+                                 int64_t row_blocks_max, int64_t row_tiles_max, int32_t* row_ptr,
+                                 int32_t* col_idx, int32_t* row_idx, int32_t* col_ptr,
+                                 int32_t* trans_idx, int32_t* row_tiles, int32_t* expert_order,
+                                 int32_t* meta, int group, hipStream_t stream);
 
-hipError_t launch_sdd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int epi, int dtype,
+hipError_t launch_sdd(const GemmParams& p, int64_t row_tiles_max, int trans_b, int epi, int dtype,
                       hipStream_t s);
-hipError_t launch_dsd(const GemmParams& p, int64_t row_pairs_max, int trans_b, int c_dtype,
+hipError_t launch_dsd(const GemmParams& p, int64_t row_tiles_max, int trans_b, int c_dtype,
                       int dtype, hipStream_t s);
 hipError_t launch_dstd(const GemmParams& p, int trans_c, int dtype, hipStream_t s);
 

@@ -7,19 +7,20 @@
 // this metadata, mapping each (expert, token-row range) to its nonzero
 // blocks, together with the transpose metadata in a single kernel.
 //
-// It also emits the schedules the products run on: the row pairs
-// (consecutive block rows of one expert share their column list, so a
-// 256-row tile of two such rows reads one set of weight columns), and the
-// experts in descending order of their row count, so the weight-gradient
-// product, whose tile cost grows with the expert's rows, starts its longest
-// tiles first.
+// It also emits the schedules the products run on: the row tiles (the
+// consecutive block rows of one expert share their column list, so a
+// 256-row tile of two 128-row or four 64-row block rows reads one set of
+// weight columns), and the experts in descending order of their row count,
+// so the weight-gradient product, whose tile cost grows with the expert's
+// rows, starts its longest tiles first.
 //
-// The first layer's output is block-diagonal: row block r belongs to the
-// expert whose bin holds row 128 r, and that expert owns the F column
-// blocks e*F .. e*F + F - 1.  So every entry is computed independently from
-// the bin offsets: thread g fills row_ptr[g], BCSR entry g and transpose
-// entry g.  Each workgroup first stages s_e = bin_offsets[e] / 128 in LDS
-// and finds the owner of a row block by binary search.
+// The first layer's output is block-diagonal: row block r (br rows: 128,
+// or 64 for the block-size study's bins of 64 rows) belongs to the expert
+// whose bin holds row br * r, and that expert owns the F column blocks
+// e*F .. e*F + F - 1.  So every entry is computed independently from the
+// bin offsets: thread g fills row_ptr[g], BCSR entry g and transpose entry
+// g.  Each workgroup first stages s_e = bin_offsets[e] / br in LDS and
+// finds the owner of a row block by binary search.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "scan.hpp"
@@ -41,27 +42,35 @@ __device__ __forceinline__ int owner_of(const int* s, int E, int64_t r) {
 }
 
 __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
-    const int32_t* __restrict__ bin_offsets, int E, int F, int64_t row_blocks_max,
+    const int32_t* __restrict__ bin_offsets, int E, int F, int br, int64_t row_blocks_max,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int32_t* __restrict__ row_idx,
     int32_t* __restrict__ col_ptr, int32_t* __restrict__ trans_idx,
-    int32_t* __restrict__ row_pairs, int32_t* __restrict__ expert_order,
+    int32_t* __restrict__ row_tiles, int32_t* __restrict__ expert_order,
     int32_t* __restrict__ meta, int group) {
     __shared__ int s[kMaxExperts + 1];   // bin start in row blocks
-    __shared__ int pp[kMaxExperts + 1];  // first row pair of each expert
+    __shared__ int pp[kMaxExperts + 1];  // first row tile of each expert
     __shared__ int wsum[kTopoThreads / kWave];
-    for (int e = threadIdx.x; e <= E; e += kTopoThreads) s[e] = bin_offsets[e] / kBlock;
+    __shared__ int misaligned;
+    const int q = 256 / br;  // block rows per tile
+    if (threadIdx.x == 0) misaligned = 0;
     __syncthreads();
-    // row pairs: expert e's R_e row blocks form ceil(R_e / 2) pairs of
-    // consecutive rows (the last one single when R_e is odd); exclusive scan
+    for (int e = threadIdx.x; e <= E; e += kTopoThreads) {
+        const int b = bin_offsets[e];
+        s[e] = b / br;
+        if (b % br) misaligned = 1;  // a bin that does not start on the block grid
+    }
+    __syncthreads();
+    // row tiles: expert e's R_e row blocks form ceil(R_e / q) tiles of q
+    // consecutive rows (the last one shorter); exclusive scan
     const int per = (E + kTopoThreads - 1) / kTopoThreads;
     const int lo = threadIdx.x * per, hi = min(lo + per, E);
     int sum = 0;
-    for (int e = lo; e < hi; ++e) sum += (s[e + 1] - s[e] + 1) / 2;
+    for (int e = lo; e < hi; ++e) sum += (s[e + 1] - s[e] + q - 1) / q;
     int total;
     int run = block_excl_scan<kTopoThreads / kWave>(sum, wsum, total);
     for (int e = lo; e < hi; ++e) {
         pp[e] = run;
-        run += (s[e + 1] - s[e] + 1) / 2;
+        run += (s[e + 1] - s[e] + q - 1) / q;
     }
     if (threadIdx.x == kTopoThreads - 1) pp[E] = total;
     __syncthreads();
@@ -80,14 +89,15 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
         expert_order[rank] = (int32_t)g;
     }
 
-    if (R > row_blocks_max) {
-        // the routing needs more rows than the topology holds: publish an
-        // empty topology (every product then writes nothing / zeros) and
-        // raise the overflow flag instead of writing out of bounds
+    if (R > row_blocks_max || misaligned) {
+        // the routing needs more rows than the topology holds, or its bins
+        // are off the block grid: publish an empty topology (every product
+        // then writes nothing / zeros) and raise the status flag instead of
+        // writing out of bounds
         if (g == 0) {
             meta[0] = 0;
             meta[1] = 0;
-            meta[2] = 1;
+            meta[2] = misaligned ? 2 : 1;
             meta[3] = 0;
         }
         if (g <= row_blocks_max) row_ptr[g] = 0;
@@ -101,16 +111,17 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
         meta[3] = pp[E];
     }
     if (g < pp[E]) {
-        // the expert's row pairs go in groups of `group` (the last one
-        // shorter): the products take a group's tiles together
+        // the expert's tiles go in groups of `group` (the last one shorter):
+        // the products take a group's tiles together
         const int e = owner_of(pp, E, g);
         const int j = (int)(g - pp[e]);
         const int Re = s[e + 1] - s[e];
-        const int r0 = s[e] + 2 * j;
-        const int npairs = pp[e + 1] - pp[e];
+        const int r0 = s[e] + q * j;
+        const int ntiles = pp[e + 1] - pp[e];
         const int off = j % group;
-        const int size = min(group, npairs - (j - off));
-        row_pairs[g] = (r0 << 7) | ((size - 1) << 4) | (off << 1) | (2 * j + 1 < Re ? 1 : 0);
+        const int size = min(group, ntiles - (j - off));
+        const int rows = min(q, Re - q * j);
+        row_tiles[g] = (r0 << 8) | ((size - 1) << 5) | (off << 2) | (rows - 1);
     }
     // BCSR block pointer: every non-empty row block holds F blocks
     if (g <= row_blocks_max) row_ptr[g] = (int32_t)((g < R ? g : R) * F);
@@ -137,20 +148,20 @@ __global__ __launch_bounds__(kTopoThreads) void build_topology_kernel(
     if (g == (int64_t)E * F) col_ptr[g] = (int32_t)nnz;
 }
 
-hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int64_t row_blocks_max,
-                                 int64_t row_pairs_max, int32_t* row_ptr, int32_t* col_idx,
-                                 int32_t* row_idx, int32_t* col_ptr, int32_t* trans_idx,
-                                 int32_t* row_pairs, int32_t* expert_order, int32_t* meta,
-                                 int group, hipStream_t stream) {
+hipError_t launch_build_topology(const int32_t* bin_offsets, int E, int F, int br,
+                                 int64_t row_blocks_max, int64_t row_tiles_max, int32_t* row_ptr,
+                                 int32_t* col_idx, int32_t* row_idx, int32_t* col_ptr,
+                                 int32_t* trans_idx, int32_t* row_tiles, int32_t* expert_order,
+                                 int32_t* meta, int group, hipStream_t stream) {
     int64_t n = row_blocks_max * F;
-    if (row_pairs_max > n) n = row_pairs_max;
+    if (row_tiles_max > n) n = row_tiles_max;
     if (row_blocks_max + 1 > n) n = row_blocks_max + 1;
     if ((int64_t)E * F + 1 > n) n = (int64_t)E * F + 1;
     if (E > n) n = E;
     const int grid = (int)((n + kTopoThreads - 1) / kTopoThreads);
     hipLaunchKernelGGL(build_topology_kernel, dim3(grid), dim3(kTopoThreads), 0, stream,
-                       bin_offsets, E, F, row_blocks_max, row_ptr, col_idx, row_idx, col_ptr,
-                       trans_idx, row_pairs, expert_order, meta, group);
+                       bin_offsets, E, F, br, row_blocks_max, row_ptr, col_idx, row_idx, col_ptr,
+                       trans_idx, row_tiles, expert_order, meta, group);
     return hipGetLastError();
 }
 

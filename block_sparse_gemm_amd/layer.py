@@ -43,7 +43,7 @@ class Shape:
     yp_dtype: str = "bf16"     # storage of Yp / dXp
     renorm: bool = False
     backward: bool = False
-    bin_rows: int = 128        # expert bins padded to a multiple of this (128 or 256)
+    bin_rows: int = 128        # expert bins padded to a multiple of this (64, 128 or 256)
 
     @classmethod
     def of(cls, cfg) -> "Shape":
@@ -87,8 +87,11 @@ class Layer:
         i32 = dict(dtype=torch.int32, device=dev)
         A = s.T * s.k
         self.Tp_max = bsg.max_padded_rows(s.T, s.k, s.E, s.bin_rows)
-        self.topo = bsg.Topology(self.Tp_max, s.E, s.f, device=dev)
+        # bins of 64 rows need blocks of 64 rows (a block holds one expert's rows)
+        self.block_rows = 64 if s.bin_rows == 64 else bsg.BLOCK
+        self.topo = bsg.Topology(self.Tp_max, s.E, s.f, device=dev, block_rows=self.block_rows)
         nnz_max = self.topo.nnz_max
+        br = self.block_rows
         dt, ydt = s.tdtype, s.yp_tdtype
         self.expert_idx = torch.zeros(A, **i32)
         self.gate = torch.zeros(A, dtype=torch.float32, device=dev)
@@ -99,11 +102,11 @@ class Layer:
                                     dtype=torch.uint8, device=dev)
         self.row_src = torch.zeros(self.Tp_max, **i32)
         self.xp = torch.zeros(self.Tp_max, s.d, dtype=dt, device=dev)
-        self.act = torch.zeros(nnz_max * bsg.BLOCK, bsg.BLOCK, dtype=dt, device=dev)
+        self.act = torch.zeros(nnz_max * br, bsg.BLOCK, dtype=dt, device=dev)
         # what the backward keeps of the forward, block-major like A: GeLU'(h),
         # or for SwiGLU two planes, silu(g) then u * silu'(g)
         planes = 2 if s.act == "swiglu" else 1
-        self.gp = torch.zeros(planes * nnz_max * bsg.BLOCK, bsg.BLOCK, dtype=dt, device=dev) \
+        self.gp = torch.zeros(planes * nnz_max * br, bsg.BLOCK, dtype=dt, device=dev) \
             if s.backward else None
         self.yp = torch.zeros(self.Tp_max, s.d, dtype=ydt, device=dev)
         self.y = torch.zeros(s.T, s.d, dtype=dt, device=dev)
@@ -158,7 +161,7 @@ class Layer:
 
     def plane(self, blocks, i):
         """Plane i of a two-plane block array (a view)."""
-        n = self.topo.nnz_max * bsg.BLOCK
+        n = self.topo.nnz_max * self.block_rows
         return blocks[i * n:(i + 1) * n]
 
     def backward(self, dy, W1, W2, W3=None):
@@ -232,11 +235,11 @@ class Layer:
     def sparse_rows(self, blocks: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:
         """Gather full rows [len(rows), f] of a block-major sparse operand
         (host-side inspection helper; rows are padded-row indices)."""
-        F = self.topo.F
-        b = blocks.view(-1, bsg.BLOCK, bsg.BLOCK)
+        F, br = self.topo.F, self.block_rows
+        b = blocks.view(-1, br, bsg.BLOCK)
         r = rows.long()
-        base = (r // bsg.BLOCK) * F
-        out = [b[base + j, r % bsg.BLOCK] for j in range(F)]
+        base = (r // br) * F
+        out = [b[base + j, r % br] for j in range(F)]
         return torch.cat(out, dim=1)
 
 

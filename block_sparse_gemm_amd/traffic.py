@@ -41,7 +41,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # every source the GEMM kernels are compiled from, and the launch parameters
 # (tile grouping) set in the C ABI
 GEMM_SRCS = [os.path.join(ROOT, "block_sparse_gemm_amd", "csrc", n)
-             for n in ("gemm.hip", "common.hpp", "kernels.hpp", "api.cpp")]
+             for n in ("gemm.hpp", "gemm.hip", "gemm_br128.hip", "gemm_br64.hip", "common.hpp",
+                       "kernels.hpp", "api.cpp")]
 COPY_BYTES = 1 << 29           # 512 MiB read and 512 MiB written by the calibration copy
 COPY_NAMES = ("copyBuffer", "MulFunctor")   # the memcpy blit kernel, else x * 1
 

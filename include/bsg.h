@@ -40,8 +40,9 @@
  *
  * Symbols: T tokens, d model width, E experts, f per-expert hidden width,
  * k experts per token, F = f/128 column blocks per expert, A = T*k
- * assignments, Tp = padded row count, R = Tp/128 row blocks,
- * nnz = R*F nonzero blocks.
+ * assignments, Tp = padded row count, BR = block rows (128, the block of
+ * section 1.3, or 64 for the block-size study), R = Tp/BR row blocks,
+ * nnz = R*F nonzero blocks of BR x 128.
  */
 #ifndef BSG_H
 #define BSG_H
@@ -80,44 +81,48 @@ typedef void* bsg_stream_t;
 
 /* Upper bounds for the topology arrays (pure host function results). */
 typedef struct {
-    int64_t row_blocks_max; /* Tp_max / 128                              */
+    int64_t row_blocks_max; /* Tp_max / BR                                */
     int64_t nnz_max;        /* row_blocks_max * F                         */
     int64_t n_cols;         /* E * F column blocks                        */
-    int64_t row_pairs_max;  /* (row_blocks_max + min(E, row_blocks_max) + 1) / 2 */
+    int64_t row_tiles_max;  /* (row_blocks_max + (Q - 1) * (min(E, row_blocks_max) + 1)) / Q,
+                               Q = 256 / BR block rows per tile          */
 } bsg_topo_sizes;
 
 /*
  * Hybrid BCSR-COO topology of the first layer's output, a [Tp x E*f]
- * matrix of 128x128 blocks where block (r, c) is nonzero when row block r
- * lies in the bin of the expert that owns column block c (section 1.3,
- * "hybrid BCSR-COO format" and "transpose indices").  All arrays are
- * caller-allocated device int32 arrays of the stated capacity:
+ * matrix of BR x 128 blocks (BR = block_rows: 128, the block of section
+ * 1.3, or 64 for the block-size study, whose bins of 64 rows cannot share a
+ * 128-row block) where block (r, c) is nonzero when row block r lies in the
+ * bin of the expert that owns column block c (section 1.3, "hybrid BCSR-COO
+ * format" and "transpose indices").  All arrays are caller-allocated device
+ * int32 arrays of the stated capacity:
  *   row_ptr   [row_blocks_max + 1] BCSR block pointer; entries past R hold nnz
  *   col_idx   [nnz_max]  global column block of each block, BCSR order
  *   row_idx   [nnz_max]  materialised row block of each block (COO half)
  *   col_ptr   [E*F + 1]  start of each column's run in trans_idx
  *   trans_idx [nnz_max]  BCSR block ids listed column by column,
  *                        ascending row inside a column (no data copied)
- *   row_pairs [row_pairs_max] the schedule of the products: consecutive
- *                        block rows of one expert taken two at a time
- *                        (a last single row when the expert has an odd
- *                        number), each expert's pairs cut into groups of
- *                        G = 1, 2, 4 or 8 (the last one shorter), G set
- *                        from Tp_max and E; entry = (first row << 7) |
- *                        ((group size - 1) << 4) | (place in the group
- *                        << 1) | (pair ? 1 : 0)
+ *   row_tiles [row_tiles_max] the schedule of the products: each
+ *                        expert's block rows taken 256 rows at a time
+ *                        (Q = 256 / BR consecutive block rows, fewer at
+ *                        the expert's end), each expert's tiles cut into
+ *                        groups of G = 1, 2, 4 or 8 (the last one
+ *                        shorter), G set from Tp_max and E; entry =
+ *                        (first block row << 8) | ((group size - 1) << 5)
+ *                        | (place in the group << 2) | (block rows - 1)
  *   expert_order [E]     the experts in descending order of their row
  *                        blocks (ties: lower id first), the order in which
  *                        dstd schedules its tiles (longest first)
- *   meta      [4]        written on the device: {nnz, R, overflow, pairs};
- *                        overflow = 1 when the routing needs more than
- *                        Tp_max rows: the topology is then published empty
- *                        (nnz = R = 0, all pointers 0) and every product
- *                        writes nothing, or zeros for dstd
- * E, F and Tp_max are host values describing the capacity.
- * Sparse operands ("blocks") are stored block-major, [nnz_max][128][128],
+ *   meta      [4]        written on the device: {nnz, R, status, tiles};
+ *                        status = 1 when the routing needs more than
+ *                        Tp_max rows, 2 when a bin offset is not a
+ *                        multiple of BR: the topology is then published
+ *                        empty (nnz = R = 0, all pointers 0) and every
+ *                        product writes nothing, or zeros for dstd
+ * E, F, block_rows and Tp_max are host values describing the capacity.
+ * Sparse operands ("blocks") are stored block-major, [nnz_max][BR][128],
  * each block row-major, in BCSR order.  A two-plane block array is
- * [2][nnz_max][128][128] with nnz_max = (Tp_max / 128) * F: plane 1 starts
+ * [2][nnz_max][BR][128] with nnz_max = (Tp_max / BR) * F: plane 1 starts
  * nnz_max blocks after plane 0.
  */
 typedef struct {
@@ -126,28 +131,32 @@ typedef struct {
     int32_t* row_idx;
     int32_t* col_ptr;
     int32_t* trans_idx;
-    int32_t* row_pairs;
+    int32_t* row_tiles;
     int32_t* expert_order;
     int32_t* meta;
     int32_t E;
     int32_t F;
+    int32_t block_rows; /* BR: 128, or 64 for bins of 64 rows */
     int64_t Tp_max;
 } bsg_topology;
 
 /* ------------------------------------------------------------ size queries */
 
 /* Upper bound on Tp for any routing with bins padded to a multiple of
- * bin_rows (128, the block of section 1.3, or 256):
+ * bin_rows (128, the block of section 1.3, or 64 or 256 for the block-size
+ * study):
  *   bin_rows * floor((A + (bin_rows - 1) * min(E, A)) / bin_rows),  A = T*k
  * (each non-empty expert pads by at most bin_rows - 1 rows).  Returns -1 on
  * invalid sizes or an unsupported bin_rows. */
 int64_t bsg_max_padded_rows(int64_t T, int k, int E, int bin_rows);
 
-/* Capacities of the topology arrays for Tp_max padded rows.  A host-side
- * helper for sizing the caller's buffers; the pages define no such call
- * (the capacities follow from the block grid of section 1.3: Tp_max/128
- * row blocks of F blocks each, E*F column blocks). */
-bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, bsg_topo_sizes* out /* host */);
+/* Capacities of the topology arrays for Tp_max padded rows in blocks of
+ * block_rows (128 or 64) rows.  A host-side helper for sizing the caller's
+ * buffers; the pages define no such call (the capacities follow from the
+ * block grid of section 1.3: Tp_max/BR row blocks of F blocks each, E*F
+ * column blocks). */
+bsg_status bsg_topology_sizes(int64_t Tp_max, int E, int f, int block_rows,
+                              bsg_topo_sizes* out /* host */);
 
 /* Bytes of device workspace bsg_route needs (0 on invalid sizes): per-chunk
  * expert counts of the deterministic placement (64 tokens a chunk).  A
@@ -167,8 +176,8 @@ size_t bsg_route_workspace_bytes(int64_t T, int k, int E);
  *   counts [E] int32 tokens per expert; bin_offsets [E+1] int32 exclusive
  *   scan of ceil(counts/bin_rows)*bin_rows in ascending expert id
  *   (Tp = bin_offsets[E]).  bin_rows is 128 (section 1.3's padding to the
- *   block) or 256 (coarser bins for the block-size study); 64 returns
- *   BSG_EUNSUPPORTED (it needs product tiles with 64-row halves).
+ *   block), or 64 or 256 (finer and coarser bins for the block-size study;
+ *   bins of 64 rows need a topology of 64-row blocks).
  *   dest_row [T*k] int32: row of the padded, expert-grouped layout that
  *   assignment a = t*k + j occupies; inside a bin, ascending a.
  *   workspace: bsg_route_workspace_bytes(T, k, E) device bytes.
@@ -260,7 +269,9 @@ bsg_status bsg_permute_pad_gate_backward(const void* dy, int dtype, int64_t T, i
  * (section 1.4, last paragraph): maps each expert's token row range to its
  * nonzero blocks.  Fills every array of *topo (see bsg_topology) from
  * bin_offsets [E+1]; f is the per-expert hidden width (multiple of 128).
- * topo->E, topo->F = f/128 and topo->Tp_max must match the arguments.
+ * topo->E, topo->F = f/128 and topo->Tp_max must match the arguments;
+ * topo->block_rows is 128 or 64, and every bin offset must be a multiple of
+ * it (else meta's status is 2 and the topology is published empty).
  */
 bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
                               const bsg_topology* topo /* host struct */, bsg_stream_t stream);
@@ -268,11 +279,11 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
 /*
  * sdd - sampled dense-dense product (section 1.2, first layer):
  * for every nonzero block b = (r, c):
- *   acc_b[m][n] = sum_k a[128r + m][k] * B[k][128c + n],  k < K,
+ *   acc_b[m][n] = sum_k a[BR*r + m][k] * B[k][128c + n],  k < K,
  * where a is [Tp_max, K] row-major with leading dimension lda and
  *   trans_b = 0: B[k][n] = b[k*ldb + n]    (b is [K, E*f], e.g. W1)
  *   trans_b = 1: B[k][n] = b[n*ldb + k]    (b is [E*f, K], e.g. W2 for dgrad)
- * and the epilogue writes out_blocks[b] (block-major [nnz_max][128][128]):
+ * and the epilogue writes out_blocks[b] (block-major [nnz_max][BR][128]):
  *   NONE      acc
  *   GELU      gelu(acc); if aux_out != NULL also aux_out[b] = gelu'(acc), the
  *             derivative the backward needs (stored in dtype)
@@ -295,7 +306,7 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
 /*
  * dsd - dense = sparse x dense (section 1.2, second layer; walks each block
  * row through the BCSR row pointer as section 1.3 describes):
- *   c[128r + m][n] = sum over blocks b of row r, sum_j blocks[b][m][j] *
+ *   c[BR*r + m][n] = sum over blocks b of row r, sum_j blocks[b][m][j] *
  *                    B[128*col_idx[b] + j][n],  n < N,
  *   trans_b = 0: B[k][n] = b[k*ldb + n]  (b is [E*f, N], e.g. W2)
  *   trans_b = 1: B[k][n] = b[n*ldb + k]  (b is [N, E*f], e.g. W1 for dgrad)
@@ -332,7 +343,7 @@ bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, co
  * "transpose indices": the blocks of each column are visited through
  * trans_idx, their rows found through row_idx):
  *   C[128c + m][n] = sum over blocks b of column c, sum_j blocks[b][j][m] *
- *                    dmat[128*row_idx[b] + j][n],  n < N
+ *                    dmat[BR*row_idx[b] + j][n],  n < N
  * dmat is [Tp_max, N] with leading dimension ldd.  trans_c = 0 stores
  * C at c[(128c + m)*ldc + n] ([E*f, N], e.g. dW2); trans_c = 1 stores it
  * transposed at c[n*ldc + 128c + m] ([N, E*f], e.g. dW1).  Columns with no

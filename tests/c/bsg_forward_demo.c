@@ -88,7 +88,7 @@ int main(int argc, char** argv) {
         fprintf(stderr, "bad sizes\n");
         return 2;
     }
-    BSG_OK_(bsg_topology_sizes(Tp_max, E, f, &sz));
+    BSG_OK_(bsg_topology_sizes(Tp_max, E, f, BSG_BLOCK, &sz));
     const size_t ws_bytes = bsg_route_workspace_bytes(T, k, E);
     const int64_t A = T * k, ncol = (int64_t)E * f;
 
@@ -121,11 +121,12 @@ int main(int argc, char** argv) {
     HIP_OK(hipMalloc((void**)&topo.row_idx, (size_t)sz.nnz_max * 4));
     HIP_OK(hipMalloc((void**)&topo.col_ptr, (size_t)(sz.n_cols + 1) * 4));
     HIP_OK(hipMalloc((void**)&topo.trans_idx, (size_t)sz.nnz_max * 4));
-    HIP_OK(hipMalloc((void**)&topo.row_pairs, (size_t)sz.row_pairs_max * 4));
+    HIP_OK(hipMalloc((void**)&topo.row_tiles, (size_t)sz.row_tiles_max * 4));
     HIP_OK(hipMalloc((void**)&topo.expert_order, (size_t)E * 4));
     HIP_OK(hipMalloc((void**)&topo.meta, 4 * 4));
     topo.E = E;
     topo.F = f / BSG_BLOCK;
+    topo.block_rows = BSG_BLOCK;
     topo.Tp_max = Tp_max;
 
     /* an invalid call is refused before any launch (K not a multiple of 64) */

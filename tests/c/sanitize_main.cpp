@@ -75,11 +75,12 @@ static bsg_topology fake_topo(int E, int f, int64_t Tp) {
     t.row_idx = (int32_t*)0x30000;
     t.col_ptr = (int32_t*)0x40000;
     t.trans_idx = (int32_t*)0x50000;
-    t.row_pairs = (int32_t*)0x70000;
+    t.row_tiles = (int32_t*)0x70000;
     t.expert_order = (int32_t*)0x80000;
     t.meta = (int32_t*)0x60000;
     t.E = E;
     t.F = f / 128;
+    t.block_rows = 128;
     t.Tp_max = Tp;
     return t;
 }
@@ -96,10 +97,12 @@ static void abi_checks() {
     EXPECT(bsg_route_workspace_bytes(INT64_MAX, 32, 1024) == 0);
     EXPECT(bsg_route_workspace_bytes(65536, 2, 64) == 1024 * 64 * 4);
     bsg_topo_sizes ts;
-    EXPECT(bsg_topology_sizes(139136, 64, 4096, &ts) == BSG_OK && ts.nnz_max == 1087 * 32);
-    EXPECT(bsg_topology_sizes(INT64_MAX / 128 * 128, 1024, 128 << 20, &ts) == BSG_EINVAL);
-    EXPECT(bsg_topology_sizes(1280, 4, 200, &ts) == BSG_EINVAL);
-    EXPECT(bsg_topology_sizes(1280, 4, 256, nullptr) == BSG_EINVAL);
+    EXPECT(bsg_topology_sizes(139136, 64, 4096, 128, &ts) == BSG_OK && ts.nnz_max == 1087 * 32);
+    EXPECT(bsg_topology_sizes(139136, 64, 4096, 64, &ts) == BSG_OK && ts.nnz_max == 2174 * 32);
+    EXPECT(bsg_topology_sizes(INT64_MAX / 128 * 128, 1024, 128 << 20, 64, &ts) == BSG_EINVAL);
+    EXPECT(bsg_topology_sizes(1280, 4, 200, 128, &ts) == BSG_EINVAL);
+    EXPECT(bsg_topology_sizes(1280, 4, 256, 100, &ts) == BSG_EINVAL);
+    EXPECT(bsg_topology_sizes(1280, 4, 256, 128, nullptr) == BSG_EINVAL);
 
     // route and its allocation-free twin
     const int before = g_launches;
@@ -116,8 +119,9 @@ static void abi_checks() {
            BSG_EUNSUPPORTED);
     EXPECT(bsg_route(nullptr, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, nullptr) ==
            BSG_EINVAL);
-    EXPECT(bsg_route(fl, 100, 8, 2, 0, 64, ip, fp, ip, ip, ip, P, 1 << 20, nullptr) ==
-           BSG_EUNSUPPORTED);
+    EXPECT(bsg_route(fl, 100, 8, 2, 0, 64, ip, fp, ip, ip, ip, P, 1 << 20, nullptr) == BSG_OK);
+    EXPECT(bsg_route(fl, 100, 8, 2, 0, 32, ip, fp, ip, ip, ip, P, 1 << 20, nullptr) ==
+           BSG_EINVAL);
 
     // permute_pad, the gate backward, combine
     const int64_t Tp = bsg_max_padded_rows(100, 2, 8, 128);
@@ -145,6 +149,13 @@ static void abi_checks() {
     // topology and products
     bsg_topology t = fake_topo(4, 256, 1024);
     EXPECT(bsg_build_topology(ip, 4, 256, 1024, &t, nullptr) == BSG_OK);
+    t.block_rows = 64;
+    EXPECT(bsg_build_topology(ip, 4, 256, 1024, &t, nullptr) == BSG_OK);
+    EXPECT(bsg_sdd(P, 256, P, nullptr, 1024, 0, 256, &t, BSG_EPI_GELU, nullptr, P, P, BSG_BF16,
+                   nullptr) == BSG_OK);
+    t.block_rows = 32;
+    EXPECT(bsg_build_topology(ip, 4, 256, 1024, &t, nullptr) == BSG_EINVAL);
+    t.block_rows = 128;
     EXPECT(bsg_build_topology(ip, 5, 256, 1024, &t, nullptr) == BSG_EINVAL);
     bsg_topology big = fake_topo(1024, 128 * 32768, INT64_MAX / 128 * 128);
     EXPECT(bsg_build_topology(ip, 1024, 128 * 32768, big.Tp_max, &big, nullptr) == BSG_EINVAL);

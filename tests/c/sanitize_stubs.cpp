@@ -49,9 +49,9 @@ hipError_t launch_permute_gate_backward(const void*, int, int64_t, int, int, con
     return hipSuccess;
 }
 
-hipError_t launch_build_topology(const int32_t*, int, int, int64_t, int64_t, int32_t*, int32_t*,
-                                 int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, int,
-                                 hipStream_t) {
+hipError_t launch_build_topology(const int32_t*, int, int, int, int64_t, int64_t, int32_t*,
+                                 int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*,
+                                 int32_t*, int, hipStream_t) {
     ++g_launches;
     return hipSuccess;
 }

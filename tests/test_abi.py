@@ -42,13 +42,21 @@ def test_size_queries(L):
         assert bsg.max_padded_rows(T, k, E) == want
         want = (A + 255 * min(E, A)) // 256 * 256
         assert bsg.max_padded_rows(T, k, E, 256) == want
+        want = (A + 63 * min(E, A)) // 64 * 64
+        assert bsg.max_padded_rows(T, k, E, 64) == want
     assert bsg.max_padded_rows(0, 1, 1) == -1
     assert bsg.max_padded_rows(4, 3, 2) == -1
-    assert bsg.max_padded_rows(4, 1, 2, 64) == -1
+    assert bsg.max_padded_rows(4, 1, 2, 32) == -1
     assert bsg.max_padded_rows(4, 1, 2, 200) == -1
     s = bsg.topology_sizes(139136, 64, 4096)
     assert (s.row_blocks_max, s.nnz_max, s.n_cols) == (1087, 1087 * 32, 64 * 32)
-    assert s.row_pairs_max == (1087 + 64 + 1) // 2
+    assert s.row_tiles_max == (1087 + 64 + 1) // 2
+    # blocks of 64 rows: tiles of four block rows
+    s = bsg.topology_sizes(139136, 64, 4096, 64)
+    assert (s.row_blocks_max, s.nnz_max) == (2174, 2174 * 32)
+    assert s.row_tiles_max == (2174 + 3 * (64 + 1)) // 4
+    with pytest.raises(bsg.BsgError):
+        bsg.topology_sizes(1280, 4, 256, 32)
     assert bsg.route_workspace_bytes(65536, 2, 64) == 1024 * 64 * 4
     assert bsg.route_workspace_bytes(65, 1, 3) == 2 * 3 * 4
     assert bsg.route_workspace_bytes(10, 3, 2) == 0
@@ -85,7 +93,7 @@ def test_route_validation(L):
     assert call(ws=None) == bsg.EINVAL
     assert call(wsb=4) == bsg.EINVAL and "workspace" in _err(L)
     assert call(counts=C.c_void_p(0x10002)) == bsg.EINVAL
-    assert call(bin=64) == bsg.EUNSUPPORTED
+    assert call(bin=32) == bsg.EINVAL
     assert call(bin=100) == bsg.EINVAL
 
 
@@ -124,8 +132,8 @@ def test_permute_pad_validation(L):
     assert L.bsg_permute_pad(*b) == bsg.EINVAL and "Tp_max" in _err(L)
     b = list(base); b[10] = 256  # the 256-row bins need a larger Tp_max
     assert L.bsg_permute_pad(*b) == bsg.EINVAL and "Tp_max" in _err(L)
-    b = list(base); b[10] = 64
-    assert L.bsg_permute_pad(*b) == bsg.EUNSUPPORTED
+    b = list(base); b[10] = 32
+    assert L.bsg_permute_pad(*b) == bsg.EINVAL
     b = list(base); b[13] = MIS
     assert L.bsg_permute_pad(*b) == bsg.EINVAL
     b = list(base); b[4] = 9
@@ -153,7 +161,7 @@ def test_permute_pad_gate_backward_validation(L):
     assert call(ld=64) == bsg.EINVAL
     assert call(d=100) == bsg.EINVAL
     assert call(dt=bsg.F32, ypt=bsg.BF16) == bsg.EUNSUPPORTED
-    assert call(bin=64) == bsg.EUNSUPPORTED
+    assert call(bin=32) == bsg.EINVAL
     assert call(E=64, k=40) == bsg.EUNSUPPORTED
 
 
@@ -182,7 +190,7 @@ def test_dsd_combine_top1_validation(L):
 
 def fake_topo(E=4, f=256, Tp=1024, **over):
     t = bsg.TopologyStruct(0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x70000, 0x80000,
-                           0x60000, E, f // 128, Tp)
+                           0x60000, E, f // 128, 128, Tp)
     for k, v in over.items():
         setattr(t, k, v)
     return t
@@ -201,6 +209,9 @@ def test_build_topology_validation(L):
     assert L.bsg_build_topology(P, 4, 256, 1024, C.byref(t4), None) == bsg.EINVAL
     t3 = fake_topo(Tp=1000)
     assert L.bsg_build_topology(P, 4, 256, 1000, C.byref(t3), None) == bsg.EINVAL
+    t5 = fake_topo(block_rows=96)
+    assert L.bsg_build_topology(P, 4, 256, 1024, C.byref(t5), None) == bsg.EINVAL
+    assert "block_rows" in _err(L)
 
 
 def test_sdd_validation(L):
@@ -330,7 +341,7 @@ def test_route_noalloc_validation(L):
     assert call(T=0) == bsg.EINVAL
     assert call(k=9) == bsg.EINVAL
     assert call(E=64, k=40) == bsg.EUNSUPPORTED
-    assert call(bin=64) == bsg.EUNSUPPORTED
+    assert call(bin=32) == bsg.EINVAL
     assert call(counts=C.c_void_p(0x10002)) == bsg.EINVAL
     # ceil(T / 64) * E * 4 bytes of counts: 1025 chunks x 1024 experts > 4 MiB
     assert bsg.route_workspace_bytes(64 * 1025, 1, 1024) > bsg.ROUTE_SCRATCH_BYTES

@@ -124,10 +124,12 @@ def check_case(orc, case: Case, seed=0):
     Tp = int(r["bin_offsets"][cfg.E])
     assert np.array_equal(L.row_src[:Tp].cpu().numpy(), r["row_src"]), "row_src"
 
-    # ---- topology: bit-exact
+    # ---- topology: bit-exact (blocks of 64 rows go with bins of 64)
     F = cfg.f // 128
-    t = orc.topology(r["bin_offsets"], cfg.E, F)
-    nnz, R = t["nnz"], Tp // 128
+    BR = 64 if cfg.bin_rows == 64 else 128
+    Q = 256 // BR
+    t = orc.topology(r["bin_offsets"], cfg.E, F, BR)
+    nnz, R = t["nnz"], Tp // BR
     meta = L.topo.meta.cpu().numpy()
     assert meta[0] == nnz and meta[1] == R
     assert np.array_equal(L.topo.row_ptr[:R + 1].cpu().numpy(), t["row_ptr"])
@@ -135,25 +137,24 @@ def check_case(orc, case: Case, seed=0):
     for key in ("col_idx", "row_idx", "trans_idx"):
         assert np.array_equal(getattr(L.topo, key)[:nnz].cpu().numpy(), t[key]), key
     assert np.array_equal(L.topo.col_ptr.cpu().numpy(), t["col_ptr"]), "col_ptr"
-    # the products' schedule: each expert's block rows two at a time, the
-    # pairs in groups of G (from Tp_max and E), each entry with its place in
-    # its group and the group's size
+    # the products' schedule: each expert's block rows Q at a time (256 rows),
+    # the tiles in groups of G (from Tp_max and E), each entry with its place
+    # in its group, the group's size and the tile's block rows
     rpe = L.Tp_max // (256 * cfg.E)
     G = 8 if (rpe >= 8 and cfg.E <= 16) else 4 if rpe >= 4 else 2 if rpe >= 2 else 1
-    want_pairs = []
+    want_tiles = []
     for e in range(cfg.E):
-        s0, s1 = r["bin_offsets"][e] // 128, r["bin_offsets"][e + 1] // 128
-        starts = list(range(s0, s1, 2))
+        s0, s1 = r["bin_offsets"][e] // BR, r["bin_offsets"][e + 1] // BR
+        starts = list(range(s0, s1, Q))
         for j, r0 in enumerate(starts):
             off = j % G
             size = min(G, len(starts) - (j - off))
-            want_pairs.append((r0 << 7) | ((size - 1) << 4) | (off << 1)
-                              | (1 if r0 + 1 < s1 else 0))
-    assert meta[3] == len(want_pairs)
-    assert L.topo.row_pairs[:len(want_pairs)].cpu().numpy().tolist() == want_pairs
+            want_tiles.append((r0 << 8) | ((size - 1) << 5) | (off << 2) | (min(Q, s1 - r0) - 1))
+    assert meta[3] == len(want_tiles)
+    assert L.topo.row_tiles[:len(want_tiles)].cpu().numpy().tolist() == want_tiles
     # the weight-gradient schedule: experts by descending row blocks, ties to
     # the lower id
-    rb = np.diff(r["bin_offsets"]) // 128
+    rb = np.diff(r["bin_offsets"]) // BR
     want_order = sorted(range(cfg.E), key=lambda e: (-rb[e], e))
     assert L.topo.expert_order.cpu().numpy().tolist() == want_order, "expert_order"
 
@@ -278,6 +279,14 @@ SMALL = {
                                  x_std=0.5)),
     # bins padded to 256 rows (every expert an even number of block rows)
     "bins256_bf16": Case(_small("bins256_bf16", bin_rows=256)),
+    # bins of 64 rows in blocks of 64 rows: tiles of up to four block rows
+    "bins64_bf16": Case(_small("bins64_bf16", bin_rows=64)),
+    "bins64_f32": Case(_small("bins64_f32", T=700, d=256, E=6, f=256, k=2, dtype="f32",
+                              x_std=0.5, bin_rows=64)),
+    "bins64_swiglu": Case(_small("bins64_swiglu", T=600, d=384, E=4, f=384, k=2,
+                                 act="swiglu", renorm=True, yp_dtype="f32", bin_rows=64)),
+    "bins64_top1_bf16": Case(_small("bins64_top1_bf16", T=900, d=384, E=5, f=256, k=1,
+                                    bin_rows=64)),
     "bins256_swiglu": Case(_small("bins256_swiglu", T=500, d=256, E=4, f=256, k=2,
                                   act="swiglu", renorm=True, yp_dtype="f32", bin_rows=256)),
 }
@@ -308,6 +317,14 @@ def _edge_cases():
     cases["max_experts"] = Case(_small("max_experts", T=3000, d=128, E=1024, f=128, k=2,
                                        renorm=True), n_tokens=200, n_wgrad=64)
     cases["max_topk"] = Case(_small("max_topk", T=200, d=128, E=40, f=128, k=32, renorm=True))
+    # bins of 64 rows: experts ending in tiles of 1, 2, 3 and 4 block rows of
+    # 64, one expert of seven block rows (4 + 3), one without tokens
+    ex = np.repeat(np.arange(6), [59, 125, 182, 256, 447, 0])
+    cfg = _small("bins64_slots", T=1069, d=256, E=6, f=384, k=1, bin_rows=64)
+    cases["bins64_slots"] = Case(cfg, logits=_assign_logits(1069, 6, ex))
+    cfg = _small("bins64_slots_swiglu", T=1069, d=256, E=6, f=256, k=1, act="swiglu",
+                 bin_rows=64)
+    cases["bins64_slots_swiglu"] = Case(cfg, logits=_assign_logits(1069, 6, ex))
     # ties in the logits (lower id wins)
     cfg = _small("ties", T=256, d=128, E=8, f=128, k=2)
     lg = np.random.default_rng(4).integers(-2, 3, size=(256, 8)).astype(np.float32)
@@ -370,33 +387,41 @@ def _bf16_draw(rng, shape, std):
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(v)).reshape(shape)
 
 
+@pytest.mark.parametrize("bin_rows", [128, 64])
 @pytest.mark.parametrize("name", list(GROUPS))
-def test_products_at_tile_groups(orc, name):
+def test_products_at_tile_groups(orc, name, bin_rows):
     """SDD, DSD and DSTD called directly on seeded operands shared with the
     oracle, on the topologies of the tile-group cases (groups of 4 and 8 row
-    pairs with half tiles and short last groups, column-pair groups with a
-    short last group): every output element against the oracle's block
-    products, with every epilogue, operand layout and output form the layer
-    uses at these shapes.  Only the accumulation (fp32 against fp64) and the
-    final rounding differ between the two sides, so the bar applies as is."""
+    tiles with partial tiles and short last groups, column-pair groups with a
+    short last group), in blocks of 128 rows and, over bins of 64, of 64 rows
+    (tiles ending in 1, 2 or 3 of their 4 block rows): every output element
+    against the oracle's block products, with every epilogue, operand layout
+    and output form the layer uses at these shapes.  Only the accumulation
+    (fp32 against fp64) and the final rounding differ between the two sides,
+    so the bar applies as is."""
     from block_sparse_gemm_amd import bsg, layer
     cfg, counts, G = GROUPS[name]
-    _say(f"[products] {name} T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} k={cfg.k} act={cfg.act}")
+    cfg = cfg.replace(bin_rows=bin_rows)
+    BR = 64 if bin_rows == 64 else 128
+    _say(f"[products] {name} T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} k={cfg.k} act={cfg.act} "
+         f"bin_rows={bin_rows}")
     lg = _picks_logits(cfg.T, cfg.E, cfg.k, counts, seed=31)
     L = layer.Layer(layer.Shape.of(cfg))
     bsg.route(torch.from_numpy(lg).cuda(), cfg.k, cfg.renorm, L.expert_idx, L.gate, L.dest_row,
-              L.counts, L.bin_offsets, L.route_ws)
+              L.counts, L.bin_offsets, L.route_ws, bin_rows=bin_rows)
     bsg.build_topology(L.bin_offsets, cfg.E, cfg.f, L.Tp_max, L.topo)
     torch.cuda.synchronize()
-    r = orc.route(lg, cfg.k, cfg.renorm)
+    r = orc.route(lg, cfg.k, cfg.renorm, bin_rows)
     bo = r["bin_offsets"]
     assert np.array_equal(L.bin_offsets.cpu().numpy(), bo)
+    assert L.topo.meta[2].item() == 0
     E, F, d, f = cfg.E, cfg.f // 128, cfg.d, cfg.f
-    Tp, nnz, nnz_max = int(bo[E]), int(bo[E]) // 128 * F, L.topo.nnz_max
+    Tp, nnz, nnz_max = int(bo[E]), int(bo[E]) // BR * F, L.topo.nnz_max
     rng = np.random.default_rng(41)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
-    blocks_of = lambda t, planes=1: t.view(planes, nnz_max, 128, 128)[:, :nnz].float() \
-        .cpu().double().numpy().reshape(planes * nnz, 128, 128)
+    blocks_of = lambda t, planes=1: t.view(planes, nnz_max, BR, 128)[:, :nnz].float() \
+        .cpu().double().numpy().reshape(planes * nnz, BR, 128)
+    P = dict(block_rows=BR)
     report = {}
 
     def compare(label, got, want):
@@ -408,63 +433,63 @@ def test_products_at_tile_groups(orc, name):
     sw = cfg.act == "swiglu"
     W3 = _bf16_draw(rng, (d, E * f), 0.05) if sw else None
     planes = 2 if sw else 1
-    out = torch.zeros(planes * nnz_max * 128, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(planes * nnz_max * BR, 128, dtype=torch.bfloat16, device="cuda")
     aux = torch.zeros_like(out)
     # forward SDD, saving the backward's factor(s)
     if sw:
-        bsg.sdd(dev(xp), dev(W1), d, L.topo, "silu_mul", out[:nnz_max * 128], b2=dev(W3),
+        bsg.sdd(dev(xp), dev(W1), d, L.topo, "silu_mul", out[:nnz_max * BR], b2=dev(W3),
                 aux_out=aux)
-        A, SQ = orc.sdd(xp, W1, d, bo, E, F, "silu_mul", b2=W3, want_aux=True)
+        A, SQ = orc.sdd(xp, W1, d, bo, E, F, "silu_mul", b2=W3, want_aux=True, **P)
         torch.cuda.synchronize()
-        compare("sdd A", blocks_of(out[:nnz_max * 128]), A)
+        compare("sdd A", blocks_of(out[:nnz_max * BR]), A)
         compare("sdd S, Q", blocks_of(aux, 2), SQ)
     else:
         bsg.sdd(dev(xp), dev(W1), d, L.topo, "gelu", out, aux_out=aux)
-        A, Gp = orc.sdd(xp, W1, d, bo, E, F, "gelu", want_aux=True)
+        A, Gp = orc.sdd(xp, W1, d, bo, E, F, "gelu", want_aux=True, **P)
         torch.cuda.synchronize()
         compare("sdd A", blocks_of(out), A)
         compare("sdd G", blocks_of(aux), Gp)
     # backward SDD: B transposed (W2 as stored), saved factor(s) in
     dyp = _bf16_draw(rng, (L.Tp_max, d), 1.0)
-    saved = _bf16_draw(rng, (planes * nnz_max * 128, 128), 1.0)
-    saved_used = saved.reshape(planes, nnz_max, 128, 128)[:, :nnz].reshape(-1)
+    saved = _bf16_draw(rng, (planes * nnz_max * BR, 128), 1.0)
+    saved_used = saved.reshape(planes, nnz_max, BR, 128)[:, :nnz].reshape(-1)
     bsg.sdd(dev(dyp), dev(W2), d, L.topo, "silu_mul_bwd" if sw else "gelu_bwd", out,
             trans_b=True, aux_in=dev(saved))
     want = orc.sdd(dyp, W2, d, bo, E, F, "silu_mul_bwd" if sw else "gelu_bwd", trans_b=True,
-                   aux_in=saved_used)
+                   aux_in=saved_used, **P)
     torch.cuda.synchronize()
     compare("sdd_bwd dH", blocks_of(out, planes), want)
     # DSD: W2 as stored, bf16 rows; and B transposed with fp32 rows (two sets for SwiGLU)
-    blk = _bf16_draw(rng, (planes * nnz_max * 128, 128), 1.0)
-    blk_used = blk.reshape(planes, nnz_max, 128, 128)[:, :nnz].reshape(planes * nnz, 128, 128)
+    blk = _bf16_draw(rng, (planes * nnz_max * BR, 128), 1.0)
+    blk_used = blk.reshape(planes, nnz_max, BR, 128)[:, :nnz].reshape(planes * nnz, BR, 128)
     c16 = torch.zeros(L.Tp_max, d, dtype=torch.bfloat16, device="cuda")
-    bsg.dsd(dev(blk[:nnz_max * 128]), L.topo, dev(W2), d, c16)
-    want = orc.dsd(blk_used[:nnz], bo, E, F, W2, d)
+    bsg.dsd(dev(blk[:nnz_max * BR]), L.topo, dev(W2), d, c16)
+    want = orc.dsd(blk_used[:nnz], bo, E, F, W2, d, **P)
     torch.cuda.synchronize()
     compare("dsd", c16[:Tp].double().cpu().numpy(), want)
     c32 = torch.zeros(L.Tp_max, d, dtype=torch.float32, device="cuda")
     if sw:
-        bsg.dsd(dev(blk[:nnz_max * 128]), L.topo, dev(W1), d, c32, trans_b=True,
-                blocks2=dev(blk[nnz_max * 128:]), b2=dev(W3))
+        bsg.dsd(dev(blk[:nnz_max * BR]), L.topo, dev(W1), d, c32, trans_b=True,
+                blocks2=dev(blk[nnz_max * BR:]), b2=dev(W3))
         want = orc.dsd(blk_used[:nnz], bo, E, F, W1, d, prec="f32", trans_b=True,
-                       blocks2=blk_used[nnz:], b2=W3)
+                       blocks2=blk_used[nnz:], b2=W3, **P)
     else:
         bsg.dsd(dev(blk), L.topo, dev(W1), d, c32, trans_b=True)
-        want = orc.dsd(blk_used, bo, E, F, W1, d, prec="f32", trans_b=True)
+        want = orc.dsd(blk_used, bo, E, F, W1, d, prec="f32", trans_b=True, **P)
     torch.cuda.synchronize()
     compare("dsd (B transposed, fp32 rows)", c32[:Tp].double().cpu().numpy(), want)
     # DSTD through the transpose index, stored as is and transposed
     dm = torch.zeros(L.Tp_max, d, dtype=torch.bfloat16, device="cuda")
     dm[:Tp] = dev(xp[:Tp])                                 # rows past Tp are never read
-    want = orc.dstd(blk_used[:nnz], bo, E, F, xp[:Tp], d)
+    want = orc.dstd(blk_used[:nnz], bo, E, F, xp[:Tp], d, **P)
     dW = torch.zeros(E * f, d, dtype=torch.bfloat16, device="cuda")
     dWt = torch.zeros(d, E * f, dtype=torch.bfloat16, device="cuda")
-    bsg.dstd(dev(blk[:nnz_max * 128]), L.topo, dm, d, dW)
-    bsg.dstd(dev(blk[:nnz_max * 128]), L.topo, dm, d, dWt, trans_c=True)
+    bsg.dstd(dev(blk[:nnz_max * BR]), L.topo, dm, d, dW)
+    bsg.dstd(dev(blk[:nnz_max * BR]), L.topo, dm, d, dWt, trans_c=True)
     torch.cuda.synchronize()
     compare("dstd", dW.double().cpu().numpy(), want)
     compare("dstd (transposed)", dWt.double().cpu().numpy().T, want)
-    _say(f"[products] {name} ok; max|d|/max|o|: " +
+    _say(f"[products] {name} bin_rows={bin_rows} ok; max|d|/max|o|: " +
          ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
 
 
@@ -520,6 +545,11 @@ FULL = {
     "moe_small": Case(synth.CONFIGS["moe_small"], n_tokens=64, n_wgrad=24),
     "mixtral": Case(synth.CONFIGS["mixtral"], n_tokens=12),
     "mixtral_train": Case(synth.CONFIGS["mixtral_train"], n_tokens=8, n_wgrad=8),
+    "moe_xs_bins64": Case(synth.CONFIGS["moe_xs"].replace(name="moe_xs_bins64", bin_rows=64),
+                          n_tokens=96),
+    "moe_small_bins64": Case(synth.CONFIGS["moe_small"].replace(name="moe_small_bins64",
+                                                                bin_rows=64),
+                             n_tokens=48, n_wgrad=16),
     "moe_small_bins256": Case(synth.CONFIGS["moe_small"].replace(name="moe_small_bins256",
                                                                  bin_rows=256),
                               n_tokens=48, n_wgrad=16),
