@@ -31,7 +31,7 @@ EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
            "bsg_route_noalloc",
            "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
-           "bsg_build_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
+           "bsg_build_topology", "bsg_route_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_stream_copy", "bsg_status_string", "bsg_last_error")
 
 
@@ -89,6 +89,9 @@ def lib():
                                                     vp, vp]
         L.bsg_build_topology.restype = i32
         L.bsg_build_topology.argtypes = [vp, i32, i32, i64, C.POINTER(TopologyStruct), vp]
+        L.bsg_route_topology.restype = i32
+        L.bsg_route_topology.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
+                                         i32, i64, C.POINTER(TopologyStruct), vp]
         L.bsg_sdd.restype = i32
         L.bsg_sdd.argtypes = [vp, i64, vp, vp, i64, i32, i32, C.POINTER(TopologyStruct), i32, vp,
                               vp, vp, i32, vp]
@@ -237,6 +240,17 @@ def permute_pad_gate_backward(dy, k, dest_row, gate, counts, bin_offsets, E, Tp_
 def build_topology(bin_offsets, E, f, Tp_max, topo: Topology):
     _check("build_topology", lib().bsg_build_topology(_ptr(bin_offsets), E, f, Tp_max,
                                                       C.byref(topo.struct), _stream()))
+
+
+def route_topology(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets, workspace,
+                   f, Tp_max, topo: Topology, bin_rows=BLOCK):
+    """route + build_topology, the topology written by the routing's own launch."""
+    T, E = logits.shape
+    _check("route_topology", lib().bsg_route_topology(
+        _ptr(logits), T, E, k, int(bool(renorm)), bin_rows, _ptr(expert_idx), _ptr(gate),
+        _ptr(dest_row), _ptr(counts), _ptr(bin_offsets), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), f, Tp_max, C.byref(topo.struct),
+        _stream()))
 
 
 def sdd(a, b, K, topo: Topology, epilogue, out_blocks, b2=None, trans_b=False, aux_in=None,

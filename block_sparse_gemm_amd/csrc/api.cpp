@@ -65,7 +65,8 @@ bsg_status check_topology(const bsg_topology* t) {
     // row_tiles entries keep the first block row in 23 bits
     REQUIRE(t->Tp_max / t->block_rows < (int64_t(1) << 23), "too many block rows for row tiles");
     REQUIRE(t->Tp_max / t->block_rows <= INT32_MAX &&
-                (t->Tp_max / t->block_rows) * (int64_t)t->F < INT32_MAX,
+                (t->Tp_max / t->block_rows) * (int64_t)t->F < INT32_MAX &&
+                (int64_t)t->E * t->F < INT32_MAX,
             "too many blocks for int32 ids");
     REQUIRE_PTR(t->row_ptr);
     REQUIRE_PTR(t->col_idx);
@@ -193,7 +194,7 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, i
     REQUIRE(workspace_bytes >= bsg_route_workspace_bytes(T, k, E), "workspace too small (%zu < %zu)",
             workspace_bytes, bsg_route_workspace_bytes(T, k, E));
     return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
-                                        counts, bin_offsets, (int32_t*)workspace,
+                                        counts, bin_offsets, (int32_t*)workspace, bsg::TopoJob{},
                                         (hipStream_t)stream),
                       "route");
 }
@@ -214,7 +215,8 @@ bsg_status bsg_route_noalloc(const float* logits, int64_t T, int E, int k, int r
     const hipError_t e = bsg::route_scratch((hipStream_t)stream, &scratch);
     if (e != hipSuccess) return hip_status(e, "route_noalloc scratch");
     return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
-                                        counts, bin_offsets, scratch, (hipStream_t)stream),
+                                        counts, bin_offsets, scratch, bsg::TopoJob{},
+                                        (hipStream_t)stream),
                       "route_noalloc");
 }
 
@@ -323,23 +325,60 @@ static int tile_group(int64_t Tp_max, int E) {
     return (rpe >= 8 && E <= 16) ? 8 : rpe >= 4 ? 4 : rpe >= 2 ? 2 : 1;
 }
 
-bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
-                              const bsg_topology* topo, bsg_stream_t stream) {
-    REQUIRE_PTR(bin_offsets);
+static bsg_status check_topology_args(int E, int f, int64_t Tp_max, const bsg_topology* topo) {
     REQUIRE(E >= 1 && E <= BSG_MAX_EXPERTS, "E must be in [1, %d]", BSG_MAX_EXPERTS);
     REQUIRE(f >= BSG_BLOCK && f % BSG_BLOCK == 0, "f must be a positive multiple of 128");
     bsg_status s = check_topology(topo);
     if (s != BSG_OK) return s;
     REQUIRE(topo->E == E && topo->F == f / BSG_BLOCK && topo->Tp_max == Tp_max,
             "topo capacity does not match E, f, Tp_max");
+    return BSG_OK;
+}
+
+// What the topology kernels need of a validated topology.
+static bsg::TopoJob topo_job(const bsg_topology* t) {
+    bsg::TopoJob j{};
+    j.o = bsg::TopoArrays{t->row_ptr, t->col_idx,   t->row_idx,      t->col_ptr,
+                          t->trans_idx, t->row_tiles, t->expert_order, t->meta};
+    j.F = t->F;
+    j.br = t->block_rows;
+    j.group = tile_group(t->Tp_max, t->E);
+    j.on = 1;
+    j.row_blocks_max = t->Tp_max / t->block_rows;
+    j.row_tiles_max = row_tiles_max(j.row_blocks_max, t->E, t->block_rows);
+    return j;
+}
+
+bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t Tp_max,
+                              const bsg_topology* topo, bsg_stream_t stream) {
+    REQUIRE_PTR(bin_offsets);
+    const bsg_status s = check_topology_args(E, f, Tp_max, topo);
+    if (s != BSG_OK) return s;
+    const bsg::TopoJob j = topo_job(topo);
     return hip_status(
-        bsg::launch_build_topology(bin_offsets, E, topo->F, topo->block_rows,
-                                   Tp_max / topo->block_rows,
-                                   row_tiles_max(Tp_max / topo->block_rows, E, topo->block_rows),
-                                   topo->row_ptr, topo->col_idx, topo->row_idx, topo->col_ptr,
-                                   topo->trans_idx, topo->row_tiles, topo->expert_order,
-                                   topo->meta, tile_group(Tp_max, E), (hipStream_t)stream),
+        bsg::launch_build_topology(bin_offsets, E, j.F, j.br, j.row_blocks_max, j.row_tiles_max,
+                                   j.o.row_ptr, j.o.col_idx, j.o.row_idx, j.o.col_ptr,
+                                   j.o.trans_idx, j.o.row_tiles, j.o.expert_order, j.o.meta,
+                                   j.group, (hipStream_t)stream),
         "build_topology");
+}
+
+bsg_status bsg_route_topology(const float* logits, int64_t T, int E, int k, int renorm,
+                              int bin_rows, int32_t* expert_idx, float* gate, int32_t* dest_row,
+                              int32_t* counts, int32_t* bin_offsets, void* workspace,
+                              size_t workspace_bytes, int f, int64_t Tp_max,
+                              const bsg_topology* topo, bsg_stream_t stream) {
+    bsg_status s =
+        check_route(logits, T, E, k, bin_rows, expert_idx, gate, dest_row, counts, bin_offsets);
+    if (s != BSG_OK) return s;
+    REQUIRE_PTR(workspace);
+    REQUIRE(workspace_bytes >= bsg_route_workspace_bytes(T, k, E), "workspace too small (%zu < %zu)",
+            workspace_bytes, bsg_route_workspace_bytes(T, k, E));
+    if ((s = check_topology_args(E, f, Tp_max, topo)) != BSG_OK) return s;
+    return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
+                                        counts, bin_offsets, (int32_t*)workspace, topo_job(topo),
+                                        (hipStream_t)stream),
+                      "route_topology");
 }
 
 static bsg::GemmParams gemm_params(const bsg_topology* t) {

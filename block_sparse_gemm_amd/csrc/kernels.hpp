@@ -69,6 +69,19 @@ struct GemmParams {
                           // DSD take their groups from row_tiles
 };
 
+// The arrays of a topology (bsg_topology's device pointers).
+struct TopoArrays {
+    int32_t *row_ptr, *col_idx, *row_idx, *col_ptr, *trans_idx, *row_tiles, *expert_order, *meta;
+};
+
+// A topology for the routing to build in its placement launch, from the bin
+// offsets it has just formed (on = 0: none).  Fields as launch_build_topology.
+struct TopoJob {
+    TopoArrays o;
+    int F, br, group, on;
+    int64_t row_blocks_max, row_tiles_max;
+};
+
 // Bytes of the file-scope device array behind the allocation-free routing
 // entry point (per GPU): 4 MiB, one count per (64-token chunk, expert).
 constexpr size_t kRouteScratchBytes = size_t(4) << 20;
@@ -78,7 +91,8 @@ hipError_t route_scratch(hipStream_t stream, int32_t** out);
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
-                        int32_t* bin_offsets, int32_t* workspace, hipStream_t stream);
+                        int32_t* bin_offsets, int32_t* workspace, const TopoJob& topo,
+                        hipStream_t stream);
 
 hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
                                  const int32_t* expert_idx, const int32_t* dest_row,

@@ -3,29 +3,35 @@
 // George Lin's Blog (MegaBlocks/FlexMoE post), section 1.4: tokens are
 // routed to experts and regrouped from batch order into expert order, each
 // group padded to a multiple of the 128 block size (section 1.3), or of a
-// coarser bin (256 rows) for the block-size study.  The
+// finer or coarser bin (64 or 256 rows) for the block-size study.  The
 // pages leave the gate's form open; this follows top-k on the logits with a
 // softmax gate.
 //
-// Three launches, no atomics on global memory, so every integer result is
+// Two launches, no atomics on global memory, so every integer result is
 // identical on every run:
 //   1. route_topk     one workgroup per 64-token chunk, one wavefront per
 //                     token at a time (4 each, loaded up front): top-k by
-//                     wave reductions, softmax gate; an LDS histogram.  Up
-//                     to 64 experts and top-16 (route_topk_seg): the 4
-//                     tokens of a wave side by side, 16 lanes each.
-//   2. route_scan     one workgroup per expert: exclusive scan of that
-//                     expert's per-chunk counts (in place) and its total,
-//                     by wave shuffles and one barrier.
-//   3. route_place    one workgroup per chunk: padded bin offsets, then the
-//                     rank of each assignment among the chunk's earlier
-//                     assignments to the same expert, found with wave64
-//                     ballots on the expert id bits.
+//                     wave reductions, softmax gate; an LDS histogram, the
+//                     chunk's row of a chunk-major count matrix.  Up to 64
+//                     experts and top-16 (route_topk_seg): the 4 tokens of a
+//                     wave side by side, 16 lanes each.
+//   2. route_place    one workgroup per 16 chunks: every workgroup sums the
+//                     count matrix (per-expert totals, and the counts of the
+//                     chunks before its own), forms the padded bin offsets,
+//                     then ranks each of its assignments among the earlier
+//                     ones of the same expert with wave64 ballots on the
+//                     expert id bits.  It can also write the topology of
+//                     those bins (topology.hpp), so route + topology is two
+//                     launches.
+// Routings too large for every workgroup to read the whole count matrix
+// scan it first in a launch of its own (route_scan, one workgroup per
+// expert).
 #include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
 #include "scan.hpp"
+#include "topology.hpp"
 
 namespace bsg {
 
@@ -74,7 +80,7 @@ template <int NV>
 __global__ __launch_bounds__(kTopkThreads) void route_topk(
     const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
     int32_t* __restrict__ expert_idx, float* __restrict__ gate,
-    int32_t* __restrict__ chunk_counts, int nchunks) {
+    int32_t* __restrict__ chunk_counts) {
     __shared__ int hist[kMaxExperts];
     for (int e = threadIdx.x; e < E; e += kTopkThreads) hist[e] = 0;
 
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk(
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kTopkThreads)
-        chunk_counts[(int64_t)e * nchunks + blockIdx.x] = hist[e];
+        chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
 // E <= 64, k <= 16: a wave's 4 tokens side by side, 16 lanes each (lane s of
@@ -161,7 +167,7 @@ template <int NV>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_seg(
     const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
     int32_t* __restrict__ expert_idx, float* __restrict__ gate,
-    int32_t* __restrict__ chunk_counts, int nchunks) {
+    int32_t* __restrict__ chunk_counts) {
     constexpr int kSeg = 16;
     static_assert(kTokPerWave * kSeg == kWave, "the wave's tokens fill its lanes");
     __shared__ int hist[kSeg * NV];
@@ -238,71 +244,194 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_seg(
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kTopkThreads)
-        chunk_counts[(int64_t)e * nchunks + blockIdx.x] = hist[e];
+        chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Exclusive scan of one expert's chunk counts, in place; total -> counts[e].
+// Exclusive scan of one expert's chunk counts (column e of the chunk-major
+// count matrix), in place; total -> counts[e].  Only for routings too large
+// for the placement to sum the counts itself.
 __global__ __launch_bounds__(kRouteThreads) void route_scan(int32_t* __restrict__ chunk_counts,
-                                                            int nchunks,
+                                                            int nchunks, int E,
                                                             int32_t* __restrict__ counts) {
     __shared__ int wsum[kRouteWaves];
-    int32_t* row = chunk_counts + (int64_t)blockIdx.x * nchunks;
+    int32_t* col = chunk_counts + blockIdx.x;
     const int per = (nchunks + kRouteThreads - 1) / kRouteThreads;
     const int lo = threadIdx.x * per;
     const int hi = min(lo + per, nchunks);
     int s = 0;
-    for (int c = lo; c < hi; ++c) s += row[c];
+    for (int c = lo; c < hi; ++c) s += col[(int64_t)c * E];
     int total;
     int run = block_excl_scan<kRouteWaves>(s, wsum, total);  // exclusive prefix of this segment
     for (int c = lo; c < hi; ++c) {
-        const int v = row[c];
-        row[c] = run;
+        const int v = col[(int64_t)c * E];
+        col[(int64_t)c * E] = run;
         run += v;
     }
     if (threadIdx.x == kRouteThreads - 1) counts[blockIdx.x] = total;
 }
 
-// Bin offsets + stable in-chunk ranks -> dest_row.
-__global__ __launch_bounds__(kRouteThreads) void route_place(
-    const int32_t* __restrict__ expert_idx, int64_t T, int E, int k,
-    const int32_t* __restrict__ chunk_base, int nchunks, const int32_t* __restrict__ counts,
-    int bin_rows, int32_t* __restrict__ dest_row, int32_t* __restrict__ bin_offsets) {
-    __shared__ int bins[kMaxExperts + 1];
-    __shared__ int wsum[kRouteWaves];
-    __shared__ int running[kMaxExperts];
-    __shared__ int wcnt[kRouteWaves][kMaxExperts];
+constexpr int kPlaceThreads = 1024;
+constexpr int kPlaceWaves = kPlaceThreads / kWave;  // 16
+constexpr int kPlaceChunks = 16;                     // chunks (1024 tokens) per workgroup
+// Every placement workgroup sums the whole count matrix itself when it has
+// at most this many entries and the routing at most this many chunks (the
+// matrix is then read from L2 by at most 64 workgroups); larger routings
+// scan it in a launch of their own first.
+constexpr int64_t kSelfScanCounts = 65536;
+constexpr int kSelfScanChunks = 1024;
 
-    // padded sizes, exclusive scan over ascending expert id
-    const int per = (E + kRouteThreads - 1) / kRouteThreads;
-    const int lo = threadIdx.x * per;
-    const int hi = min(lo + per, E);
-    int s = 0;
-    for (int e = lo; e < hi; ++e) s += (counts[e] + bin_rows - 1) / bin_rows * bin_rows;
-    for (int e = threadIdx.x; e < E; e += kRouteThreads) running[e] = 0;
-    int total;
-    int run = block_excl_scan<kRouteWaves>(s, wsum, total);
-    for (int e = lo; e < hi; ++e) {
-        bins[e] = run;
-        run += (counts[e] + bin_rows - 1) / bin_rows * bin_rows;
+// Per-expert totals and this workgroup's starting ranks (the assignments
+// of chunks before c0) from the raw chunk-major counts, into LDS (both
+// cleared by the caller).  VEC: E is a power of two in [4, 1024] and the
+// counts are 16-byte aligned, so a thread's 4-count vectors always hold
+// the same 4 experts and it sums them in registers.
+template <bool VEC>
+__device__ __forceinline__ void sum_chunk_counts(const int32_t* __restrict__ cc, int nchunks,
+                                                 int E, int c0, int* tot, int* pre) {
+    const int64_t n = (int64_t)nchunks * E;
+    if constexpr (VEC) {
+        const int4* v4 = (const int4*)cc;
+        const int64_t n4 = n / 4;
+        const int e0 = (4 * threadIdx.x) & (E - 1);
+        int t[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
+        int64_t i = threadIdx.x;
+        for (; i + 7 * kPlaceThreads < n4; i += 8 * kPlaceThreads) {
+            int4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = v4[i + u * kPlaceThreads];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bool before = (4 * (i + u * kPlaceThreads)) / E < c0;
+                t[0] += v[u].x; t[1] += v[u].y; t[2] += v[u].z; t[3] += v[u].w;
+                if (before) { p[0] += v[u].x; p[1] += v[u].y; p[2] += v[u].z; p[3] += v[u].w; }
+            }
+        }
+        for (; i < n4; i += kPlaceThreads) {
+            const int4 v = v4[i];
+            t[0] += v.x; t[1] += v.y; t[2] += v.z; t[3] += v.w;
+            if ((4 * i) / E < c0) { p[0] += v.x; p[1] += v.y; p[2] += v.z; p[3] += v.w; }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (t[q]) atomicAdd(&tot[e0 + q], t[q]);  // LDS only: integer sums, order-free
+            if (p[q]) atomicAdd(&pre[e0 + q], p[q]);
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < n; i += kPlaceThreads) {
+            const int v = cc[i];
+            if (!v) continue;
+            const int e = (int)(i % E);
+            atomicAdd(&tot[e], v);
+            if (i / E < c0) atomicAdd(&pre[e], v);
+        }
     }
-    if (threadIdx.x == kRouteThreads - 1) bins[E] = total;
-    __syncthreads();
-    if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e <= E; e += kRouteThreads) bin_offsets[e] = bins[e];
+}
 
+// Counts, padded bin offsets and dest_row; with `topo.on`, also the
+// topology of those bins.  Every workgroup forms the bins; the first
+// `nplace` workgroups then place, workgroup w the assignments of chunks
+// [16 w, 16 w + 16): the rank of each assignment among the earlier ones of
+// its expert, from the count of the earlier chunks plus wave64 ballots on
+// the expert id bits inside the workgroup.  The workgroups after them write
+// the topology (topology.hpp) meanwhile, so it costs no launch and little
+// time of its own.  SCANNED: route_scan has already turned the counts into
+// per-expert exclusive prefixes and totals; else each workgroup sums them
+// itself.
+template <bool SCANNED, bool VEC>
+__global__ __launch_bounds__(kPlaceThreads) void route_place(
+    const int32_t* __restrict__ expert_idx, int64_t T, int E, int k,
+    const int32_t* __restrict__ chunk_counts, int nchunks, int nplace,
+    int32_t* __restrict__ counts, int bin_rows, int32_t* __restrict__ dest_row,
+    int32_t* __restrict__ bin_offsets, TopoJob topo) {
+    __shared__ int tot[kMaxExperts];
+    __shared__ int running[kMaxExperts];
+    __shared__ int bins[kMaxExperts + 1];
+    __shared__ int2 wsum2[kPlaceWaves];
+    __shared__ int wcnt[kPlaceWaves][kMaxExperts];
+    __shared__ TopoLds<kPlaceThreads> tl;
+
+    const bool placer = (int)blockIdx.x < nplace;
+    const int c0 = placer ? (int)blockIdx.x * kPlaceChunks : 0;
+    const int64_t A = T * k;
+    const int64_t a0 = placer ? min((int64_t)c0 * kRouteChunk * k, A) : 0;
+    const int64_t a1 = placer ? min(a0 + (int64_t)kPlaceChunks * kRouteChunk * k, A) : 0;
+    // the first round's expert ids, loaded while the counts are summed
+    const int e_first = (a0 + threadIdx.x < a1) ? expert_idx[a0 + threadIdx.x] : 0;
+
+    if constexpr (SCANNED) {
+        for (int e = threadIdx.x; e < E; e += kPlaceThreads) {
+            tot[e] = counts[e];
+            running[e] = placer ? chunk_counts[(int64_t)c0 * E + e] : 0;
+        }
+    } else {
+        for (int e = threadIdx.x; e < E; e += kPlaceThreads) tot[e] = running[e] = 0;
+    }
+    for (int i = threadIdx.x; i < kPlaceWaves * E; i += kPlaceThreads) wcnt[i / E][i % E] = 0;
+    if (threadIdx.x == 0) tl.misaligned = 0;
+    __syncthreads();
+    if constexpr (!SCANNED) {
+        sum_chunk_counts<VEC>(chunk_counts, nchunks, E, c0, tot, running);
+        __syncthreads();
+        if (blockIdx.x == 0)
+            for (int e = threadIdx.x; e < E; e += kPlaceThreads) counts[e] = tot[e];
+    }
+
+    // padded sizes, exclusive scan over ascending expert id; with a
+    // topology, the same scan also counts each expert's 256-row tiles and
+    // leaves the topology's LDS state (bin starts in block rows, first tile
+    // of each expert) ready
+    {
+        const int br = topo.on ? topo.br : kBlock;
+        const int per = (E + kPlaceThreads - 1) / kPlaceThreads;
+        const int lo = threadIdx.x * per;
+        const int hi = min(lo + per, E);
+        int2 v = make_int2(0, 0);
+        for (int e = lo; e < hi; ++e) {
+            const int pe = (tot[e] + bin_rows - 1) / bin_rows * bin_rows;
+            v.x += pe;
+            v.y += (pe + 255) / 256;
+        }
+        int2 total;
+        int2 run = block_excl_scan2<kPlaceWaves>(v, wsum2, total);
+        for (int e = lo; e < hi; ++e) {
+            const int pe = (tot[e] + bin_rows - 1) / bin_rows * bin_rows;
+            bins[e] = run.x;
+            tl.s[e] = run.x / br;
+            tl.pp[e] = run.y;
+            if (run.x % br) tl.misaligned = 1;  // a bin off the block grid
+            run.x += pe;
+            run.y += (pe + 255) / 256;
+        }
+        if (threadIdx.x == kPlaceThreads - 1) {
+            bins[E] = total.x;
+            tl.s[E] = total.x / br;
+            tl.pp[E] = total.y;
+            if (total.x % br) tl.misaligned = 1;
+        }
+        __syncthreads();
+    }
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e <= E; e += kPlaceThreads) bin_offsets[e] = bins[e];
+
+    if (!placer) {
+        if (topo.on) {
+            topo_order(tl, E, (int)((blockIdx.x - nplace) * kPlaceWaves + threadIdx.x / kWave),
+                       (int)((gridDim.x - nplace) * kPlaceWaves), topo.o.expert_order);
+            topo_write<kPlaceThreads>((int64_t)(blockIdx.x - nplace) * kPlaceThreads + threadIdx.x,
+                                      tl, E, topo.F, topo.br, topo.row_blocks_max, topo.group,
+                                      topo.o);
+        }
+        return;
+    }
+
+    // rounds of 1024 assignments; wcnt starts each round cleared
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    const int64_t a0 = (int64_t)blockIdx.x * kRouteChunk * k;
-    const int64_t a1 = min(a0 + (int64_t)kRouteChunk * k, T * k);
-
-    for (int64_t base = a0; base < a1; base += kRouteThreads) {
-        for (int i = threadIdx.x; i < kRouteWaves * E; i += kRouteThreads)
-            (&wcnt[0][0])[(i / E) * kMaxExperts + i % E] = 0;
-        __syncthreads();
+    for (int64_t base = a0; base < a1; base += kPlaceThreads) {
         const int64_t a = base + threadIdx.x;
         const bool valid = a < a1;
-        const int e = valid ? expert_idx[a] : 0;
+        const int e = base == a0 ? e_first : (valid ? expert_idx[a] : 0);
         // lanes of this wave holding the same expert id
         uint64_t match = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
@@ -312,17 +441,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_place(
         const int rank = __popcll(match & lanemask_lt());
         if (valid && rank == 0) wcnt[wave][e] = __popcll(match);
         __syncthreads();
-        if (valid) {
-            int off = running[e];
-            for (int w = 0; w < wave; ++w) off += wcnt[w][e];
-            dest_row[a] = bins[e] + chunk_base[(int64_t)e * nchunks + blockIdx.x] + off + rank;
+        // per expert: each wave's first rank (the expert's running count plus
+        // the earlier waves' counts), in place of the counts
+        for (int x = threadIdx.x; x < E; x += kPlaceThreads) {
+            int run = running[x];
+#pragma unroll
+            for (int w = 0; w < kPlaceWaves; ++w) {
+                const int c = wcnt[w][x];
+                wcnt[w][x] = run;
+                run += c;
+            }
+            running[x] = run;
         }
         __syncthreads();
-        for (int x = threadIdx.x; x < E; x += kRouteThreads) {
-            int add = 0;
-            for (int w = 0; w < kRouteWaves; ++w) add += wcnt[w][x];
-            running[x] += add;
-        }
+        if (valid) dest_row[a] = bins[e] + wcnt[wave][e] + rank;
+        __syncthreads();
+        for (int i = threadIdx.x; i < kPlaceWaves * E; i += kPlaceThreads) wcnt[i / E][i % E] = 0;
         __syncthreads();
     }
 }
@@ -405,14 +539,15 @@ hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, i
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
-                        int32_t* bin_offsets, int32_t* workspace, hipStream_t stream) {
+                        int32_t* bin_offsets, int32_t* workspace, const TopoJob& topo,
+                        hipStream_t stream) {
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
 #define BSG_TOPK(NV)                                                                         \
     hipLaunchKernelGGL(route_topk<NV>, dim3(nchunks), dim3(kTopkThreads), 0, stream, logits, T, \
-                       E, k, renorm, expert_idx, gate, workspace, nchunks)
+                       E, k, renorm, expert_idx, gate, workspace)
 #define BSG_TOPK_SEG(NV)                                                                     \
     hipLaunchKernelGGL(route_topk_seg<NV>, dim3(nchunks), dim3(kTopkThreads), 0, stream, logits, \
-                       T, E, k, renorm, expert_idx, gate, workspace, nchunks)
+                       T, E, k, renorm, expert_idx, gate, workspace)
     if (E <= 16 && k <= 16) BSG_TOPK_SEG(1);
     else if (E <= 32 && k <= 16) BSG_TOPK_SEG(2);
     else if (E <= 64 && k <= 16) BSG_TOPK_SEG(4);
@@ -423,10 +558,31 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
     else BSG_TOPK(16);
 #undef BSG_TOPK_SEG
 #undef BSG_TOPK
-    hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace, nchunks,
-                       counts);
-    hipLaunchKernelGGL(route_place, dim3(nchunks), dim3(kRouteThreads), 0, stream, expert_idx, T,
-                       E, k, workspace, nchunks, counts, bin_rows, dest_row, bin_offsets);
+    // placing workgroups, then (with a topology) the topology's
+    const int nplace = (nchunks + kPlaceChunks - 1) / kPlaceChunks;
+    int64_t grid = nplace;
+    if (topo.on)
+        grid += (topo_threads(E, topo.F, topo.row_blocks_max, topo.row_tiles_max) +
+                 kPlaceThreads - 1) / kPlaceThreads;
+    const bool self_scan =
+        (int64_t)nchunks * E <= kSelfScanCounts && nchunks <= kSelfScanChunks;
+    if (self_scan) {
+        const bool vec = E >= 4 && (E & (E - 1)) == 0 && ((uintptr_t)workspace & 15) == 0;
+        if (vec)
+            hipLaunchKernelGGL((route_place<false, true>), dim3(grid), dim3(kPlaceThreads), 0,
+                               stream, expert_idx, T, E, k, workspace, nchunks, nplace, counts, bin_rows,
+                               dest_row, bin_offsets, topo);
+        else
+            hipLaunchKernelGGL((route_place<false, false>), dim3(grid), dim3(kPlaceThreads), 0,
+                               stream, expert_idx, T, E, k, workspace, nchunks, nplace, counts, bin_rows,
+                               dest_row, bin_offsets, topo);
+    } else {
+        hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace,
+                           nchunks, E, counts);
+        hipLaunchKernelGGL((route_place<true, false>), dim3(grid), dim3(kPlaceThreads), 0, stream,
+                           expert_idx, T, E, k, workspace, nchunks, nplace, counts, bin_rows,
+                           dest_row, bin_offsets, topo);
+    }
     return hipGetLastError();
 }
 

@@ -277,6 +277,21 @@ bsg_status bsg_build_topology(const int32_t* bin_offsets, int E, int f, int64_t 
                               const bsg_topology* topo /* host struct */, bsg_stream_t stream);
 
 /*
+ * route_topology - bsg_route followed by bsg_build_topology(bin_offsets, E,
+ * f, Tp_max, topo), with the topology written by the routing's own
+ * placement launch (section 1.4: the routing forms the bins, and the
+ * topology with its transpose metadata follows from them alone).  Every
+ * output, bit for bit, and every argument rule and error are those of the
+ * two calls; two launches in all for routings of at most 65536 tokens whose
+ * ceil(T/64) * E per-chunk counts number at most 65536, three above that.
+ */
+bsg_status bsg_route_topology(const float* logits, int64_t T, int E, int k, int renorm,
+                              int bin_rows, int32_t* expert_idx, float* gate, int32_t* dest_row,
+                              int32_t* counts, int32_t* bin_offsets, void* workspace,
+                              size_t workspace_bytes, int f, int64_t Tp_max,
+                              const bsg_topology* topo /* host struct */, bsg_stream_t stream);
+
+/*
  * sdd - sampled dense-dense product (section 1.2, first layer):
  * for every nonzero block b = (r, c):
  *   acc_b[m][n] = sum_k a[BR*r + m][k] * B[k][128c + n],  k < K,

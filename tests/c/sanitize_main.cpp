@@ -10,9 +10,11 @@
 
 #include <vector>
 
+#include "../../block_sparse_gemm_amd/csrc/kernels.hpp"
 #include "../../include/bsg.h"
 
 extern int g_launches;
+extern bsg::TopoJob g_route_topo;
 
 // ---- the oracle's C entry points (oracle/oracle.c)
 extern "C" {
@@ -159,6 +161,26 @@ static void abi_checks() {
     EXPECT(bsg_build_topology(ip, 5, 256, 1024, &t, nullptr) == BSG_EINVAL);
     bsg_topology big = fake_topo(1024, 128 * 32768, INT64_MAX / 128 * 128);
     EXPECT(bsg_build_topology(ip, 1024, 128 * 32768, big.Tp_max, &big, nullptr) == BSG_EINVAL);
+    // route + topology in one call: the routing launch carries the topology
+    {
+        bsg_topology rt = fake_topo(8, 256, bsg_max_padded_rows(100, 2, 8, 128));
+        const int n0 = g_launches;
+        EXPECT(bsg_route_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, 256,
+                                  rt.Tp_max, &rt, nullptr) == BSG_OK);
+        EXPECT(g_launches == n0 + 1 && g_route_topo.on == 1 && g_route_topo.F == 2 &&
+               g_route_topo.br == 128 && g_route_topo.o.meta == rt.meta &&
+               g_route_topo.row_blocks_max == rt.Tp_max / 128);
+        EXPECT(bsg_route(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, nullptr) ==
+                   BSG_OK &&
+               g_route_topo.on == 0);
+        EXPECT(bsg_route_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, 384,
+                                  rt.Tp_max, &rt, nullptr) == BSG_EINVAL);
+        EXPECT(bsg_route_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 4, 256,
+                                  rt.Tp_max, &rt, nullptr) == BSG_EINVAL);
+        EXPECT(bsg_route_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, 256,
+                                  rt.Tp_max, nullptr, nullptr) == BSG_EINVAL);
+        EXPECT(g_launches == n0 + 2);
+    }
     EXPECT(bsg_sdd(P, 256, P, nullptr, 1024, 0, 256, &t, BSG_EPI_GELU, nullptr, P, P, BSG_BF16,
                    nullptr) == BSG_OK);
     EXPECT(bsg_sdd(P, 256, P, P, 1024, 0, 256, &t, BSG_EPI_SILU_MUL, nullptr, P, P, BSG_BF16,

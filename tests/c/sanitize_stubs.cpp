@@ -7,7 +7,8 @@
 
 #include "../../block_sparse_gemm_amd/csrc/kernels.hpp"
 
-int g_launches = 0;  // read by the driver
+int g_launches = 0;             // read by the driver
+bsg::TopoJob g_route_topo = {};  // the last routing launch's topology job
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "host-only build"; }
 
@@ -21,8 +22,9 @@ hipError_t route_scratch(hipStream_t, int32_t** out) {
 }
 
 hipError_t launch_route(const float*, int64_t, int, int, int, int, int32_t*, float*, int32_t*,
-                        int32_t*, int32_t*, int32_t*, hipStream_t) {
+                        int32_t*, int32_t*, int32_t*, const TopoJob& topo, hipStream_t) {
     ++g_launches;
+    g_route_topo = topo;
     return hipSuccess;
 }
 

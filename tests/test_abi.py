@@ -214,6 +214,33 @@ def test_build_topology_validation(L):
     assert "block_rows" in _err(L)
 
 
+def test_route_topology_validation(L):
+    """Every argument rule of route and of build_topology, checked before any
+    launch (the pointers are never dereferenced)."""
+    t = fake_topo(E=8)
+    ok = [P, 100, 8, 2, 0, 128, P, P, P, P, P, P, 1 << 20, 256, 1024, C.byref(t), None]
+    names = ["logits", "T", "E", "k", "renorm", "bin", "expert_idx", "gate", "dest_row",
+             "counts", "bin_offsets", "ws", "wsb", "f", "Tp", "topo", "stream"]
+
+    def call(**over):
+        a = list(ok)
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_route_topology(*a)
+
+    assert call(logits=None) == bsg.EINVAL
+    assert call(k=9) == bsg.EINVAL
+    assert call(E=64, k=40) == bsg.EUNSUPPORTED
+    assert call(wsb=4) == bsg.EINVAL and "workspace" in _err(L)
+    assert call(bin=32) == bsg.EINVAL
+    assert call(f=384) == bsg.EINVAL and "capacity" in _err(L)
+    assert call(f=200) == bsg.EINVAL
+    assert call(Tp=2048) == bsg.EINVAL
+    assert call(topo=None) == bsg.EINVAL
+    t2 = fake_topo(E=8, meta=None)
+    assert call(topo=C.byref(t2)) == bsg.EINVAL
+
+
 def test_sdd_validation(L):
     t = fake_topo(E=4, f=256)
     ncol = 4 * 256

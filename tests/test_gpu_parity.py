@@ -537,6 +537,68 @@ def test_deterministic(orc):
         assert torch.equal(getattr(L1, name), getattr(L2, name)), name
 
 
+_TOPO_KEYS = ("row_ptr", "col_idx", "row_idx", "col_ptr", "trans_idx", "row_tiles",
+              "expert_order", "meta")
+
+
+@pytest.mark.parametrize("T,E,k,ws_offset", [
+    (70000, 64, 2, 0),    # more than 1024 chunks: the count matrix is scanned first
+    (20000, 1024, 1, 0),  # more than 65536 counts, the most experts
+    (3000, 64, 2, 4),     # a workspace off the 16-byte grid: counts summed one by one
+    (65536, 2, 1, 0),     # 1024 chunks, two experts: the largest self-summed routing
+    (1000, 8, 3, 0),      # 4-count vectors of a power-of-two expert count
+])
+def test_route_topology_launch_paths(orc, T, E, k, ws_offset):
+    """route + topology in one call equals route followed by build_topology
+    bit for bit, and both equal the oracle, on each of the placement's ways
+    of forming the counts (scanned first, summed as vectors, summed one by
+    one)."""
+    from block_sparse_gemm_amd import bsg
+    _say(f"[parity] route_topology T={T} E={E} k={k} ws_offset={ws_offset}")
+    f = 256
+    lg = np.random.default_rng(T + E).standard_normal((T, E)).astype(np.float32)
+    lg[:, 0] += 0.75  # mild skew
+    r = orc.route(lg, k, False, 128)
+    t = orc.topology(r["bin_offsets"], E, f // 128, 128)
+    Tp_max = bsg.max_padded_rows(T, k, E)
+    logits = torch.from_numpy(lg).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    nbytes = bsg.route_workspace_bytes(T, k, E)
+    outs = []
+    for fused in (True, False):
+        o = dict(expert_idx=torch.full((T * k,), -7, **i32),
+                 gate=torch.zeros(T * k, dtype=torch.float32, device="cuda"),
+                 dest_row=torch.full((T * k,), -7, **i32), counts=torch.full((E,), -7, **i32),
+                 bin_offsets=torch.full((E + 1,), -7, **i32))
+        ws = torch.full((nbytes + 16,), 0xAB, dtype=torch.uint8, device="cuda")
+        ws = ws[ws_offset:ws_offset + nbytes]
+        topo = bsg.Topology(Tp_max, E, f)
+        for key in _TOPO_KEYS:
+            getattr(topo, key).fill_(-7)
+        if fused:
+            bsg.route_topology(logits, k, False, o["expert_idx"], o["gate"], o["dest_row"],
+                               o["counts"], o["bin_offsets"], ws, f, Tp_max, topo)
+        else:
+            bsg.route(logits, k, False, o["expert_idx"], o["gate"], o["dest_row"], o["counts"],
+                      o["bin_offsets"], ws)
+            bsg.build_topology(o["bin_offsets"], E, f, Tp_max, topo)
+        torch.cuda.synchronize()
+        o = {key: v.cpu().numpy() for key, v in o.items()}
+        o.update({key: getattr(topo, key).cpu().numpy() for key in _TOPO_KEYS})
+        outs.append(o)
+    for key in outs[0]:
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+    o = outs[0]
+    for key in ("expert_idx", "dest_row", "counts", "bin_offsets"):
+        assert np.array_equal(o[key], r[key]), key
+    nnz, R = t["nnz"], int(r["bin_offsets"][E]) // 128
+    assert o["meta"][0] == nnz and o["meta"][1] == R and o["meta"][2] == 0
+    assert np.array_equal(o["row_ptr"][:R + 1], t["row_ptr"])
+    for key in ("col_idx", "row_idx", "trans_idx"):
+        assert np.array_equal(o[key][:nnz], t[key]), key
+    assert np.array_equal(o["col_ptr"], t["col_ptr"])
+
+
 # ------------------------------------------------------ full-size workloads
 
 FULL = {
