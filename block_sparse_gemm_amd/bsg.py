@@ -31,7 +31,7 @@ EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
            "bsg_route_noalloc",
            "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
-           "bsg_build_topology", "bsg_route_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
+           "bsg_build_topology", "bsg_route_topology", "bsg_route_permute_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_stream_copy", "bsg_status_string", "bsg_last_error")
 
 
@@ -92,6 +92,10 @@ def lib():
         L.bsg_route_topology.restype = i32
         L.bsg_route_topology.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
                                          i32, i64, C.POINTER(TopologyStruct), vp]
+        L.bsg_route_permute_topology.restype = i32
+        L.bsg_route_permute_topology.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                 vp, sz, vp, i32, i32, i64, vp, vp, i32,
+                                                 C.POINTER(TopologyStruct), vp]
         L.bsg_sdd.restype = i32
         L.bsg_sdd.argtypes = [vp, i64, vp, vp, i64, i32, i32, C.POINTER(TopologyStruct), i32, vp,
                               vp, vp, i32, vp]
@@ -250,6 +254,20 @@ def route_topology(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_of
         _ptr(logits), T, E, k, int(bool(renorm)), bin_rows, _ptr(expert_idx), _ptr(gate),
         _ptr(dest_row), _ptr(counts), _ptr(bin_offsets), _ptr(workspace),
         workspace.numel() * workspace.element_size(), f, Tp_max, C.byref(topo.struct),
+        _stream()))
+
+
+def route_permute_topology(logits, k, renorm, expert_idx, gate, dest_row, counts, bin_offsets,
+                           workspace, x, Tp_max, row_src, xp, f=0, topo: Topology = None,
+                           bin_rows=BLOCK):
+    """route + permute_pad (no scale) + build_topology (topo may be None) in
+    the routing's two launches."""
+    T, E = logits.shape
+    _check("route_permute_topology", lib().bsg_route_permute_topology(
+        _ptr(logits), T, E, k, int(bool(renorm)), bin_rows, _ptr(expert_idx), _ptr(gate),
+        _ptr(dest_row), _ptr(counts), _ptr(bin_offsets), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(x), dtype_code(x), x.shape[1],
+        Tp_max, _ptr(row_src), _ptr(xp), f, C.byref(topo.struct) if topo is not None else None,
         _stream()))
 
 

@@ -195,7 +195,7 @@ bsg_status bsg_route(const float* logits, int64_t T, int E, int k, int renorm, i
             workspace_bytes, bsg_route_workspace_bytes(T, k, E));
     return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
                                         counts, bin_offsets, (int32_t*)workspace, bsg::TopoJob{},
-                                        (hipStream_t)stream),
+                                        bsg::PermJob{}, (hipStream_t)stream),
                       "route");
 }
 
@@ -216,7 +216,7 @@ bsg_status bsg_route_noalloc(const float* logits, int64_t T, int E, int k, int r
     if (e != hipSuccess) return hip_status(e, "route_noalloc scratch");
     return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
                                         counts, bin_offsets, scratch, bsg::TopoJob{},
-                                        (hipStream_t)stream),
+                                        bsg::PermJob{}, (hipStream_t)stream),
                       "route_noalloc");
 }
 
@@ -377,8 +377,44 @@ bsg_status bsg_route_topology(const float* logits, int64_t T, int E, int k, int 
     if ((s = check_topology_args(E, f, Tp_max, topo)) != BSG_OK) return s;
     return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
                                         counts, bin_offsets, (int32_t*)workspace, topo_job(topo),
-                                        (hipStream_t)stream),
+                                        bsg::PermJob{}, (hipStream_t)stream),
                       "route_topology");
+}
+
+bsg_status bsg_route_permute_topology(const float* logits, int64_t T, int E, int k, int renorm,
+                                      int bin_rows, int32_t* expert_idx, float* gate,
+                                      int32_t* dest_row, int32_t* counts, int32_t* bin_offsets,
+                                      void* workspace, size_t workspace_bytes, const void* x,
+                                      int dtype, int d, int64_t Tp_max, int32_t* row_src,
+                                      void* xp, int f, const bsg_topology* topo,
+                                      bsg_stream_t stream) {
+    bsg_status s =
+        check_route(logits, T, E, k, bin_rows, expert_idx, gate, dest_row, counts, bin_offsets);
+    if (s != BSG_OK) return s;
+    REQUIRE_PTR(workspace);
+    REQUIRE(workspace_bytes >= bsg_route_workspace_bytes(T, k, E), "workspace too small (%zu < %zu)",
+            workspace_bytes, bsg_route_workspace_bytes(T, k, E));
+    // the permutation's rules (bsg_permute_pad's, without a scale)
+    REQUIRE(dtype_ok(dtype), "unknown dtype %d", dtype);
+    REQUIRE(d >= 1 && d <= kMaxWidth && (d * elt_bytes(dtype)) % 16 == 0,
+            "d must keep rows 16-byte aligned");
+    REQUIRE(Tp_max >= bsg_max_padded_rows(T, k, E, bin_rows), "Tp_max below the padded-row bound");
+    REQUIRE_VEC_PTR(x);
+    REQUIRE_VEC_PTR(xp);
+    REQUIRE_PTR(row_src);
+    if (topo != nullptr && (s = check_topology_args(E, f, Tp_max, topo)) != BSG_OK) return s;
+    bsg::PermJob pj{};
+    pj.x = x;
+    pj.xp = xp;
+    pj.row_src = row_src;
+    pj.chunks = d * elt_bytes(dtype) / 16;
+    pj.on = 1;
+    pj.Tp_max = Tp_max;
+    return hip_status(bsg::launch_route(logits, T, E, k, renorm, bin_rows, expert_idx, gate, dest_row,
+                                        counts, bin_offsets, (int32_t*)workspace,
+                                        topo ? topo_job(topo) : bsg::TopoJob{}, pj,
+                                        (hipStream_t)stream),
+                      "route_permute_topology");
 }
 
 static bsg::GemmParams gemm_params(const bsg_topology* t) {

@@ -82,6 +82,18 @@ struct TopoJob {
     int64_t row_blocks_max, row_tiles_max;
 };
 
+// A permutation for the routing to do in its placement launch (what
+// launch_permute_pad does with no scale): each placing workgroup copies the
+// rows of the tokens it has just placed (on = 0: none).
+struct PermJob {
+    const void* x;     // [T, chunks] 16-byte chunks
+    void* xp;          // [Tp_max, chunks]
+    int32_t* row_src;  // [Tp_max]
+    int chunks;        // 16-byte chunks per row
+    int on;
+    int64_t Tp_max;
+};
+
 // Bytes of the file-scope device array behind the allocation-free routing
 // entry point (per GPU): 4 MiB, one count per (64-token chunk, expert).
 constexpr size_t kRouteScratchBytes = size_t(4) << 20;
@@ -92,7 +104,7 @@ hipError_t route_scratch(hipStream_t stream, int32_t** out);
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, const TopoJob& topo,
-                        hipStream_t stream);
+                        const PermJob& perm, hipStream_t stream);
 
 hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, int renorm,
                                  const int32_t* expert_idx, const int32_t* dest_row,

@@ -26,6 +26,7 @@
 // Routings too large for every workgroup to read the whole count matrix
 // scan it first in a launch of its own (route_scan, one workgroup per
 // expert).
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -272,13 +273,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(int32_t* __restrict_
 
 constexpr int kPlaceThreads = 1024;
 constexpr int kPlaceWaves = kPlaceThreads / kWave;  // 16
-constexpr int kPlaceChunks = 16;                     // chunks (1024 tokens) per workgroup
+constexpr int kPlaceChunks = 16;  // chunks (1024 tokens) per placing workgroup
+// With the permutation in the same launch, a placing workgroup takes fewer
+// chunks (so that enough workgroups copy rows), at most this many of its
+// assignments, whose rows it keeps in LDS for the copy.
+constexpr int kPermMax = 4096;
 // Every placement workgroup sums the whole count matrix itself when it has
-// at most this many entries and the routing at most this many chunks (the
-// matrix is then read from L2 by at most 64 workgroups); larger routings
-// scan it in a launch of their own first.
+// at most this many entries, the routing at most this many chunks and the
+// placing workgroups together read at most kSelfScanReads counts; larger
+// routings scan it in a launch of their own first.
 constexpr int64_t kSelfScanCounts = 65536;
 constexpr int kSelfScanChunks = 1024;
+constexpr int64_t kSelfScanReads = int64_t(1) << 23;
 
 // Per-expert totals and this workgroup's starting ranks (the assignments
 // of chunks before c0) from the raw chunk-major counts, into LDS (both
@@ -295,12 +301,12 @@ __device__ __forceinline__ void sum_chunk_counts(const int32_t* __restrict__ cc,
         const int e0 = (4 * threadIdx.x) & (E - 1);
         int t[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
         int64_t i = threadIdx.x;
-        for (; i + 7 * kPlaceThreads < n4; i += 8 * kPlaceThreads) {
-            int4 v[8];
+        for (; i + 3 * kPlaceThreads < n4; i += 4 * kPlaceThreads) {
+            int4 v[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = v4[i + u * kPlaceThreads];
+            for (int u = 0; u < 4; ++u) v[u] = v4[i + u * kPlaceThreads];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 const bool before = (4 * (i + u * kPlaceThreads)) / E < c0;
                 t[0] += v[u].x; t[1] += v[u].y; t[2] += v[u].z; t[3] += v[u].w;
                 if (before) { p[0] += v[u].x; p[1] += v[u].y; p[2] += v[u].z; p[3] += v[u].w; }
@@ -328,33 +334,41 @@ __device__ __forceinline__ void sum_chunk_counts(const int32_t* __restrict__ cc,
 }
 
 // Counts, padded bin offsets and dest_row; with `topo.on`, also the
-// topology of those bins.  Every workgroup forms the bins; the first
-// `nplace` workgroups then place, workgroup w the assignments of chunks
-// [16 w, 16 w + 16): the rank of each assignment among the earlier ones of
-// its expert, from the count of the earlier chunks plus wave64 ballots on
-// the expert id bits inside the workgroup.  The workgroups after them write
-// the topology (topology.hpp) meanwhile, so it costs no launch and little
-// time of its own.  SCANNED: route_scan has already turned the counts into
-// per-expert exclusive prefixes and totals; else each workgroup sums them
-// itself.
-template <bool SCANNED, bool VEC>
-__global__ __launch_bounds__(kPlaceThreads) void route_place(
+// topology of those bins; with PERM, also the permuted, padded copy of x.
+// Every workgroup forms the bins; the first `nplace` workgroups then place,
+// workgroup w the assignments of chunks [cpw w, cpw (w + 1)): the rank of
+// each assignment among the earlier ones of its expert, from the count of
+// the earlier chunks plus wave64 ballots on the expert id bits inside the
+// workgroup.  With PERM each of them then copies its tokens' rows to their
+// places and zero-fills the pad rows of experts w, w + nplace, ...  The
+// workgroups after them write the topology (topology.hpp) meanwhile, so it
+// costs no launch and little time of its own.  SCANNED: route_scan has
+// already turned the counts into per-expert exclusive prefixes and totals;
+// else each workgroup sums them itself.
+template <bool SCANNED, bool VEC, bool PERM>
+// Eight waves per SIMD (at most 64 VGPRs): two workgroups share a CU, so the
+// whole grid (placing and topology workgroups) is resident from the start.
+__global__ __launch_bounds__(kPlaceThreads) __attribute__((amdgpu_waves_per_eu(8))) void route_place(
     const int32_t* __restrict__ expert_idx, int64_t T, int E, int k,
-    const int32_t* __restrict__ chunk_counts, int nchunks, int nplace,
+    const int32_t* __restrict__ chunk_counts, int nchunks, int nplace, int cpw,
     int32_t* __restrict__ counts, int bin_rows, int32_t* __restrict__ dest_row,
-    int32_t* __restrict__ bin_offsets, TopoJob topo) {
+    int32_t* __restrict__ bin_offsets, TopoJob topo, PermJob perm) {
+    __shared__ int pdest[PERM ? kPermMax : 1];  // rows of this workgroup's assignments
     __shared__ int tot[kMaxExperts];
     __shared__ int running[kMaxExperts];
     __shared__ int bins[kMaxExperts + 1];
     __shared__ int2 wsum2[kPlaceWaves];
-    __shared__ int wcnt[kPlaceWaves][kMaxExperts];
+    // per wave and expert, kPlaceWaves x E (dynamic LDS: 4 KB at 64
+    // experts, so two workgroups share a CU and every workgroup of the
+    // launch is resident at once)
+    extern __shared__ int wcnt[];
     __shared__ TopoLds<kPlaceThreads> tl;
 
     const bool placer = (int)blockIdx.x < nplace;
-    const int c0 = placer ? (int)blockIdx.x * kPlaceChunks : 0;
+    const int c0 = placer ? (int)blockIdx.x * cpw : 0;
     const int64_t A = T * k;
     const int64_t a0 = placer ? min((int64_t)c0 * kRouteChunk * k, A) : 0;
-    const int64_t a1 = placer ? min(a0 + (int64_t)kPlaceChunks * kRouteChunk * k, A) : 0;
+    const int64_t a1 = placer ? min(a0 + (int64_t)cpw * kRouteChunk * k, A) : 0;
     // the first round's expert ids, loaded while the counts are summed
     const int e_first = (a0 + threadIdx.x < a1) ? expert_idx[a0 + threadIdx.x] : 0;
 
@@ -366,7 +380,7 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place(
     } else {
         for (int e = threadIdx.x; e < E; e += kPlaceThreads) tot[e] = running[e] = 0;
     }
-    for (int i = threadIdx.x; i < kPlaceWaves * E; i += kPlaceThreads) wcnt[i / E][i % E] = 0;
+    for (int i = threadIdx.x; i < kPlaceWaves * E; i += kPlaceThreads) wcnt[i] = 0;
     if (threadIdx.x == 0) tl.misaligned = 0;
     __syncthreads();
     if constexpr (!SCANNED) {
@@ -439,7 +453,7 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place(
             match &= ((e >> b) & 1) ? ones : ~ones;
         }
         const int rank = __popcll(match & lanemask_lt());
-        if (valid && rank == 0) wcnt[wave][e] = __popcll(match);
+        if (valid && rank == 0) wcnt[wave * E + e] = __popcll(match);
         __syncthreads();
         // per expert: each wave's first rank (the expert's running count plus
         // the earlier waves' counts), in place of the counts
@@ -447,17 +461,65 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place(
             int run = running[x];
 #pragma unroll
             for (int w = 0; w < kPlaceWaves; ++w) {
-                const int c = wcnt[w][x];
-                wcnt[w][x] = run;
+                const int c = wcnt[w * E + x];
+                wcnt[w * E + x] = run;
                 run += c;
             }
             running[x] = run;
         }
         __syncthreads();
-        if (valid) dest_row[a] = bins[e] + wcnt[wave][e] + rank;
+        if (valid) {
+            const int r = bins[e] + wcnt[wave * E + e] + rank;
+            dest_row[a] = r;
+            if constexpr (PERM) pdest[a - a0] = r;
+        }
         __syncthreads();
-        for (int i = threadIdx.x; i < kPlaceWaves * E; i += kPlaceThreads) wcnt[i / E][i % E] = 0;
+        for (int i = threadIdx.x; i < kPlaceWaves * E; i += kPlaceThreads) wcnt[i] = 0;
         __syncthreads();
+    }
+
+    if constexpr (PERM) {
+        // the permuted copy: token t's row is read once and written to the
+        // rows of its k assignments (the rounds above end with a barrier, so
+        // pdest is complete); rows at or past Tp_max are never written
+        const u32x4* __restrict__ x = (const u32x4*)perm.x;
+        u32x4* __restrict__ xp = (u32x4*)perm.xp;
+        const int chunks = perm.chunks;
+        // each wave takes kCopyTokens tokens at a time and loads all their
+        // chunks before it stores any, so several loads per lane are in
+        // flight (one token at a time left the copy latency-bound)
+        constexpr int kCopyTokens = 4;
+        const int64_t t0 = a0 / k, t1 = a1 / k;
+        for (int64_t tb = t0 + (int64_t)wave * kCopyTokens; tb < t1;
+             tb += (int64_t)kPlaceWaves * kCopyTokens) {
+            const int nu = (int)min((int64_t)kCopyTokens, t1 - tb);
+            const int* pd = pdest + (tb - t0) * k;
+            for (int c = lane; c < chunks; c += kWave) {
+                u32x4 v[kCopyTokens];
+#pragma unroll
+                for (int u = 0; u < kCopyTokens; ++u)
+                    if (u < nu) v[u] = x[(tb + u) * chunks + c];
+#pragma unroll
+                for (int u = 0; u < kCopyTokens; ++u) {
+                    if (u >= nu) break;
+                    for (int j = 0; j < k; ++j) {
+                        const int64_t r = pd[u * k + j];
+                        if (r < perm.Tp_max) xp[r * chunks + c] = v[u];
+                    }
+                }
+            }
+            for (int q = lane; q < nu * k; q += kWave)
+                if (pd[q] < perm.Tp_max) perm.row_src[pd[q]] = (int32_t)(tb * k + q);
+        }
+        // the pad rows of experts blockIdx.x, + nplace, ...: zeros, row_src -1
+        for (int e = blockIdx.x; e < E; e += nplace) {
+            const int64_t hi = min((int64_t)bins[e + 1], perm.Tp_max);
+            for (int64_t r = (int64_t)bins[e] + tot[e] + wave; r < hi; r += kPlaceWaves) {
+                u32x4* dst = xp + r * chunks;
+                for (int c = lane; c < chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
+                if (lane == 0) perm.row_src[r] = -1;
+            }
+        }
     }
 }
 
@@ -540,7 +602,7 @@ hipError_t launch_route_backward(const float* logits, int64_t T, int E, int k, i
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm, int bin_rows,
                         int32_t* expert_idx, float* gate, int32_t* dest_row, int32_t* counts,
                         int32_t* bin_offsets, int32_t* workspace, const TopoJob& topo,
-                        hipStream_t stream) {
+                        const PermJob& perm, hipStream_t stream) {
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
 #define BSG_TOPK(NV)                                                                         \
     hipLaunchKernelGGL(route_topk<NV>, dim3(nchunks), dim3(kTopkThreads), 0, stream, logits, T, \
@@ -558,31 +620,41 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renorm
     else BSG_TOPK(16);
 #undef BSG_TOPK_SEG
 #undef BSG_TOPK
+    // chunks per placing workgroup: 16, or with the permutation about one
+    // placing workgroup per CU (each keeps at most kPermMax rows in LDS)
+    int cpw = kPlaceChunks;
+    if (perm.on) {
+        const int maxc = kPermMax / (kRouteChunk * k);  // >= 2: k <= 32
+        cpw = std::min(maxc, std::max(1, (nchunks + 255) / 256));
+    }
     // placing workgroups, then (with a topology) the topology's
-    const int nplace = (nchunks + kPlaceChunks - 1) / kPlaceChunks;
+    const int nplace = (nchunks + cpw - 1) / cpw;
     int64_t grid = nplace;
     if (topo.on)
         grid += (topo_threads(E, topo.F, topo.row_blocks_max, topo.row_tiles_max) +
                  kPlaceThreads - 1) / kPlaceThreads;
-    const bool self_scan =
-        (int64_t)nchunks * E <= kSelfScanCounts && nchunks <= kSelfScanChunks;
-    if (self_scan) {
-        const bool vec = E >= 4 && (E & (E - 1)) == 0 && ((uintptr_t)workspace & 15) == 0;
-        if (vec)
-            hipLaunchKernelGGL((route_place<false, true>), dim3(grid), dim3(kPlaceThreads), 0,
-                               stream, expert_idx, T, E, k, workspace, nchunks, nplace, counts, bin_rows,
-                               dest_row, bin_offsets, topo);
-        else
-            hipLaunchKernelGGL((route_place<false, false>), dim3(grid), dim3(kPlaceThreads), 0,
-                               stream, expert_idx, T, E, k, workspace, nchunks, nplace, counts, bin_rows,
-                               dest_row, bin_offsets, topo);
-    } else {
+    const bool self_scan = (int64_t)nchunks * E <= kSelfScanCounts &&
+                           nchunks <= kSelfScanChunks &&
+                           (int64_t)nplace * nchunks * E <= kSelfScanReads;
+    const bool vec = E >= 4 && (E & (E - 1)) == 0 && ((uintptr_t)workspace & 15) == 0;
+    const size_t wcnt_bytes = (size_t)kPlaceWaves * E * sizeof(int);
+#define BSG_PLACE(S, V, P)                                                                     \
+    hipLaunchKernelGGL((route_place<S, V, P>), dim3(grid), dim3(kPlaceThreads), wcnt_bytes,      \
+                       stream, expert_idx, T, E, k, workspace, nchunks, nplace, cpw, counts,    \
+                       bin_rows, dest_row, bin_offsets, topo, perm)
+    if (!self_scan)
         hipLaunchKernelGGL(route_scan, dim3(E), dim3(kRouteThreads), 0, stream, workspace,
                            nchunks, E, counts);
-        hipLaunchKernelGGL((route_place<true, false>), dim3(grid), dim3(kPlaceThreads), 0, stream,
-                           expert_idx, T, E, k, workspace, nchunks, nplace, counts, bin_rows,
-                           dest_row, bin_offsets, topo);
+    if (perm.on) {
+        if (!self_scan) BSG_PLACE(true, false, true);
+        else if (vec) BSG_PLACE(false, true, true);
+        else BSG_PLACE(false, false, true);
+    } else {
+        if (!self_scan) BSG_PLACE(true, false, false);
+        else if (vec) BSG_PLACE(false, true, false);
+        else BSG_PLACE(false, false, false);
     }
+#undef BSG_PLACE
     return hipGetLastError();
 }
 

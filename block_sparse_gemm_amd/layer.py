@@ -1,8 +1,8 @@
 """The dropless-MoE expert layer as a chain of the library's calls.
 
 Forward (George Lin's Blog, MegaBlocks/FlexMoE post, sections 1.2-1.4):
-    route (+ build_topology, written by the routing's placement launch)
-    -> permute_pad -> sdd (+ activation) -> dsd -> unpermute_combine
+    route (+ permute_pad and build_topology, both done by the routing's
+    placement launch) -> sdd (+ activation) -> dsd -> unpermute_combine
 Backward (plain calculus on the same products, weight gradients through the
 transpose index as section 1.3 describes):
     permute_pad(dy, scale = gate) + route_backward(dy, Yp) = dlogits (the
@@ -141,11 +141,9 @@ class Layer:
         s, t = self.s, self.topo
         c = self._call
         self.logits = logits  # the gate backward differentiates through it
-        c("route", bsg.route_topology, logits, s.k, s.renorm, self.expert_idx, self.gate,
-          self.dest_row, self.counts, self.bin_offsets, self.route_ws, s.f, self.Tp_max, t,
-          bin_rows=s.bin_rows)
-        c("permute_pad", bsg.permute_pad, x, s.k, self.dest_row, None, self.counts,
-          self.bin_offsets, s.E, self.Tp_max, self.row_src, self.xp, bin_rows=s.bin_rows)
+        c("route_permute_topology", bsg.route_permute_topology, logits, s.k, s.renorm, self.expert_idx, self.gate,
+          self.dest_row, self.counts, self.bin_offsets, self.route_ws, x, self.Tp_max,
+          self.row_src, self.xp, s.f, t, bin_rows=s.bin_rows)
         if s.act == "swiglu":
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "silu_mul", self.act, b2=W3, aux_out=self.gp)
         else:

@@ -292,6 +292,27 @@ bsg_status bsg_route_topology(const float* logits, int64_t T, int E, int k, int 
                               const bsg_topology* topo /* host struct */, bsg_stream_t stream);
 
 /*
+ * route_permute_topology - the forward's front in two launches (section 1.4:
+ * route, then the fused gather + pad permutation, then the topology):
+ * bsg_route, then bsg_permute_pad(x, dtype, T, d, k, dest_row, NULL,
+ * counts, bin_offsets, E, bin_rows, Tp_max, row_src, xp), then, when topo
+ * is not NULL, bsg_build_topology(bin_offsets, E, f, Tp_max, topo).  The
+ * routing's placement launch also copies each token's row to its k places
+ * (read once, written k times), zero-fills the pad rows and writes row_src.
+ * Every output, bit for bit, and every argument rule and error are those of
+ * the three calls (f is read only with a topology).  Two launches for
+ * routings whose placement can sum the per-chunk counts itself, three
+ * above that.
+ */
+bsg_status bsg_route_permute_topology(const float* logits, int64_t T, int E, int k, int renorm,
+                                      int bin_rows, int32_t* expert_idx, float* gate,
+                                      int32_t* dest_row, int32_t* counts, int32_t* bin_offsets,
+                                      void* workspace, size_t workspace_bytes, const void* x,
+                                      int dtype, int d, int64_t Tp_max, int32_t* row_src,
+                                      void* xp, int f, const bsg_topology* topo /* or NULL */,
+                                      bsg_stream_t stream);
+
+/*
  * sdd - sampled dense-dense product (section 1.2, first layer):
  * for every nonzero block b = (r, c):
  *   acc_b[m][n] = sum_k a[BR*r + m][k] * B[k][128c + n],  k < K,

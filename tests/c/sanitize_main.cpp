@@ -15,6 +15,7 @@
 
 extern int g_launches;
 extern bsg::TopoJob g_route_topo;
+extern bsg::PermJob g_route_perm;
 
 // ---- the oracle's C entry points (oracle/oracle.c)
 extern "C" {
@@ -180,6 +181,30 @@ static void abi_checks() {
         EXPECT(bsg_route_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, 256,
                                   rt.Tp_max, nullptr, nullptr) == BSG_EINVAL);
         EXPECT(g_launches == n0 + 2);
+        // ... and with the permutation as well (topology optional)
+        const int n1 = g_launches;
+        EXPECT(bsg_route_permute_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, P,
+                                          BSG_BF16, 256, rt.Tp_max, ip, P, 256, &rt,
+                                          nullptr) == BSG_OK);
+        EXPECT(g_launches == n1 + 1 && g_route_topo.on == 1 && g_route_perm.on == 1 &&
+               g_route_perm.chunks == 32 && g_route_perm.Tp_max == rt.Tp_max);
+        EXPECT(bsg_route_permute_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, P,
+                                          BSG_F32, 128, rt.Tp_max, ip, P, 0, nullptr,
+                                          nullptr) == BSG_OK);
+        EXPECT(g_route_topo.on == 0 && g_route_perm.on == 1 && g_route_perm.chunks == 32);
+        EXPECT(bsg_route_permute_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20,
+                                          MIS, BSG_BF16, 256, rt.Tp_max, ip, P, 256, &rt,
+                                          nullptr) == BSG_EINVAL);
+        EXPECT(bsg_route_permute_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, P,
+                                          BSG_BF16, 100, rt.Tp_max, ip, P, 256, &rt,
+                                          nullptr) == BSG_EINVAL);
+        EXPECT(bsg_route_permute_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, P,
+                                          BSG_BF16, 256, rt.Tp_max - 128, ip, P, 256, nullptr,
+                                          nullptr) == BSG_EINVAL);
+        EXPECT(bsg_route_permute_topology(fl, 100, 8, 2, 0, 128, ip, fp, ip, ip, ip, P, 1 << 20, P,
+                                          BSG_BF16, 256, rt.Tp_max, ip, P, 384, &rt,
+                                          nullptr) == BSG_EINVAL);
+        EXPECT(g_launches == n1 + 2);
     }
     EXPECT(bsg_sdd(P, 256, P, nullptr, 1024, 0, 256, &t, BSG_EPI_GELU, nullptr, P, P, BSG_BF16,
                    nullptr) == BSG_OK);

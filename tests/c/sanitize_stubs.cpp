@@ -9,6 +9,7 @@
 
 int g_launches = 0;             // read by the driver
 bsg::TopoJob g_route_topo = {};  // the last routing launch's topology job
+bsg::PermJob g_route_perm = {};  // and its permutation job
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "host-only build"; }
 
@@ -22,9 +23,11 @@ hipError_t route_scratch(hipStream_t, int32_t** out) {
 }
 
 hipError_t launch_route(const float*, int64_t, int, int, int, int, int32_t*, float*, int32_t*,
-                        int32_t*, int32_t*, int32_t*, const TopoJob& topo, hipStream_t) {
+                        int32_t*, int32_t*, int32_t*, const TopoJob& topo, const PermJob& perm,
+                        hipStream_t) {
     ++g_launches;
     g_route_topo = topo;
+    g_route_perm = perm;
     return hipSuccess;
 }
 

@@ -241,6 +241,35 @@ def test_route_topology_validation(L):
     assert call(topo=C.byref(t2)) == bsg.EINVAL
 
 
+def test_route_permute_topology_validation(L):
+    """The rules of route, permute_pad (without a scale) and build_topology,
+    checked before any launch; the topology is optional."""
+    Tp = bsg.max_padded_rows(100, 2, 8)
+    t = fake_topo(E=8, Tp=Tp)
+    ok = [P, 100, 8, 2, 0, 128, P, P, P, P, P, P, 1 << 20, P, bsg.BF16, 256, Tp, P, P, 256,
+          C.byref(t), None]
+    names = ["logits", "T", "E", "k", "renorm", "bin", "expert_idx", "gate", "dest_row",
+             "counts", "bin_offsets", "ws", "wsb", "x", "dt", "d", "Tp", "row_src", "xp", "f",
+             "topo", "stream"]
+
+    def call(**over):
+        a = list(ok)
+        for key, v in over.items():
+            a[names.index(key)] = v
+        return L.bsg_route_permute_topology(*a)
+
+    assert call(logits=None) == bsg.EINVAL
+    assert call(wsb=4) == bsg.EINVAL and "workspace" in _err(L)
+    assert call(x=C.c_void_p(0x10004)) == bsg.EINVAL
+    assert call(xp=None) == bsg.EINVAL
+    assert call(row_src=None) == bsg.EINVAL
+    assert call(d=100) == bsg.EINVAL
+    assert call(dt=7) == bsg.EINVAL
+    assert call(Tp=256) == bsg.EINVAL and "padded-row bound" in _err(L)
+    assert call(f=384) == bsg.EINVAL and "capacity" in _err(L)
+    assert call(bin=32) == bsg.EINVAL
+
+
 def test_sdd_validation(L):
     t = fake_topo(E=4, f=256)
     ncol = 4 * 256

@@ -541,57 +541,82 @@ _TOPO_KEYS = ("row_ptr", "col_idx", "row_idx", "col_ptr", "trans_idx", "row_tile
               "expert_order", "meta")
 
 
-@pytest.mark.parametrize("T,E,k,ws_offset", [
-    (70000, 64, 2, 0),    # more than 1024 chunks: the count matrix is scanned first
-    (20000, 1024, 1, 0),  # more than 65536 counts, the most experts
-    (3000, 64, 2, 4),     # a workspace off the 16-byte grid: counts summed one by one
-    (65536, 2, 1, 0),     # 1024 chunks, two experts: the largest self-summed routing
-    (1000, 8, 3, 0),      # 4-count vectors of a power-of-two expert count
+@pytest.mark.parametrize("T,E,k,ws_offset,dtype", [
+    (70000, 64, 2, 0, "bf16"),    # more than 1024 chunks: the count matrix is scanned first
+    (20000, 1024, 1, 0, "bf16"),  # more than 65536 counts, the most experts
+    (3000, 64, 2, 4, "f32"),      # a workspace off the 16-byte grid: counts summed one by one
+    (65536, 2, 1, 0, "bf16"),     # 1024 chunks, two experts: the largest self-summed routing
+    (1000, 8, 3, 0, "f32"),       # 4-count vectors of a power-of-two expert count
+    (2000, 40, 32, 0, "bf16"),    # top-32: two chunks a placing workgroup at most
 ])
-def test_route_topology_launch_paths(orc, T, E, k, ws_offset):
-    """route + topology in one call equals route followed by build_topology
-    bit for bit, and both equal the oracle, on each of the placement's ways
-    of forming the counts (scanned first, summed as vectors, summed one by
-    one)."""
-    from block_sparse_gemm_amd import bsg
-    _say(f"[parity] route_topology T={T} E={E} k={k} ws_offset={ws_offset}")
-    f = 256
-    lg = np.random.default_rng(T + E).standard_normal((T, E)).astype(np.float32)
+def test_route_topology_launch_paths(orc, T, E, k, ws_offset, dtype):
+    """route + topology, and route + permutation (+ topology), in the
+    routing's own launches equal route, permute_pad and build_topology
+    called one by one, bit for bit, and all equal the oracle, on each of the
+    placement's ways of forming the counts (scanned first, summed as
+    vectors, summed one by one)."""
+    from block_sparse_gemm_amd import bsg, layer
+    _say(f"[parity] route_topology T={T} E={E} k={k} ws_offset={ws_offset} dtype={dtype}")
+    f, d = 256, 128
+    rng = np.random.default_rng(T + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
     lg[:, 0] += 0.75  # mild skew
+    xt = synth._draw(rng, (T, d), 1.0, dtype)
     r = orc.route(lg, k, False, 128)
     t = orc.topology(r["bin_offsets"], E, f // 128, 128)
+    Tp = int(r["bin_offsets"][E])
     Tp_max = bsg.max_padded_rows(T, k, E)
     logits = torch.from_numpy(lg).cuda()
+    x = layer.from_numpy(xt, dtype)
     i32 = dict(dtype=torch.int32, device="cuda")
     nbytes = bsg.route_workspace_bytes(T, k, E)
-    outs = []
-    for fused in (True, False):
+    outs = {}
+    for mode in ("topology", "permute", "permute_no_topology", "separate"):
         o = dict(expert_idx=torch.full((T * k,), -7, **i32),
                  gate=torch.zeros(T * k, dtype=torch.float32, device="cuda"),
                  dest_row=torch.full((T * k,), -7, **i32), counts=torch.full((E,), -7, **i32),
-                 bin_offsets=torch.full((E + 1,), -7, **i32))
+                 bin_offsets=torch.full((E + 1,), -7, **i32),
+                 row_src=torch.full((Tp_max,), -7, **i32),
+                 xp=torch.full((Tp_max, d), 3.0, dtype=x.dtype, device="cuda"))
         ws = torch.full((nbytes + 16,), 0xAB, dtype=torch.uint8, device="cuda")
         ws = ws[ws_offset:ws_offset + nbytes]
         topo = bsg.Topology(Tp_max, E, f)
         for key in _TOPO_KEYS:
             getattr(topo, key).fill_(-7)
-        if fused:
+        if mode == "topology":
             bsg.route_topology(logits, k, False, o["expert_idx"], o["gate"], o["dest_row"],
                                o["counts"], o["bin_offsets"], ws, f, Tp_max, topo)
+        elif mode.startswith("permute"):
+            tp = topo if mode == "permute" else None
+            bsg.route_permute_topology(logits, k, False, o["expert_idx"], o["gate"],
+                                       o["dest_row"], o["counts"], o["bin_offsets"], ws, x,
+                                       Tp_max, o["row_src"], o["xp"], f, tp)
         else:
             bsg.route(logits, k, False, o["expert_idx"], o["gate"], o["dest_row"], o["counts"],
                       o["bin_offsets"], ws)
+            bsg.permute_pad(x, k, o["dest_row"], None, o["counts"], o["bin_offsets"], E, Tp_max,
+                            o["row_src"], o["xp"])
             bsg.build_topology(o["bin_offsets"], E, f, Tp_max, topo)
         torch.cuda.synchronize()
-        o = {key: v.cpu().numpy() for key, v in o.items()}
-        o.update({key: getattr(topo, key).cpu().numpy() for key in _TOPO_KEYS})
-        outs.append(o)
-    for key in outs[0]:
-        assert np.array_equal(outs[0][key], outs[1][key]), key
-    o = outs[0]
+        o = {key: v.cpu() for key, v in o.items()}
+        o.update({key: getattr(topo, key).cpu() for key in _TOPO_KEYS})
+        outs[mode] = o
+    sep = outs["separate"]
+    for mode, o in outs.items():
+        keys = list(o)
+        if mode == "topology":
+            keys = [kk for kk in keys if kk not in ("row_src", "xp")]
+        if mode == "permute_no_topology":
+            keys = [kk for kk in keys if kk not in _TOPO_KEYS]
+        for key in keys:
+            assert torch.equal(o[key], sep[key]), (mode, key)
+    o = {key: v.numpy() for key, v in sep.items() if key != "xp"}
     for key in ("expert_idx", "dest_row", "counts", "bin_offsets"):
         assert np.array_equal(o[key], r[key]), key
-    nnz, R = t["nnz"], int(r["bin_offsets"][E]) // 128
+    assert np.array_equal(o["row_src"][:Tp], r["row_src"]), "row_src"
+    xp_want = orc.permute_pad(xt.values, k, r["dest_row"], Tp, prec=dtype)
+    assert np.array_equal(layer.to_numpy_f64(sep["xp"][:Tp]), xp_want), "xp"
+    nnz, R = t["nnz"], Tp // 128
     assert o["meta"][0] == nnz and o["meta"][1] == R and o["meta"][2] == 0
     assert np.array_equal(o["row_ptr"][:R + 1], t["row_ptr"])
     for key in ("col_idx", "row_idx", "trans_idx"):
