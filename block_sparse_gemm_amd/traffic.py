@@ -63,11 +63,11 @@ def call_name(kernel: str):
 
     Template arguments: dtype, mode (0 SDD, 1 dual-B SDD, 2 DSD, 3 DSTD, 4
     two-set DSD), B K-contiguous, epilogue (3 and 4: the backward ones), out
-    dtype, swap (false: transposed DSTD output).  dW1 and dW3 run the same
-    instantiation and share its figure."""
-    m = re.search(r"gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)>", kernel)
+    dtype, swap (false: transposed DSTD output), block rows.  dW1 and dW3 run
+    the same instantiation and share its figure."""
+    m = re.search(r"gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)(?:, (\d+))?>", kernel)
     if m:
-        _, mode, b_kc, epi, _, swap = m.groups()
+        _, mode, b_kc, epi, _, swap, _ = m.groups()
         if mode in ("0", "1"):
             return "sdd_bwd" if epi in ("3", "4") else "sdd"
         if mode == "2":
@@ -238,12 +238,14 @@ _EPIS = {"0": "", "1": "+gelu", "2": "+silu_mul", "3": "+gelu_bwd", "4": "+silu_
 def kernel_label(name: str) -> str:
     """A readable name for a kernel of the stats table: GEMM instantiations
     by product, epilogue, B operand layout and output type."""
-    m = re.match(r"void bsg::gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)>", name)
+    m = re.match(r"void bsg::gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)(?:, (\d+))?>",
+                 name)
     if m:
-        _, mode, bk, epi, out, swap = m.groups()
+        _, mode, bk, epi, out, swap, br = m.groups()
         return (f"gemm {_MODES.get(mode, mode)}{_EPIS.get(epi, '+' + epi)} "
                 f"(B {'K' if bk == 'true' else 'MN'}-contig, out {'bf16' if out == '1' else 'f32'}"
-                f"{'' if swap == 'true' else ', transposed'})")
+                f"{'' if swap == 'true' else ', transposed'}"
+                f"{', blocks of ' + br + ' rows' if br and br != '128' else ''})")
     return re.sub(r"\(.*", "", name).replace("void ", "")[:70]
 
 
