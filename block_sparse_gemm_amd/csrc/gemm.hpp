@@ -978,7 +978,9 @@ __device__ __forceinline__ bool half_tile(const GemmParams& P) {
 
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP, int BR>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + 3 * kIdxCap * 4];
+    // the operand ring, then (DSD / DSTD) the staged K-block indices
+    constexpr bool kIdx = MODE != kModeSdd && MODE != kModeSddOne;
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + (kIdx ? 3 * kIdxCap * 4 : 0)];
     if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
         if (half_tile<MODE, BR>(P)) {
             gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem);
