@@ -32,7 +32,11 @@ bracketed by events; the timed steps record events around the dominant call
 only, since each event costs GPU time (about 4 us a call pair here).
 ``forward_products`` times the forward products alone (SDD + GeLU writing A
 only, DSD writing Yp) with their rooflines and the ratio to a dense
-hipBLASLt GEMM (torch.matmul) of the same executed shape.
+hipBLASLt GEMM (torch.matmul) of the same executed shape, and the SDD with
+no activation beside it (what the GeLU epilogue costs).  ``mfma_ceiling``
+times the same GEMM kernel and hipBLASLt on one dense 8192^3 bf16 product
+(every row in one expert): the practical MFMA ceiling beside the published
+peak.
 ``data_movement`` times permute_pad, the backward's dy permutation with the
 gate backward and unpermute_combine alone (for top-1 layers also on a top-2
 routing of the same tokens), each after a 512 MiB write that flushes the
@@ -76,6 +80,8 @@ def parse():
     ap.add_argument("--compare-schedules", action="store_true",
                     help="after the timed steps, also time the other backward schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the 8192^3 dense product (context only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     return ap.parse_args()
@@ -392,9 +398,13 @@ def main():
     fwd = {}
     if cfg.act == "gelu":
         W1f, W2f = W1, W2
+        sdd_dense = dense_ms(Tp, cfg.d, cfg.f)
         prods = {
             "sdd_gelu": (lambda: bsg.sdd(L.xp, W1f, cfg.d, t, "gelu", L.act),
-                         Tp * cfg.d * es + weight + plane, dense_ms(Tp, cfg.d, cfg.f)),
+                         Tp * cfg.d * es + weight + plane, sdd_dense),
+            # the same product with no activation: what the GeLU epilogue costs
+            "sdd_no_activation": (lambda: bsg.sdd(L.xp, W1f, cfg.d, t, "none", L.act),
+                                  Tp * cfg.d * es + weight + plane, sdd_dense),
             "dsd": (lambda: bsg.dsd(L.act, t, W2f, cfg.d, L.yp),
                     plane + weight + Tp * cfg.d * ypes, dense_ms(Tp, cfg.f, cfg.d)),
         }
@@ -413,6 +423,28 @@ def main():
                          "frac_of_attainable": round(tf / att, 4),
                          "dense_gemm_same_shape_ms": round(dms, 4),
                          "dense_ratio": round(dms / ms, 3)}
+
+    # context: what the GEMM kernel and hipBLASLt reach on one large dense
+    # bf16 product (8192 x 8192 x 8192, every row in one expert), the
+    # practical MFMA ceiling on this GPU beside the published peak
+    ceiling = None
+    if cfg.dtype == "bf16" and not args.no_mfma_ceiling:
+        n = 8192
+        a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        tc = bsg.Topology(n, 1, n)
+        bsg.build_topology(torch.tensor([0, n], dtype=torch.int32, device="cuda"), 1, n, n, tc)
+        c = torch.empty(n * n, dtype=torch.bfloat16, device="cuda")
+        bsg.sdd(a, b, n, tc, "none", c)
+        ms_ours = event_ms(lambda: bsg.sdd(a, b, n, tc, "none", c), 5)
+        torch.matmul(a, b)
+        ms_blas = event_ms(lambda: torch.matmul(a, b), 5)
+        fl = 2.0 * n * n * n
+        ceiling = {"shape_mnk": [n, n, n],
+                   "sdd_tflops": round(fl / (ms_ours * 1e-3) / 1e12, 1),
+                   "hipblaslt_tflops": round(fl / (ms_blas * 1e-3) / 1e12, 1),
+                   "sdd_frac_of_mfma_peak": round(fl / (ms_ours * 1e-3) / 1e12 / MFMA_PEAK_BF16, 4)}
+        del a, b, c, tc
 
     # context: the other backward schedule, a few steps after the timed region
     other = None
@@ -509,6 +541,7 @@ def main():
         # every call timed alone in a probe pass before the timed steps
         "kernels": kernels,
         "forward_products": fwd or None,
+        "mfma_ceiling": ceiling,
         "data_movement": dm,
         "hbm_copy_ceiling": copy_ceiling,
         "schedule": "two streams" if two else "one stream",

@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
     BSG_OK = 0,
     BSG_EINVAL = -1,       /* null pointer, bad size, misaligned pointer, bad code */
-    BSG_EUNSUPPORTED = -2, /* valid request this build does not implement */
+    BSG_EUNSUPPORTED = -2, /* valid request the library does not implement */
     BSG_EHIP = -3          /* the HIP runtime rejected a launch */
 } bsg_status;
 
