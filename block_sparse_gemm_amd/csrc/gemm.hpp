@@ -540,8 +540,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
     // (The two-plane prefetch does not fit beside the registers of a B
     // operand read as stored; that variant reads the factors at use.)
     constexpr bool TWO_IN = EPI == kEpiSiluMulBwd;
-    constexpr bool PRE = (EPI == kEpiGeluBwd || (TWO_IN && BK)) && OUT == kBf16;
-    constexpr bool PRE_EARLY = PRE && !TWO_IN;
+    constexpr bool PRE = TWO_IN && BK && OUT == kBf16;
+    // GeLU backward (bf16): the saved derivative goes straight into LDS with
+    // direct loads, 32-row slabs of the wave's block (8 KB each, whole
+    // 256-byte rows, so every load covers whole lines), and is read back in
+    // the accumulator layout.  Slab 0 lands in a per-wave 8 KB buffer past the
+    // ring, requested before the last K-tile; slabs 1 and 2 in the upper half
+    // of the wave's staging region once the ring is free; slab 3 in the
+    // buffer again once slab 0 has been read.
+    constexpr bool GLDS = EPI == kEpiGeluBwd && OUT == kBf16;
     u32x2 hsave[2][NI][4];
     u32x2 qsave[TWO_IN ? 2 : 1][NI][4];
     auto hload = [&](int mi, int buf) {
@@ -559,6 +566,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
                     qsave[buf][ni][g] = *(const u32x2*)((const char*)P.aux_in + (P.plane + off) * 2);
             }
     };
+
+    // direct loads of derivative slab `sl` (rows 32 sl .. + 31 of this wave's
+    // rows, one 128-column block) into an 8 KB LDS buffer, row r at 256 r with
+    // its 16-byte chunk c at slot c ^ (r & 15), the layout the epilogue's
+    // staging uses; 8 loads, each 4 rows
+    auto gslab = [&](int sl, uint32_t dst) {
+        const int hh = HALF ? 0 : sl >> 1;
+        const char* src = uniform_ptr((const char*)P.aux_in +
+                                      ((int64_t)hblk(hh) * BR * kBlock +
+                                       (int64_t)(hin(hh) + 32 * (sl & 1)) * kBlock) * 2);
+        const int rr = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 4 * j + rr;
+            dma16(dst + j * 1024, src, (uint32_t)(r * 256 + (((lane & 15) ^ (r & 15)) << 4)));
+        }
+    };
+    const uint32_t gbuf = lds_u32(lds) + kLdsBytes + wave * 8192;  // slabs 0 and 3
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -673,8 +698,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
         }
         // last K-tile (every direct load has landed: the counter holds only
         // what the epilogue's prefetch adds)
-        if constexpr (PRE_EARLY) {
-            if (active) hload(0, 0);
+        if constexpr (GLDS) {
+            if (active) gslab(0, gbuf);
         }
         first_half(kt, nk);
         second_half(kt, false, false);
@@ -710,12 +735,40 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
     constexpr bool STAGE = OUT == kBf16;
     if constexpr (STAGE) __syncthreads();  // every wave is done with the operand ring
     if (!active) return;
-    if constexpr (PRE && !PRE_EARLY) hload(0, 0);
+    if constexpr (PRE) hload(0, 0);
 
     // staging: row r (256 bytes) of a 64-row sub-region holds 16 chunks of
     // 16 bytes, chunk c at slot c ^ (r & 15), so the 16 lanes reading one row
     // and the 16 rows one accumulator write touches both spread over all banks
     lds_t* region = lds + wave * (kLdsBytes / 4);
+    if constexpr (GLDS) {
+        gslab(1, lds_u32(region) + 16384);
+        if constexpr (NMI > 2) gslab(2, lds_u32(region) + 24576);
+    }
+    // the LDS buffer that holds derivative slab sl
+    auto gsrc = [&](int sl) -> const lds_t* {
+        return sl == 1 ? region + 16384 : sl == 2 ? region + 24576 : lds + kLdsBytes + wave * 8192;
+    };
+    // wait until slab mi has landed.  Direct loads and stores retire in issue
+    // order; in flight behind slab mi: full tiles, slabs 1 and 2 behind 0,
+    // slab 2 behind 1, slab 3 and half 0's 16 stores behind 2, the stores
+    // behind 3; half tiles, slab 1 behind 0
+    auto gwait = [&](int mi) {
+        if constexpr (NMI > 2) {
+            if (mi == 0) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else if (mi == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else if (mi == 2) {
+                if (hpresent(0)) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            } else {
+                if (hpresent(0)) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        } else {
+            if (mi == 0) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+    };
     auto stage_put = [&](lds_t* sub, int mi, int ni, int g, const float* v) {
         const int row = (SWAP ? 32 * mi : 32 * ni) % 64 + l32;
         const int chunk = SWAP ? 4 * ni + g : 4 * mi + g;
@@ -828,6 +881,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
                 if constexpr (PRE) {
                     if (b == 0 && mi + 1 < NMI) hload(mi + 1, (mi + 1) & 1);
                 }
+                if constexpr (GLDS) {
+                    if (b == 0) gwait(mi);
+                }
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     float v[4];
@@ -876,8 +932,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
                         } else if constexpr (EPI == kEpiGeluBwd) {
                             // dH = dA * GeLU'(h), the derivative saved by the forward
                             float gv[4];
-                            if constexpr (PRE) unpack(hsave[mi & 1][ni][g], gv);
-                            else load4<OUT>((const char*)P.aux_in + off * OES, gv);
+                            if constexpr (GLDS)
+                                unpack(*(const __attribute__((address_space(3))) u32x2*)(
+                                           gsrc(mi) + l32 * 256 +
+                                           (((4 * ni + g) ^ (l32 & 15)) << 4) + lh * 8),
+                                       gv);
+                            else
+                                load4<OUT>((const char*)P.aux_in + off * OES, gv);
 #pragma unroll
                             for (int s = 0; s < 4; ++s) v[s] *= gv[s];
                         } else if constexpr (EPI == kEpiSiluMulBwd) {
@@ -925,6 +986,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
                 // keep the scheduler from hoisting every accumulator read of
                 // the epilogue at once (register pressure)
                 __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // slab 0 has been read: slab 3 goes into its buffer while half 0 is
+        // flushed
+        if constexpr (GLDS && NMI > 2) {
+            if (h == 0) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                gslab(3, gbuf);
             }
         }
         // the staged half goes out only when its slot is present (an absent
@@ -980,7 +1049,10 @@ template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP, int BR>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     // the operand ring, then (DSD / DSTD) the staged K-block indices
     constexpr bool kIdx = MODE != kModeSdd && MODE != kModeSddOne;
-    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes + (kIdx ? 3 * kIdxCap * 4 : 0)];
+    // (GeLU backward, bf16) four 8 KB buffers of the saved derivative
+    constexpr bool kGbuf = EPI == kEpiGeluBwd && OUT == kBf16;
+    __shared__ __attribute__((aligned(1024))) char
+        smem[kLdsBytes + (kIdx ? 3 * kIdxCap * 4 : 0) + (kGbuf ? 4 * 8192 : 0)];
     if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
         if (half_tile<MODE, BR>(P)) {
             gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem);
