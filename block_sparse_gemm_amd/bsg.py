@@ -31,7 +31,8 @@ EPILOGUES = {"none": EPI_NONE, "gelu": EPI_GELU, "silu_mul": EPI_SILU_MUL,
 SYMBOLS = ("bsg_max_padded_rows", "bsg_topology_sizes", "bsg_route_workspace_bytes", "bsg_route",
            "bsg_route_noalloc",
            "bsg_route_backward", "bsg_permute_pad", "bsg_permute_pad_gate_backward",
-           "bsg_build_topology", "bsg_route_topology", "bsg_route_permute_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_combine_top1", "bsg_dstd",
+           "bsg_build_topology", "bsg_route_topology", "bsg_route_permute_topology", "bsg_sdd", "bsg_dsd", "bsg_dsd_workspace_bytes",
+           "bsg_dsd_combine_top1", "bsg_dstd",
            "bsg_unpermute_combine", "bsg_stream_copy", "bsg_status_string", "bsg_last_error")
 
 
@@ -101,7 +102,9 @@ def lib():
                               vp, vp, i32, vp]
         L.bsg_dsd.restype = i32
         L.bsg_dsd.argtypes = [vp, vp, C.POINTER(TopologyStruct), vp, vp, i64, i32, i32, vp, i64,
-                              i32, i32, vp]
+                              i32, i32, vp, sz, vp]
+        L.bsg_dsd_workspace_bytes.restype = i32
+        L.bsg_dsd_workspace_bytes.argtypes = [vp, C.POINTER(i64)]
         L.bsg_dsd_combine_top1.restype = i32
         L.bsg_dsd_combine_top1.argtypes = [vp, C.POINTER(TopologyStruct), vp, i64, i32, i32, vp,
                                            i64, vp, vp, vp, i64, i32, vp]
@@ -279,10 +282,22 @@ def sdd(a, b, K, topo: Topology, epilogue, out_blocks, b2=None, trans_b=False, a
                                 _ptr(aux_out), dtype_code(a), _stream()))
 
 
-def dsd(blocks, topo: Topology, b, N, c, trans_b=False, blocks2=None, b2=None):
+def dsd(blocks, topo: Topology, b, N, c, trans_b=False, blocks2=None, b2=None, workspace=None):
+    """bsg_dsd; workspace (a device tensor, or None) lets the product split
+    its last round (see dsd_workspace_bytes)."""
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("dsd", lib().bsg_dsd(_ptr(blocks), _ptr(blocks2), C.byref(topo.struct), _ptr(b),
                                 _ptr(b2), _ld(b), int(bool(trans_b)), N, _ptr(c), _ld(c),
-                                dtype_code(c), dtype_code(blocks), _stream()))
+                                dtype_code(c), dtype_code(blocks), _ptr(workspace), nbytes,
+                                _stream()))
+
+
+def dsd_workspace_bytes() -> int:
+    """Bytes of a bsg_dsd workspace that allows every split of its last round
+    on the current device (one 256 KiB share per compute unit)."""
+    out = C.c_int64(0)
+    _check("dsd_workspace_bytes", lib().bsg_dsd_workspace_bytes(_stream(), C.byref(out)))
+    return int(out.value)
 
 
 def dsd_combine_top1(blocks, topo: Topology, b, N, c, row_src, gate, y, trans_b=False):

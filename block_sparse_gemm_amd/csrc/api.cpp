@@ -7,9 +7,13 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "kernels.hpp"
 
 static_assert(bsg::kRouteScratchBytes == BSG_ROUTE_SCRATCH_BYTES, "one scratch size");
+static_assert(bsg::kSplitShareBytes == BSG_DSD_SHARE_BYTES, "one share size");
 
 namespace {
 
@@ -487,9 +491,41 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
                       "sdd");
 }
 
+// Compute units of the stream's device, looked up once per device.
+static hipError_t device_cus(hipStream_t stream, int* ncu) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int cus[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
+            hipSuccess)
+            return e;
+        if (n <= 0) return hipErrorInvalidDevice;
+        cus[dev] = n;
+    }
+    *ncu = cus[dev];
+    return hipSuccess;
+}
+
+bsg_status bsg_dsd_workspace_bytes(bsg_stream_t stream, int64_t* bytes) {
+    REQUIRE(bytes != nullptr, "bytes is NULL");
+    int ncu = 0;
+    const hipError_t e = device_cus((hipStream_t)stream, &ncu);
+    if (e != hipSuccess) return hip_status(e, "dsd_workspace_bytes");
+    *bytes = (int64_t)ncu * bsg::kSplitShareBytes;
+    return ok();
+}
+
 bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* topo,
                    const void* b, const void* b2, int64_t ldb, int trans_b, int N, void* c,
-                   int64_t ldc, int c_dtype, int dtype, bsg_stream_t stream) {
+                   int64_t ldc, int c_dtype, int dtype, void* workspace, size_t workspace_bytes,
+                   bsg_stream_t stream) {
     REQUIRE(dtype_ok(dtype) && dtype_ok(c_dtype), "unknown dtype");
     if (dtype == BSG_F32 && c_dtype != BSG_F32)
         return fail(BSG_EUNSUPPORTED, "fp32 operands need an fp32 output");
@@ -514,6 +550,12 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
         REQUIRE_VEC_PTR(b2);
         REQUIRE((int64_t)topo->E * topo->F < bsg::kSecondSet, "too many column blocks");
     }
+    if (workspace) {
+        REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+        REQUIRE(workspace_bytes >= 2 * (size_t)bsg::kSplitShareBytes,
+                "workspace too small (%zu < %d): two tile shares at least", workspace_bytes,
+                2 * bsg::kSplitShareBytes);
+    }
     bsg::GemmParams p = gemm_params(topo);
     p.a = blocks;
     p.a2 = blocks2;
@@ -524,6 +566,15 @@ bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* 
     p.ldc = ldc;
     p.N = N;
     p.ntn = (N + 255) / 256;
+    // the last round's split: only tiles of at least kSplitMinBlocks K-blocks
+    if (workspace && (int64_t)topo->F * (blocks2 ? 2 : 1) >= bsg::kSplitMinBlocks) {
+        int ncu = 0;
+        const hipError_t e = device_cus((hipStream_t)stream, &ncu);
+        if (e != hipSuccess) return hip_status(e, "dsd");
+        p.ws = (float*)workspace;
+        p.ws_units = (int)std::min<size_t>(workspace_bytes / bsg::kSplitShareBytes, INT32_MAX);
+        p.ncu = ncu;
+    }
     return hip_status(bsg::launch_dsd(p, tiles_max(topo), trans_b,
                                       c_dtype, dtype, (hipStream_t)stream),
                       "dsd");

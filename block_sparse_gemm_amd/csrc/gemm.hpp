@@ -65,6 +65,10 @@ constexpr int kSegs = kPanelBytes / 1024;      // 1 KB segments per panel
 constexpr int kStageBytes = 4 * kPanelBytes;   // A0 A1 B0 B1
 constexpr int kStages = 4;
 constexpr int kLdsBytes = kStages * kStageBytes;
+// Split DSD tiles: fp32 partial sums of one 256 x 256 tile (256 KB), and at
+// most this many K-segments a tile
+constexpr int kSplitFloats = kSplitShareBytes / 4;
+constexpr int kMaxSplit = 8;
 constexpr int kSegsPerWave = kSegs / 4;          // per panel
 constexpr int kLoadsPerTile = 4 * kSegsPerWave;  // per wave and K-tile
 constexpr int kIdxCap = 2048;                    // K-blocks of one tile staged in LDS at a time
@@ -281,7 +285,8 @@ struct KIdx {
 // half wn, as 2 x 4 accumulators, and the absent half's panel is not loaded
 // (6 direct loads per K-tile instead of 8).
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP, bool HALF, int BR>
-__device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int tile, int seg,
+                                          int nseg, float* part) {
     constexpr int ES = Elt<DT>::kBytes;
     constexpr int KT = Elt<DT>::kKt;
     static_assert(BR == 128 || BR == 64, "blocks of 128 or 64 rows");
@@ -300,28 +305,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
     constexpr int NMI = HALF ? 2 : 4;     // 32-row A fragments per wave
     lds_t* lds = (lds_t*)smem;
 
-    // ---- tile count (device-side sizes) and XCD-aware remap
+    // ---- the tile: SDD / DSD, `tile` in the group order (the launch's
+    // wrapper maps workgroups to tiles); DSTD, from the workgroup index here
     const int F = P.F;
-    int ntiles, tn;  // tiles, tiles along N
-    if constexpr (MODE == kModeSdd) tn = (F + 1) / 2;
-    else if constexpr (MODE == kModeSddOne) tn = F;
-    else tn = P.ntn;
-    if constexpr (MODE == kModeDstd) ntiles = P.E * ((F + 1) / 2) * tn;
-    else ntiles = P.meta[3] * tn;
-    if ((int)blockIdx.x >= ntiles) return;
+    const int tn = MODE == kModeSdd ? (F + 1) / 2 : MODE == kModeSddOne ? F : P.ntn;
     // tm: row pair (SDD / DSD) or expert column pair (DSTD); tq: N tile
     int tm, tq;
     if constexpr (MODE == kModeDstd) {
         // a DSTD tile's K is its expert's rows: experts longest first, each
         // expert's tiles in groups of column pairs x N tiles
+        const int ntiles = P.E * ((F + 1) / 2) * tn;
+        if ((int)blockIdx.x >= ntiles) return;
         const int cpe = (F + 1) / 2, per_e = cpe * tn;
-        const int tile = xcd_chunked(blockIdx.x, ntiles, kDstdChunk);
-        const int rank = tile / per_e;
+        const int t = xcd_chunked(blockIdx.x, ntiles, kDstdChunk);
+        const int rank = t / per_e;
         int j;
-        grouped_tile(tile - rank * per_e, cpe, tn, P.group, j, tq);
+        grouped_tile(t - rank * per_e, cpe, tn, P.group, j, tq);
         tm = P.expert_order[rank] * cpe + j;
     } else {
-        row_tile_of(P.row_tiles, xcd_remap(blockIdx.x, ntiles), tn, tm, tq);
+        row_tile_of(P.row_tiles, tile, tn, tm, tq);
     }
 
     // the wave index is uniform: keep it (and every LDS stage address derived
@@ -708,10 +710,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
     if constexpr (SDD) {
         run(P.K / KT);
     } else {
-        // the tile's K-blocks in chunks of kIdxCap, their indices staged per chunk
-        for (int c0 = 0; c0 < nblk; c0 += kIdxCap) {
-            const int nb = min(kIdxCap, nblk - c0);
-            if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+        // the tile's K-blocks (segment seg of nseg: a split tile's share) in
+        // chunks of kIdxCap, their indices staged per chunk
+        const int kb0 = (int)((int64_t)seg * nblk / nseg);
+        const int kb1 = (int)((int64_t)(seg + 1) * nblk / nseg);
+        for (int c0 = kb0; c0 < kb1; c0 += kIdxCap) {
+            const int nb = min(kIdxCap, kb1 - c0);
+            if (c0 > kb0) __syncthreads();  // every wave is done with the previous chunk
             for (int p = threadIdx.x; p < nb; p += kGemmThreads) {
                 const KIdx r = fetch(c0 + p);
                 ib0[p] = r.b0;
@@ -720,6 +725,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
             }
             __syncthreads();
             run(nb * KPB);
+        }
+    }
+
+    // ---- a split tile's share (DSD): its fp32 partial sums go to `part` in
+    // the accumulator layout (per wave, per 32 x 32 block, 16 values a lane,
+    // 4 KB contiguous); the reduction launch adds the shares in segment order
+    if constexpr (DSD) {
+        if (part) {
+            float* wp = part + wave * (kSplitFloats / 4) + lane * 16;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(f32x4*)(wp + (mi * 4 + ni) * 1024 + 4 * q) =
+                            f32x4{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1],
+                                  acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
+            return;
         }
     }
 
@@ -1031,17 +1055,31 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem) {
     }
 }
 
-// Whether this workgroup's SDD / DSD tile is a half tile (at most 128 of its
-// rows present): the same tile order as gemm_tile's, then the row tile's
-// count of present block rows.  Workgroups beyond the live tile count say no
-// (gemm_tile exits).
+// Split of a DSD launch's last, partly filled round: with ntiles tiles on
+// ncu CUs, the tail (ntiles mod ncu tiles) is cut into S K-segments each, S =
+// min(ncu / tail, kMaxSplit, units / tail), so the last round runs tail x S
+// shares of 1/S of a tile instead of tail whole tiles on a nearly idle chip.
+// No split (full = ntiles) when S < 2 or no workspace.  Both launches of a
+// split product compute the same plan from the same device-side tile count.
+struct SplitPlan {
+    int full, tail, S;
+};
+__device__ __forceinline__ SplitPlan split_plan(int ntiles, int ncu, int units) {
+    SplitPlan p{ntiles, 0, 1};
+    if (ncu <= 0 || units <= 0) return p;
+    const int tail = ntiles % ncu;
+    if (tail == 0) return p;
+    const int S = min(min(ncu / tail, kMaxSplit), units / tail);
+    if (S < 2) return p;
+    return SplitPlan{ntiles - tail, tail, S};
+}
+
+// Whether SDD / DSD tile `tile` (group order) is a half tile: its row
+// tile's count of present block rows is at most 128 rows' worth.
 template <int MODE, int BR>
-__device__ __forceinline__ bool half_tile(const GemmParams& P) {
-    const int tn = MODE == kModeSdd ? (P.F + 1) / 2 : P.ntn;
-    const int ntiles = P.meta[3] * tn;
-    if ((int)blockIdx.x >= ntiles) return false;
+__device__ __forceinline__ bool half_tile(const GemmParams& P, int tile, int tn) {
     int tm, tq;
-    row_tile_of(P.row_tiles, xcd_remap(blockIdx.x, ntiles), tn, tm, tq);
+    row_tile_of(P.row_tiles, tile, tn, tm, tq);
     return __builtin_amdgcn_readfirstlane((P.row_tiles[tm] & 3) + 1) <= kBlock / BR;
 }
 
@@ -1053,13 +1091,92 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
     constexpr bool kGbuf = EPI == kEpiGeluBwd && OUT == kBf16;
     __shared__ __attribute__((aligned(1024))) char
         smem[kLdsBytes + (kIdx ? 3 * kIdxCap * 4 : 0) + (kGbuf ? 4 * 8192 : 0)];
-    if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
-        if (half_tile<MODE, BR>(P)) {
-            gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem);
+    if constexpr (MODE == kModeDstd) {
+        gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, false, BR>(P, smem, 0, 0, 1, nullptr);
+    } else {
+        // SDD / DSD: workgroup -> tile, XCD-aware (each XCD a contiguous range
+        // of the group order); a split DSD's last round: workgroup -> share
+        const int tn = MODE == kModeSdd ? (P.F + 1) / 2 : MODE == kModeSddOne ? P.F : P.ntn;
+        const int ntiles = P.meta[3] * tn;
+        SplitPlan pl{ntiles, 0, 1};
+        if constexpr (MODE == kModeDsd || MODE == kModeDsd2) {
+            if (P.ws) pl = split_plan(ntiles, P.ncu, P.ws_units);
+        }
+        const int b = blockIdx.x;
+        int tile, seg = 0, nseg = 1;
+        float* part = nullptr;
+        if (b < pl.full) {
+            tile = xcd_remap(b, pl.full);
+        } else if (b < pl.full + pl.tail * pl.S) {
+            const int u = b - pl.full;
+            tile = pl.full + u / pl.S;
+            seg = u % pl.S;
+            nseg = pl.S;
+            part = P.ws + (int64_t)u * kSplitFloats;
+        } else {
             return;
         }
+        if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
+            if (half_tile<MODE, BR>(P, tile, tn)) {
+                gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem, tile, seg, nseg, part);
+                return;
+            }
+        }
+        gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, false, BR>(P, smem, tile, seg, nseg, part);
     }
-    gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, false, BR>(P, smem);
+}
+
+// The second launch of a split DSD: workgroup i sums the S shares of tail
+// tile full + i in segment order (shares as gemm_tile writes them) and
+// stores the tile as the plain DSD epilogue does, row-major C.  MODE and BK
+// name the product it completes (as gemm_kernel's arguments do) and select
+// nothing else.
+template <int MODE, bool BK, int OUT, int BR>
+__global__ __launch_bounds__(kGemmThreads) void dsd_reduce_kernel(GemmParams P) {
+    const SplitPlan pl = split_plan(P.meta[3] * P.ntn, P.ncu, P.ws_units);
+    if ((int)blockIdx.x >= pl.tail) return;
+    const int tile = pl.full + blockIdx.x;
+    int tm, tq;
+    row_tile_of(P.row_tiles, tile, P.ntn, tm, tq);
+    const int ent = __builtin_amdgcn_readfirstlane(P.row_tiles[tm]);
+    const int r0 = ent >> 8, nq = (ent & 3) + 1;
+    constexpr int QB = kBlock / BR;
+    const bool half = nq <= QB;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 1, wn = wave >> 1, l32 = lane & 31, lh = lane >> 5;
+    const int64_t n0 = (int64_t)tq * 256;
+    if (wn == 1 && n0 + 128 >= P.N) return;  // absent N half
+    constexpr int OES = OUT == kBf16 ? 2 : 4;
+    const float* src = P.ws + (int64_t)blockIdx.x * pl.S * kSplitFloats + wave * (kSplitFloats / 4) +
+                       lane * 16;
+    const int nmi = half ? 2 : 4;
+    for (int mi = 0; mi < nmi; ++mi) {
+        // rows of fragment mi inside the tile, and whether its block row is present
+        const int hrow = half ? 64 * wm : 128 * wm + 64 * (mi >> 1);
+        if (hrow / BR >= nq) continue;
+        const int64_t row = (int64_t)BR * r0 + hrow + 32 * (mi & 1) + l32;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            f32x4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int sgm = 0; sgm < pl.S; ++sgm) {
+                const float* sp = src + (int64_t)sgm * kSplitFloats + (mi * 4 + ni) * 1024;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 x = *(const f32x4*)(sp + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[q][e] += x[e];
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t col = n0 + wn * 128 + 32 * ni + 8 * g + 4 * lh;
+                const float w[4] = {v[g][0], v[g][1], v[g][2], v[g][3]};
+                store4<OUT>((char*)P.out + (row * P.ldc + col) * OES, w);
+            }
+        }
+    }
 }
 
 // ----------------------------------------------------------------- launch
@@ -1128,17 +1245,44 @@ static hipError_t dispatch_dsd(const GemmParams& p, int64_t grid, int trans_b, i
                    : launch<kBf16, MODE, false, kEpiNone, kF32, true, BR>(p, grid, s);
 }
 
+template <int MODE, int OUT, int BR>
+static void launch_reduce(const GemmParams& p, int trans_b, hipStream_t s) {
+    if (trans_b)
+        hipLaunchKernelGGL((dsd_reduce_kernel<MODE, true, OUT, BR>), dim3((unsigned)p.ncu),
+                           dim3(kGemmThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((dsd_reduce_kernel<MODE, false, OUT, BR>), dim3((unsigned)p.ncu),
+                           dim3(kGemmThreads), 0, s, p);
+}
+
 template <int BR>
 hipError_t launch_dsd_br(const GemmParams& p, int64_t row_tiles_max, int trans_b, int c_dtype,
                          int dtype, hipStream_t s) {
     const int64_t grid = row_tiles_max * p.ntn;
     if (p.scat_out) {  // top-1 rows to token order: bf16 throughout, one block set
-        if (dtype != kBf16 || c_dtype != kBf16 || p.a2) return hipErrorInvalidValue;
+        if (dtype != kBf16 || c_dtype != kBf16 || p.a2 || p.ws) return hipErrorInvalidValue;
         return trans_b ? launch<kBf16, kModeDsd, true, kEpiScatter, kBf16, true, BR>(p, grid, s)
                        : launch<kBf16, kModeDsd, false, kEpiScatter, kBf16, true, BR>(p, grid, s);
     }
-    return p.a2 ? dispatch_dsd<kModeDsd2, BR>(p, grid, trans_b, c_dtype, dtype, s)
-                : dispatch_dsd<kModeDsd, BR>(p, grid, trans_b, c_dtype, dtype, s);
+    if (!p.ws)
+        return p.a2 ? dispatch_dsd<kModeDsd2, BR>(p, grid, trans_b, c_dtype, dtype, s)
+                    : dispatch_dsd<kModeDsd, BR>(p, grid, trans_b, c_dtype, dtype, s);
+    // split last round: up to ncu more workgroups for the shares, then the
+    // reduction of the split tiles
+    if (p.ncu <= 0 || p.ws_units < 2) return hipErrorInvalidValue;
+    const int64_t g2 = grid + p.ncu;
+    hipError_t e = p.a2 ? dispatch_dsd<kModeDsd2, BR>(p, g2, trans_b, c_dtype, dtype, s)
+                        : dispatch_dsd<kModeDsd, BR>(p, g2, trans_b, c_dtype, dtype, s);
+    if (e != hipSuccess || grid <= 0) return e;
+    const int out = dtype == kF32 ? kF32 : c_dtype;
+    if (p.a2) {
+        if (out == kBf16) launch_reduce<kModeDsd2, kBf16, BR>(p, trans_b, s);
+        else launch_reduce<kModeDsd2, kF32, BR>(p, trans_b, s);
+    } else {
+        if (out == kBf16) launch_reduce<kModeDsd, kBf16, BR>(p, trans_b, s);
+        else launch_reduce<kModeDsd, kF32, BR>(p, trans_b, s);
+    }
+    return hipGetLastError();
 }
 
 template <int BR>

@@ -32,6 +32,12 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kRouteChunk = 64;  // tokens per routing chunk
 
+// A DSD's split last round: one share holds the fp32 partial sums of one
+// 256 x 256 tile; a tile is split only when it walks at least this many
+// K-blocks (shorter tiles do not repay the shares' traffic).
+constexpr int kSplitShareBytes = 256 * 256 * 4;
+constexpr int kSplitMinBlocks = 32;
+
 struct GemmParams {
     const void* a;       // SDD: dense rows; DSD / DSTD: sparse blocks
     const void* a2;      // two-set DSD: the second block set
@@ -67,6 +73,12 @@ struct GemmParams {
     int br;               // rows of a block: 128, or 64 for bins of 64 rows
     int group;            // DSTD: column pairs per group of an expert's tiles (>= 1); SDD and
                           // DSD take their groups from row_tiles
+    // DSD (plain epilogue): workspace for the split of the last round (NULL:
+    // no split), in shares of one tile's fp32 partial sums (256 KB each), and
+    // the GPU's compute units
+    float* ws;
+    int ws_units;
+    int ncu;
 };
 
 // The arrays of a topology (bsg_topology's device pointers).

@@ -84,6 +84,13 @@ class Layer:
         # no dXp)
         self.fuse_top1 = s.k == 1 and s.dtype == "bf16" and s.yp_tdtype == torch.bfloat16
         dev = torch.device(device)
+        # plain DSDs whose tiles walk at least 32 K-blocks (f >= 4096, or the
+        # SwiGLU backward's two block sets) split their last, partly filled
+        # round of tiles through this workspace (None: never)
+        F = s.f // bsg.BLOCK
+        long_k = F >= 32 or (s.act == "swiglu" and s.backward and 2 * F >= 32)
+        self.dsd_ws = torch.empty(bsg.dsd_workspace_bytes() // 4, dtype=torch.float32,
+                                  device=dev) if long_k and not self.fuse_top1 else None
         i32 = dict(dtype=torch.int32, device=dev)
         A = s.T * s.k
         self.Tp_max = bsg.max_padded_rows(s.T, s.k, s.E, s.bin_rows)
@@ -152,7 +159,7 @@ class Layer:
             c("dsd", bsg.dsd_combine_top1, self.act, t, W2, s.d, self.yp, self.row_src,
               self.gate, self.y)
             return self.y
-        c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp)
+        c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp, workspace=self.dsd_ws)
         c("unpermute_combine", bsg.unpermute_combine, self.yp, self.dest_row, self.gate, s.T,
           s.k, s.d, self.y)
         return self.y
@@ -180,9 +187,10 @@ class Layer:
                 return
             if sw:
                 c("dsd_bwd", bsg.dsd, dh0, t, W1, s.d, self.dxp, trans_b=True,
-                  blocks2=self.plane(self.dh, 1), b2=W3)
+                  blocks2=self.plane(self.dh, 1), b2=W3, workspace=self.dsd_ws)
             else:
-                c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True)
+                c("dsd_bwd", bsg.dsd, self.dh, t, W1, s.d, self.dxp, trans_b=True,
+                  workspace=self.dsd_ws)
             c("unpermute_combine_bwd", bsg.unpermute_combine, self.dxp, self.dest_row, None,
               s.T, s.k, s.d, self.dx)
 

@@ -65,6 +65,10 @@ def call_name(kernel: str):
     two-set DSD), B K-contiguous, epilogue (3 and 4: the backward ones), out
     dtype, swap (false: transposed DSTD output), block rows.  dW1 and dW3 run
     the same instantiation and share its figure."""
+    m = re.search(r"dsd_reduce_kernel<(\d+), (\w+), (\d+), (\d+)>", kernel)
+    if m:  # the second launch of a split DSD, named by the product it completes
+        mode, b_kc = m.group(1), m.group(2)
+        return "dsd_bwd" if mode == "4" or b_kc == "true" else "dsd"
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\w+), (\d+), (\d+), (\w+)(?:, (\d+))?>", kernel)
     if m:
         _, mode, b_kc, epi, _, swap, _ = m.groups()
@@ -153,8 +157,14 @@ def summarize(args):
         fb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
         ent = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
                "kernel": kern[:120]}
-        if kern.find("gemm_kernel") >= 0:
+        if kern.find("gemm_kernel") >= 0 or kern.find("dsd_reduce_kernel") >= 0:
             ent["source_sha"] = sha
+        if name in result:  # a call of two launches (a split DSD): per call, both
+            prev = result[name]
+            ent = dict(prev, fetch_bytes=prev["fetch_bytes"] + ent["fetch_bytes"],
+                       write_bytes=prev["write_bytes"] + ent["write_bytes"],
+                       bytes_per_launch=prev["bytes_per_launch"] + ent["bytes_per_launch"],
+                       kernel=prev["kernel"] + " + " + ent["kernel"][:60])
         result[name] = ent
         if name == "dstd_dw1":
             result["dstd_dw3"] = ent
@@ -246,6 +256,12 @@ def kernel_label(name: str) -> str:
                 f"(B {'K' if bk == 'true' else 'MN'}-contig, out {'bf16' if out == '1' else 'f32'}"
                 f"{'' if swap == 'true' else ', transposed'}"
                 f"{', blocks of ' + br + ' rows' if br and br != '128' else ''})")
+    m = re.match(r"void bsg::dsd_reduce_kernel<(\d+), (\w+), (\d+), (\d+)>", name)
+    if m:
+        mode, bk, out, br = m.groups()
+        return (f"split-DSD sum of shares ({_MODES.get(mode, mode)}, B "
+                f"{'K' if bk == 'true' else 'MN'}-contig, out {'bf16' if out == '1' else 'f32'}"
+                f"{', blocks of ' + br + ' rows' if br != '128' else ''})")
     return re.sub(r"\(.*", "", name).replace("void ", "")[:70]
 
 

@@ -352,10 +352,36 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
  * fp32 accumulation.
  * c is [Tp_max, N] with leading dimension ldc in c_dtype (bf16 or fp32);
  * rows >= Tp are untouched.  N must be a positive multiple of 128.
+ *
+ * workspace (optional, NULL for none; caller-owned device memory, 256-byte
+ * aligned, workspace_bytes >= 2 * BSG_DSD_SHARE_BYTES) lets the product split
+ * its last, partly filled round of 256 x 256 tiles: when the tiles do not
+ * fill whole rounds of the GPU's compute units, each of the last round's
+ * tiles is cut into 2 to 8 K-segments whose fp32 partial sums (one share of
+ * BSG_DSD_SHARE_BYTES each) go to the workspace, and a second launch adds
+ * them in segment order and stores the tile.  Deterministic; the split
+ * tiles' sums associate differently from an unsplit run (fp32 rounding).
+ * Used only when a tile walks at least 32 K-blocks (f >= 4096, or the two
+ * block sets together); otherwise, or with fewer shares than needed, the
+ * workspace is ignored.  bsg_dsd_workspace_bytes gives the size that allows
+ * every split.  Calls sharing one workspace must not overlap in time.
  */
 bsg_status bsg_dsd(const void* blocks, const void* blocks2, const bsg_topology* topo,
                    const void* b, const void* b2, int64_t ldb, int trans_b, int N, void* c,
-                   int64_t ldc, int c_dtype, int dtype, bsg_stream_t stream);
+                   int64_t ldc, int c_dtype, int dtype, void* workspace, size_t workspace_bytes,
+                   bsg_stream_t stream);
+
+/* One share of bsg_dsd's workspace: the fp32 partial sums of a 256 x 256 tile. */
+#define BSG_DSD_SHARE_BYTES 262144
+
+/*
+ * dsd_workspace_bytes - the bsg_dsd workspace that lets every split of its
+ * last round happen on the device of `stream` (the current device for the
+ * null stream): one share per compute unit.  A host-side size helper the
+ * post does not define; it queries the device once (HIP errors reported as
+ * BSG_EHIP).
+ */
+bsg_status bsg_dsd_workspace_bytes(bsg_stream_t stream, int64_t* bytes);
 
 /*
  * dsd_combine_top1 - bsg_dsd followed by bsg_unpermute_combine for top-1

@@ -144,7 +144,7 @@ int main(int argc, char** argv) {
     BSG_OK_(bsg_build_topology(bin_offsets, E, f, Tp_max, &topo, NULL));
     BSG_OK_(bsg_sdd(xp, d, w1, NULL, ncol, 0, d, &topo, BSG_EPI_GELU, NULL, act, NULL, BSG_BF16,
                     NULL));
-    BSG_OK_(bsg_dsd(act, NULL, &topo, w2, NULL, d, 0, d, yp, d, BSG_BF16, BSG_BF16, NULL));
+    BSG_OK_(bsg_dsd(act, NULL, &topo, w2, NULL, d, 0, d, yp, d, BSG_BF16, BSG_BF16, NULL, 0, NULL));
     BSG_OK_(bsg_unpermute_combine(yp, BSG_BF16, d, dest_row, gate, T, k, d, y, BSG_BF16, NULL));
     HIP_OK(hipDeviceSynchronize());
 

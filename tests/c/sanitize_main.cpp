@@ -16,6 +16,7 @@
 extern int g_launches;
 extern bsg::TopoJob g_route_topo;
 extern bsg::PermJob g_route_perm;
+extern bsg::GemmParams g_dsd;
 
 // ---- the oracle's C entry points (oracle/oracle.c)
 extern "C" {
@@ -217,10 +218,31 @@ static void abi_checks() {
     EXPECT(bsg_sdd(P, 16909320, P, nullptr, 1024, 0, 256, &t, BSG_EPI_GELU, nullptr, P, P,
                    BSG_BF16, nullptr) == BSG_EUNSUPPORTED);
     EXPECT(bsg_dsd(P, nullptr, &t, P, nullptr, 256, 0, 256, P, 256, BSG_BF16, BSG_BF16,
+                   nullptr, 0, nullptr) == BSG_OK);
+    EXPECT(bsg_dsd(P, P, &t, P, P, 1024, 1, 256, P, 256, BSG_F32, BSG_BF16, nullptr, 0,
                    nullptr) == BSG_OK);
-    EXPECT(bsg_dsd(P, P, &t, P, P, 1024, 1, 256, P, 256, BSG_F32, BSG_BF16, nullptr) == BSG_OK);
     EXPECT(bsg_dsd(P, nullptr, &t, P, nullptr, INT64_MAX, 0, 256, P, 256, BSG_BF16, BSG_BF16,
-                   nullptr) == BSG_EINVAL);
+                   nullptr, 0, nullptr) == BSG_EINVAL);
+    // the workspace: ignored for short tiles (F = 4 K-blocks a row here),
+    // rejected when misaligned or under two shares
+    EXPECT(bsg_dsd(P, nullptr, &t, P, nullptr, 256, 0, 256, P, 256, BSG_BF16, BSG_BF16, P,
+                   1 << 20, nullptr) == BSG_OK &&
+           g_dsd.ws == nullptr);
+    EXPECT(bsg_dsd(P, nullptr, &t, P, nullptr, 256, 0, 256, P, 256, BSG_BF16, BSG_BF16, MIS,
+                   1 << 20, nullptr) == BSG_EINVAL);
+    EXPECT(bsg_dsd(P, nullptr, &t, P, nullptr, 256, 0, 256, P, 256, BSG_BF16, BSG_BF16, P,
+                   BSG_DSD_SHARE_BYTES, nullptr) == BSG_EINVAL);
+    {
+        int64_t wsb = 0;
+        EXPECT(bsg_dsd_workspace_bytes(nullptr, &wsb) == BSG_OK &&
+               wsb == 256 * (int64_t)BSG_DSD_SHARE_BYTES);
+        EXPECT(bsg_dsd_workspace_bytes(nullptr, nullptr) == BSG_EINVAL);
+        // long tiles (f = 4096: 32 K-blocks) take the split
+        bsg_topology lt = fake_topo(4, 4096, 1024);
+        EXPECT(bsg_dsd(P, nullptr, &lt, P, nullptr, 256, 0, 256, P, 256, BSG_BF16, BSG_BF16, P,
+                       3 * (size_t)BSG_DSD_SHARE_BYTES, nullptr) == BSG_OK &&
+               g_dsd.ws == (float*)P && g_dsd.ws_units == 3 && g_dsd.ncu == 256);
+    }
     EXPECT(bsg_dsd_combine_top1(P, &t, P, 256, 0, 256, nullptr, 0, ip, fp, P, 256, BSG_BF16,
                                 nullptr) == BSG_OK);
     EXPECT(bsg_dstd(P, &t, P, 256, 256, P, 1024, 1, BSG_BF16, nullptr) == BSG_OK);

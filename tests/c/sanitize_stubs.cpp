@@ -11,7 +11,23 @@ int g_launches = 0;             // read by the driver
 bsg::TopoJob g_route_topo = {};  // the last routing launch's topology job
 bsg::PermJob g_route_perm = {};  // and its permutation job
 
+bsg::GemmParams g_dsd = {};      // the last DSD launch's parameters
+
 extern "C" const char* hipGetErrorString(hipError_t) { return "host-only build"; }
+// the compute-unit lookup behind bsg_dsd's split and its size query: one
+// device with 256 compute units
+extern "C" hipError_t hipGetDevice(int* dev) {
+    *dev = 0;
+    return hipSuccess;
+}
+extern "C" hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* dev) {
+    *dev = 0;
+    return hipSuccess;
+}
+extern "C" hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+    *value = 256;
+    return hipSuccess;
+}
 
 namespace bsg {
 
@@ -66,8 +82,9 @@ hipError_t launch_sdd(const GemmParams&, int64_t, int, int, int, hipStream_t) {
     return hipSuccess;
 }
 
-hipError_t launch_dsd(const GemmParams&, int64_t, int, int, int, hipStream_t) {
+hipError_t launch_dsd(const GemmParams& p, int64_t, int, int, int, hipStream_t) {
     ++g_launches;
+    g_dsd = p;
     return hipSuccess;
 }
 

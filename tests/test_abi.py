@@ -307,9 +307,13 @@ def test_dsd_dstd_validation(L):
     ncol = 4 * 256
 
     def dsd(blocks=P, blocks2=None, b=P, b2=None, ldb=256, trans_b=0, N=256, c=P, ldc=256,
-            c_dtype=bsg.BF16, dtype=bsg.BF16):
+            c_dtype=bsg.BF16, dtype=bsg.BF16, ws=None, ws_bytes=0):
         return L.bsg_dsd(blocks, blocks2, C.byref(t), b, b2, ldb, trans_b, N, c, ldc, c_dtype,
-                         dtype, None)
+                         dtype, ws, ws_bytes, None)
+
+    # the split workspace: 256-byte aligned, two 256 KiB shares at least
+    assert dsd(ws=MIS, ws_bytes=1 << 20) == bsg.EINVAL and "aligned" in _err(L)
+    assert dsd(ws=P, ws_bytes=(1 << 18) + 4096) == bsg.EINVAL and "two tile shares" in _err(L)
 
     assert dsd(N=200) == bsg.EINVAL
     assert dsd(ldb=128) == bsg.EINVAL
@@ -369,7 +373,7 @@ def test_leading_dimensions_beyond_32bit_panel_offsets(L):
 
     def dsd(ldb, trans_b):
         return L.bsg_dsd(P, None, C.byref(t), P, None, ldb, trans_b, 256, P, 256, bsg.BF16,
-                         bsg.BF16, None)
+                         bsg.BF16, None, 0, None)
 
     assert dsd(km, 0) == bsg.EUNSUPPORTED
     assert dsd(kc, 1) == bsg.EUNSUPPORTED

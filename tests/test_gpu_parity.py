@@ -493,6 +493,104 @@ def test_products_at_tile_groups(orc, name, bin_rows):
          ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
 
 
+# DSD with a split last round (a tile walks >= 32 K-blocks).  few_tiles:
+# 16 tiles (d = 384: an absent N half in every second column tile, a half row
+# pair), all of them in the split round, 8 shares each; the same over bins of
+# 64 (64-row blocks, a tile with one block row); two_sets: the SwiGLU input
+# gradient (2 x 16 K-blocks), 10 tiles with two half row pairs; tail_of_many:
+# 280 tiles on the 256 CUs of an MI355X, 256 whole and the last 24 (the last
+# group of 3 row pairs, one of them half) split 8 ways.
+SPLIT = {
+    "few_tiles": (_small("split_few", T=1536, d=384, E=4, f=4096, k=1),
+                  [650, 450, 300, 136], 128),
+    "few_tiles_bins64": (_small("split_few64", T=1536, d=384, E=4, f=4096, k=1),
+                         [650, 450, 300, 136], 64),
+    "two_sets": (_small("split_two", T=1024, d=256, E=4, f=2048, k=2, act="swiglu"),
+                 [800, 600, 400, 248], 128),
+    "tail_of_many": (_small("split_tail", T=8832, d=2048, E=1, f=4096, k=1), [8832], 128),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT))
+def test_dsd_split_last_round(orc, name):
+    """bsg_dsd with a workspace: the last round's tiles are cut into K-segments
+    whose fp32 partial sums a second launch adds in segment order.  Against
+    the oracle (every element, or for tail_of_many 64 sampled rows, half of
+    them in the split tiles, from the product's definition in fp64); against
+    the same product without the workspace (only the split tiles' fp32 sums
+    associate differently); and bit-identical on a second run."""
+    from block_sparse_gemm_amd import bsg, layer
+    cfg, counts, bin_rows = SPLIT[name]
+    cfg = cfg.replace(bin_rows=bin_rows)
+    BR = 64 if bin_rows == 64 else 128
+    _say(f"[split] {name} T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} k={cfg.k} act={cfg.act} "
+         f"bin_rows={bin_rows}")
+    lg = _picks_logits(cfg.T, cfg.E, cfg.k, counts, seed=37)
+    L = layer.Layer(layer.Shape.of(cfg.replace(backward=False)))
+    bsg.route(torch.from_numpy(lg).cuda(), cfg.k, cfg.renorm, L.expert_idx, L.gate, L.dest_row,
+              L.counts, L.bin_offsets, L.route_ws, bin_rows=bin_rows)
+    bsg.build_topology(L.bin_offsets, cfg.E, cfg.f, L.Tp_max, L.topo)
+    torch.cuda.synchronize()
+    bo = orc.route(lg, cfg.k, cfg.renorm, bin_rows)["bin_offsets"]
+    assert np.array_equal(L.bin_offsets.cpu().numpy(), bo)
+    E, F, d, f = cfg.E, cfg.f // 128, cfg.d, cfg.f
+    Tp, nnz, nnz_max = int(bo[E]), int(bo[E]) // BR * F, L.topo.nnz_max
+    sw = cfg.act == "swiglu"
+    planes = 2 if sw else 1
+    rng = np.random.default_rng(43)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    blk = _bf16_draw(rng, (planes * nnz_max * BR, 128), 1.0)
+    blk_used = blk.reshape(planes, nnz_max, BR, 128)[:, :nnz].reshape(planes * nnz, BR, 128)
+    W = _bf16_draw(rng, (d, E * f), 0.05)           # W1 [d, E*f]: B transposed
+    W3 = _bf16_draw(rng, (d, E * f), 0.05) if sw else None
+    ws = torch.empty(bsg.dsd_workspace_bytes() // 4, dtype=torch.float32, device="cuda")
+    a_dev = dev(blk)
+    w_dev, w3_dev = dev(W), (dev(W3) if sw else None)
+    kw = dict(trans_b=True)
+    if sw:
+        kw.update(blocks2=a_dev[nnz_max * BR:], b2=w3_dev)
+    a0 = a_dev[:nnz_max * BR]
+    outs = {}
+    for c_dtype in (torch.float32, torch.bfloat16):
+        ref = torch.zeros(L.Tp_max, d, dtype=c_dtype, device="cuda")
+        got = torch.zeros_like(ref)
+        again = torch.zeros_like(ref)
+        bsg.dsd(a0, L.topo, w_dev, d, ref, **kw)
+        bsg.dsd(a0, L.topo, w_dev, d, got, workspace=ws, **kw)
+        bsg.dsd(a0, L.topo, w_dev, d, again, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        outs[c_dtype] = (ref[:Tp].double().cpu().numpy(), got[:Tp].double().cpu().numpy())
+        assert torch.equal(got, again), "split DSD not deterministic"
+    report = {}
+    got32 = outs[torch.float32][1]
+    if name != "tail_of_many":
+        want = orc.dsd(blk_used[:nnz], bo, E, F, W, d, prec="f32", trans_b=True,
+                       block_rows=BR, **(dict(blocks2=blk_used[nnz:], b2=W3) if sw else {}))
+        check_float("split dsd fp32 rows", got32, want, "bf16", report)
+        want16 = orc.dsd(blk_used[:nnz], bo, E, F, W, d, trans_b=True, block_rows=BR,
+                         **(dict(blocks2=blk_used[nnz:], b2=W3) if sw else {}))
+        check_float("split dsd bf16 rows", outs[torch.bfloat16][1], want16, "bf16", report)
+    else:
+        # rows: 32 from the split tiles (the last 3 row pairs), 32 from the rest
+        split_rows = rng.choice(np.arange(Tp - 3 * 256 + 128, Tp), 32, replace=False)
+        other = rng.choice(np.arange(0, Tp - 3 * 256), 32, replace=False)
+        rows = np.sort(np.concatenate([split_rows, other]))
+        # row r of the product: the F blocks of its block row (block id rb * F + j
+        # in BCSR order, one expert) against W^T
+        Wt = W.T.astype(np.float64)
+        want = np.stack([np.concatenate([blk[((r // BR) * F + j) * BR + r % BR] for j in range(F)])
+                         .astype(np.float64) @ Wt for r in rows])
+        check_float("split dsd sampled rows", got32[rows], want, "bf16", report)
+    # the split changes only how the tail tiles' fp32 sums associate
+    ref32 = outs[torch.float32][0]
+    rel = np.max(np.abs(got32 - ref32)) / max(np.max(np.abs(ref32)), 1e-30)
+    assert rel <= 1e-5, f"split vs whole tiles (fp32): {rel}"
+    r16, g16 = outs[torch.bfloat16]
+    assert np.all(np.abs(g16 - r16) <= 2.0 ** -7 * np.maximum(1.0, np.abs(r16)))
+    report["split vs whole (fp32)"] = float(rel)
+    _say(f"[split] {name} ok; " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
+
+
 @pytest.mark.parametrize("name", list(GROUPS))
 def test_tile_groups_full(orc, name):
     """The whole layer at groups of 4 and 8 row pairs, every output element
