@@ -421,6 +421,28 @@ bsg_status bsg_route_permute_topology(const float* logits, int64_t T, int E, int
                       "route_permute_topology");
 }
 
+// Compute units of the stream's device, looked up once per device.
+static hipError_t device_cus(hipStream_t stream, int* ncu) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int cus[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
+            hipSuccess)
+            return e;
+        if (n <= 0) return hipErrorInvalidDevice;
+        cus[dev] = n;
+    }
+    *ncu = cus[dev];
+    return hipSuccess;
+}
+
 static bsg::GemmParams gemm_params(const bsg_topology* t) {
     bsg::GemmParams p{};
     p.row_ptr = t->row_ptr;
@@ -486,31 +508,12 @@ bsg_status bsg_sdd(const void* a, int64_t lda, const void* b, const void* b2, in
     p.lda = lda;
     p.ldb = ldb;
     p.K = K;
+    // the compute units size the split of a sparse last round
+    const hipError_t e = device_cus((hipStream_t)stream, &p.ncu);
+    if (e != hipSuccess) return hip_status(e, "sdd");
     return hip_status(bsg::launch_sdd(p, tiles_max(topo), trans_b,
                                       epilogue, dtype, (hipStream_t)stream),
                       "sdd");
-}
-
-// Compute units of the stream's device, looked up once per device.
-static hipError_t device_cus(hipStream_t stream, int* ncu) {
-    constexpr int kMaxDevices = 64;
-    static std::mutex mu;
-    static int cus[kMaxDevices] = {};
-    int dev = 0;
-    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cus[dev] == 0) {
-        int n = 0;
-        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) !=
-            hipSuccess)
-            return e;
-        if (n <= 0) return hipErrorInvalidDevice;
-        cus[dev] = n;
-    }
-    *ncu = cus[dev];
-    return hipSuccess;
 }
 
 bsg_status bsg_dsd_workspace_bytes(bsg_stream_t stream, int64_t* bytes) {

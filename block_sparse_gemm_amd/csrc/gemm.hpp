@@ -349,6 +349,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
         const int ent = P.row_tiles[tm];
         r0 = ent >> 8;
         nq = (ent & 3) + 1;
+        if constexpr (SDD) {
+            // a row tile of the SDD's split last round: half seg of it (its
+            // first QB block rows, or the rest)
+            if (nseg == 2) {
+                r0 += seg * QB;
+                nq = seg == 0 ? min(nq, QB) : nq - QB;
+            }
+        }
         m1 = nq > QB;
     }
     // row_ptr of each slot's block row (an absent slot: the last present one)
@@ -1055,15 +1063,29 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
     }
 }
 
+struct SplitPlan {
+    int full, tail, S;
+};
+
+// The SDD's last round, after at least one full round, when at most half the
+// CUs would run it: each of its t tiles runs as two half tiles (the row
+// tile's first 128 rows, then the rest), 2t workgroups of about two thirds
+// of a tile's time each.  The activation needs the whole K sum, so the SDD
+// splits along M, not K.
+__device__ __forceinline__ SplitPlan sdd_plan(int ntiles, int ncu) {
+    SplitPlan p{ntiles, 0, 1};
+    if (ncu <= 0 || ntiles < ncu) return p;
+    const int tail = ntiles % ncu;
+    if (tail == 0 || 2 * tail > ncu) return p;
+    return SplitPlan{ntiles - tail, tail, 2};
+}
+
 // Split of a DSD launch's last, partly filled round: with ntiles tiles on
 // ncu CUs, the tail (ntiles mod ncu tiles) is cut into S K-segments each, S =
 // min(ncu / tail, kMaxSplit, units / tail), so the last round runs tail x S
 // shares of 1/S of a tile instead of tail whole tiles on a nearly idle chip.
 // No split (full = ntiles) when S < 2 or no workspace.  Both launches of a
 // split product compute the same plan from the same device-side tile count.
-struct SplitPlan {
-    int full, tail, S;
-};
 __device__ __forceinline__ SplitPlan split_plan(int ntiles, int ncu, int units) {
     SplitPlan p{ntiles, 0, 1};
     if (ncu <= 0 || units <= 0) return p;
@@ -1101,6 +1123,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         SplitPlan pl{ntiles, 0, 1};
         if constexpr (MODE == kModeDsd || MODE == kModeDsd2) {
             if (P.ws) pl = split_plan(ntiles, P.ncu, P.ws_units);
+        } else if constexpr (MODE == kModeSdd) {
+            pl = sdd_plan(ntiles, P.ncu);
         }
         const int b = blockIdx.x;
         int tile, seg = 0, nseg = 1;
@@ -1112,9 +1136,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
             tile = pl.full + u / pl.S;
             seg = u % pl.S;
             nseg = pl.S;
-            part = P.ws + (int64_t)u * kSplitFloats;
+            if constexpr (MODE == kModeDsd || MODE == kModeDsd2) part = P.ws + (int64_t)u * kSplitFloats;
         } else {
             return;
+        }
+        if constexpr (MODE == kModeSdd) {
+            if (nseg == 2) {  // half seg of a split row tile (nothing when it has no second half)
+                int tm, tq;
+                row_tile_of(P.row_tiles, tile, tn, tm, tq);
+                if (seg == 1 && ((P.row_tiles[tm] & 3) + 1) <= kBlock / BR) return;
+                gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem, tile, seg, nseg, part);
+                return;
+            }
         }
         if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
             if (half_tile<MODE, BR>(P, tile, tn)) {
@@ -1227,7 +1260,8 @@ hipError_t launch_sdd_br(const GemmParams& p, int64_t row_tiles_max, int trans_b
                    ? launch<kBf16, kModeSddOne, false, kEpiSiluMul, kBf16, true, BR>(p, grid, s)
                    : launch<kF32, kModeSddOne, false, kEpiSiluMul, kF32, true, BR>(p, grid, s);
     }
-    const int64_t grid = row_tiles_max * ((p.F + 1) / 2);
+    // (+ ncu / 2: the second halves of a split last round)
+    const int64_t grid = row_tiles_max * ((p.F + 1) / 2) + p.ncu / 2;
     return dtype == kBf16 ? dispatch_sdd<kBf16, BR>(p, grid, trans_b, epi, s)
                           : dispatch_sdd<kF32, BR>(p, grid, trans_b, epi, s);
 }

@@ -591,6 +591,55 @@ def test_dsd_split_last_round(orc, name):
     _say(f"[split] {name} ok; " + ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
 
 
+@pytest.mark.parametrize("bin_rows", [128, 64])
+def test_sdd_split_last_round(orc, bin_rows):
+    """An SDD launch of 288 tiles on the 256 CUs of an MI355X: the last 32
+    (the last group: one full row tile, one holding a single block row, each
+    x 16 column pairs) run as two half tiles each, the second half of the
+    single-block-row tile as nothing.  Every element of A, G (forward with
+    GeLU' kept) and dH (backward) against the oracle."""
+    from block_sparse_gemm_amd import bsg, layer
+    cfg = _small("split_sdd", T=4408, d=256, E=2, f=4096, k=1, bin_rows=bin_rows)
+    counts = [2048, 2360]
+    BR = 64 if bin_rows == 64 else 128
+    _say(f"[sdd split] T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} bin_rows={bin_rows}")
+    lg = _picks_logits(cfg.T, cfg.E, cfg.k, counts, seed=47)
+    L = layer.Layer(layer.Shape.of(cfg))
+    bsg.route(torch.from_numpy(lg).cuda(), cfg.k, cfg.renorm, L.expert_idx, L.gate, L.dest_row,
+              L.counts, L.bin_offsets, L.route_ws, bin_rows=bin_rows)
+    bsg.build_topology(L.bin_offsets, cfg.E, cfg.f, L.Tp_max, L.topo)
+    torch.cuda.synchronize()
+    bo = orc.route(lg, cfg.k, cfg.renorm, bin_rows)["bin_offsets"]
+    assert np.array_equal(L.bin_offsets.cpu().numpy(), bo)
+    assert L.topo.meta[3].item() * (cfg.f // 256) == 288      # row tiles x column pairs
+    E, F, d = cfg.E, cfg.f // 128, cfg.d
+    nnz, nnz_max = int(bo[E]) // BR * F, L.topo.nnz_max
+    rng = np.random.default_rng(53)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    blocks_of = lambda t: t.view(nnz_max, BR, 128)[:nnz].float().cpu().double().numpy()
+    P = dict(block_rows=BR)
+    report = {}
+    xp = _bf16_draw(rng, (L.Tp_max, d), 1.0)
+    W1 = _bf16_draw(rng, (d, E * cfg.f), 0.05)
+    W2 = _bf16_draw(rng, (E * cfg.f, d), 0.05)
+    out = torch.zeros(nnz_max * BR, 128, dtype=torch.bfloat16, device="cuda")
+    aux = torch.zeros_like(out)
+    bsg.sdd(dev(xp), dev(W1), d, L.topo, "gelu", out, aux_out=aux)
+    A, Gp = orc.sdd(xp, W1, d, bo, E, F, "gelu", want_aux=True, **P)
+    torch.cuda.synchronize()
+    check_float("sdd A", blocks_of(out), A, "bf16", report)
+    check_float("sdd G", blocks_of(aux), Gp, "bf16", report)
+    dyp = _bf16_draw(rng, (L.Tp_max, d), 1.0)
+    saved = _bf16_draw(rng, (nnz_max * BR, 128), 1.0)
+    bsg.sdd(dev(dyp), dev(W2), d, L.topo, "gelu_bwd", out, trans_b=True, aux_in=dev(saved))
+    want = orc.sdd(dyp, W2, d, bo, E, F, "gelu_bwd", trans_b=True,
+                   aux_in=saved.reshape(nnz_max, BR, 128)[:nnz].reshape(-1), **P)
+    torch.cuda.synchronize()
+    check_float("sdd_bwd dH", blocks_of(out), want, "bf16", report)
+    _say(f"[sdd split] bin_rows={bin_rows} ok; max|d|/max|o|: " +
+         ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
+
+
 @pytest.mark.parametrize("name", list(GROUPS))
 def test_tile_groups_full(orc, name):
     """The whole layer at groups of 4 and 8 row pairs, every output element
