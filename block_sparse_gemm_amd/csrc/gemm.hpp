@@ -1132,11 +1132,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         if (b < pl.full) {
             tile = xcd_remap(b, pl.full);
         } else if (b < pl.full + pl.tail * pl.S) {
-            const int u = b - pl.full;
-            tile = pl.full + u / pl.S;
-            seg = u % pl.S;
+            // the split round: each XCD a contiguous range of (segment, tile)
+            // in segment-major order, so the shares it runs at once cover one
+            // K-segment of neighbouring tiles and share their operand panels
+            const int v = xcd_remap(b - pl.full, pl.tail * pl.S);
+            const int i = v % pl.tail;
+            seg = v / pl.tail;
+            tile = pl.full + i;
             nseg = pl.S;
-            if constexpr (MODE == kModeDsd || MODE == kModeDsd2) part = P.ws + (int64_t)u * kSplitFloats;
+            if constexpr (MODE == kModeDsd || MODE == kModeDsd2)
+                part = P.ws + ((int64_t)i * pl.S + seg) * kSplitFloats;
         } else {
             return;
         }
