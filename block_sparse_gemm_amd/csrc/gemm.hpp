@@ -1145,17 +1145,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
         } else {
             return;
         }
-        if constexpr (MODE == kModeSdd) {
-            if (nseg == 2) {  // half seg of a split row tile (nothing when it has no second half)
-                int tm, tq;
-                row_tile_of(P.row_tiles, tile, tn, tm, tq);
-                if (seg == 1 && ((P.row_tiles[tm] & 3) + 1) <= kBlock / BR) return;
-                gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem, tile, seg, nseg, part);
-                return;
-            }
-        }
         if constexpr (MODE == kModeSdd || MODE == kModeDsd || MODE == kModeDsd2) {
-            if (half_tile<MODE, BR>(P, tile, tn)) {
+            // one call site per body: a half tile, or half `seg` of a split SDD
+            // row tile (nothing when the row tile has no second half)
+            const bool half = half_tile<MODE, BR>(P, tile, tn);
+            bool run_half = half;
+            if constexpr (MODE == kModeSdd) {
+                if (nseg == 2) {
+                    if (seg == 1 && half) return;
+                    run_half = true;
+                }
+            }
+            if (run_half) {
                 gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, true, BR>(P, smem, tile, seg, nseg, part);
                 return;
             }

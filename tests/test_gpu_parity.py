@@ -636,6 +636,17 @@ def test_sdd_split_last_round(orc, bin_rows):
                    aux_in=saved.reshape(nnz_max, BR, 128)[:nnz].reshape(-1), **P)
     torch.cuda.synchronize()
     check_float("sdd_bwd dH", blocks_of(out), want, "bf16", report)
+    # the SwiGLU backward product on the same split: two saved planes in, two out
+    out2 = torch.zeros(2 * nnz_max * BR, 128, dtype=torch.bfloat16, device="cuda")
+    saved2 = _bf16_draw(rng, (2 * nnz_max * BR, 128), 1.0)
+    bsg.sdd(dev(dyp), dev(W2), d, L.topo, "silu_mul_bwd", out2, trans_b=True,
+            aux_in=dev(saved2))
+    want = orc.sdd(dyp, W2, d, bo, E, F, "silu_mul_bwd", trans_b=True,
+                   aux_in=saved2.reshape(2, nnz_max, BR, 128)[:, :nnz].reshape(-1), **P)
+    torch.cuda.synchronize()
+    got2 = out2.view(2, nnz_max, BR, 128)[:, :nnz].float().cpu().double().numpy()
+    check_float("sdd_bwd (SwiGLU) dHg, dHu", got2.reshape(2 * nnz, BR, 128), want, "bf16",
+                report)
     _say(f"[sdd split] bin_rows={bin_rows} ok; max|d|/max|o|: " +
          ", ".join(f"{k}={v:.2e}" for k, v in report.items()))
 
