@@ -1194,27 +1194,35 @@ __global__ __launch_bounds__(kGemmThreads) void dsd_reduce_kernel(GemmParams P) 
         const int hrow = half ? 64 * wm : 128 * wm + 64 * (mi >> 1);
         if (hrow / BR >= nq) continue;
         const int64_t row = (int64_t)BR * r0 + hrow + 32 * (mi & 1) + l32;
+        // the 4 x 4 accumulator vectors of row fragment mi, summed share by
+        // share (each share's 16 loads in flight together)
+        f32x4 v[4][4];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            f32x4 v[4];
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int sgm = 0; sgm < pl.S; ++sgm) {
-                const float* sp = src + (int64_t)sgm * kSplitFloats + (mi * 4 + ni) * 1024;
+            for (int q = 0; q < 4; ++q) v[ni][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sgm = 0; sgm < pl.S; ++sgm) {
+            const float* sp = src + (int64_t)sgm * kSplitFloats + mi * 4 * 1024;
+            f32x4 x[4][4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 x = *(const f32x4*)(sp + 4 * q);
+            for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[q][e] += x[e];
-                }
-            }
+                for (int q = 0; q < 4; ++q) x[ni][q] = *(const f32x4*)(sp + ni * 1024 + 4 * q);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[ni][q][e] += x[ni][q][e];
+        }
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t col = n0 + wn * 128 + 32 * ni + 8 * g + 4 * lh;
-                const float w[4] = {v[g][0], v[g][1], v[g][2], v[g][3]};
+                const float w[4] = {v[ni][g][0], v[ni][g][1], v[ni][g][2], v[ni][g][3]};
                 store4<OUT>((char*)P.out + (row * P.ldc + col) * OES, w);
             }
-        }
     }
 }
 
