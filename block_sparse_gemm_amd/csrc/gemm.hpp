@@ -284,6 +284,10 @@ struct KIdx {
 // rows: wave (wm, wn) takes rows 64 wm .. 64 wm + 63 x the 128 columns of N
 // half wn, as 2 x 4 accumulators, and the absent half's panel is not loaded
 // (6 direct loads per K-tile instead of 8).
+// tile: the SDD / DSD tile in group order (DSTD maps its own).  seg of nseg:
+// for a split DSD tile, the share of its K-blocks to sum, written to `part`
+// (fp32, no epilogue); for a split SDD row tile (nseg = 2, HALF), which half
+// of its block rows to run.  Unsplit: 0 of 1, part NULL.
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP, bool HALF, int BR>
 __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int tile, int seg,
                                           int nseg, float* part) {
