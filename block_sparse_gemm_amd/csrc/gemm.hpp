@@ -51,6 +51,14 @@
 // panels in that XCD's L2.  DSTD tiles, whose K is the expert's row count,
 // go expert by expert in descending size (longest first), in chunks dealt
 // to the XCDs in turn.
+//
+// Last round.  When the tiles do not fill whole rounds of the GPU's compute
+// units and the last round would leave most of them idle, an SDD runs that
+// round's tiles as two half tiles each (split along M: its activation needs
+// the whole K sum), and a DSD given a workspace cuts them into K-segments
+// whose fp32 partial sums a second launch adds in segment order
+// (dsd_reduce_kernel): the kernel boundary orders the shares before their
+// sum, so no workgroup waits on another.
 #pragma once
 
 #include "common.hpp"
