@@ -563,6 +563,14 @@ def test_dsd_split_last_round(orc, name):
         assert torch.equal(got, again), "split DSD not deterministic"
     report = {}
     got32 = outs[torch.float32][1]
+    if not sw:
+        # B as stored ([E*f, d], W2's layout) holding the same values: the same
+        # products in the same order, so the same bits
+        stored = torch.zeros(L.Tp_max, d, dtype=torch.float32, device="cuda")
+        bsg.dsd(a0, L.topo, dev(np.ascontiguousarray(W.T)), d, stored, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(stored[:Tp].double().cpu().numpy(), got32), \
+            "split DSD: B as stored differs from B transposed"
     if name != "tail_of_many":
         want = orc.dsd(blk_used[:nnz], bo, E, F, W, d, prec="f32", trans_b=True,
                        block_rows=BR, **(dict(blocks2=blk_used[nnz:], b2=W3) if sw else {}))
