@@ -867,26 +867,38 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
             for (int h = 0; h < NH; ++h) sc_g[h] = sc_a[h] >= 0 ? P.scat_gate[sc_a[h]] : 1.0f;
         }
     }
+    // Eight rows a batch: every shuffle and LDS read of the batch is issued
+    // before the first store, so their latencies overlap instead of adding up
+    // row by row (the stores sit under a per-row mask: pad rows go nowhere).
     auto scatter_flush = [&](const lds_t* sub, int h) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int chunk = lane & 15;
         const int64_t col = n0 + wn * 128 + chunk * 8;
-#pragma unroll 4
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = 4 * rr + (lane >> 4);
-            const int a = __shfl(sc_a[h], row, kWave);
-            const float g = __shfl(sc_g[h], row, kWave);
-            const u32x4 u = *(const __attribute__((address_space(3))) u32x4*)(
-                sub + row * 256 + ((chunk ^ (row & 15)) << 4));
-            if (a >= 0) {
-                u32x4 o = u;
+#pragma unroll
+        for (int r8 = 0; r8 < 16; r8 += 8) {
+            int a[8];
+            float g[8];
+            u32x4 u[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 4 * (r8 + i) + (lane >> 4);
+                a[i] = __shfl(sc_a[h], row, kWave);
+                g[i] = __shfl(sc_g[h], row, kWave);
+                u[i] = *(const __attribute__((address_space(3))) u32x4*)(
+                    sub + row * 256 + ((chunk ^ (row & 15)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                u32x4 o = u[i];
                 if (P.scat_gate) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = pack_bf16x2(g * __uint_as_float(u[i] << 16),
-                                           g * __uint_as_float(u[i] & 0xffff0000u));
+                    for (int j = 0; j < 4; ++j)
+                        o[j] = pack_bf16x2(g[i] * __uint_as_float(u[i][j] << 16),
+                                           g[i] * __uint_as_float(u[i][j] & 0xffff0000u));
                 }
-                __builtin_nontemporal_store(o, (u32x4*)((char*)P.scat_out + ((int64_t)a * P.scat_ld + col) * 2));
+                if (a[i] >= 0)
+                    __builtin_nontemporal_store(
+                        o, (u32x4*)((char*)P.scat_out + ((int64_t)a[i] * P.scat_ld + col) * 2));
             }
         }
     };
@@ -1066,6 +1078,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
                     stage_flush(region + 16384, hbase(h) + P.plane * OES, orow);
                 }
             } else if constexpr (EPI == kEpiScatter) {
+                // take the rows' assignments and gates (loaded at the start of
+                // the epilogue, long landed) before the first store: a wait for
+                // them later would also wait for every store issued since
+                if (h == 0) {
+#pragma unroll
+                    for (int hh = 0; hh < NH; ++hh) asm volatile("" ::"v"(sc_a[hh]), "v"(sc_g[hh]));
+                }
                 if (P.out && hpresent(h)) stage_flush(region, hbase(h), orow);
                 scatter_flush(region, h);
             } else {
