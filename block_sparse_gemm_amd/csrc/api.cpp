@@ -447,9 +447,7 @@ static bsg::GemmParams gemm_params(const bsg_topology* t) {
     bsg::GemmParams p{};
     p.row_ptr = t->row_ptr;
     p.col_idx = t->col_idx;
-    p.row_idx = t->row_idx;
     p.col_ptr = t->col_ptr;
-    p.trans_idx = t->trans_idx;
     p.row_tiles = t->row_tiles;
     p.expert_order = t->expert_order;
     p.meta = t->meta;

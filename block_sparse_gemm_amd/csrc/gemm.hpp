@@ -21,13 +21,21 @@
 //         their nonzero blocks; K = d.  Dual-B (SwiGLU): one block of W1 and
 //         the same block of W3 side by side, combined as silu(g) * u.
 //   DSD   a pair of block rows x 256 output columns; K walks the rows'
-//         blocks through row_ptr, their weight rows through col_idx.  The
-//         two-set form (SwiGLU input gradient) walks them twice: the gate
-//         projection's blocks against W1, then the up projection's against
-//         W3, into one accumulator.
+//         blocks (from row_ptr) and their weight rows.  The two-set form
+//         (SwiGLU input gradient) walks them twice: the gate projection's
+//         blocks against W1, then the up projection's against W3, into one
+//         accumulator.
 //   DSTD  a pair of block columns x 256 output columns; K walks the
-//         columns' blocks through col_ptr / trans_idx, and their dense rows
-//         through row_idx.
+//         columns' blocks (the expert's block rows, from col_ptr) and their
+//         dense rows.
+// The topology is the block-diagonal one of section 1.3 (each block row
+// holds exactly its expert's F column blocks, in order), so the K-block
+// indices the transpose and row indices list are closed forms: block row r's
+// p-th block is row_ptr[r] + p = r F + p, in column e F + p; block column
+// e F + j holds block rows s_e .. s_e + R_e - 1, its p-th block being
+// (s_e + p) F + j, where col_ptr[e F + j] = F s_e + j R_e.  The kernels
+// compute them instead of reading the lists, so a tile starts after two
+// dependent loads (its row_ptr or col_ptr entries) rather than four.
 //
 // Pipeline.  Operand panels go from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging) through a ring of kStages
@@ -79,7 +87,6 @@ constexpr int kSplitFloats = kSplitShareBytes / 4;
 constexpr int kMaxSplit = 8;
 constexpr int kSegsPerWave = kSegs / 4;          // per panel
 constexpr int kLoadsPerTile = 4 * kSegsPerWave;  // per wave and K-tile
-constexpr int kIdxCap = 2048;                    // K-blocks of one tile staged in LDS at a time
 
 // Tile order (see xcd_chunked): consecutive DSTD tiles kept on one XCD.
 constexpr int kDstdChunk = 8;
@@ -275,12 +282,6 @@ __device__ __forceinline__ void row_tile_of(const int32_t* __restrict__ row_tile
     tm = first + local % size;
 }
 
-// Indices of one K-block for both M halves.
-struct KIdx {
-    int b0, b1;  // block of M half 0 / 1
-    int row;     // DSD: weight row block (column of the block); DSTD: dense row block
-};
-
 // MODE: kModeSdd, kModeSddOne (dual-B SwiGLU: one block per tile),
 // kModeDsd, kModeDsd2 (two block sets), kModeDstd.  BK: B operand
 // K-contiguous.
@@ -400,39 +401,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
 
     // ---- K extent in K-blocks (DSD / DSTD); the two-set DSD walks the row's
     // blocks twice, first in set one, then in set two
-    int nblk = 0, cp0 = 0, cp1 = 0, rowlen = 0;
+    // and what the K-block indices are computed from: DSD, the row's first
+    // weight row block c0 (its expert's first column, e F); DSTD, the
+    // expert's first block row s_e and the two columns' places j0, j1 in it
+    int nblk = 0, rowlen = 0, c0 = 0, se = 0, j0 = 0, j1 = 0;
     if constexpr (DSD) {
         rowlen = P.row_ptr[r0 + 1] - rp0;
         nblk = MODE == kModeDsd2 ? 2 * rowlen : rowlen;
+        if (rowlen > 0) c0 = P.col_idx[rp0];
     } else if constexpr (MODE == kModeDstd) {
-        cp0 = P.col_ptr[mrow0];
-        cp1 = P.col_ptr[mrow1];
-        nblk = P.col_ptr[mrow0 + 1] - cp0;
+        const int cp0 = P.col_ptr[mrow0];
+        nblk = P.col_ptr[mrow0 + 1] - cp0;  // R_e
+        const int e = mrow0 / F;
+        j0 = mrow0 - e * F;
+        j1 = mrow1 - e * F;
+        se = (cp0 - j0 * nblk) / F;  // col_ptr[e F + j] = F s_e + j R_e
     }
-    auto fetch = [&](int p) -> KIdx {
-        KIdx r{0, 0, 0};
-        if constexpr (DSD) {
-            int set = 0;
-            if (MODE == kModeDsd2 && p >= rowlen) {
-                p -= rowlen;
-                set = kSecondSet;
-            }
-            r.b0 = rp0 + p;  // slot 0's block; the other slots' are at their row_ptr deltas
-            r.row = P.col_idx[r.b0] | set;
-        } else if constexpr (MODE == kModeDstd) {
-            r.b0 = P.trans_idx[cp0 + p];
-            r.b1 = P.trans_idx[cp1 + p];
-            r.row = P.row_idx[r.b0];
-        }
-        return r;
-    };
-
-    // ---- K-block indices of the current chunk of the tile's K-blocks,
-    // staged in LDS (DSD / DSTD): block of each M half and its dense row
-    // block, read in order per K-tile
-    int* ib0 = (int*)(smem + kLdsBytes);
-    int* ib1 = ib0 + kIdxCap;
-    int* irow = ib1 + kIdxCap;
 
     // ---- per-lane load offsets (constant over K)
     const int64_t lda_b = (SDD ? P.lda : kBlock) * ES;  // A row (or k-row) stride
@@ -455,22 +439,30 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
     struct Bases {
         const char *a0, *a1, *b0, *b1;
     };
-    // the K-block indices of K-tile t (DSD / DSTD), read from LDS ahead of use
+    // the K-block indices of K-tile t (DSD / DSTD; K-blocks from kb0 on): the
+    // block of each M half and its dense row block (DSD: weight row block,
+    // kSecondSet marking the second set of the two-set form)
     struct TIdx {
         int b0, b1, row;
     };
+    int kb0 = 0;
     auto tidx = [&](int t) -> TIdx {
         TIdx r{0, 0, 0};
         if constexpr (DSD) {
-            const int p = t / KPB;
-            r.b0 = ib0[p] + dA[0];
-            r.b1 = ib0[p] + dA[1];
-            r.row = irow[p];
+            int p = kb0 + t / KPB;
+            int set = 0;
+            if (MODE == kModeDsd2 && p >= rowlen) {
+                p -= rowlen;
+                set = kSecondSet;
+            }
+            r.b0 = rp0 + p + dA[0];
+            r.b1 = rp0 + p + dA[1];
+            r.row = (c0 + p) | set;
         } else if constexpr (MODE == kModeDstd) {
-            const int p = t / KPB;
-            r.b0 = ib0[p];
-            r.b1 = ib1[p];
-            r.row = irow[p];
+            const int p = kb0 + t / KPB;
+            r.b0 = (se + p) * F + j0;
+            r.b1 = (se + p) * F + j1;
+            r.row = se + p;
         }
         return r;
     };
@@ -730,22 +722,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
     if constexpr (SDD) {
         run(P.K / KT);
     } else {
-        // the tile's K-blocks (segment seg of nseg: a split tile's share) in
-        // chunks of kIdxCap, their indices staged per chunk
-        const int kb0 = (int)((int64_t)seg * nblk / nseg);
+        // the tile's K-blocks (segment seg of nseg: a split tile's share)
+        kb0 = (int)((int64_t)seg * nblk / nseg);
         const int kb1 = (int)((int64_t)(seg + 1) * nblk / nseg);
-        for (int c0 = kb0; c0 < kb1; c0 += kIdxCap) {
-            const int nb = min(kIdxCap, kb1 - c0);
-            if (c0 > kb0) __syncthreads();  // every wave is done with the previous chunk
-            for (int p = threadIdx.x; p < nb; p += kGemmThreads) {
-                const KIdx r = fetch(c0 + p);
-                ib0[p] = r.b0;
-                ib1[p] = r.b1;
-                irow[p] = r.row;
-            }
-            __syncthreads();
-            run(nb * KPB);
-        }
+        run((kb1 - kb0) * KPB);
     }
 
     // ---- a split tile's share (DSD): its fp32 partial sums go to `part` in
@@ -1138,12 +1118,11 @@ __device__ __forceinline__ bool half_tile(const GemmParams& P, int tile, int tn)
 
 template <int DT, int MODE, bool BK, int EPI, int OUT, bool SWAP, int BR>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmParams P) {
-    // the operand ring, then (DSD / DSTD) the staged K-block indices
-    constexpr bool kIdx = MODE != kModeSdd && MODE != kModeSddOne;
+    // the operand ring
     // (GeLU backward, bf16) four 8 KB buffers of the saved derivative
     constexpr bool kGbuf = EPI == kEpiGeluBwd && OUT == kBf16;
     __shared__ __attribute__((aligned(1024))) char
-        smem[kLdsBytes + (kIdx ? 3 * kIdxCap * 4 : 0) + (kGbuf ? 4 * 8192 : 0)];
+        smem[kLdsBytes + (kGbuf ? 4 * 8192 : 0)];
     if constexpr (MODE == kModeDstd) {
         gemm_tile<DT, MODE, BK, EPI, OUT, SWAP, false, BR>(P, smem, 0, 0, 1, nullptr);
     } else {

@@ -57,11 +57,11 @@ struct GemmParams {
     void* scat_out;
     int64_t scat_ld;
     int64_t lda, ldb, ldc;
+    // the topology (its row and transpose index lists are closed forms of
+    // row_ptr and col_ptr, which the kernels compute instead of reading)
     const int32_t* row_ptr;
     const int32_t* col_idx;
-    const int32_t* row_idx;
     const int32_t* col_ptr;
-    const int32_t* trans_idx;
     const int32_t* row_tiles;  // tiles of up to 256 rows of one expert (block rows sharing a
                                // column list)
     const int32_t* expert_order;  // experts by descending row count
