@@ -445,7 +445,6 @@ static hipError_t device_cus(hipStream_t stream, int* ncu) {
 
 static bsg::GemmParams gemm_params(const bsg_topology* t) {
     bsg::GemmParams p{};
-    p.row_ptr = t->row_ptr;
     p.col_idx = t->col_idx;
     p.col_ptr = t->col_ptr;
     p.row_tiles = t->row_tiles;

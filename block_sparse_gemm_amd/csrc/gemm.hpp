@@ -34,8 +34,10 @@
 // p-th block is row_ptr[r] + p = r F + p, in column e F + p; block column
 // e F + j holds block rows s_e .. s_e + R_e - 1, its p-th block being
 // (s_e + p) F + j, where col_ptr[e F + j] = F s_e + j R_e.  The kernels
-// compute them instead of reading the lists, so a tile starts after two
-// dependent loads (its row_ptr or col_ptr entries) rather than four.
+// compute them instead of reading the lists (row_ptr[r] = r F too), so an
+// SDD or DSD tile reads one index entry (its rows' first column block) after
+// its row_tiles entry, and a DSTD tile its two col_ptr entries after its
+// expert_order entry, before the first operand loads.
 //
 // Pipeline.  Operand panels go from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging) through a ring of kStages
@@ -372,11 +374,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
         }
         m1 = nq > QB;
     }
-    // row_ptr of each slot's block row (an absent slot: the last present one)
+    // first block of each slot's block row (an absent slot: the last present
+    // one): every block row holds its expert's F blocks, so row_ptr[r] = r F
     int rps[2 * QB];
     if constexpr (SDD || DSD) {
 #pragma unroll
-        for (int i = 0; i < 2 * QB; ++i) rps[i] = P.row_ptr[r0 + min(i, nq - 1)];
+        for (int i = 0; i < 2 * QB; ++i) rps[i] = (r0 + min(i, nq - 1)) * F;
     }
     // the slot of the A rows this wave loads into panel p (each wave loads
     // 32 consecutive rows of a panel, so they lie in one slot)
@@ -385,14 +388,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
     bool n1;
     int bcol0 = 0, bcol1 = 0;  // SDD: column blocks of B
     const int rp0 = (SDD || DSD) ? rps[0] : 0;  // the slots share this column list
+    // the rows' first column block, e F (the tile's one index load): their
+    // p-th block lies in column block e F + p
+    const int cb0 = (SDD || DSD) ? P.col_idx[rp0] : 0;
     if constexpr (MODE == kModeSdd) {
-        const int nr = P.row_ptr[r0 + 1] - rp0;
-        n1 = 2 * tq + 1 < nr;
-        bcol0 = P.col_idx[rp0 + 2 * tq];
-        bcol1 = n1 ? P.col_idx[rp0 + 2 * tq + 1] : bcol0;
+        n1 = 2 * tq + 1 < F;
+        bcol0 = cb0 + 2 * tq;
+        bcol1 = n1 ? bcol0 + 1 : bcol0;
     } else if constexpr (MODE == kModeSddOne) {
         n1 = DUAL;
-        bcol0 = bcol1 = P.col_idx[rp0 + tq];
+        bcol0 = bcol1 = cb0 + tq;
     } else {
         n1 = tq * 256 + 128 < P.N;
     }
@@ -406,9 +411,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
     // expert's first block row s_e and the two columns' places j0, j1 in it
     int nblk = 0, rowlen = 0, c0 = 0, se = 0, j0 = 0, j1 = 0;
     if constexpr (DSD) {
-        rowlen = P.row_ptr[r0 + 1] - rp0;
+        rowlen = F;
         nblk = MODE == kModeDsd2 ? 2 * rowlen : rowlen;
-        if (rowlen > 0) c0 = P.col_idx[rp0];
+        c0 = cb0;
     } else if constexpr (MODE == kModeDstd) {
         const int cp0 = P.col_ptr[mrow0];
         nblk = P.col_ptr[mrow0 + 1] - cp0;  // R_e

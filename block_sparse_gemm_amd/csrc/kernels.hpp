@@ -57,9 +57,8 @@ struct GemmParams {
     void* scat_out;
     int64_t scat_ld;
     int64_t lda, ldb, ldc;
-    // the topology (its row and transpose index lists are closed forms of
-    // row_ptr and col_ptr, which the kernels compute instead of reading)
-    const int32_t* row_ptr;
+    // the topology (its block pointer, row and transpose index lists are
+    // closed forms of col_idx and col_ptr, which the kernels compute)
     const int32_t* col_idx;
     const int32_t* col_ptr;
     const int32_t* row_tiles;  // tiles of up to 256 rows of one expert (block rows sharing a

@@ -120,11 +120,11 @@ typedef struct {
  *                        empty (nnz = R = 0, all pointers 0) and every
  *                        product writes nothing, or zeros for dstd
  * E, F, block_rows and Tp_max are host values describing the capacity.
- * The products read row_ptr, col_idx, col_ptr, row_tiles, expert_order and
- * meta; the entries of row_idx and trans_idx are closed forms of row_ptr and
- * col_ptr on this block-diagonal structure, which the products compute, so
- * a topology handed to them must have that structure (any bsg_build_topology
- * output has).
+ * The products read col_idx, col_ptr, row_tiles, expert_order and meta;
+ * the entries of row_ptr (r F), row_idx and trans_idx are closed forms on
+ * this block-diagonal structure, which the products compute, so a topology
+ * handed to them must have that structure (any bsg_build_topology output
+ * has).
  * Sparse operands ("blocks") are stored block-major, [nnz_max][BR][128],
  * each block row-major, in BCSR order.  A two-plane block array is
  * [2][nnz_max][BR][128] with nnz_max = (Tp_max / BR) * F: plane 1 starts
