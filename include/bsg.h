@@ -407,8 +407,8 @@ bsg_status bsg_dsd_combine_top1(const void* blocks, const bsg_topology* topo, co
 
 /*
  * dstd - dense = sparse^T x dense, the weight gradient (section 1.3,
- * "transpose indices": the blocks of each column are visited through
- * trans_idx, their rows found through row_idx):
+ * "transpose indices": the blocks of each column are those trans_idx lists,
+ * their rows those row_idx gives; the kernel computes both from col_ptr):
  *   C[128c + m][n] = sum over blocks b of column c, sum_j blocks[b][j][m] *
  *                    dmat[BR*row_idx[b] + j][n],  n < N
  * dmat is [Tp_max, N] with leading dimension ldd.  trans_c = 0 stores
