@@ -80,8 +80,8 @@ class Layer:
         # stream.  Set it to choose the schedule.
         self.overlap = s.backward and 2.0 * s.T * s.k * s.d * s.f <= 4e11
         # top-1 bf16 layers: the combine runs in the DSD's epilogue (forward:
-        # Yp and y; backward with GeLU experts: dx straight from the product,
-        # no dXp)
+        # y, and Yp when a backward follows; backward with GeLU experts: dx
+        # straight from the product, no dXp)
         self.fuse_top1 = s.k == 1 and s.dtype == "bf16" and s.yp_tdtype == torch.bfloat16
         dev = torch.device(device)
         # plain DSDs whose tiles walk at least 32 K-blocks (f >= 4096, or the
@@ -156,8 +156,10 @@ class Layer:
         else:
             c("sdd", bsg.sdd, self.xp, W1, s.d, t, "gelu", self.act, aux_out=self.gp)
         if self.fuse_top1:
-            c("dsd", bsg.dsd_combine_top1, self.act, t, W2, s.d, self.yp, self.row_src,
-              self.gate, self.y)
+            # Yp is kept only for the gate gradient: a forward-only layer
+            # writes y alone
+            c("dsd", bsg.dsd_combine_top1, self.act, t, W2, s.d, self.yp if s.backward else None,
+              self.row_src, self.gate, self.y)
             return self.y
         c("dsd", bsg.dsd, self.act, t, W2, s.d, self.yp, workspace=self.dsd_ws)
         c("unpermute_combine", bsg.unpermute_combine, self.yp, self.dest_row, self.gate, s.T,

@@ -179,14 +179,19 @@ def check_case(orc, case: Case, seed=0):
     elif cfg.backward:
         check_float("G", f64(L.sparse_rows(L.gp, rows)), G, prec, report)
     # the bar follows the workload's arithmetic (bf16 operands, fp32
-    # accumulation) even where Yp is stored in fp32
-    check_float("Yp", f64(L.yp[rows.long()]), Yp, prec, report)
+    # accumulation) even where Yp is stored in fp32.  A forward-only top-1
+    # layer writes y alone (its DSD's rows reach y through the combine, so
+    # y carries them)
+    yp_written = cfg.backward or not L.fuse_top1
+    if yp_written:
+        check_float("Yp", f64(L.yp[rows.long()]), Yp, prec, report)
     check_float("y", f64(L.y[torch.from_numpy(toks).cuda()]), O.forward_tokens(toks), prec,
                 report)
     # pad rows of A and Yp are exactly zero
     pad = torch.from_numpy(np.nonzero(r["row_src"] < 0)[0]).cuda()
     if len(pad):
-        assert torch.count_nonzero(L.yp[pad.long()]).item() == 0, "Yp pad rows"
+        if yp_written:
+            assert torch.count_nonzero(L.yp[pad.long()]).item() == 0, "Yp pad rows"
         assert torch.count_nonzero(L.sparse_rows(L.act, pad)).item() == 0, "A pad rows"
 
     # ---- backward floats
@@ -910,8 +915,8 @@ def test_top1_fused_combine_is_bit_identical(bwd):
         torch.cuda.synchronize()
         outs.append((L.y.clone(), L.yp.clone(), L.dx.clone() if bwd else None))
     assert torch.equal(outs[0][0], outs[1][0])
-    assert torch.equal(outs[0][1], outs[1][1])
-    if bwd:
+    if bwd:  # a forward-only top-1 layer writes no Yp
+        assert torch.equal(outs[0][1], outs[1][1])
         assert torch.equal(outs[0][2], outs[1][2])
 
 
