@@ -334,11 +334,11 @@ def _edge_cases():
     cfg = _small("ties", T=256, d=128, E=8, f=128, k=2)
     lg = np.random.default_rng(4).integers(-2, 3, size=(256, 8)).astype(np.float32)
     cases["ties"] = Case(cfg, logits=lg)
-    # more K-blocks per product tile than the kernel stages at once (2048):
-    # a block row of 2050 blocks (DSD walks it in two chunks) ...
+    # long K walks with closed-form K-block indices: a block row of 2050
+    # blocks (the DSD's K) ...
     cfg = _small("long_block_rows", T=200, d=128, E=1, f=128 * 2050, k=1)
     cases["long_block_rows"] = Case(cfg, n_tokens=16, n_wgrad=16)
-    # ... and a block column of 2050 blocks (DSTD walks it in two chunks)
+    # ... and a block column of 2050 blocks (the DSTD's K)
     cfg = _small("long_block_cols", T=128 * 2049 + 5, d=128, E=1, f=128, k=1)
     cases["long_block_cols"] = Case(cfg, n_tokens=16, n_wgrad=16)
     return cases
