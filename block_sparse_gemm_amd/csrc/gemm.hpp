@@ -404,16 +404,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
     const int64_t n0 = (int64_t)tq * 256;
     const int64_t n1off = n1 ? 128 : 0;  // an absent N half mirrors half 0
 
-    // ---- K extent in K-blocks (DSD / DSTD); the two-set DSD walks the row's
-    // blocks twice, first in set one, then in set two
-    // and what the K-block indices are computed from: DSD, the row's first
-    // weight row block c0 (its expert's first column, e F); DSTD, the
-    // expert's first block row s_e and the two columns' places j0, j1 in it
-    int nblk = 0, rowlen = 0, c0 = 0, se = 0, j0 = 0, j1 = 0;
+    // ---- K extent in K-blocks (DSD / DSTD; the two-set DSD walks the row's
+    // blocks twice, first in set one, then in set two), and what a DSTD
+    // tile's K-block indices follow from: its expert's first block row s_e
+    // and the two columns' places j0, j1 in the expert (a DSD tile's follow
+    // from rp0 and cb0)
+    int nblk = 0, rowlen = 0, se = 0, j0 = 0, j1 = 0;
     if constexpr (DSD) {
         rowlen = F;
         nblk = MODE == kModeDsd2 ? 2 * rowlen : rowlen;
-        c0 = cb0;
     } else if constexpr (MODE == kModeDstd) {
         const int cp0 = P.col_ptr[mrow0];
         nblk = P.col_ptr[mrow0 + 1] - cp0;  // R_e
@@ -462,7 +461,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, char* smem, int t
             }
             r.b0 = rp0 + p + dA[0];
             r.b1 = rp0 + p + dA[1];
-            r.row = (c0 + p) | set;
+            r.row = (cb0 + p) | set;
         } else if constexpr (MODE == kModeDstd) {
             const int p = kb0 + t / KPB;
             r.b0 = (se + p) * F + j0;
